@@ -1,0 +1,187 @@
+/* tk.h -- C ABI of libtk: one persistent, grid-resident HIP kernel per
+ * functional training step on MI355X (gfx950).
+ *
+ * The operations mirror the execution boundary of the trainkernel pages
+ * (trainkernel runtime.py: `compile_program`, `CompiledProgram.allocate`,
+ * `run_into`, `__call__`, `resource_usage`, `ExecutionBuffers`) and the
+ * generator's statistics (codegen.py: `GeneratedKernel`).
+ *
+ * Conventions for every entry point:
+ *   - Return a tk_status; on anything but TK_OK, tk_last_error() holds a
+ *     message ("tk: ...") for the calling thread.  Nothing is launched and no
+ *     caller memory is written when a check fails.
+ *   - Tensors are caller-owned views (tk_tensor); libtk never frees them.
+ *     Sizes and strides are in elements.  Device pointers must be memory of
+ *     the program's device.
+ *   - Programs are immutable after tk_compile and may be used from several
+ *     threads and streams at once given distinct output and workspace
+ *     buffers (the pages: "Calls allocate independent buffers for stream
+ *     safety").
+ */
+#ifndef TK_H
+#define TK_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { TK_F32 = 0, TK_F16 = 1, TK_BF16 = 2, TK_I8 = 3 } tk_dtype;
+
+typedef enum {
+  TK_OK = 0,
+  TK_E_ARG = 1,          /* null pointer, bad option value, malformed call */
+  TK_E_PARSE = 2,        /* program text does not parse */
+  TK_E_UNSUPPORTED = 3,  /* op, dtype, layout or size outside the supported subset */
+  TK_E_SHAPE = 4,        /* shape mismatch (program or buffer) */
+  TK_E_STRIDE = 5,       /* stride / contiguity mismatch */
+  TK_E_DTYPE = 6,        /* dtype mismatch */
+  TK_E_DEVICE = 7,       /* wrong device, not gfx950, or no device for a run */
+  TK_E_ALIAS = 8,        /* buffers overlap where they must not */
+  TK_E_WORKSPACE = 9,    /* workspace too small, misaligned, or on the wrong device */
+  TK_E_COUNT = 10,       /* wrong number of inputs / outputs */
+  TK_E_HIP = 11,         /* a HIP runtime call failed (message has the HIP error) */
+  TK_E_ABORTED = 12      /* a launch stopped at a timed-out grid barrier */
+} tk_status;
+
+/* A caller-owned tensor view.  `storage_base`/`storage_bytes` give the whole
+ * allocation the view lives in (used for the aliasing rules, like storage
+ * identity in the pages' `run_into`); when storage_base is NULL the view's own
+ * extent is used. */
+typedef struct {
+  void* data;
+  int32_t dtype;          /* tk_dtype */
+  int32_t ndim;           /* 0..8 */
+  int64_t shape[8];
+  int64_t strides[8];     /* elements */
+  const void* storage_base;
+  uint64_t storage_bytes;
+  int32_t device;
+  int32_t requires_grad;  /* nonzero: rejected as an in-place target */
+} tk_tensor;
+
+/* Compile options (the pages' `generate` keywords, codegen.py).  Zero-filled
+ * means defaults; tk_default_options fills the documented defaults. */
+typedef struct {
+  int32_t blocks_per_cu;       /* 1..8, default 1 (pages: blocks_per_sm) */
+  int32_t max_blocks;          /* 0 = no cap */
+  int32_t fuse_pointwise;      /* default 1: inline single-use pointwise values */
+  int32_t fuse_epilogues;      /* default 1: fuse pointwise chains into GEMM tiles */
+  int32_t inline_input_casts;  /* default 1 */
+  int32_t split_k_gemv;        /* default 1: one-row products use the split-K GEMV */
+  int32_t threads_per_block;   /* must be 256 (4 wave64) or 0 */
+  int32_t fuse_updates;        /* default 1: fold an in-place SGD update into its
+                                  weight-gradient GEMM tile when proven safe */
+  int32_t barrier_every_op;    /* debug: one op per stage */
+  int32_t num_cus;             /* plan-only compiles: CU count to plan for (0: 256) */
+  int32_t gemm_split_k;        /* 0: automatic; else force split-K parts for MFMA GEMMs */
+  int32_t reserved[5];
+} tk_options;
+
+/* Plan and kernel statistics (pages: `GeneratedKernel` and `resource_usage`). */
+typedef struct {
+  uint64_t workspace_bytes;      /* bytes the workspace must hold (header + arena) */
+  int32_t n_stages;
+  int32_t grid_barriers;         /* n_stages - 1 */
+  int32_t materialized_ops;
+  int32_t inlined_ops;
+  int32_t fused_epilogues;       /* GEMM/GEMV tiles carrying a pointwise chain */
+  int32_t side_epilogues;
+  int32_t fused_updates;
+  int32_t matrix_core_ops;       /* contractions on MFMA */
+  int32_t direct_outputs;        /* values written straight into caller outputs */
+  int32_t direct_state_commits;  /* in-place outputs written straight into inputs */
+  int32_t staged_commits;
+  int32_t grid_size;             /* workgroups per launch */
+  int32_t max_work_items;
+  int32_t num_cus;
+  int32_t blocks_per_cu;         /* resident workgroups per CU used */
+  int32_t occupancy;             /* max resident workgroups per CU (0 in plan-only mode) */
+  int32_t vgprs, sgprs, lds_bytes, scratch_bytes;
+  int32_t n_tasks;
+  int32_t reserved[5];
+} tk_stats;
+
+typedef struct tk_program tk_program;
+
+/* Allocator callback for tk_allocate: returns `bytes` of device memory on
+ * `device` owned by the caller (NULL on failure).  `bytes` may be 0. */
+typedef void* (*tk_alloc_fn)(void* ctx, uint64_t bytes, int32_t device);
+
+void tk_default_options(tk_options* opts);
+
+/* Parse and validate a `tkir 1` program, schedule it and upload its plan.
+ * device >= 0: that device must be gfx950; its CU count and the kernel's
+ * occupancy size the grid.  device == -1: plan only (no HIP calls at all); the
+ * program can be queried, dumped and validated against, but not run.
+ * Rejections follow the pages' generator and compile_program: non-finite
+ * scalars, unsupported ops/dtypes, bad shapes/strides/broadcasts, invalid
+ * in-place maps, option ranges. */
+tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int32_t device, tk_program** out);
+
+tk_status tk_query(const tk_program* prog, tk_stats* out);
+
+/* Write a human-readable schedule (stages, tasks, arena) into buf (always
+ * NUL-terminated when len > 0).  *needed receives the full length + 1. */
+tk_status tk_dump_plan(const tk_program* prog, char* buf, size_t len, size_t* needed);
+
+/* Fill `outputs` (n_out descriptors) and `workspace` for a run on `inputs`
+ * (pages: `allocate`).  In-place output slots receive their input's own
+ * descriptor; other outputs and the workspace come from `alloc` (contiguous,
+ * the program's output dtype/shape).  The workspace header is initialised on
+ * `stream` (synchronously before return). */
+tk_status tk_allocate(const tk_program* prog, const tk_tensor* inputs, size_t n_in, tk_alloc_fn alloc, void* ctx,
+                      tk_tensor* outputs, size_t n_out, tk_tensor* workspace, void* stream);
+
+/* Run every check of tk_run_into without touching the GPU (pages:
+ * `_validate_inputs` and the buffer checks of `run_into`): counts; each input's
+ * device, dtype, shape and exact strides; each output's device, dtype, shape
+ * and contiguity; workspace device, size (>= workspace_bytes), 256-byte
+ * alignment; in-place slots bound to their declared input with identical
+ * strides; in-place targets not aliased by another input and not
+ * requires_grad; outputs and workspace pairwise disjoint and disjoint from all
+ * inputs except declared in-place targets. */
+tk_status tk_validate_into(const tk_program* prog, const tk_tensor* inputs, size_t n_in, const tk_tensor* outputs,
+                           size_t n_out, const tk_tensor* workspace);
+
+/* Validate, then launch the step on `stream` (a hipStream_t, NULL = default
+ * stream) and return without waiting (pages: `run_into`).  One cooperative
+ * launch; every stage ends in a global-memory grid barrier.  The workspace
+ * header must have been initialised once (tk_allocate or tk_workspace_init);
+ * it stays valid across launches.  Reuse of outputs/workspace must be ordered
+ * by the caller; calls overlapping on one workspace race. */
+tk_status tk_run_into(const tk_program* prog, const tk_tensor* inputs, size_t n_in, const tk_tensor* outputs,
+                      size_t n_out, const tk_tensor* workspace, void* stream);
+
+/* Zero the workspace header (barrier state, abort flag) on `stream` with a
+ * small kernel (safe under graph capture). */
+tk_status tk_workspace_init(const tk_program* prog, const tk_tensor* workspace, void* stream);
+
+/* Synchronise `stream` and read the workspace header: *aborted = 1 when a
+ * launch stopped at a timed-out barrier (*stage = the stage it stopped in). */
+tk_status tk_workspace_status(const tk_tensor* workspace, void* stream, int32_t* aborted, int32_t* stage);
+
+/* Debug/measurement switches for subsequent launches of this program:
+ * timestamps (workgroup 0 records arrival/departure ticks of every barrier in
+ * the workspace header), stagger_seed (nonzero: every workgroup sleeps a seeded
+ * pseudo-random time before each work item), deadline_ticks (barrier wait
+ * limit in 100 MHz ticks; 0 restores the default of 4 s). */
+tk_status tk_set_debug(tk_program* prog, int32_t timestamps, uint32_t stagger_seed, uint64_t deadline_ticks);
+
+/* Copy the per-stage barrier timestamps (2 * n_stages u64, arrival and
+ * departure of workgroup 0, 100 MHz ticks) out of a workspace (synchronises
+ * `stream`). */
+tk_status tk_read_timestamps(const tk_program* prog, const tk_tensor* workspace, void* stream, uint64_t* out,
+                             size_t n);
+
+void tk_destroy(tk_program* prog);
+
+/* Thread-local message of the last failed call on this thread. */
+const char* tk_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TK_H */

@@ -1,0 +1,152 @@
+// Device-resident plan of one compiled whole-step program.
+//
+// The host scheduler (tk_compile.cpp) turns a program into a list of stages;
+// the persistent kernel (tk_device.hip) walks the stages, runs every work item
+// of a stage, and separates consecutive stages with one grid barrier.  This
+// header is the contract between the two: plain structs, no pointers (bases are
+// slots filled per launch), identical layout on host and device.
+//
+// The pages' generator (trainkernel codegen.py, `_Generator.generate`) emits one
+// straight-line kernel per program with a grid sync between dependent
+// operators; here the same schedule is data, interpreted by one AOT-compiled
+// kernel, so nothing is compiled at run time.
+#pragma once
+#include <stdint.h>
+
+namespace tkplan {
+
+enum DType : uint8_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
+
+constexpr int kBlock = 256;         // threads per workgroup (4 wave64)
+constexpr int kMaxBases = 240;      // pointer slots per launch (inputs, outputs, workspace)
+constexpr int kMaxDims = 4;         // iteration dims after collapsing
+constexpr int kMaxSlots = 4;        // saved values in the expression machine
+constexpr uint32_t kHeaderBytes = 16384;  // workspace header (barrier, status, timestamps)
+constexpr uint32_t kMaxTimedStages = 480;
+
+// Workspace header layout (bytes).  Each word sits on its own 64-byte line.
+constexpr uint32_t kHdrCount = 0;      // barrier arrivals in the current generation
+constexpr uint32_t kHdrGen = 64;       // barrier generation (monotonic)
+constexpr uint32_t kHdrAbort = 128;    // nonzero: a barrier timed out; the launch stopped
+constexpr uint32_t kHdrAbortStage = 192;
+constexpr uint32_t kHdrStamps = 1024;  // optional: u64 [stage][2] arrival/departure ticks of workgroup 0
+
+// Addressing of one operand over a task's iteration space: element
+// (c0..c3) lives at bases[base] + (offset + sum c_i * stride[i]) * size(dtype).
+struct DView {
+  int64_t offset;
+  int64_t stride[kMaxDims];
+  uint16_t base;
+  uint8_t dtype;
+  uint8_t pad[5];
+};
+static_assert(sizeof(DView) == 48, "DView layout");
+
+// Expression machine.  One accumulator vector (W elements per thread), a few
+// saved slots; each instruction reads the accumulator and at most one other
+// operand (a view load, a scalar, or a slot) and optionally rounds its result
+// to a storage dtype (round-to-nearest-even), as every pointwise op of the
+// pages rounds to its output dtype.
+enum VmOp : uint8_t {
+  VM_LOAD = 1,   // acc = operand
+  VM_ADD,        // acc = acc + a*x        (rev: x + a*acc)
+  VM_SUB,        // acc = acc - a*x        (rev: x - a*acc)
+  VM_MUL,        // acc = acc * x
+  VM_DIV,        // acc = acc / x          (rev: x / acc)
+  VM_NEG,        // acc = -acc
+  VM_RELU,       // acc = acc < 0 ? 0 : acc
+  VM_SQUARE,     // acc = acc * acc
+  VM_POW,        // acc = powf(acc, a)
+  VM_TB,         // threshold_backward: rev=0: (x <= a) ? 0 : acc ; rev=1: (acc <= a) ? 0 : x
+  VM_SAVE,       // slot[arg] = acc
+  VM_STORE,      // view[arg] = acc (converted to the view's dtype)
+  VM_SCALE,      // acc = a * acc (addmm alpha)
+  VM_ZERO,       // acc = 0
+};
+enum VmSrc : uint8_t { SRC_NONE = 0, SRC_VIEW = 1, SRC_SCALAR = 2, SRC_SLOT = 3 };
+constexpr uint8_t RND_NONE = 0xff;
+
+struct DIns {
+  uint8_t op;
+  uint8_t src;
+  uint8_t rnd;   // dtype to round the result to, or RND_NONE
+  uint8_t rev;
+  uint16_t arg;  // view index (SRC_VIEW / VM_STORE) or slot index
+  uint16_t pad;
+  float a;       // alpha, threshold or exponent
+  float s;       // scalar operand (SRC_SCALAR)
+};
+static_assert(sizeof(DIns) == 16, "DIns layout");
+
+enum TaskKind : uint8_t {
+  T_EW = 1,        // elementwise expression over an iteration space
+  T_GEMM_MFMA,     // tiled contraction on matrix cores (bf16/f16 operands)
+  T_GEMM_SIMT,     // tiled contraction with fp32 FMA (any dtypes)
+  T_GEMM_REDUCE,   // split-K: sum partial tiles in fixed order, then epilogue
+  T_GEMV_Q8,       // one-row product with an int8 blockwise-scaled weight
+  T_GEMV,          // one-row product with a float weight
+  T_RED_ROWS,      // reduce trailing iteration dims (rows x R)
+  T_RED_COLS,      // reduce leading iteration dims (R x cols)
+  T_RED_FINAL,     // combine per-part partials in fixed order, then epilogue
+};
+
+// Flags
+constexpr uint32_t F_MEAN = 1u;        // divide the sum by `count`
+constexpr uint32_t F_PARTIAL = 2u;     // write fp32 partials to scratch instead of finishing
+
+struct DTask {
+  uint8_t kind;
+  uint8_t width;       // elements per thread chunk (8 or 1)
+  uint8_t ndim;        // iteration dims
+  uint8_t tile;        // GEMM tile code
+  uint32_t flags;
+  uint32_t n_items;    // work items of this task in its stage
+  uint32_t item_begin; // first item index within the stage
+  uint32_t expr_first; // expression program (instructions): element source,
+  uint32_t expr_len;   //   or the epilogue of a contraction
+  uint32_t fin_first;  // reductions: the finishing program (mean, rounding, store)
+  uint32_t fin_len;
+  uint32_t dims[kMaxDims];  // iteration shape (elementwise / reduction source / GEMM output [m, n])
+  uint32_t m, n, k;         // contraction sizes; reductions: rows/cols and reduced size
+  uint32_t split;           // split-K parts / reduction parts
+  uint32_t kchunk;          // K elements per split part / rows per reduction part
+  uint32_t tiles_m, tiles_n;
+  uint16_t va, vb, vs, vx;  // operand views (A, B, scale, extra)
+  uint64_t scratch;         // byte offset of fp32 partials in the workspace
+  float count;              // mean divisor
+  uint32_t pad2;
+};
+
+struct DStage {
+  uint32_t task_first;
+  uint32_t n_tasks;
+  uint32_t n_items;
+  uint32_t flags;
+};
+
+struct DHeader {
+  uint32_t magic;
+  uint32_t n_stages;
+  uint32_t n_tasks;
+  uint32_t n_views;
+  uint32_t n_ins;
+  uint32_t off_stages, off_tasks, off_views, off_ins;  // byte offsets from the plan start
+  uint32_t bytes;
+};
+constexpr uint32_t kPlanMagic = 0x31706b74u;  // "tkp1"
+
+// Kernel launch arguments (passed by value as the kernel argument block).
+struct KArgs {
+  const uint8_t* plan;
+  uint8_t* ws;                 // workspace: header then arena
+  uint64_t deadline_ticks;     // barrier wait limit (100 MHz ticks); 0 = default
+  uint32_t flags;              // K_* debug switches
+  uint32_t stagger_seed;
+  uint32_t n_bases;
+  uint32_t pad;
+  void* bases[kMaxBases];
+};
+constexpr uint32_t K_TIMESTAMPS = 1u;
+constexpr uint32_t K_STAGGER = 2u;
+
+}  // namespace tkplan

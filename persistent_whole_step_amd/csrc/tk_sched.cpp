@@ -1,0 +1,1709 @@
+// Scheduler: program -> stages of device tasks.
+//
+// The decisions follow the trainkernel generator (codegen.py, `_Generator`):
+//  * epilogue fusion, pass 1: a non-returned contraction followed by a chain of
+//    single-use, shape-preserving pointwise ops is replaced by one tile task
+//    writing the chain's last value (identity-viewed chain links, contiguous
+//    external operands produced before the contraction);
+//  * pass 2 ("side epilogues"): the tile also writes returned pointwise
+//    descendants of a kept (or discarded) root;
+//  * inlining of single-use pointwise values and of casts of inputs;
+//  * the direct in-place commit proof and staged (transactional) commits;
+//  * output bindings, workspace reuse after the last reader, hazard-driven
+//    barrier placement (read/write region overlap), grid sizing.
+// Additions of this design, all value-preserving:
+//  * ops are levelled (1 + the latest stage they depend on, including
+//    write-after-read on in-place targets), so independent ops share a stage;
+//  * pass 3 folds a proven-direct in-place pointwise update (e.g. SGD) into the
+//    tile of the contraction that produces its only non-input operand, when
+//    that contraction reads nothing of the target;
+//  * workspace values keep their storage dtype (2-byte bf16/f16) instead of
+//    float32, with identical values;
+//  * long reductions and split-K contractions are two stages with fp32
+//    partials combined in a fixed order, covering every element.
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <functional>
+#include <sstream>
+
+#include "tk_internal.hpp"
+
+namespace tk {
+
+using namespace tkplan;
+
+namespace {
+
+constexpr uint64_t kAlign = 256;
+
+uint64_t align_up(uint64_t v, uint64_t a) { return (v + a - 1) / a * a; }
+
+static const char* kind_name(uint8_t k) {
+  switch (k) {
+    case T_EW: return "ew";
+    case T_GEMM_MFMA: return "gemm_mfma";
+    case T_GEMM_SIMT: return "gemm_simt";
+    case T_GEMM_REDUCE: return "gemm_splitk_reduce";
+    case T_GEMV_Q8: return "gemv_q8";
+    case T_GEMV: return "gemv";
+    case T_RED_ROWS: return "reduce_rows";
+    case T_RED_COLS: return "reduce_cols";
+    case T_RED_FINAL: return "reduce_final";
+  }
+  return "?";
+}
+
+// Where a materialized value lives.
+struct Loc {
+  int base = -1;        // base slot
+  int64_t offset = 0;   // elements
+  uint8_t dtype = DT_F32;
+  bool valid() const { return base >= 0; }
+};
+
+// Expression tree over one op's iteration space.
+struct Node {
+  enum Kind { LEAF, SCALAR, SLOT, OP } kind = LEAF;
+  int view = -1;       // LEAF: index into the task's view table
+  float value = 0;     // SCALAR
+  int slot = -1;       // SLOT
+  int op = -1;         // OP: program op index
+  std::vector<Node> kids;
+};
+
+struct Entry {            // one scheduled (materialized) unit
+  int op = -1;            // program op index (the contraction for fused tiles)
+  std::vector<int> chain; // pass 1 / pass 3 chain ops
+  std::vector<int> side;  // pass 2 descendants
+  bool discard_root = false;
+  bool update = false;    // pass 3
+  int kind = 0;           // 0 op, 1 output copy, 2 staged commit
+  int slot = -1;          // output slot for copies/commits
+  int level = 0;
+  bool two_phase = false;
+  int avail() const { return level + (two_phase ? 1 : 0); }
+  std::vector<std::string> reads_vals;    // materialized values read
+  std::set<std::string> reads_inputs;     // input buffers read (through inline)
+  std::set<std::string> writes_vals;      // values written
+  int writes_input = -1;                  // input index written (direct in-place / commit)
+  int order = 0;
+};
+
+struct Builder {
+  const Program& P;
+  const Options& O;
+  int n_in, n_out, ws_base;
+  std::map<std::string, int> input_idx, producer;
+  std::map<std::string, std::vector<int>> users;  // with multiplicity (one per operand reference)
+  std::map<std::string, int> refcount;
+  std::set<std::string> output_bufs;
+  std::map<std::string, int> output_count;
+  std::set<std::string> aliased;   // declared in-place output buffers
+
+  std::map<int, Entry> fused;      // by contraction op index
+  std::set<int> skip;              // ops computed inside a fused tile
+  std::set<int> inlined;
+  std::set<std::string> inlined_bufs;
+  std::vector<Entry> sched;
+  std::map<int, int> direct;       // output slot -> input index
+  std::map<std::string, int> bound;  // value -> output slot written directly
+  std::map<std::string, Loc> loc;    // value -> storage
+  std::map<std::string, uint64_t> arena_off;  // value -> byte offset in arena
+
+  // device tables
+  std::vector<DView> views;
+  std::vector<DIns> ins;
+  std::vector<std::vector<DTask>> stage_tasks;
+  std::vector<std::vector<std::string>> stage_desc;
+  std::map<int, uint64_t> scratch_off;  // sched index -> scratch byte offset
+  std::map<int, uint64_t> scratch_bytes;
+  uint64_t arena_bytes = 0;
+  tk_stats st{};
+
+  Builder(const Program& p, const Options& o) : P(p), O(o) {
+    n_in = (int)p.inputs.size();
+    n_out = (int)p.outputs.size();
+    ws_base = n_in + n_out;
+    if (ws_base + 1 > kMaxBases) raise(TK_E_UNSUPPORTED, "too many inputs and outputs for one launch");
+    for (int i = 0; i < n_in; ++i) input_idx[p.inputs[i].buf] = i;
+    for (int j = 0; j < (int)p.ops.size(); ++j) {
+      producer[p.ops[j].out.buf] = j;
+      for (auto& a : p.ops[j].args)
+        if (!a.scalar) {
+          users[a.spec.buf].push_back(j);
+          refcount[a.spec.buf]++;
+        }
+    }
+    for (auto& o2 : p.outputs) {
+      output_bufs.insert(o2.buf);
+      output_count[o2.buf]++;
+    }
+    for (auto& kv : p.inplace) aliased.insert(p.outputs[kv.first].buf);
+  }
+
+  const Op& op(int j) const { return P.ops[j]; }
+  bool is_input(const std::string& b) const { return input_idx.count(b) != 0; }
+  int prod(const std::string& b) const {
+    auto it = producer.find(b);
+    return it == producer.end() ? -1 : it->second;
+  }
+  bool is_contraction(int j) const { return op(j).cls == OC_MM || op(j).cls == OC_MM_Q8; }
+  static bool identity_view(const Spec& s, const std::vector<int64_t>& shape) {
+    return s.shape == shape && s.offset == 0 && s.contiguous();
+  }
+
+  // ------------------------------------------------------------ fusion --
+  void pass1() {
+    for (int mi = 0; mi < (int)P.ops.size(); ++mi) {
+      const Op& mm = op(mi);
+      if (!is_contraction(mi) || output_bufs.count(mm.out.buf)) continue;
+      std::vector<int> chain;
+      std::string cur = mm.out.buf;
+      for (;;) {
+        auto uit = users.find(cur);
+        if (uit == users.end() || uit->second.size() != 1) break;
+        int nj = uit->second[0];
+        const Op& nx = op(nj);
+        if (nx.cls != OC_POINTWISE || output_bufs.count(nx.out.buf)) break;
+        const std::vector<int64_t>& cur_shape = op(prod(cur)).out.shape;
+        bool ok = true;
+        for (auto& a : nx.args)
+          if (!a.scalar && a.spec.buf == cur && !identity_view(a.spec, cur_shape)) ok = false;
+        if (!ok) break;
+        chain.push_back(nj);
+        cur = nx.out.buf;
+      }
+      if (chain.empty()) continue;
+      bool safe = true;
+      std::set<std::string> chain_bufs = {mm.out.buf};
+      for (int c : chain) chain_bufs.insert(op(c).out.buf);
+      for (int c : chain) {
+        if (op(c).out.shape != mm.out.shape) safe = false;
+        for (auto& a : op(c).args) {
+          if (a.scalar || chain_bufs.count(a.spec.buf)) continue;
+          if (a.spec.offset != 0 || !a.spec.contiguous()) safe = false;
+          if (prod(a.spec.buf) >= mi) safe = false;
+        }
+      }
+      if (!safe) continue;
+      Entry e;
+      e.op = mi;
+      e.chain = chain;
+      fused[mi] = e;
+      for (int c : chain) skip.insert(c);
+    }
+  }
+
+  void pass2() {
+    for (int mi = 0; mi < (int)P.ops.size(); ++mi) {
+      const Op& mm = op(mi);
+      if (!is_contraction(mi) || fused.count(mi) || skip.count(mi)) continue;
+      std::set<std::string> known = {mm.out.buf};
+      std::vector<int> chain;
+      for (int j = mi + 1; j < (int)P.ops.size(); ++j) {
+        const Op& nx = op(j);
+        if (nx.cls != OC_POINTWISE || skip.count(j)) continue;
+        bool touches = false;
+        for (auto& a : nx.args)
+          if (!a.scalar && known.count(a.spec.buf)) touches = true;
+        if (!touches) continue;
+        if (nx.out.shape != mm.out.shape || aliased.count(nx.out.buf)) continue;
+        bool ok = true;
+        for (auto& a : nx.args) {
+          if (a.scalar) continue;
+          if (known.count(a.spec.buf)) {
+            if (!identity_view(a.spec, mm.out.shape)) ok = false;
+          } else if (prod(a.spec.buf) >= mi) {
+            ok = false;
+          }
+        }
+        if (!ok) continue;
+        chain.push_back(j);
+        known.insert(nx.out.buf);
+      }
+      std::set<std::string> derived = known;
+      derived.erase(mm.out.buf);
+      std::set<std::string> returned;
+      for (auto& d : derived)
+        if (output_bufs.count(d)) returned.insert(d);
+      std::set<std::string> needed = returned;
+      for (auto it = chain.rbegin(); it != chain.rend(); ++it)
+        if (needed.count(op(*it).out.buf))
+          for (auto& a : op(*it).args)
+            if (!a.scalar && derived.count(a.spec.buf)) needed.insert(a.spec.buf);
+      std::vector<int> kept;
+      for (int c : chain)
+        if (needed.count(op(c).out.buf)) kept.push_back(c);
+      std::set<std::string> dkept;
+      for (auto& d : derived)
+        if (needed.count(d)) dkept.insert(d);
+      if (returned.empty()) continue;
+      bool ok = true;
+      // every reader of a non-returned derived value must be inside the tile
+      for (auto& d : dkept) {
+        if (returned.count(d)) continue;
+        for (int u : users[d])
+          if (!dkept.count(op(u).out.buf)) ok = false;
+      }
+      // returned values must be bindable straight into their output buffer
+      for (auto& r : returned) {
+        bool bindable = false;
+        for (int s = 0; s < n_out; ++s) {
+          const Spec& o2 = P.outputs[s];
+          if (o2.buf != r || P.inplace.count(s)) continue;
+          const Spec& pv = op(prod(r)).out;
+          if (o2.offset == 0 && o2.shape == pv.shape && o2.contiguous() && o2.dtype == pv.dtype) bindable = true;
+        }
+        if (!bindable) ok = false;
+      }
+      if ((int)kept.size() + 1 > kMaxSlots - 1) ok = false;  // slot budget of the tile program
+      if (!ok) continue;
+      Entry e;
+      e.op = mi;
+      e.side = kept;
+      bool root_only_chain = !output_bufs.count(mm.out.buf);
+      for (int u : users[mm.out.buf])
+        if (!dkept.count(op(u).out.buf)) root_only_chain = false;
+      e.discard_root = root_only_chain;
+      fused[mi] = e;
+      for (int c : kept) skip.insert(c);
+    }
+  }
+
+  // ---------------------------------------------------------- inlining --
+  void choose_inline() {
+    for (int j = 0; j < (int)P.ops.size(); ++j) {
+      const Op& o2 = op(j);
+      if (!O.fuse_pointwise || o2.cls != OC_POINTWISE || skip.count(j)) continue;
+      if (output_bufs.count(o2.out.buf)) continue;
+      bool input_cast = O.inline_input_casts && o2.opcode == "cast" && !o2.args[0].scalar && is_input(o2.args[0].spec.buf);
+      if (!(refcount[o2.out.buf] == 1 || input_cast)) continue;
+      // Readers must see the value through an identity view and must not be
+      // contraction operands (the matrix loaders read storage).
+      bool ok = true;
+      for (int u : users[o2.out.buf]) {
+        const Op& uo = op(u);
+        for (size_t ai = 0; ai < uo.args.size(); ++ai) {
+          const Arg& a = uo.args[ai];
+          if (a.scalar || a.spec.buf != o2.out.buf) continue;
+          if (!identity_view(a.spec, o2.out.shape)) ok = false;
+          if (uo.cls == OC_MM || uo.cls == OC_MM_Q8)
+            if (!(uo.has_bias() && ai == 0)) ok = false;
+        }
+      }
+      if (ok) {
+        inlined.insert(j);
+        inlined_bufs.insert(o2.out.buf);
+      }
+    }
+  }
+
+  // Input buffers reachable from a view through inlined producers.
+  std::set<std::string> raw_inputs(const Spec& s) const {
+    if (is_input(s.buf)) return {s.buf};
+    if (inlined_bufs.count(s.buf)) {
+      std::set<std::string> r;
+      for (auto& a : op(prod(s.buf)).args)
+        if (!a.scalar) {
+          auto q = raw_inputs(a.spec);
+          r.insert(q.begin(), q.end());
+        }
+      return r;
+    }
+    return {};
+  }
+  // Materialized values reachable from a view through inlined producers.
+  void root_values(const Spec& s, std::vector<std::string>& out) const {
+    if (is_input(s.buf)) return;
+    if (inlined_bufs.count(s.buf)) {
+      for (auto& a : op(prod(s.buf)).args)
+        if (!a.scalar) root_values(a.spec, out);
+      return;
+    }
+    out.push_back(s.buf);
+  }
+  bool identity_access(const Spec& s, const std::string& target, const std::vector<int64_t>& shape) const {
+    if (!raw_inputs(s).count(target)) return true;
+    if (s.shape != shape || s.offset != 0 || !s.contiguous()) return false;
+    if (s.buf == target) return true;
+    for (auto& a : op(prod(s.buf)).args)
+      if (!a.scalar && !identity_access(a.spec, target, shape)) return false;
+    return true;
+  }
+
+  // Ops (by program index) and their operands as read by an entry.
+  std::vector<const Arg*> entry_args(const Entry& e) const {
+    std::vector<const Arg*> r;
+    if (e.kind != 0) return r;
+    for (auto& a : op(e.op).args) r.push_back(&a);
+    for (int c : e.chain)
+      for (auto& a : op(c).args) r.push_back(&a);
+    for (int c : e.side)
+      for (auto& a : op(c).args) r.push_back(&a);
+    return r;
+  }
+  std::set<std::string> internal_bufs(const Entry& e) const {
+    std::set<std::string> s;
+    if (e.kind != 0) return s;
+    s.insert(op(e.op).out.buf);
+    for (int c : e.chain) s.insert(op(c).out.buf);
+    for (int c : e.side) s.insert(op(c).out.buf);
+    return s;
+  }
+  std::string final_buf(const Entry& e) const {
+    if (!e.chain.empty()) return op(e.chain.back()).out.buf;
+    return op(e.op).out.buf;
+  }
+
+  void build_schedule() {
+    for (int j = 0; j < (int)P.ops.size(); ++j) {
+      if (fused.count(j)) {
+        sched.push_back(fused[j]);
+      } else if (!skip.count(j) && !inlined.count(j)) {
+        Entry e;
+        e.op = j;
+        sched.push_back(e);
+      }
+    }
+    for (size_t i = 0; i < sched.size(); ++i) sched[i].order = (int)i;
+  }
+
+  // Values an entry writes to storage.
+  std::vector<std::string> written(const Entry& e) const {
+    std::vector<std::string> w;
+    if (e.kind != 0) return w;
+    if (!e.side.empty()) {
+      if (!e.discard_root) w.push_back(op(e.op).out.buf);
+      for (int c : e.side)
+        if (output_bufs.count(op(c).out.buf)) w.push_back(op(c).out.buf);
+      return w;
+    }
+    w.push_back(final_buf(e));
+    return w;
+  }
+
+  // ----------------------------------------------- direct in-place proof --
+  void prove_direct() {
+    for (auto& kv : P.inplace) {
+      int slot = kv.first, tidx = kv.second;
+      const Spec& out = P.outputs[slot];
+      const std::string& target = P.inputs[tidx].buf;
+      int owner = -1;
+      for (size_t i = 0; i < sched.size(); ++i)
+        for (auto& w : written(sched[i]))
+          if (w == out.buf) owner = (int)i;
+      if (owner < 0) continue;
+      const Entry& e = sched[owner];
+      if (e.kind != 0 || op(e.op).cls != OC_POINTWISE || !e.chain.empty() || !e.side.empty()) continue;
+      if (output_count[out.buf] != 1) continue;
+      if (out.offset != 0 || !out.contiguous()) continue;
+      bool named = false;
+      for (auto& o2 : P.outputs)
+        if (o2.buf == target) named = true;
+      if (named) continue;
+      bool later = false;
+      for (size_t i = owner + 1; i < sched.size(); ++i)
+        for (auto* a : entry_args(sched[i]))
+          if (!a->scalar && raw_inputs(a->spec).count(target)) later = true;
+      if (later) continue;
+      bool ident = true;
+      for (auto& a : op(e.op).args)
+        if (!a.scalar && !identity_access(a.spec, target, out.shape)) ident = false;
+      if (!ident) continue;
+      direct[slot] = tidx;
+    }
+  }
+
+  // Pass 3: fold a direct pointwise update into the contraction tile that
+  // produces its only materialized operand.
+  void pass3() {
+    if (!O.fuse_updates || !O.fuse_epilogues) return;
+    for (auto& kv : direct) {
+      int slot = kv.first;
+      const std::string& target = P.inputs[kv.second].buf;
+      const std::string& ubuf = P.outputs[slot].buf;
+      int uo = -1;
+      for (size_t i = 0; i < sched.size(); ++i)
+        if (sched[i].kind == 0 && sched[i].chain.empty() && sched[i].side.empty() && op(sched[i].op).out.buf == ubuf)
+          uo = (int)i;
+      if (uo < 0) continue;
+      const Op& u = op(sched[uo].op);
+      // the one operand produced by a contraction
+      int mm_sched = -1;
+      std::string mbuf;
+      bool ok = true;
+      for (auto& a : u.args) {
+        if (a.scalar || is_input(a.spec.buf)) continue;
+        if (inlined_bufs.count(a.spec.buf)) { ok = false; break; }
+        int pj = prod(a.spec.buf);
+        if (!is_contraction(pj)) { ok = false; break; }
+        if (!mbuf.empty() && mbuf != a.spec.buf) { ok = false; break; }
+        mbuf = a.spec.buf;
+      }
+      if (!ok || mbuf.empty()) continue;
+      int mj = prod(mbuf);
+      for (size_t i = 0; i < sched.size(); ++i)
+        if (sched[i].kind == 0 && sched[i].op == mj) mm_sched = (int)i;
+      if (mm_sched < 0) continue;
+      Entry& me = sched[mm_sched];
+      if (!me.chain.empty() || !me.side.empty()) continue;
+      if (output_bufs.count(mbuf) || users[mbuf].size() != 1) continue;
+      if (u.out.shape != op(mj).out.shape) continue;
+      for (auto& a : u.args) {
+        if (a.scalar) continue;
+        if (a.spec.buf == mbuf && !identity_view(a.spec, op(mj).out.shape)) ok = false;
+        if (a.spec.buf != mbuf && (a.spec.offset != 0 || !a.spec.contiguous())) ok = false;
+      }
+      // the tile must read nothing of the target
+      for (auto& a : op(mj).args)
+        if (!a.scalar && raw_inputs(a.spec).count(target)) ok = false;
+      if (!ok) continue;
+      // The fused tile takes the update's place in program order (after every
+      // reader of the target), so ordering constraints stay acyclic.
+      Entry fusedE = me;
+      fusedE.chain.push_back(sched[uo].op);
+      fusedE.update = true;
+      skip.insert(sched[uo].op);
+      sched[uo] = fusedE;
+      sched.erase(sched.begin() + mm_sched);
+    }
+    for (size_t i = 0; i < sched.size(); ++i) sched[i].order = (int)i;
+  }
+
+  // ---------------------------------------------------------- bindings --
+  void bind_outputs() {
+    std::map<std::string, const Entry*> writer;
+    for (auto& e : sched)
+      for (auto& w : written(e)) writer[w] = &e;
+    for (int s = 0; s < n_out; ++s) {
+      if (P.inplace.count(s) && !direct.count(s)) continue;
+      const Spec& o2 = P.outputs[s];
+      auto it = writer.find(o2.buf);
+      if (it == writer.end()) continue;
+      const Spec& pv = op(prod(o2.buf)).out;
+      if (pv.dtype == o2.dtype && o2.offset == 0 && o2.numel() == pv.numel() && o2.contiguous() &&
+          !bound.count(o2.buf))
+        bound[o2.buf] = s;
+    }
+    // every returned side-epilogue value must be bound (pass 2 checked bindability)
+    for (auto& e : sched)
+      for (int c : e.side)
+        if (output_bufs.count(op(c).out.buf) && !bound.count(op(c).out.buf))
+          raise(TK_E_UNSUPPORTED, "internal: side epilogue without a direct output binding");
+  }
+
+  // ---------------------------------------------------------- leveling --
+  void add_copies_and_commits() {
+    for (int s = 0; s < n_out; ++s) {
+      const Spec& o2 = P.outputs[s];
+      if (P.inplace.count(s) && !direct.count(s)) {
+        Entry c;
+        c.kind = 2;
+        c.slot = s;
+        c.writes_input = P.inplace.at(s);
+        sched.push_back(c);
+        continue;
+      }
+      auto b = bound.find(o2.buf);
+      if (b != bound.end() && b->second == s) continue;
+      Entry c;
+      c.kind = 1;
+      c.slot = s;
+      sched.push_back(c);
+    }
+  }
+
+  void collect_rw() {
+    for (auto& e : sched) {
+      e.reads_vals.clear();
+      e.reads_inputs.clear();
+      e.writes_vals.clear();
+      if (e.kind == 0) {
+        auto internal = internal_bufs(e);
+        for (auto* a : entry_args(e)) {
+          if (a->scalar || internal.count(a->spec.buf)) continue;
+          root_values(a->spec, e.reads_vals);
+          auto r = raw_inputs(a->spec);
+          e.reads_inputs.insert(r.begin(), r.end());
+        }
+        for (auto& w : written(e)) e.writes_vals.insert(w);
+        for (auto& kv : direct)
+          if (e.writes_vals.count(P.outputs[kv.first].buf)) e.writes_input = kv.second;
+      } else {
+        const Spec& o2 = P.outputs[e.slot];
+        if (is_input(o2.buf))
+          e.reads_inputs.insert(o2.buf);
+        else
+          e.reads_vals.push_back(o2.buf);
+      }
+    }
+  }
+
+  void level() {
+    std::map<std::string, int> writer;
+    for (size_t i = 0; i < sched.size(); ++i)
+      for (auto& w : sched[i].writes_vals) writer[w] = (int)i;
+    for (auto& e : sched) e.level = 0;
+    for (int iter = 0; iter < 1000; ++iter) {
+      bool changed = false;
+      int prev_last = -1;
+      for (size_t i = 0; i < sched.size(); ++i) {
+        Entry& e = sched[i];
+        int L = 0;
+        for (auto& v : e.reads_vals) {
+          auto it = writer.find(v);
+          if (it == writer.end()) raise(TK_E_ARG, "internal: value '" + v + "' has no writer");
+          if ((size_t)it->second != i) L = std::max(L, sched[it->second].avail() + 1);
+        }
+        if (e.writes_input >= 0) {
+          const std::string& t = P.inputs[e.writes_input].buf;
+          for (size_t r = 0; r < sched.size(); ++r)
+            if (r != i && sched[r].reads_inputs.count(t)) L = std::max(L, sched[r].avail() + 1);
+        }
+        if (e.kind == 2) {  // staged commits also follow every other write of the step
+          for (size_t r = 0; r < sched.size(); ++r)
+            if (sched[r].kind == 0) L = std::max(L, sched[r].avail() + 1);
+        }
+        if (O.barrier_every_op && prev_last >= 0) L = std::max(L, prev_last + 1);
+        if (L != e.level) {
+          e.level = L;
+          changed = true;
+        }
+        prev_last = e.avail();
+      }
+      if (!changed) return;
+    }
+    raise(TK_E_ARG, "internal: leveling did not converge (cyclic dependencies)");
+  }
+
+  // ------------------------------------------------------------- arena --
+  void plan_arena() {
+    // Location of every stored value.
+    for (auto& e : sched)
+      for (auto& w : e.writes_vals) {
+        Loc l;
+        l.dtype = op(prod(w)).out.dtype;
+        auto b = bound.find(w);
+        if (b != bound.end()) {
+          l.base = n_in + b->second;
+          l.offset = 0;
+        } else {
+          l.base = ws_base;
+        }
+        loc[w] = l;
+      }
+    // Liveness in levels.
+    std::map<std::string, int> wlevel, lastread;
+    std::map<std::string, int> first_order;
+    for (auto& e : sched)
+      for (auto& w : e.writes_vals) {
+        wlevel[w] = e.avail();
+        lastread[w] = e.avail();
+        first_order[w] = e.order;
+      }
+    for (auto& e : sched)
+      for (auto& v : e.reads_vals) lastread[v] = std::max(lastread[v], e.avail());
+    struct Block { std::string name; int start, last; uint64_t bytes; int order; int sched_idx; };
+    std::vector<Block> blocks;
+    for (auto& kv : loc) {
+      if (kv.second.base != ws_base) continue;
+      const Spec& pv = op(prod(kv.first)).out;
+      uint64_t bytes = align_up(std::max<uint64_t>(1, pv.numel() * dtype_size(pv.dtype)), kAlign);
+      blocks.push_back({kv.first, wlevel[kv.first], lastread[kv.first], bytes, first_order[kv.first], -1});
+    }
+    for (size_t i = 0; i < sched.size(); ++i)
+      if (scratch_bytes.count((int)i))
+        blocks.push_back({"#scratch" + std::to_string(i), sched[i].level, sched[i].avail(),
+                          align_up(scratch_bytes[(int)i], kAlign), sched[i].order, (int)i});
+    std::sort(blocks.begin(), blocks.end(), [](const Block& a, const Block& b) {
+      return a.start != b.start ? a.start < b.start : a.order < b.order;
+    });
+    struct Live { uint64_t off, bytes; int last; };
+    std::vector<Live> live;
+    std::vector<std::pair<uint64_t, uint64_t>> freel;  // (offset, bytes)
+    uint64_t top = 0;
+    auto coalesce = [&]() {
+      std::sort(freel.begin(), freel.end());
+      std::vector<std::pair<uint64_t, uint64_t>> m;
+      for (auto& f : freel) {
+        if (!m.empty() && m.back().first + m.back().second == f.first)
+          m.back().second += f.second;
+        else
+          m.push_back(f);
+      }
+      freel = m;
+    };
+    for (auto& b : blocks) {
+      // release blocks whose last reader finished before this level
+      std::vector<Live> keep;
+      for (auto& l : live) {
+        if (l.last < b.start)
+          freel.push_back({l.off, l.bytes});
+        else
+          keep.push_back(l);
+      }
+      live = keep;
+      coalesce();
+      int best = -1;
+      for (size_t i = 0; i < freel.size(); ++i)
+        if (freel[i].second >= b.bytes && (best < 0 || freel[i].second < freel[best].second)) best = (int)i;
+      uint64_t off;
+      if (best >= 0) {
+        off = freel[best].first;
+        if (freel[best].second > b.bytes)
+          freel[best] = {off + b.bytes, freel[best].second - b.bytes};
+        else
+          freel.erase(freel.begin() + best);
+      } else {
+        off = top;
+        top += b.bytes;
+      }
+      live.push_back({off, b.bytes, b.last});
+      if (b.sched_idx >= 0) {
+        scratch_off[b.sched_idx] = kHeaderBytes + off;
+      } else {
+        arena_off[b.name] = off;
+        Loc& l = loc[b.name];
+        l.offset = (int64_t)((kHeaderBytes + off) / dtype_size(l.dtype));
+      }
+    }
+    arena_bytes = top;
+  }
+
+  // ----------------------------------------------------- expressions --
+  struct ExprCtx {
+    std::vector<int64_t> space;  // task iteration shape (uncollapsed)
+    std::vector<DView> vtab;     // views over `space` (uncollapsed, rank = space.size())
+    std::map<std::string, int> slot_of;  // tile values held in slots
+  };
+
+  // A view of stored data over the task space: dims map[i] of the reading
+  // op's space go to task dims (or -1: broadcast to coordinate 0).
+  DView lift(const Spec& s, const std::vector<int>& map, const Loc& where, size_t rank) {
+    DView v{};
+    v.base = (uint16_t)where.base;
+    v.dtype = s.dtype;
+    v.offset = where.offset + s.offset;
+    for (int d = 0; d < kMaxDims; ++d) v.stride[d] = 0;
+    std::vector<int64_t> st(rank, 0);
+    const size_t r = s.shape.size(), R = map.size();
+    for (size_t j = 0; j < r; ++j) {
+      if (s.shape[j] == 1) continue;
+      int td = map[R - r + j];
+      if (td < 0) continue;
+      st[td] += s.strides[j];
+    }
+    // temporarily stash full-rank strides; collapsed later
+    vstride_full.push_back(st);
+    return v;
+  }
+  std::vector<std::vector<int64_t>> vstride_full;  // parallel to ExprCtx::vtab during building
+
+  Loc storage_of(const std::string& buf) {
+    if (is_input(buf)) {
+      Loc l;
+      l.base = input_idx[buf];
+      l.offset = 0;
+      l.dtype = P.inputs[input_idx[buf]].dtype;
+      return l;
+    }
+    auto it = loc.find(buf);
+    if (it == loc.end()) raise(TK_E_ARG, "internal: value '" + buf + "' has no storage");
+    return it->second;
+  }
+
+  // Build the tree of an operand read through `s` by an op with iteration map `map`.
+  Node operand_node(ExprCtx& cx, const Arg& a, const std::vector<int>& map) {
+    Node n;
+    if (a.scalar) {
+      n.kind = Node::SCALAR;
+      n.value = a.value;
+      return n;
+    }
+    auto sl = cx.slot_of.find(a.spec.buf);
+    if (sl != cx.slot_of.end()) {
+      n.kind = Node::SLOT;
+      n.slot = sl->second;
+      return n;
+    }
+    if (inlined_bufs.count(a.spec.buf)) {
+      // identity view of the producer: its dims align with the view's dims
+      std::vector<int> pm(a.spec.shape.size());
+      const size_t r = a.spec.shape.size(), R = map.size();
+      for (size_t j = 0; j < r; ++j) pm[j] = a.spec.shape[j] == 1 ? -1 : map[R - r + j];
+      return op_node(cx, prod(a.spec.buf), pm);
+    }
+    n.kind = Node::LEAF;
+    n.view = (int)cx.vtab.size();
+    cx.vtab.push_back(lift(a.spec, map, storage_of(a.spec.buf), cx.space.size()));
+    return n;
+  }
+
+  Node op_node(ExprCtx& cx, int j, const std::vector<int>& map) {
+    const Op& o2 = op(j);
+    Node n;
+    n.kind = Node::OP;
+    n.op = j;
+    for (auto& a : o2.args) n.kids.push_back(operand_node(cx, a, map));
+    return n;
+  }
+
+  static bool simple(const Node& n) { return n.kind != Node::OP; }
+
+  void emit_load(std::vector<DIns>& code, const Node& n) {
+    DIns d{};
+    d.op = VM_LOAD;
+    d.rnd = RND_NONE;
+    set_src(d, n);
+    code.push_back(d);
+  }
+  static void set_src(DIns& d, const Node& n) {
+    if (n.kind == Node::LEAF) {
+      d.src = SRC_VIEW;
+      d.arg = (uint16_t)n.view;
+    } else if (n.kind == Node::SCALAR) {
+      d.src = SRC_SCALAR;
+      d.s = n.value;
+    } else if (n.kind == Node::SLOT) {
+      d.src = SRC_SLOT;
+      d.arg = (uint16_t)n.slot;
+    }
+  }
+
+  // Emit code leaving the node's value (rounded to its dtype) in the accumulator.
+  void emit(std::vector<DIns>& code, const Node& n, int free_slot) {
+    if (simple(n)) {
+      emit_load(code, n);
+      return;
+    }
+    const Op& o2 = op(n.op);
+    const std::string& c = o2.opcode;
+    const uint8_t rnd = o2.out.dtype == DT_F32 ? RND_NONE : o2.out.dtype;
+    DIns d{};
+    d.rnd = rnd;
+    auto unary = [&](uint8_t vop, float a) {
+      emit(code, n.kids[0], free_slot);
+      d.op = vop;
+      d.a = a;
+      d.src = SRC_NONE;
+      code.push_back(d);
+    };
+    if (c == "full") {
+      Node s;
+      s.kind = Node::SCALAR;
+      s.value = o2.attrs.count("value") ? o2.attrs.at("value") : (n.kids.empty() ? 0.0f : n.kids[0].value);
+      emit_load(code, s);
+      code.back().rnd = rnd;
+      return;
+    }
+    if (c == "neg") return unary(VM_NEG, 0);
+    if (c == "relu") return unary(VM_RELU, 0);
+    if (c == "cast") {
+      emit(code, n.kids[0], free_slot);
+      if (rnd != RND_NONE) {
+        DIns r{};
+        r.op = VM_SCALE;  // 1 * x is exact; the instruction carries the rounding
+        r.a = 1.0f;
+        r.rnd = rnd;
+        code.push_back(r);
+      }
+      return;
+    }
+    if (c == "pow") {
+      float e = n.kids.size() > 1 ? n.kids[1].value : o2.attr("exponent", 2.0f);
+      if (e == 2.0f) return unary(VM_SQUARE, 0);
+      return unary(VM_POW, e);
+    }
+    uint8_t vop = 0;
+    float a = 0;
+    if (c == "add") { vop = VM_ADD; a = o2.attr("alpha", 1.0f); }
+    else if (c == "sub") { vop = VM_SUB; a = o2.attr("alpha", 1.0f); }
+    else if (c == "mul") { vop = VM_MUL; }
+    else if (c == "div") { vop = VM_DIV; }
+    else if (c == "threshold_backward") { vop = VM_TB; a = o2.attr("threshold", 0.0f); }
+    else raise(TK_E_UNSUPPORTED, "unsupported pointwise operation " + c);
+    const Node &x = n.kids[0], &y = n.kids[1];
+    d.op = vop;
+    d.a = a;
+    if (simple(y)) {
+      emit(code, x, free_slot);
+      set_src(d, y);
+      d.rev = 0;
+    } else if (simple(x)) {
+      emit(code, y, free_slot);
+      set_src(d, x);
+      d.rev = 1;
+    } else {
+      if (free_slot >= kMaxSlots) raise(TK_E_UNSUPPORTED, "expression too deep for the tile program");
+      emit(code, x, free_slot);
+      DIns sv{};
+      sv.op = VM_SAVE;
+      sv.arg = (uint16_t)free_slot;
+      sv.rnd = RND_NONE;
+      code.push_back(sv);
+      emit(code, y, free_slot + 1);
+      d.src = SRC_SLOT;
+      d.arg = (uint16_t)free_slot;
+      d.rev = 1;
+    }
+    code.push_back(d);
+  }
+
+  void emit_store(std::vector<DIns>& code, ExprCtx& cx, const std::string& buf, const std::vector<int>& map) {
+    const Spec& pv = op(prod(buf)).out;
+    Spec s = pv;  // contiguous view of the value itself
+    DIns st{};
+    st.op = VM_STORE;
+    st.rnd = RND_NONE;
+    st.arg = (uint16_t)cx.vtab.size();
+    cx.vtab.push_back(lift(s, map, storage_of(buf), cx.space.size()));
+    code.push_back(st);
+  }
+
+  // Collapse the task space and the views' strides; returns the collapsed dims.
+  std::vector<int64_t> collapse(ExprCtx& cx, bool allow = true) {
+    std::vector<int64_t> dims = cx.space;
+    std::vector<std::vector<int64_t>> st = vstride_full;
+    // drop size-1 dims
+    std::vector<int64_t> d2;
+    std::vector<std::vector<int64_t>> s2(st.size());
+    for (size_t d = 0; d < dims.size(); ++d) {
+      if (dims[d] == 1 && dims.size() > 1) continue;
+      d2.push_back(dims[d]);
+      for (size_t v = 0; v < st.size(); ++v) s2[v].push_back(st[v][d]);
+    }
+    dims = d2;
+    st = s2;
+    if (allow) {
+      for (size_t d = 0; d + 1 < dims.size();) {
+        bool ok = true;
+        for (auto& s : st)
+          if (s[d] != s[d + 1] * dims[d + 1]) ok = false;
+        if (ok) {
+          dims[d] *= dims[d + 1];
+          dims.erase(dims.begin() + d + 1);
+          for (auto& s : st) {
+            s[d] = s[d + 1];
+            s.erase(s.begin() + d + 1);
+          }
+        } else {
+          ++d;
+        }
+      }
+    }
+    if (dims.empty()) {
+      dims.push_back(1);
+      for (auto& s : st) s.push_back(0);
+    }
+    if (dims.size() > (size_t)kMaxDims) raise(TK_E_UNSUPPORTED, "iteration space needs more than 4 dims after collapsing");
+    for (size_t v = 0; v < cx.vtab.size(); ++v)
+      for (size_t d = 0; d < dims.size(); ++d) cx.vtab[v].stride[d] = st[v][d];
+    return dims;
+  }
+
+  uint32_t commit_views(ExprCtx& cx) {
+    uint32_t first = (uint32_t)views.size();
+    for (auto& v : cx.vtab) views.push_back(v);
+    if (views.size() > 65000) raise(TK_E_UNSUPPORTED, "too many operand views");
+    return first;
+  }
+  uint32_t commit_code(std::vector<DIns>& code, uint32_t view_base) {
+    uint32_t first = (uint32_t)ins.size();
+    for (auto d : code) {
+      if (d.src == SRC_VIEW || d.op == VM_STORE) d.arg = (uint16_t)(d.arg + view_base);
+      ins.push_back(d);
+    }
+    return first;
+  }
+
+  // --------------------------------------------------------- planning --
+  struct GemmChoice { uint8_t kind; uint8_t tile; uint32_t split, kchunk, tm, tn; };
+
+  GemmChoice choose_gemm(const Op& mm) const {
+    const Spec &A = mm.A(), &B = mm.B();
+    const int64_t m = A.shape[0], k = A.shape[1], n = mm.out.shape[1];
+    GemmChoice g{};
+    if (mm.cls == OC_MM_Q8) {
+      if (m != 1) raise(TK_E_UNSUPPORTED, "int8-weight products support one activation row");
+      g.kind = T_GEMV_Q8;
+      g.tm = 1;
+      g.tn = (uint32_t)((n + 15) / 16);
+      g.split = 1;
+      return g;
+    }
+    const bool mfma_dtype = A.dtype == B.dtype && (A.dtype == DT_BF16 || A.dtype == DT_F16);
+    if (!mfma_dtype || m <= 4 || k <= 8 || n <= 4) {
+      g.kind = T_GEMM_SIMT;
+      g.tile = 0;
+      g.tm = (uint32_t)((m + 63) / 64);
+      g.tn = (uint32_t)((n + 63) / 64);
+      g.split = 1;
+      g.kchunk = (uint32_t)k;
+      return g;
+    }
+    g.kind = T_GEMM_MFMA;
+    const double G = (double)O.num_cus * std::max(1, O.blocks_per_cu);
+    double best = 1e300;
+    const int tiles[2][2] = {{128, 128}, {64, 64}};
+    const double eff[2] = {1.0, 0.55};
+    for (int t = 0; t < 2; ++t) {
+      const int bm = tiles[t][0], bn = tiles[t][1];
+      const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn;
+      for (int S : {1, 2, 4, 8}) {
+        if (O.gemm_split_k > 0 && S != O.gemm_split_k) continue;
+        int64_t kc = ((k + S - 1) / S + 63) / 64 * 64;
+        int64_t Se = (k + kc - 1) / kc;
+        if (Se != S) continue;
+        if (S > 1 && kc < 256 && O.gemm_split_k == 0) continue;
+        double items = (double)(tm * tn * Se);
+        double waves = std::ceil(items / G);
+        double t_us = waves * (2.0 * bm * bn * kc) / (9.8e12 * eff[t]) * 1e6;
+        if (Se > 1) t_us += (double)m * n * Se * 8.0 / 6e12 * 1e6 + 3.0;
+        if (t_us < best - 1e-9) {
+          best = t_us;
+          g.tile = (uint8_t)t;
+          g.split = (uint32_t)Se;
+          g.kchunk = (uint32_t)kc;
+          g.tm = (uint32_t)tm;
+          g.tn = (uint32_t)tn;
+        }
+      }
+    }
+    if (best >= 1e300) raise(TK_E_UNSUPPORTED, "no GEMM tiling for the requested split");
+    return g;
+  }
+
+  // Reduction geometry.
+  struct RedChoice {
+    uint8_t kind;              // T_RED_ROWS / T_RED_COLS
+    std::vector<int> perm;     // iteration order of the source dims
+    int64_t rows, R;           // kept size, reduced size
+    uint32_t parts, kchunk;    // parts per output (rows) / row parts (cols)
+    bool colform;
+  };
+
+  RedChoice choose_reduce(const Op& r) const {
+    const Spec& x = r.args[0].spec;
+    const int rank = (int)x.shape.size();
+    std::vector<bool> red(rank, false);
+    if (r.dims_all) {
+      for (int d = 0; d < rank; ++d) red[d] = true;
+    } else {
+      for (auto d : r.dims) red[((d % rank) + rank) % rank] = true;
+    }
+    RedChoice c{};
+    int64_t kept = 1, rr = 1;
+    for (int d = 0; d < rank; ++d) (red[d] ? rr : kept) *= x.shape[d];
+    c.rows = kept;
+    c.R = rr;
+    // leading-dims reduction -> column form
+    int first_kept = rank;
+    for (int d = 0; d < rank; ++d)
+      if (!red[d]) { first_kept = d; break; }
+    bool prefix = true;
+    for (int d = first_kept; d < rank; ++d)
+      if (red[d]) prefix = false;
+    c.colform = prefix && first_kept > 0 && first_kept < rank;
+    if (c.colform) {
+      c.kind = T_RED_COLS;
+      for (int d = 0; d < rank; ++d) c.perm.push_back(d);
+      int64_t parts = std::min<int64_t>(64, std::max<int64_t>(1, (rr + 127) / 128));
+      int64_t kc = (rr + parts - 1) / parts;
+      parts = (rr + kc - 1) / std::max<int64_t>(1, kc);
+      c.parts = (uint32_t)std::max<int64_t>(1, parts);
+      c.kchunk = (uint32_t)std::max<int64_t>(1, kc);
+    } else {
+      c.kind = T_RED_ROWS;
+      for (int d = 0; d < rank; ++d)
+        if (!red[d]) c.perm.push_back(d);
+      for (int d = 0; d < rank; ++d)
+        if (red[d]) c.perm.push_back(d);
+      int64_t parts = std::min<int64_t>(256, std::max<int64_t>(1, (rr + 4095) / 4096));
+      int64_t kc = ((rr + parts - 1) / parts + 7) / 8 * 8;
+      parts = rr == 0 ? 1 : (rr + kc - 1) / kc;
+      c.parts = (uint32_t)std::max<int64_t>(1, parts);
+      c.kchunk = (uint32_t)std::max<int64_t>(8, kc);
+    }
+    return c;
+  }
+
+  bool two_phase_of(const Entry& e) const {
+    if (e.kind != 0) return false;
+    const Op& o2 = op(e.op);
+    if (o2.cls == OC_MM || o2.cls == OC_MM_Q8) return choose_gemm(o2).split > 1;
+    if (o2.cls == OC_REDUCE) return choose_reduce(o2).parts > 1;
+    return false;
+  }
+
+  void size_scratch() {
+    for (size_t i = 0; i < sched.size(); ++i) {
+      const Entry& e = sched[i];
+      if (!e.two_phase) continue;
+      const Op& o2 = op(e.op);
+      if (o2.cls == OC_REDUCE) {
+        auto rc = choose_reduce(o2);
+        scratch_bytes[(int)i] = (uint64_t)rc.rows * rc.parts * 4;
+      } else {
+        auto g = choose_gemm(o2);
+        scratch_bytes[(int)i] = (uint64_t)g.split * o2.out.numel() * 4;
+      }
+    }
+  }
+
+  // ------------------------------------------------------ task emission --
+  void put(int level, DTask t, const std::string& desc) {
+    if ((int)stage_tasks.size() <= level) {
+      stage_tasks.resize(level + 1);
+      stage_desc.resize(level + 1);
+    }
+    stage_tasks[level].push_back(t);
+    stage_desc[level].push_back(desc);
+  }
+
+  static DTask blank(uint8_t kind) {
+    DTask t;
+    std::memset(&t, 0, sizeof(t));
+    t.kind = kind;
+    t.width = 1;
+    t.ndim = 1;
+    for (int d = 0; d < kMaxDims; ++d) t.dims[d] = 1;
+    return t;
+  }
+
+  static uint32_t ew_items(int64_t numel) { return (uint32_t)std::max<int64_t>(1, (numel + 2047) / 2048); }
+
+  void emit_pointwise(const Entry& e) {
+    const Op& o2 = op(e.op);
+    ExprCtx cx;
+    vstride_full.clear();
+    cx.space = o2.out.shape;
+    std::vector<int> map(cx.space.size());
+    for (size_t d = 0; d < map.size(); ++d) map[d] = (int)d;
+    Node root = op_node(cx, e.op, map);
+    std::vector<DIns> code;
+    emit(code, root, 0);
+    emit_store(code, cx, o2.out.buf, map);
+    auto dims = collapse(cx);
+    DTask t = blank(T_EW);
+    t.ndim = (uint8_t)dims.size();
+    for (size_t d = 0; d < dims.size(); ++d) t.dims[d] = (uint32_t)dims[d];
+    t.width = (dims.back() % 8 == 0) ? 8 : 1;
+    uint32_t vb = commit_views(cx);
+    t.expr_first = commit_code(code, vb);
+    t.expr_len = (uint32_t)code.size();
+    t.n_items = o2.out.numel() == 0 ? 0 : ew_items(o2.out.numel());
+    put(e.level, t, o2.name + " (" + o2.opcode + ")");
+  }
+
+  // Output copy or staged commit: read the value through the output view,
+  // convert to the output dtype, write the destination contiguously.
+  void emit_copy(const Entry& e) {
+    const Spec& o2 = P.outputs[e.slot];
+    ExprCtx cx;
+    vstride_full.clear();
+    cx.space = o2.shape;
+    std::vector<int> map(cx.space.size());
+    for (size_t d = 0; d < map.size(); ++d) map[d] = (int)d;
+    std::vector<DIns> code;
+    DIns ld{};
+    ld.op = VM_LOAD;
+    ld.src = SRC_VIEW;
+    ld.rnd = RND_NONE;
+    ld.arg = (uint16_t)cx.vtab.size();
+    Spec src = o2;
+    Loc sl = storage_of(o2.buf);
+    src.dtype = sl.dtype;
+    cx.vtab.push_back(lift(src, map, sl, cx.space.size()));
+    code.push_back(ld);
+    Spec dst = o2;
+    dst.strides.clear();
+    int64_t acc = 1;
+    dst.strides.resize(o2.shape.size());
+    for (size_t i = o2.shape.size(); i-- > 0;) {
+      dst.strides[i] = acc;
+      acc *= o2.shape[i];
+    }
+    dst.offset = 0;
+    Loc dl;
+    dl.base = n_in + e.slot;
+    dl.offset = 0;
+    dl.dtype = o2.dtype;
+    DIns st{};
+    st.op = VM_STORE;
+    st.rnd = RND_NONE;
+    st.arg = (uint16_t)cx.vtab.size();
+    cx.vtab.push_back(lift(dst, map, dl, cx.space.size()));
+    code.push_back(st);
+    auto dims = collapse(cx);
+    DTask t = blank(T_EW);
+    t.ndim = (uint8_t)dims.size();
+    for (size_t d = 0; d < dims.size(); ++d) t.dims[d] = (uint32_t)dims[d];
+    t.width = (dims.back() % 8 == 0) ? 8 : 1;
+    uint32_t vb = commit_views(cx);
+    t.expr_first = commit_code(code, vb);
+    t.expr_len = (uint32_t)code.size();
+    t.n_items = o2.numel() == 0 ? 0 : ew_items(o2.numel());
+    put(e.level, t, std::string(e.kind == 2 ? "commit" : "copy") + " out[" + std::to_string(e.slot) + "] <- " + o2.buf);
+  }
+
+  // Epilogue of a contraction tile, over the [m, n] output space.
+  void build_epilogue(const Entry& e, ExprCtx& cx, std::vector<DIns>& code) {
+    const Op& mm = op(e.op);
+    std::vector<int> map = {0, 1};
+    // root = alpha*acc + beta*bias (addmm forms), rounded to the root dtype
+    const uint8_t rrnd = mm.out.dtype == DT_F32 ? RND_NONE : mm.out.dtype;
+    if (mm.has_bias()) {
+      float alpha = mm.attr("alpha", 1.0f), beta = mm.attr("beta", 1.0f);
+      if (alpha == 0.0f && beta == 0.0f) {
+        DIns z{};
+        z.op = VM_ZERO;
+        z.rnd = rrnd;
+        code.push_back(z);
+      } else if (beta == 0.0f) {
+        DIns s{};
+        s.op = VM_SCALE;
+        s.a = alpha;
+        s.rnd = rrnd;
+        code.push_back(s);
+      } else if (alpha == 0.0f) {
+        Node b = operand_node(cx, mm.args[0], map);
+        emit(code, b, 1);
+        DIns s{};
+        s.op = VM_SCALE;
+        s.a = beta;
+        s.rnd = rrnd;
+        code.push_back(s);
+      } else {
+        DIns s{};
+        s.op = VM_SCALE;
+        s.a = alpha;
+        s.rnd = RND_NONE;
+        code.push_back(s);
+        Node b = operand_node(cx, mm.args[0], map);
+        if (simple(b)) {
+          DIns ad{};
+          ad.op = VM_ADD;
+          ad.a = beta;
+          ad.rnd = rrnd;
+          set_src(ad, b);
+          code.push_back(ad);
+        } else {
+          DIns sv{};
+          sv.op = VM_SAVE;
+          sv.arg = 0;
+          sv.rnd = RND_NONE;
+          code.push_back(sv);
+          emit(code, b, 1);  // bias expression
+          DIns ad{};
+          ad.op = VM_ADD;  // acc(bias) ; slot0 + beta*acc
+          ad.a = beta;
+          ad.rev = 1;
+          ad.src = SRC_SLOT;
+          ad.arg = 0;
+          ad.rnd = rrnd;
+          code.push_back(ad);
+        }
+      }
+    } else if (rrnd != RND_NONE) {
+      DIns s{};
+      s.op = VM_SCALE;
+      s.a = 1.0f;
+      s.rnd = rrnd;
+      code.push_back(s);
+    }
+    if (!e.side.empty()) {
+      // root in slot 0; each descendant computed from tile values
+      DIns sv{};
+      sv.op = VM_SAVE;
+      sv.arg = 0;
+      sv.rnd = RND_NONE;
+      code.push_back(sv);
+      cx.slot_of[mm.out.buf] = 0;
+      if (!e.discard_root) emit_store(code, cx, mm.out.buf, map);
+      int next = 1;
+      for (size_t i = 0; i < e.side.size(); ++i) {
+        int c = e.side[i];
+        Node n = op_node(cx, c, map);
+        emit(code, n, next + 1);
+        const std::string& ob = op(c).out.buf;
+        if (output_bufs.count(ob)) emit_store(code, cx, ob, map);
+        if (i + 1 < e.side.size()) {
+          DIns s2{};
+          s2.op = VM_SAVE;
+          s2.arg = (uint16_t)next;
+          s2.rnd = RND_NONE;
+          code.push_back(s2);
+          cx.slot_of[ob] = next++;
+        }
+      }
+      return;
+    }
+    std::string cur = mm.out.buf;
+    for (int c : e.chain) {
+      DIns sv{};
+      sv.op = VM_SAVE;
+      sv.arg = 0;
+      sv.rnd = RND_NONE;
+      code.push_back(sv);
+      cx.slot_of.clear();
+      cx.slot_of[cur] = 0;
+      Node n = op_node(cx, c, map);
+      emit(code, n, 1);
+      cur = op(c).out.buf;
+    }
+    cx.slot_of.clear();
+    emit_store(code, cx, cur, map);
+  }
+
+  DView operand_view(const Spec& s, int d0, int d1) {
+    // A rank-two operand: stride[0] along its first index, stride[1] along its second.
+    Loc l = storage_of(s.buf);
+    DView v{};
+    v.base = (uint16_t)l.base;
+    v.dtype = s.dtype;
+    v.offset = l.offset + s.offset;
+    v.stride[0] = s.strides[d0];
+    v.stride[1] = s.strides[d1];
+    return v;
+  }
+
+  void emit_contraction(size_t si) {
+    const Entry& e = sched[si];
+    const Op& mm = op(e.op);
+    const Spec &A = mm.A(), &B = mm.B();
+    const int64_t m = A.shape[0], k = A.shape[1], n = mm.out.shape[1];
+    GemmChoice g = choose_gemm(mm);
+    ExprCtx cx;
+    vstride_full.clear();
+    cx.space = {m, n};
+    std::vector<DIns> code;
+    build_epilogue(e, cx, code);
+    // no collapsing: epilogues address (row, col)
+    for (size_t v = 0; v < cx.vtab.size(); ++v) {
+      cx.vtab[v].stride[0] = vstride_full[v][0];
+      cx.vtab[v].stride[1] = vstride_full[v][1];
+    }
+    DTask t = blank(g.kind);
+    t.ndim = 2;
+    t.dims[0] = (uint32_t)m;
+    t.dims[1] = (uint32_t)n;
+    t.m = (uint32_t)m;
+    t.n = (uint32_t)n;
+    t.k = (uint32_t)k;
+    t.tile = g.tile;
+    t.split = g.split;
+    t.kchunk = g.kchunk;
+    t.tiles_m = g.tm;
+    t.tiles_n = g.tn;
+    t.width = (n % 8 == 0) ? 8 : 1;
+    // operand views go first in this task's view block
+    std::vector<DView> ops;
+    if (g.kind == T_GEMV_Q8) {
+      ops.push_back(operand_view(A, 0, 1));       // x over (row, k)
+      ops.push_back(operand_view(B, 0, 1));       // q over (n, k)
+      ops.push_back(operand_view(mm.S(), 0, 1));  // s over (n, block)
+    } else {
+      ops.push_back(operand_view(A, 0, 1));  // A over (m, k)
+      ops.push_back(operand_view(B, 0, 1));  // B over (k, n)
+    }
+    uint32_t vbase = (uint32_t)views.size();
+    for (auto& v : ops) views.push_back(v);
+    t.va = (uint16_t)vbase;
+    t.vb = (uint16_t)(vbase + 1);
+    t.vs = (uint16_t)(vbase + (ops.size() > 2 ? 2 : 1));
+    uint32_t vb = commit_views(cx);
+    uint32_t code_first = commit_code(code, vb);
+    std::string desc = mm.name + " (" + mm.opcode + " " + std::to_string(m) + "x" + std::to_string(k) + "x" +
+                       std::to_string(n) + ")";
+    if (!e.chain.empty()) {
+      desc += e.update ? " +update" : " +epilogue";
+      for (int c : e.chain) desc += " " + op(c).name;
+    }
+    if (!e.side.empty()) {
+      desc += " +side";
+      for (int c : e.side) desc += " " + op(c).name;
+      if (e.discard_root) desc += " (root discarded)";
+    }
+    if (g.split > 1) {
+      DTask p1 = t;
+      p1.flags |= F_PARTIAL;
+      p1.scratch = scratch_off.at((int)si);
+      p1.n_items = g.tm * g.tn * g.split;
+      p1.expr_first = 0;
+      p1.expr_len = 0;
+      put(e.level, p1, desc + " [split-K " + std::to_string(g.split) + " partials]");
+      DTask p2 = blank(T_GEMM_REDUCE);
+      p2.ndim = 2;
+      p2.dims[0] = (uint32_t)m;
+      p2.dims[1] = (uint32_t)n;
+      p2.m = (uint32_t)m;
+      p2.n = (uint32_t)n;
+      p2.split = g.split;
+      p2.scratch = p1.scratch;
+      p2.width = (n % 8 == 0) ? 8 : 1;
+      p2.expr_first = code_first;
+      p2.expr_len = (uint32_t)code.size();
+      p2.n_items = ew_items(m * n);
+      put(e.level + 1, p2, desc + " [split-K reduce + epilogue]");
+    } else {
+      t.expr_first = code_first;
+      t.expr_len = (uint32_t)code.size();
+      t.n_items = (m * n == 0) ? 0 : g.tm * g.tn;
+      put(e.level, t, desc);
+    }
+    if (g.kind == T_GEMM_MFMA) st.matrix_core_ops++;
+  }
+
+  void emit_reduction(size_t si) {
+    const Entry& e = sched[si];
+    const Op& r = op(e.op);
+    RedChoice rc = choose_reduce(r);
+    const Spec& x = r.args[0].spec;
+    // source expression over the permuted source space
+    ExprCtx cx;
+    vstride_full.clear();
+    for (int d : rc.perm) cx.space.push_back(x.shape[d]);
+    // map from the source op's own dims to the permuted task dims
+    std::vector<int> map(x.shape.size());
+    for (size_t i = 0; i < rc.perm.size(); ++i) map[rc.perm[i]] = (int)i;
+    Node src = operand_node(cx, r.args[0], map);
+    std::vector<DIns> code;
+    emit(code, src, 0);
+    // collapse kept and reduced parts separately
+    std::vector<int64_t> dims;
+    {
+      // Collapse within the kept group and within the reduced group only.
+      std::vector<int64_t> full = cx.space;
+      // number of leading (permuted) dims in the first group: the reduced
+      // prefix for the column form, the kept dims for the row form
+      const int rank = (int)x.shape.size();
+      std::vector<bool> red(rank, r.dims_all);
+      for (auto dd : r.dims) red[((dd % rank) + rank) % rank] = true;
+      int split_at = 0;
+      for (int d = 0; d < rank; ++d)
+        if (red[d] == rc.colform) split_at++;
+      auto group = [&](int lo, int hi, std::vector<int64_t>& gd, std::vector<std::vector<int64_t>>& gs) {
+        for (int d = lo; d < hi; ++d) {
+          if (full[d] == 1) continue;
+          if (!gd.empty()) {
+            bool ok = true;
+            for (size_t v = 0; v < vstride_full.size(); ++v)
+              if (gs[v].back() != vstride_full[v][d] * full[d]) ok = false;
+            if (ok) {
+              gd.back() *= full[d];
+              for (size_t v = 0; v < vstride_full.size(); ++v) gs[v].back() = vstride_full[v][d];
+              continue;
+            }
+          }
+          gd.push_back(full[d]);
+          for (size_t v = 0; v < vstride_full.size(); ++v) gs[v].push_back(vstride_full[v][d]);
+        }
+        if (gd.empty()) {
+          gd.push_back(1);
+          for (size_t v = 0; v < vstride_full.size(); ++v) gs[v].push_back(0);
+        }
+      };
+      std::vector<int64_t> g1, g2;
+      std::vector<std::vector<int64_t>> s1(vstride_full.size()), s2(vstride_full.size());
+      group(0, split_at, g1, s1);
+      group(split_at, (int)full.size(), g2, s2);
+      if (g1.size() + g2.size() > (size_t)kMaxDims) raise(TK_E_UNSUPPORTED, "reduction needs more than 4 iteration dims");
+      dims = g1;
+      dims.insert(dims.end(), g2.begin(), g2.end());
+      for (size_t v = 0; v < cx.vtab.size(); ++v) {
+        size_t d = 0;
+        for (auto s : s1[v]) cx.vtab[v].stride[d++] = s;
+        for (auto s : s2[v]) cx.vtab[v].stride[d++] = s;
+        for (; d < (size_t)kMaxDims; ++d) cx.vtab[v].stride[d] = 0;
+      }
+    }
+    uint32_t vb = commit_views(cx);
+    uint32_t src_first = commit_code(code, vb);
+    // finishing program over the output (1-D of `rows`)
+    ExprCtx fx;
+    vstride_full.clear();
+    fx.space = {rc.rows};
+    std::vector<DIns> fin;
+    if (r.opcode == "mean") {
+      DIns dv{};
+      dv.op = VM_DIV;
+      dv.src = SRC_SCALAR;
+      dv.s = (float)rc.R;
+      dv.rnd = RND_NONE;
+      fin.push_back(dv);
+    }
+    if (r.out.dtype != DT_F32) {
+      DIns s{};
+      s.op = VM_SCALE;
+      s.a = 1.0f;
+      s.rnd = r.out.dtype;
+      fin.push_back(s);
+    }
+    {
+      Spec flat = r.out;
+      flat.shape = {rc.rows};
+      flat.strides = {1};
+      DIns stv{};
+      stv.op = VM_STORE;
+      stv.rnd = RND_NONE;
+      stv.arg = (uint16_t)fx.vtab.size();
+      std::vector<int> m1 = {0};
+      fx.vtab.push_back(lift(flat, m1, storage_of(r.out.buf), 1));
+      fin.push_back(stv);
+      fx.vtab.back().stride[0] = vstride_full.back()[0];
+    }
+    uint32_t fvb = commit_views(fx);
+    uint32_t fin_first = commit_code(fin, fvb);
+    DTask t = blank(rc.kind);
+    t.ndim = (uint8_t)dims.size();
+    for (size_t d = 0; d < dims.size(); ++d) t.dims[d] = (uint32_t)dims[d];
+    t.expr_first = src_first;
+    t.expr_len = (uint32_t)code.size();
+    t.fin_first = fin_first;
+    t.fin_len = (uint32_t)fin.size();
+    t.split = rc.parts;
+    t.kchunk = rc.kchunk;
+    t.count = (float)rc.R;
+    t.m = (uint32_t)rc.rows;
+    t.k = (uint32_t)rc.R;
+    if (r.opcode == "mean") t.flags |= F_MEAN;
+    std::string desc = r.name + " (" + r.opcode + " " + std::to_string(rc.rows) + " outputs over " + std::to_string(rc.R) + ")";
+    if (rc.kind == T_RED_COLS) {
+      t.width = (rc.rows % 8 == 0) ? 8 : 1;
+      const uint32_t cols_per_item = 32u * t.width;
+      t.tiles_n = (uint32_t)((rc.rows + cols_per_item - 1) / cols_per_item);
+      t.n_items = rc.rows == 0 ? 0 : t.tiles_n * rc.parts;
+    } else {
+      t.width = (dims.back() % 8 == 0 && rc.R % 8 == 0) ? 8 : 1;
+      t.n_items = (uint32_t)(rc.rows * rc.parts);
+    }
+    if (rc.parts > 1) {
+      t.flags |= F_PARTIAL;
+      t.scratch = scratch_off.at((int)si);
+      put(e.level, t, desc + " [" + std::to_string(rc.parts) + " partials]");
+      DTask f = blank(T_RED_FINAL);
+      f.m = (uint32_t)rc.rows;
+      f.split = rc.parts;
+      f.scratch = t.scratch;
+      f.fin_first = fin_first;
+      f.fin_len = (uint32_t)fin.size();
+      f.count = t.count;
+      f.flags = t.flags & F_MEAN;
+      f.tile = rc.kind == T_RED_COLS ? 1 : 0;  // partial layout: [parts][rows] (cols) or [rows][parts]
+      f.n_items = (uint32_t)((rc.rows + kBlock - 1) / kBlock);
+      put(e.level + 1, f, desc + " [combine]");
+    } else {
+      put(e.level, t, desc);
+    }
+  }
+
+  // Safety net: no two tasks of a stage may touch overlapping regions unless
+  // both only read (the pages' read/write hazard rule).
+  void check_hazards() {
+    struct R { int space; uint64_t lo, hi; };
+    auto space_of = [&](int base) -> int {
+      if (base >= n_in && base < n_in + n_out) {
+        auto it = direct.find(base - n_in);
+        if (it != direct.end()) return it->second;  // same memory as the input
+      }
+      return base;
+    };
+    std::map<int, std::vector<std::pair<std::vector<R>, std::vector<R>>>> per_level;
+    std::map<int, std::vector<std::string>> per_level_name;
+    std::map<std::string, const Entry*> writer;
+    for (auto& e : sched)
+      for (auto& w : e.writes_vals) writer[w] = &e;
+    auto value_region = [&](const std::string& v) -> R {
+      if (is_input(v)) return {input_idx[v], 0, ~0ull};
+      const Loc& l = loc.at(v);
+      if (l.base == ws_base) {
+        uint64_t off = kHeaderBytes + arena_off.at(v);
+        const Spec& pv = op(prod(v)).out;
+        return {ws_base, off, off + std::max<uint64_t>(1, pv.numel() * dtype_size(pv.dtype))};
+      }
+      return {space_of(l.base), 0, ~0ull};
+    };
+    for (size_t i = 0; i < sched.size(); ++i) {
+      const Entry& e = sched[i];
+      std::vector<R> rd, wr;
+      for (auto& v : e.reads_vals) rd.push_back(value_region(v));
+      for (auto& t : e.reads_inputs) rd.push_back({input_idx[t], 0, ~0ull});
+      for (auto& w : e.writes_vals) wr.push_back(value_region(w));
+      if (e.kind != 0) wr.push_back({space_of(n_in + e.slot), 0, ~0ull});
+      if (e.kind == 2) wr.push_back({e.writes_input, 0, ~0ull});
+      const std::string nm = e.kind == 0 ? op(e.op).name : ("out[" + std::to_string(e.slot) + "]");
+      if (e.two_phase) {
+        // phase 1 reads the operands and writes fp32 partials; phase 2 reads
+        // the partials (and epilogue operands) and writes the values
+        R s{ws_base, scratch_off.at((int)i), scratch_off.at((int)i) + scratch_bytes.at((int)i)};
+        per_level[e.level].push_back({rd, {s}});
+        per_level_name[e.level].push_back(nm);
+        std::vector<R> rd2 = rd;
+        rd2.push_back(s);
+        per_level[e.level + 1].push_back({rd2, wr});
+        per_level_name[e.level + 1].push_back(nm);
+      } else {
+        per_level[e.level].push_back({rd, wr});
+        per_level_name[e.level].push_back(nm);
+      }
+    }
+    auto ov = [](const R& a, const R& b) { return a.space == b.space && a.lo < b.hi && b.lo < a.hi; };
+    for (auto& kv : per_level) {
+      auto& v = kv.second;
+      for (size_t a = 0; a < v.size(); ++a)
+        for (size_t b = 0; b < v.size(); ++b) {
+          if (a == b) continue;
+          for (auto& w : v[a].second) {
+            const std::string who = per_level_name[kv.first][a] + " vs " + per_level_name[kv.first][b];
+            for (auto& w2 : v[b].second)
+              if (ov(w, w2)) raise(TK_E_ARG, "internal: write/write hazard inside stage " + std::to_string(kv.first) + ": " + who);
+            for (auto& r2 : v[b].first)
+              if (ov(w, r2)) raise(TK_E_ARG, "internal: read/write hazard inside stage " + std::to_string(kv.first) + ": " + who);
+          }
+        }
+    }
+  }
+
+  Plan run() {
+    if (O.fuse_epilogues) {
+      pass1();
+      pass2();
+    }
+    choose_inline();
+    build_schedule();
+    prove_direct();
+    pass3();
+    bind_outputs();
+    add_copies_and_commits();
+    for (size_t i = 0; i < sched.size(); ++i) {
+      sched[i].order = (int)i;
+      sched[i].two_phase = two_phase_of(sched[i]);
+    }
+    collect_rw();
+    level();
+    size_scratch();
+    plan_arena();
+    check_hazards();
+    for (size_t i = 0; i < sched.size(); ++i) {
+      const Entry& e = sched[i];
+      if (e.kind != 0) {
+        emit_copy(e);
+        continue;
+      }
+      const Op& o2 = op(e.op);
+      if (o2.cls == OC_POINTWISE)
+        emit_pointwise(e);
+      else if (o2.cls == OC_REDUCE)
+        emit_reduction(i);
+      else
+        emit_contraction(i);
+    }
+    return encode();
+  }
+
+  Plan encode() {
+    Plan pl;
+    pl.n_in = n_in;
+    pl.n_out = n_out;
+    pl.ws_base = ws_base;
+    pl.inputs = P.inputs;
+    pl.outputs = P.outputs;
+    pl.inplace = P.inplace;
+    // drop empty levels
+    std::vector<std::vector<DTask>> stages;
+    std::vector<std::vector<std::string>> descs;
+    for (size_t L = 0; L < stage_tasks.size(); ++L) {
+      if (stage_tasks[L].empty()) continue;
+      stages.push_back(stage_tasks[L]);
+      descs.push_back(stage_desc[L]);
+    }
+    std::vector<DStage> ds;
+    std::vector<DTask> dt;
+    int max_items = 0;
+    std::ostringstream dump;
+    for (size_t s = 0; s < stages.size(); ++s) {
+      DStage d{};
+      d.task_first = (uint32_t)dt.size();
+      d.n_tasks = (uint32_t)stages[s].size();
+      uint32_t items = 0;
+      dump << "stage " << s << ":\n";
+      for (size_t t = 0; t < stages[s].size(); ++t) {
+        DTask task = stages[s][t];
+        task.item_begin = items;
+        items += task.n_items;
+        dt.push_back(task);
+        dump << "  " << kind_name(task.kind) << " items=" << task.n_items << " : " << descs[s][t] << "\n";
+      }
+      d.n_items = items;
+      max_items = std::max<int>(max_items, (int)items);
+      ds.push_back(d);
+    }
+    dump << "workspace: " << kHeaderBytes << " header + " << arena_bytes << " arena bytes\n";
+    for (auto& kv : arena_off) dump << "  arena " << kv.first << " @" << kv.second << "\n";
+    for (auto& kv : bound) dump << "  bound " << kv.first << " -> out[" << kv.second << "]\n";
+    for (auto& kv : direct) dump << "  direct in-place out[" << kv.first << "] -> in[" << kv.second << "]\n";
+    // serialize
+    DHeader h{};
+    h.magic = kPlanMagic;
+    h.n_stages = (uint32_t)ds.size();
+    h.n_tasks = (uint32_t)dt.size();
+    h.n_views = (uint32_t)views.size();
+    h.n_ins = (uint32_t)ins.size();
+    uint32_t off = (uint32_t)align_up(sizeof(DHeader), 64);
+    h.off_stages = off;
+    off = (uint32_t)align_up(off + ds.size() * sizeof(DStage), 64);
+    h.off_tasks = off;
+    off = (uint32_t)align_up(off + dt.size() * sizeof(DTask), 64);
+    h.off_views = off;
+    off = (uint32_t)align_up(off + views.size() * sizeof(DView), 64);
+    h.off_ins = off;
+    off = (uint32_t)align_up(off + ins.size() * sizeof(DIns), 64);
+    h.bytes = off;
+    pl.bytes.assign(off, 0);
+    std::memcpy(pl.bytes.data(), &h, sizeof(h));
+    if (!ds.empty()) std::memcpy(pl.bytes.data() + h.off_stages, ds.data(), ds.size() * sizeof(DStage));
+    if (!dt.empty()) std::memcpy(pl.bytes.data() + h.off_tasks, dt.data(), dt.size() * sizeof(DTask));
+    if (!views.empty()) std::memcpy(pl.bytes.data() + h.off_views, views.data(), views.size() * sizeof(DView));
+    if (!ins.empty()) std::memcpy(pl.bytes.data() + h.off_ins, ins.data(), ins.size() * sizeof(DIns));
+    pl.n_stages = (int)ds.size();
+    pl.max_items = max_items;
+    pl.workspace_bytes = kHeaderBytes + align_up(arena_bytes, kAlign);
+    pl.dump = dump.str();
+    // statistics
+    tk_stats& s = pl.stats;
+    s = st;
+    s.workspace_bytes = pl.workspace_bytes;
+    s.n_stages = (int32_t)ds.size();
+    s.grid_barriers = std::max(0, (int32_t)ds.size() - 1);
+    s.n_tasks = (int32_t)dt.size();
+    s.inlined_ops = (int32_t)inlined.size();
+    int mat = 0, fe = 0, se = 0, fu = 0;
+    for (auto& e : sched) {
+      if (e.kind != 0) continue;
+      mat++;
+      if (!e.chain.empty() && !e.update) fe++;
+      if (!e.side.empty()) se++;
+      if (e.update) fu++;
+    }
+    s.materialized_ops = mat;
+    s.fused_epilogues = fe;
+    s.side_epilogues = se;
+    s.fused_updates = fu;
+    s.direct_outputs = (int32_t)bound.size();
+    s.direct_state_commits = (int32_t)direct.size();
+    s.staged_commits = (int32_t)(P.inplace.size() - direct.size());
+    s.max_work_items = max_items;
+    s.num_cus = O.num_cus;
+    return pl;
+  }
+};
+
+}  // namespace
+
+Plan schedule_program(const Program& p, const Options& o) {
+  Builder b(p, o);
+  return b.run();
+}
+
+}  // namespace tk

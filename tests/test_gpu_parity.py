@@ -1,0 +1,264 @@
+"""GPU parity of the persistent kernel against the CPU oracle (needs gfx950).
+
+Each test prints its case before touching the GPU.  Sizes span several tiles
+and ragged tails; pointwise-only work is compared bit for bit, contractions
+and reductions under the tolerance classes of tests/parity.py, whole steps
+per node with teacher forcing, and fused vs unfused schedules bitwise.
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from persistent_whole_step_amd import programs, synth
+from persistent_whole_step_amd.programs import Program
+
+from . import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print("[case]", *a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from persistent_whole_step_amd import tk
+    tk.lib()
+
+
+# ------------------------------------------------------------ pointwise --
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
+@pytest.mark.parametrize("shape", [(3, 5), (64, 96), (257, 1000), (7,)])
+def test_pointwise_chain_bitexact(oracle_mod, dtype, shape):
+    say("pointwise", dtype, shape)
+    rng = np.random.default_rng(hash((dtype, shape)) % 2 ** 32)
+    p = Program()
+    a = p.input("a", dtype, shape)
+    b = p.input("b", dtype, shape)
+    r = p.input("r", dtype, shape[-1:])
+    t1 = p.op("add", [a, b], dtype, alpha=0.375)
+    t2 = p.op("mul", [t1, r], dtype)
+    t3 = p.op("sub", [t2, a], "f32", alpha=1.5)
+    t4 = p.op("div", [t3, b], dtype)
+    t5 = p.op("relu", [t4], dtype)
+    t6 = p.op("threshold_backward", [t2, a], dtype, threshold=0.0)
+    t7 = p.op("pow", [t6, 2.0], "f32")
+    t8 = p.op("neg", [t7], dtype)
+    p.output(t5)
+    p.output(t8)
+    p.output(p.op("cast", [t3], "bf16"))
+    ins = [synth.random_tensor(rng, shape, dtype), synth.random_tensor(rng, shape, dtype),
+           synth.random_tensor(rng, shape[-1:], dtype)]
+    want = oracle_mod.run(p.text(), ins)
+    got, _ = parity.gpu_run(p, ins)
+    for g, w, s in zip(got, want, p.outputs):
+        parity.assert_bitexact(g, w, s.dtype, s.buf)
+
+
+def test_pointwise_special_values(oracle_mod):
+    say("pointwise special values")
+    vals = np.array([-0.0, 0.0, np.nan, np.inf, -np.inf, 1e-40, -1e-40, 3.0e38, -2.5, 65520.0, 1.0 + 2 ** -8,
+                     2.0 ** -25, 6e-5, -7e-6, 1.0, -1.0], np.float32)
+    p = Program()
+    x = p.input("x", "f32", (16,))
+    y = p.input("y", "f32", (16,))
+    p.output(p.op("relu", [x], "f32"))
+    p.output(p.op("threshold_backward", [y, x], "f32", threshold=0.0))
+    p.output(p.op("cast", [x], "bf16"))
+    p.output(p.op("cast", [x], "f16"))
+    p.output(p.op("div", [y, x], "f32"))
+    p.output(p.op("mul", [x, x], "bf16"))
+    p.output(p.op("add", [x, y], "f16", alpha=3.0))
+    ins = [vals, vals[::-1].copy()]
+    want = oracle_mod.run(p.text(), ins)
+    got, _ = parity.gpu_run(p, ins)
+    for g, w, s in zip(got, want, p.outputs):
+        parity.assert_bitexact(g, w, s.dtype, s.buf)
+
+
+def test_views_broadcast_and_output_copies(oracle_mod):
+    say("views / broadcast / copies")
+    rng = np.random.default_rng(3)
+    p = Program()
+    m = p.input("m", "f32", (33, 40))
+    c = p.input("c", "f32", (33, 1))
+    s = p.op("add", [m.T, 1.0], "f32", shape=(40, 33))
+    q = p.op("mul", [m, c], "bf16")
+    p.output(s)
+    p.output(q)
+    p.outputs.append(programs.Spec(q.buf, "f32", (40, 33), (1, 40), 0))  # transposed view, widened
+    p.outputs.append(programs.Spec(m.buf, "f16", (33, 20), (40, 2), 1))  # strided input view
+    p.output(p.op("full", [], "f16", shape=(5, 3), value=-1.25))
+    ins = [synth.random_tensor(rng, (33, 40), "f32"), synth.random_tensor(rng, (33, 1), "f32")]
+    want = oracle_mod.run(p.text(), ins)
+    got, _ = parity.gpu_run(p, ins)
+    for g, w, sp in zip(got, want, p.outputs):
+        parity.assert_bitexact(g, w, sp.dtype, sp.buf)
+
+
+# ----------------------------------------------------------- reductions --
+
+@pytest.mark.parametrize("shape,dims,op", [
+    ((64, 10), [0], "sum"), ((256, 1024), [0], "sum"), ((1000, 37), [0], "sum"),
+    ((640,), None, "mean"), ((300000,), None, "sum"), ((512, 2048), None, "mean"),
+    ((7, 9, 11), [1], "sum"), ((6, 5, 4), [-1, 0], "mean"), ((0, 4), [0], "sum"), ((129, 3), [1], "sum")])
+def test_reductions(oracle_mod, shape, dims, op):
+    say("reduction", shape, dims, op)
+    rng = np.random.default_rng(5)
+    p = Program()
+    x = p.input("x", "f32", shape)
+    nd = len(shape)
+    red = set(range(nd)) if dims is None else {d % nd for d in dims}
+    out_shape = tuple(s for i, s in enumerate(shape) if i not in red)
+    sq = p.op("pow", [x, 2.0], "f32")
+    r = p.op(op, [sq], "f32", out_shape, dims=dims)
+    p.output(r)
+    p.output(p.op(op, [x], "bf16", out_shape, dims=dims))
+    ins = [synth.random_tensor(rng, shape, "f32")]
+    got, _ = parity.gpu_run(p, ins)
+    want = oracle_mod.run(p.text(), ins)
+    vals = {"x": ins[0], sq.buf: want[0] * 0}  # placeholder, replaced below
+    sqv = (ins[0].astype(np.float32) * ins[0].astype(np.float32)).astype(np.float32)
+    vals[sq.buf] = sqv
+    for j, (g, w) in enumerate(zip(got, want)):
+        opj = p.ops[1] if j == 0 else p.ops[2]
+        exact, mag = parity.reduction_reference(opj, vals)
+        parity.assert_contraction(g.reshape(out_shape), w.reshape(out_shape), exact, mag, opj.out.dtype, opj.name)
+
+
+# --------------------------------------------------------- contractions --
+
+def _mm_case(oracle_mod, m, k, n, dtype, ta=False, tb=False, bias=True, seed=0, chain=False, **opts):
+    rng = np.random.default_rng(seed)
+    p = Program()
+    A = p.input("A", dtype, (k, m) if ta else (m, k))
+    B = p.input("B", dtype, (n, k) if tb else (k, n))
+    av = A.T if ta else A
+    bv = B.T if tb else B
+    if bias:
+        bi = p.input("bias", dtype, (n,))
+        y = p.op("addmm", [bi, av, bv], dtype, (m, n), alpha=1.0, beta=1.0)
+    else:
+        y = p.op("mm", [av, bv], dtype, (m, n))
+    if chain:
+        z = p.op("relu", [y], dtype)
+        p.output(z)
+    else:
+        p.output(y)
+    ins = [synth.random_tensor(rng, (k, m) if ta else (m, k), dtype),
+           synth.random_tensor(rng, (n, k) if tb else (k, n), dtype)]
+    if bias:
+        ins.append(synth.random_tensor(rng, (n,), dtype))
+    got, prog = parity.gpu_run(p, ins, **opts)
+    want = oracle_mod.run(p.text(), ins)
+    vals = {"A": ins[0], "B": ins[1]}
+    if bias:
+        vals["bias"] = ins[2]
+    exact, mag = parity.contraction_reference(p.ops[0], vals, None)
+    if chain:
+        exact = np.maximum(exact, 0)
+    parity.assert_contraction(got[0], want[0], exact, mag, dtype, f"mm {m}x{k}x{n} {dtype} ta={ta} tb={tb}")
+    return got, want, prog
+
+
+@pytest.mark.parametrize("m,k,n", [(64, 128, 256), (64, 256, 10), (5, 7, 3), (130, 70, 65)])
+@pytest.mark.parametrize("ta,tb", [(False, False), (True, False), (False, True)])
+def test_fp32_contraction_bitexact(oracle_mod, m, k, n, ta, tb):
+    """The fp32 tile accumulates each output sequentially in k with fma, the
+    oracle's definition, so results agree bit for bit."""
+    say("fp32 mm", m, k, n, ta, tb)
+    got, want, _ = _mm_case(oracle_mod, m, k, n, "f32", ta, tb, seed=m + k + n)
+    parity.assert_bitexact(got[0], want[0], "f32", "fp32 mm")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("m,k,n,ta,tb", [
+    (256, 512, 1024, False, False), (200, 136, 72, False, False), (64, 64, 64, True, False),
+    (1024, 256, 64, True, False), (256, 64, 1024, False, True), (130, 100, 250, True, True),
+    (33, 520, 17, False, False)])
+def test_mfma_contraction(oracle_mod, dtype, m, k, n, ta, tb):
+    say("mfma mm", dtype, m, k, n, ta, tb)
+    _mm_case(oracle_mod, m, k, n, dtype, ta, tb, seed=m * 7 + n, chain=(m % 2 == 0))
+
+
+@pytest.mark.parametrize("split", [2, 4])
+def test_mfma_split_k(oracle_mod, split):
+    say("mfma split-K", split)
+    _mm_case(oracle_mod, 192, 1024, 320, "bf16", False, False, seed=split, gemm_split_k=split)
+
+
+@pytest.mark.parametrize("k,n", [(4096, 64), (96, 40), (1000, 24), (64, 7)])
+def test_gemv_q8(oracle_mod, k, n):
+    say("gemv q8", k, n)
+    rng = np.random.default_rng(k + n)
+    nb = (k + 31) // 32
+    p = Program()
+    x = p.input("x", "bf16", (1, k))
+    q = p.input("q", "i8", (n, k))
+    s = p.input("s", "f32", (n, nb))
+    b = p.input("b", "f32", (n,))
+    z = p.op("addmm_q8", [b, x, q, s], "bf16", (1, n))
+    p.output(p.op("relu", [z], "bf16"))
+    ins = [synth.random_tensor(rng, (1, k), "bf16"), synth.random_tensor(rng, (n, k), "i8"),
+           (0.01 * (1 - rng.random((n, nb)))).astype(np.float32), synth.random_tensor(rng, (n,), "f32", 0.3)]
+    got, _ = parity.gpu_run(p, ins)
+    want = oracle_mod.run(p.text(), ins)
+    exact, mag = parity.contraction_reference(p.ops[0], dict(zip(["x", "q", "s", "b"], ins)), None)
+    parity.assert_contraction(got[0], want[0], np.maximum(exact, 0), mag, "bf16", "gemv q8")
+
+
+# ------------------------------------------------------------ whole steps --
+
+SMALL = {
+    "c1": dict(programs.CONFIGS["c1"]),
+    "c2s": dict(kind="mlp", dims=(192, 320, 256, 48), batch=96, dtype="bf16", lr=1e-3),
+    "c3s": dict(kind="gemv", k=1024, n=1024, layers=3),
+    "c4s": dict(kind="mlp", dims=(256, 384, 256, 128), batch=160, dtype="bf16", lr=1e-4),
+    "c5s": dict(kind="residual", width=256, layers=4, batch=96, dtype="f16", lr=1e-4),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_whole_step_per_node(oracle_mod, name):
+    cfg = SMALL[name]
+    say("whole step per node", name)
+    base = programs.build(cfg)
+    probe = base.probe()
+    ins = programs.inputs_for(cfg, 0)
+    outs, _ = parity.gpu_run(probe, [a.copy() for a in ins])
+    vals = parity.probe_values(base, probe, outs)
+    n = parity.check_per_node(oracle_mod, base, ins, vals)
+    assert n == len(base.ops)
+
+
+@pytest.mark.parametrize("name", list(SMALL))
+def test_fused_equals_unfused(name):
+    """The fused schedule and the probe (everything materialised) agree bitwise
+    on the shared outputs."""
+    cfg = SMALL[name]
+    say("fused == probe", name)
+    base = programs.build(cfg)
+    probe = base.probe()
+    ins = programs.inputs_for(cfg, 1)
+    o1, p1 = parity.gpu_run(base, [a.copy() for a in ins])
+    o2, _ = parity.gpu_run(probe, [a.copy() for a in ins])
+    assert p1.query()["n_stages"] >= 1
+    for a, b, s in zip(o1, o2, base.outputs):
+        parity.assert_bitexact(a, b, s.dtype, s.buf)
+
+
+def test_c1_end_to_end_close_to_oracle(oracle_mod):
+    cfg = SMALL["c1"]
+    say("c1 end to end")
+    base = programs.build(cfg)
+    ins = programs.inputs_for(cfg, 2)
+    got, _ = parity.gpu_run(base, [a.copy() for a in ins])
+    want = oracle_mod.run(base.text(), [a.copy() for a in ins])
+    for g, w, s in zip(got, want, base.outputs):
+        np.testing.assert_allclose(parity.f32_of(g, s.dtype), parity.f32_of(w, s.dtype), rtol=1e-5, atol=1e-6)

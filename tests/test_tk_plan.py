@@ -1,0 +1,241 @@
+"""CPU tests of libtk without a GPU: the C ABI loads and exports every symbol
+include/tk.h declares; plan-only compiles of every workload; the scheduler's
+fusion/inlining/in-place decisions (trainkernel codegen.py `_Generator`);
+compile-time rejections; and the run-time buffer checks of tk_validate_into
+(runtime.py `run_into`) on descriptors that are never dereferenced."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from persistent_whole_step_amd import programs, tk
+from persistent_whole_step_amd.programs import Program
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "tk.h")).read()
+    return sorted(set(re.findall(r"\b(tk_[a-z_]+)\s*\(", text)) - {"tk_alloc_fn"})
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(tk.LIB_PATH)
+    names = declared_symbols()
+    assert len(names) >= 12
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c3", "c4", "c5"])
+def test_plan_only_compile_of_workloads(name):
+    p = programs.build(programs.CONFIGS[name])
+    prog = tk.compile(p.text(), device=-1)
+    q = prog.query()
+    assert q["grid_barriers"] == q["n_stages"] - 1
+    assert q["workspace_bytes"] >= 16384
+    assert q["grid_size"] >= 1 and q["grid_size"] <= 256
+    n_params = sum(1 for k, _ in p.inplace.items())
+    assert q["direct_state_commits"] == n_params
+    assert "stage 0:" in prog.dump()
+
+
+def test_mlp_schedule_decisions():
+    p = programs.build(programs.CONFIGS["c1"])
+    q = tk.compile(p.text(), device=-1).query()
+    # addmm + sub(d) chain, gm + threshold_backward chain: two epilogue fusions;
+    # every weight update folds into its gradient tile; pow is inlined into mean
+    assert q["fused_epilogues"] == 2
+    assert q["fused_updates"] == 2
+    assert q["inlined_ops"] == 1
+    assert q["n_stages"] == 7
+
+
+def test_fusion_stops_at_returned_values():
+    # pass 1 never fuses a chain whose link is a returned value
+    p = Program()
+    a = p.input("a", "f32", (8, 8))
+    b = p.input("b", "f32", (8, 8))
+    y = p.op("mm", [a, b], "f32", (8, 8))
+    z = p.op("relu", [y], "f32")
+    p.output(z)
+    q = tk.compile(p.text(), device=-1).query()
+    # relu output returned: pass 2 writes it from the tile instead (root discarded)
+    assert q["fused_epilogues"] == 0 and q["side_epilogues"] == 1 and q["n_stages"] == 1
+
+
+def test_non_identity_view_blocks_fusion():
+    p = Program()
+    a = p.input("a", "f32", (8, 8))
+    b = p.input("b", "f32", (8, 8))
+    y = p.op("mm", [a, b], "f32", (8, 8))
+    z = p.op("relu", [y.T], "f32", shape=(8, 8))   # transposed read of the root
+    w = p.op("mul", [z, 2.0], "f32")
+    p.output(w)
+    q = tk.compile(p.text(), device=-1).query()
+    assert q["fused_epilogues"] == 0 and q["n_stages"] >= 2
+
+
+def test_fusion_disabled_by_options():
+    p = programs.build(programs.CONFIGS["c1"])
+    q = tk.compile(p.text(), device=-1, fuse_epilogues=0, fuse_pointwise=0).query()
+    assert q["fused_epilogues"] == 0 and q["fused_updates"] == 0 and q["inlined_ops"] == 0
+    q2 = tk.compile(p.text(), device=-1, barrier_every_op=1).query()
+    assert q2["n_stages"] >= q2["materialized_ops"]
+
+
+def test_direct_commit_refused_when_target_read_later():
+    # W read by an op after the update: the update must be staged and committed last
+    p = Program()
+    W = p.input("W", "f32", (4, 4))
+    g = p.input("g", "f32", (4, 4))
+    Wn = p.op("sub", [W, g], "f32", alpha=0.5)
+    later = p.op("mul", [W, 2.0], "f32")
+    p.output(Wn, inplace_of=W)
+    p.output(later)
+    q = tk.compile(p.text(), device=-1).query()
+    assert q["direct_state_commits"] == 0 and q["staged_commits"] == 1
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda t: t.replace("#0x1.0000000000000p+1", "#inf"), "TK_E_ARG"),
+    (lambda t: t.replace(" mul ", " tanh "), "TK_E_UNSUPPORTED"),
+    (lambda t: t.replace("tkir 1", "tkir 9"), "TK_E_PARSE"),
+    (lambda t: t.replace("y:f32:4:1:0", "y:f32:4:2:0"), "TK_E_STRIDE"),
+    (lambda t: t + "junk", "TK_E_PARSE"),
+])
+def test_compile_rejections(mutate, code):
+    p = Program()
+    a = p.input("a", "f32", (4,))
+    p.output(p.op("mul", [a, 2.0], "f32", name="y"))
+    with pytest.raises(tk.TkError) as ei:
+        tk.compile(mutate(p.text()), device=-1)
+    assert ei.value.status_name == code
+
+
+def test_compile_rejects_bad_shapes_and_inplace():
+    p = Program()
+    a = p.input("a", "f32", (2, 3))
+    b = p.input("b", "f32", (4,))
+    p.output(p.op("add", [a, b], "f32"))
+    with pytest.raises(tk.TkError, match="broadcast"):
+        tk.compile(p.text(), device=-1)
+    p = Program()
+    a = p.input("a", "f32", (2, 3))
+    b = p.input("b", "f32", (4, 2))
+    p.output(p.op("mm", [a, b], "f32", (2, 2)))
+    with pytest.raises(tk.TkError, match="compatible"):
+        tk.compile(p.text(), device=-1)
+    p = Program()
+    a = p.input("a", "f32", (4,))
+    c = p.input("c", "f32", (4,))
+    y = p.op("mul", [a, 2.0], "f32")
+    p.output(y, inplace_of=a)
+    p.inplace[1] = 0
+    p.output(p.op("mul", [c, 2.0], "f32"))
+    with pytest.raises(tk.TkError, match="distinct"):
+        tk.compile(p.text(), device=-1)
+    p = Program()
+    a = p.input("a", "f32", (4,))
+    p.output(a)
+    p.inplace[0] = 0
+    with pytest.raises(tk.TkError, match="computed values"):
+        tk.compile(p.text(), device=-1)
+
+
+@pytest.mark.parametrize("opt,val", [("blocks_per_cu", 0), ("blocks_per_cu", 9), ("threads_per_block", 128),
+                                     ("gemm_split_k", 3), ("max_blocks", -1)])
+def test_option_ranges(opt, val):
+    p = programs.build(programs.CONFIGS["c1"])
+    with pytest.raises(tk.TkError):
+        tk.compile(p.text(), device=-1, **{opt: val})
+
+
+# ------------------------------------------------ run-time buffer checks --
+
+def _sgd_prog():
+    p = Program()
+    W = p.input("W", "f32", (4, 4))
+    g = p.input("g", "f32", (4, 4))
+    Wn = p.op("sub", [W, g], "f32", alpha=0.5)
+    p.output(Wn, inplace_of=W)
+    p.output(p.op("mul", [g, 2.0], "bf16"))
+    return p
+
+
+class Fake:
+    """Non-overlapping fake device addresses."""
+    def __init__(self):
+        self.next = 1 << 40
+
+    def take(self, nbytes):
+        a = self.next
+        self.next += ((nbytes + 4095) // 4096 + 1) * 4096
+        return a
+
+
+def _setup():
+    p = _sgd_prog()
+    prog = tk.compile(p.text(), device=-1)
+    f = Fake()
+    W = tk.describe_fake((4, 4), "f32", f.take(64))
+    g = tk.describe_fake((4, 4), "f32", f.take(64))
+    o0 = W
+    o1 = tk.describe_fake((4, 4), "bf16", f.take(32))
+    wsb = prog.query()["workspace_bytes"]
+    ws = tk.describe_fake((wsb,), "i8", f.take(wsb))
+    return prog, [W, g], [o0, o1], ws, f
+
+
+def test_validate_accepts_good_buffers():
+    prog, ins, outs, ws, _ = _setup()
+    tk.validate_fake(prog, ins, outs, ws)
+
+
+def _expect(prog, ins, outs, ws, code):
+    with pytest.raises(tk.TkError) as ei:
+        tk.validate_fake(prog, ins, outs, ws)
+    assert ei.value.status_name == code, str(ei.value)
+
+
+def test_validate_rejections():
+    prog, ins, outs, ws, f = _setup()
+    _expect(prog, ins[:1], outs, ws, "TK_E_COUNT")
+    _expect(prog, ins, outs[:1], ws, "TK_E_COUNT")
+    bad = tk.describe_fake((4, 4), "bf16", f.take(64))
+    _expect(prog, [ins[0], bad], outs, ws, "TK_E_DTYPE")
+    bad = tk.describe_fake((4, 5), "f32", f.take(80))
+    _expect(prog, [ins[0], bad], outs, ws, "TK_E_SHAPE")
+    bad = tk.describe_fake((4, 4), "f32", f.take(64), strides=(1, 4))
+    _expect(prog, [ins[0], bad], outs, ws, "TK_E_STRIDE")
+    bad = tk.describe_fake((4, 4), "bf16", f.take(64), strides=(1, 4))
+    _expect(prog, ins, [outs[0], bad], ws, "TK_E_STRIDE")
+    other = tk.describe_fake((4, 4), "f32", f.take(64), device=1)
+    _expect(prog, [ins[0], other], outs, ws, "TK_E_DEVICE")
+    small = tk.describe_fake((100,), "i8", f.take(100))
+    _expect(prog, ins, outs, small, "TK_E_WORKSPACE")
+    unaligned = tk.describe_fake((ws.shape[0],), "i8", f.take(ws.shape[0]) + 8)
+    _expect(prog, ins, outs, unaligned, "TK_E_WORKSPACE")
+    # in-place slot not bound to its input
+    _expect(prog, ins, [tk.describe_fake((4, 4), "f32", f.take(64)), outs[1]], ws, "TK_E_ALIAS")
+    # output overlapping an input / another output / the workspace
+    _expect(prog, ins, [outs[0], tk.describe_fake((4, 4), "bf16", ins[1].data)], ws, "TK_E_ALIAS")
+    _expect(prog, ins, [outs[0], tk.describe_fake((4, 4), "bf16", ws.data + 256)], ws, "TK_E_ALIAS")
+    # in-place target sharing storage with another input
+    shared = tk.describe_fake((4, 4), "f32", ins[0].data + 32, storage=(ins[0].data, 1024))
+    tgt = tk.describe_fake((4, 4), "f32", ins[0].data, storage=(ins[0].data, 1024))
+    _expect(prog, [tgt, shared], [tgt, outs[1]], ws, "TK_E_ALIAS")
+    # requires_grad on an in-place target
+    rg = tk.describe_fake((4, 4), "f32", ins[0].data)
+    rg.requires_grad = 1
+    _expect(prog, [rg, ins[1]], [rg, outs[1]], ws, "TK_E_ARG")
+
+
+def test_run_refused_for_plan_only_program():
+    prog, ins, outs, ws, _ = _setup()
+    arr_in = tk._array(ins)
+    arr_out = tk._array(outs)
+    st = tk.lib().tk_run_into(prog._h, arr_in, 2, arr_out, 2, ctypes.byref(ws), None)
+    assert tk.STATUS[st] == "TK_E_DEVICE"
