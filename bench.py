@@ -1,0 +1,300 @@
+#!/usr/bin/env python3
+"""Throughput of whole training steps run as one persistent kernel each, on one MI355X.
+
+A step is one launch of the persistent kernel over the whole compiled program
+(forward, MSE loss, explicit backward, in-place SGD), as in the whole-step
+benchmark set: the default workload is the 3-layer bf16 MLP (batch 256,
+512 -> 1024 -> 1024 -> 64, lr 1e-3).  Inputs are seeded synthetic tensors
+already resident in HBM; parameters are updated in place every step (state
+feedback) and the (x, target) batch rotates over 4 resident batches.  The
+other workloads (2-layer fp32 MLP, int8-weight GEMV stack rotating 3 weight
+sets, 4096-wide bf16 MLP, 16-layer fp16 residual MLP) are timed briefly and
+reported under "others".
+
+Prints one JSON line on stdout.  --gpus N with N > 1 is refused: this
+build runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
+PEAK_HBM_GBS = 8000.0
+WORKLOAD_NAMES = {
+    "c1": "mlp2-fp32-b64-128-256-10",
+    "c2": "mlp3-bf16-b256-512-1024-1024-64",
+    "c3": "gemv8-int8w-bf16x-4096x4096",
+    "c4": "mlp3-bf16-b1024-4096-4096-4096-1024",
+    "c5": "resmlp16-fp16-b512-w2048",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def source_hash() -> str:
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "persistent_whole_step_amd", "csrc")
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def gemv_bytes(cfg) -> int:
+    k, n, L = cfg["k"], cfg["n"], cfg["layers"]
+    nb = (k + 31) // 32
+    return L * (n * k + n * nb * 4 + n * 4 + k * 2 + n * 2)
+
+
+class Runner:
+    """Compiled program + resident input variants + prebuilt C descriptors."""
+
+    def __init__(self, name: str, seed0: int = 0, **opts):
+        import torch
+        from persistent_whole_step_amd import programs, tk
+        from tests.parity import to_torch
+        self.name = name
+        self.cfg = programs.CONFIGS[name]
+        self.prog = programs.build(self.cfg)
+        self.p = tk.compile(self.prog.text(), device=0, **opts)
+        self.stats = self.p.query()
+        cfg = self.cfg
+        if cfg["kind"] == "gemv":
+            sets = [programs.inputs_for(cfg, seed0 + j) for j in range(3)]
+            self.inputs = [[to_torch(a, s.dtype) for a, s in zip(ins, self.prog.inputs)] for ins in sets]
+        else:
+            base = [to_torch(a, s.dtype) for a, s in zip(programs.inputs_for(cfg, seed0), self.prog.inputs)]
+            self.inputs = [base]
+            for j in range(1, 4):
+                ins = programs.inputs_for(cfg, seed0 + 100 + j)
+                self.inputs.append([to_torch(ins[0], self.prog.inputs[0].dtype),
+                                    to_torch(ins[1], self.prog.inputs[1].dtype)] + base[2:])
+        self.buffers = self.p.allocate(*self.inputs[0])
+        self.variants = []
+        for ins in self.inputs:
+            bufs = tk.ExecutionBuffers(tuple(ins[self.p._inplace_map()[s]] if s in self.p._inplace_map() else o
+                                             for s, o in enumerate(self.buffers.outputs)), self.buffers.workspace)
+            self.p.validate_into(*ins, buffers=bufs)
+            ci, co, cw = self.p._descs(ins, bufs)
+            self.variants.append((ci, len(ins), co, len(bufs.outputs), cw))
+        self.run_c = tk.lib().tk_run_into
+        self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+        self.tk = tk
+
+    def step(self, i: int):
+        ci, ni, co, no, cw = self.variants[i % len(self.variants)]
+        rc = self.run_c(self.p._h, ci, ni, co, no, ctypes.byref(cw), self.stream)
+        if rc != 0:
+            raise self.tk.TkError(rc, self.tk.lib().tk_last_error().decode())
+
+    def check_not_aborted(self):
+        aborted, stage = self.p.workspace_status(self.buffers.workspace)
+        if aborted:
+            raise RuntimeError(f"{self.name}: a grid barrier timed out in stage {stage}")
+
+    def time_steps(self, steps: int, warmup: int):
+        import torch
+        for i in range(warmup):
+            self.step(i)
+        torch.cuda.synchronize()
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        start.record()
+        for i in range(steps):
+            self.step(i)
+        end.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_ms = start.elapsed_time(end)
+        self.check_not_aborted()
+        return wall, ev_ms
+
+    def kernel_ms(self, n: int = 50) -> float:
+        """Average duration of one launch, HIP events on the launch stream."""
+        import torch
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+        torch.cuda.synchronize()
+        for i, (a, b) in enumerate(evs):
+            a.record()
+            self.step(i)
+            b.record()
+        torch.cuda.synchronize()
+        ts = sorted(a.elapsed_time(b) for a, b in evs)
+        return sum(ts) / len(ts)
+
+
+def roofline(name: str, cfg, prog, kernel_ms: float, traffic):
+    from persistent_whole_step_amd import programs
+    if cfg["kind"] == "gemv":
+        b = gemv_bytes(cfg)
+        ach = b / (kernel_ms * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 2), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                "frac": round(ach / PEAK_HBM_GBS, 4), "traffic": traffic, "algorithmic_bytes": b}
+    fl = programs.contraction_flops(prog)
+    ach = fl / (kernel_ms * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[cfg["dtype"]]
+    return {"bound": "mfma", "achieved": round(ach, 3), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(ach / peak, 5), "traffic": traffic, "algorithmic_flops": fl}
+
+
+def traffic_for(name: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, when
+    it was taken on the current kernel sources (else null)."""
+    path = os.path.join(ROOT, "profiles", f"tk_persistent_{WORKLOAD_NAMES[name]}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("source_hash") != source_hash():
+        return None
+    return d.get("bytes_per_launch")
+
+
+def barrier_latency(n_small: int = 8, n_large: int = 264):
+    """Per-barrier latency: slope of launch time over the number of stages of a
+    chain of trivial one-element ops, launched on a full grid."""
+    import torch
+    from persistent_whole_step_amd import tk
+    from persistent_whole_step_amd.programs import Program
+    res = {}
+    grid = None
+    for n in (n_small, n_large):
+        p = Program()
+        x = p.input("x", "f32", (1,))
+        v = x
+        for _ in range(n):
+            v = p.op("add", [v, 1.0], "f32")
+        p.output(v)
+        prog = tk.compile(p.text(), device=0, fuse_pointwise=0, force_grid=100000)
+        grid = prog.query()["grid_size"]
+        xt = torch.zeros(1, device="cuda:0")
+        bufs = prog.allocate(xt)
+        for _ in range(5):
+            prog.run_into(xt, buffers=bufs)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        a.record()
+        for _ in range(reps):
+            prog.run_into(xt, buffers=bufs)
+        b.record()
+        torch.cuda.synchronize()
+        res[n] = a.elapsed_time(b) / reps
+        ab, _ = prog.workspace_status(bufs.workspace)
+        if ab:
+            raise RuntimeError("barrier microbenchmark aborted")
+    per = (res[n_large] - res[n_small]) / (n_large - n_small) * 1e3
+    return {"per_barrier_us": round(per, 3), "grid": grid, "launch_ms_%d_stages" % n_small: round(res[n_small], 4),
+            "launch_ms_%d_stages" % n_large: round(res[n_large], 4)}
+
+
+def cpu_baseline(name: str, seconds: float):
+    """The oracle, as it stands, on the same workload: whole steps until `seconds` pass."""
+    from oracle import oracle
+    from persistent_whole_step_amd import programs
+    cfg = programs.CONFIGS[name]
+    prog = programs.build(cfg)
+    text = prog.text()
+    ins = programs.inputs_for(cfg, 0)
+    n = 0
+    t0 = time.perf_counter()
+    while True:
+        oracle.run(text, [a.copy() for a in ins])
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or (n >= 1 and el * (n + 1) / n > 3 * seconds):
+            break
+    return {"value": round(n / el, 4), "unit": "steps/s", "cores": oracle.threads(), "kind": "oracle",
+            "sample": f"{n} full {WORKLOAD_NAMES[name]} steps (fp32 CPU oracle) in {el:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=1000)
+    ap.add_argument("--warmup", type=int, default=50)
+    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--others", default="c1,c3,c4,c5", help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--other-steps", type=int, default=100)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-barrier", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this build runs on one GPU; the multi-GPU path is design only (see DESIGN.md)",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU", file=sys.stderr)
+        sys.exit(1)
+    from persistent_whole_step_amd import tk
+    tk.lib()
+
+    log(f"[bench] workload {args.config}: compiling")
+    r = Runner(args.config)
+    log(f"[bench] {args.config}: stages={r.stats['n_stages']} grid={r.stats['grid_size']}; timing {args.steps} steps")
+    wall, ev_ms = r.time_steps(args.steps, args.warmup)
+    kms = r.kernel_ms()
+    ms_per_step = wall / args.steps * 1e3
+    value = args.steps / wall
+    line = {
+        "metric": "training steps/sec per program",
+        "value": round(value, 2),
+        "unit": "steps/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": r.cfg.get("dtype", "bf16"),
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.config], "batch": r.cfg.get("batch"), "dims": r.cfg.get("dims"),
+                   "lr": r.cfg.get("lr"), "parallelism": "single-gpu", "resident_batches": 4,
+                   "stages": r.stats["n_stages"], "grid_barriers": r.stats["grid_barriers"],
+                   "grid": r.stats["grid_size"]},
+        "event_ms_per_step": round(ev_ms / args.steps, 5),
+        "kernel_ms": round(kms, 5),
+        "roofline": roofline(args.config, r.cfg, r.prog, kms, traffic_for(args.config)),
+    }
+    log(f"[bench] {args.config}: {value:.1f} steps/s, kernel {kms * 1e3:.1f} us")
+    if not args.no_barrier:
+        log("[bench] barrier microbenchmark")
+        line["barrier"] = barrier_latency()
+    others = {}
+    for name in [x for x in args.others.split(",") if x and x != args.config]:
+        log(f"[bench] other workload {name}")
+        o = Runner(name)
+        w, _ = o.time_steps(args.other_steps, 10)
+        k = o.kernel_ms(20)
+        rf = roofline(name, o.cfg, o.prog, k, traffic_for(name))
+        others[WORKLOAD_NAMES[name]] = {"steps_per_s": round(args.other_steps / w, 2),
+                                       "ms_per_step": round(w / args.other_steps * 1e3, 4),
+                                       "kernel_ms": round(k, 4), "stages": o.stats["n_stages"],
+                                       "achieved": rf["achieved"], "unit": rf["unit"], "frac": rf["frac"]}
+        log(f"[bench] {name}: {others[WORKLOAD_NAMES[name]]}")
+        del o
+        torch.cuda.empty_cache()
+    if others:
+        line["others"] = others
+    if not args.no_cpu:
+        log("[bench] CPU oracle baseline")
+        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -77,7 +77,9 @@ typedef struct {
   int32_t barrier_every_op;    /* debug: one op per stage */
   int32_t num_cus;             /* plan-only compiles: CU count to plan for (0: 256) */
   int32_t gemm_split_k;        /* 0: automatic; else force split-K parts for MFMA GEMMs */
-  int32_t reserved[5];
+  int32_t force_grid;          /* 0: automatic; else launch exactly this many workgroups
+                                  (clamped to the co-resident capacity) */
+  int32_t reserved[4];
 } tk_options;
 
 /* Plan and kernel statistics (pages: `GeneratedKernel` and `resource_usage`). */

@@ -29,6 +29,7 @@ def lib():
         l.oracle_run.argtypes = [ctypes.c_char_p, ctypes.POINTER(ctypes.c_void_p), ctypes.c_int,
                                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int]
         l.oracle_error.restype = ctypes.c_char_p
+        l.oracle_threads.restype = ctypes.c_int
         for name in ("oracle_round_bf16", "oracle_round_f16"):
             f = getattr(l, name)
             f.restype = None
@@ -84,6 +85,10 @@ def run64(text: str, inputs):
     outs = [np.empty(shape, dtype=np.float64) for shape, _ in output_specs(text)]
     _call(text, ins, outs, 1)
     return outs
+
+
+def threads() -> int:
+    return int(lib().oracle_threads())
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

@@ -38,6 +38,10 @@
 #include <string>
 #include <vector>
 
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
 namespace {
 
 enum DType { F32, F16, BF16, I8 };
@@ -706,6 +710,15 @@ int oracle_run(const char* ir, const void* const* inputs, int n_in, void* const*
 }
 
 const char* oracle_error(void) { return g_err.c_str(); }
+
+// Threads the oracle's parallel loops use.
+int oracle_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
 
 void oracle_round_bf16(const float* x, uint16_t* out, int64_t n) {
 #pragma omp parallel for schedule(static)

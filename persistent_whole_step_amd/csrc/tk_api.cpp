@@ -107,8 +107,11 @@ void check_inputs(const tk_program* p, const tk_tensor* inputs, size_t n_in, int
     if (t.device != device) tk::raise(TK_E_DEVICE, "input " + std::to_string(i) + " is on another device");
     if (t.dtype != s.dtype) tk::raise(TK_E_DTYPE, "input " + std::to_string(i) + " does not match the compiled dtype");
     if (!matches_shape(t, s)) tk::raise(TK_E_SHAPE, "input " + std::to_string(i) + " does not match the compiled shape");
+    // Exact strides, except where no element is addressed through them
+    // (size-1 dims and empty tensors).
+    const bool empty = numel_of(t) == 0;
     for (int d = 0; d < t.ndim; ++d)
-      if (t.strides[d] != s.strides[d])
+      if (!empty && t.shape[d] > 1 && t.strides[d] != s.strides[d])
         tk::raise(TK_E_STRIDE, "input " + std::to_string(i) + " does not match the compiled strides");
     if (numel_of(t) && !t.data) tk::raise(TK_E_ARG, "input " + std::to_string(i) + " has no data");
   }
@@ -140,7 +143,8 @@ void check_buffers(const tk_program* p, const tk_tensor* inputs, size_t n_in, co
     if (it != pl.inplace.end()) {
       const tk_tensor& tgt = inputs[it->second];
       bool same_strides = t.ndim == tgt.ndim;
-      for (int d = 0; same_strides && d < t.ndim; ++d) same_strides = t.strides[d] == tgt.strides[d];
+      for (int d = 0; same_strides && d < t.ndim; ++d)
+        same_strides = t.shape[d] <= 1 || t.strides[d] == tgt.strides[d];
       if (t.data != tgt.data || !same_strides) tk::raise(TK_E_ALIAS, "inplace output must bind its declared input");
       for (size_t i = 0; i < n_in; ++i)
         if ((int)i != it->second && overlap(inputs[i], tgt))
@@ -197,6 +201,7 @@ tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int3
     if (o.gemm_split_k != 0 && o.gemm_split_k != 1 && o.gemm_split_k != 2 && o.gemm_split_k != 4 && o.gemm_split_k != 8)
       return fail(TK_E_ARG, "gemm_split_k must be 0, 1, 2, 4 or 8");
     if (o.num_cus < 0) return fail(TK_E_ARG, "num_cus must not be negative");
+    if (o.force_grid < 0) return fail(TK_E_ARG, "force_grid must not be negative");
     so.blocks_per_cu = o.blocks_per_cu;
     so.max_blocks = o.max_blocks;
     so.fuse_pointwise = o.fuse_pointwise != 0;
@@ -254,8 +259,12 @@ tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int3
       bpc = std::min(bpc, occupancy);
     }
     long grid = (long)so.num_cus * bpc;
-    grid = std::min<long>(grid, std::max(1, p->plan.max_items));
-    if (so.max_blocks > 0) grid = std::min<long>(grid, so.max_blocks);
+    if (o.force_grid > 0) {
+      grid = std::min<long>(grid, o.force_grid);
+    } else {
+      grid = std::min<long>(grid, std::max(1, p->plan.max_items));
+      if (so.max_blocks > 0) grid = std::min<long>(grid, so.max_blocks);
+    }
     p->grid = (int)std::max<long>(1, grid);
     tk_stats& s = p->plan.stats;
     s.grid_size = p->grid;
