@@ -21,12 +21,17 @@ constexpr int kBlock = 256;         // threads per workgroup (4 wave64)
 constexpr int kMaxBases = 240;      // pointer slots per launch (inputs, outputs, workspace)
 constexpr int kMaxDims = 4;         // iteration dims after collapsing
 constexpr int kMaxSlots = 4;        // saved values in the expression machine
-constexpr uint32_t kHeaderBytes = 16384;  // workspace header (barrier, status, timestamps)
+constexpr uint32_t kPlanLds = 8192;        // LDS bytes for the current stage's descriptors
+constexpr uint32_t kMaxGrid = 1024;        // workgroups per launch (barrier flag slots)
+constexpr uint32_t kFlagStride = 16;       // u32 words between two workgroups' flags (64 B)
+constexpr uint32_t kHdrArrive = 16384;     // u32 [kMaxGrid * kFlagStride] arrival epochs
+constexpr uint32_t kHdrRelease = kHdrArrive + kMaxGrid * kFlagStride * 4;  // u32 release epochs
+constexpr uint32_t kHeaderBytes = kHdrRelease + kMaxGrid * kFlagStride * 4;  // 147456: header size
 constexpr uint32_t kMaxTimedStages = 480;
 
 // Workspace header layout (bytes).  Each word sits on its own 64-byte line.
-constexpr uint32_t kHdrCount = 0;      // barrier arrivals in the current generation
-constexpr uint32_t kHdrGen = 64;       // barrier generation (monotonic)
+constexpr uint32_t kHdrEpoch = 0;      // last barrier epoch of the previous launch on this workspace
+constexpr uint32_t kHdrGen = 64;       // (unused)
 constexpr uint32_t kHdrAbort = 128;    // nonzero: a barrier timed out; the launch stopped
 constexpr uint32_t kHdrAbortStage = 192;
 constexpr uint32_t kHdrStamps = 1024;  // optional: u64 [stage][2] arrival/departure ticks of workgroup 0
@@ -117,21 +122,27 @@ struct DTask {
   uint32_t pad2;
 };
 
+// A stage's descriptors form one contiguous blob in the plan:
+// [DTask x n_tasks][DView x n_views][DIns x n_ins], indices local to the blob,
+// so a workgroup can stage the whole blob in LDS before the stage starts.
 struct DStage {
-  uint32_t task_first;
+  uint32_t blob_off;    // bytes from the plan start (16-byte aligned)
+  uint32_t blob_bytes;  // multiple of 16
   uint32_t n_tasks;
   uint32_t n_items;
-  uint32_t flags;
+  uint32_t off_views;   // bytes from the blob start
+  uint32_t off_ins;
+  uint32_t n_views;
+  uint32_t n_ins;
 };
 
 struct DHeader {
   uint32_t magic;
   uint32_t n_stages;
-  uint32_t n_tasks;
-  uint32_t n_views;
-  uint32_t n_ins;
-  uint32_t off_stages, off_tasks, off_views, off_ins;  // byte offsets from the plan start
+  uint32_t off_stages;  // bytes from the plan start
   uint32_t bytes;
+  uint32_t max_blob;    // largest stage blob
+  uint32_t pad[3];
 };
 constexpr uint32_t kPlanMagic = 0x31706b74u;  // "tkp1"
 

@@ -265,6 +265,7 @@ tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int3
       grid = std::min<long>(grid, std::max(1, p->plan.max_items));
       if (so.max_blocks > 0) grid = std::min<long>(grid, so.max_blocks);
     }
+    grid = std::min<long>(grid, (long)kMaxGrid);
     p->grid = (int)std::max<long>(1, grid);
     tk_stats& s = p->plan.stats;
     s.grid_size = p->grid;

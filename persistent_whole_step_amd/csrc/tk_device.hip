@@ -191,9 +191,8 @@ DEV void store_view(const KArgs& ka, const DView& v, const uint32_t (&c)[kMaxDim
 
 // ------------------------------------------------------ expression machine --
 
+// The current stage's descriptors (in LDS when the stage blob fits).
 struct Plan {
-  const DHeader* h;
-  const DStage* stages;
   const DTask* tasks;
   const DView* views;
   const DIns* ins;
@@ -887,41 +886,79 @@ DEV void run_item(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item
   }
 }
 
-// Grid barrier.  Arrival: every wave waits for its own stores, the workgroup
-// meets, then one lane publishes with an agent-scope release and counts in.
-// The last arrival resets the counter and advances the generation; the others
-// spin on the generation (bounded by the deadline), then acquire.
-DEV bool grid_barrier(const KArgs& ka, uint32_t stage, uint64_t deadline) {
+// Grid barrier with per-workgroup flags.  Arrival: every wave waits for its
+// own stores, the workgroup meets, one lane publishes (agent-scope release)
+// and writes its arrival flag = epoch.  The first wave of workgroup 0 polls
+// all arrival flags (4 per lane, loads issued together), then acquires and
+// writes every workgroup's release flag; each other workgroup polls its own
+// release flag and acquires.  No two workgroups spin on one address.  Epochs
+// grow monotonically across launches on a workspace (the base is kept in the
+// header), so flags never need resetting.  Every spin is bounded by the
+// deadline; a timeout sets the abort word, which every spinner also watches.
+DEV bool grid_barrier(const KArgs& ka, uint32_t epoch, uint32_t stage, uint64_t deadline) {
   __shared__ uint32_t s_ok;
+  uint32_t* arrive = (uint32_t*)(ka.ws + kHdrArrive);
+  uint32_t* release = (uint32_t*)(ka.ws + kHdrRelease);
+  uint32_t* abort = (uint32_t*)(ka.ws + kHdrAbort);
+  const uint32_t G = gridDim.x, bid = blockIdx.x;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) {
-    uint32_t* count = (uint32_t*)(ka.ws + kHdrCount);
-    uint32_t* gen = (uint32_t*)(ka.ws + kHdrGen);
-    uint32_t* abort = (uint32_t*)(ka.ws + kHdrAbort);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(arrive + bid * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if (bid == 0 && threadIdx.x < 64) {
     uint32_t ok = 1;
-    const uint32_t g = __hip_atomic_load(gen, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t prev = __hip_atomic_fetch_add(count, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (prev + 1 == gridDim.x) {
-      __hip_atomic_store(count, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(gen, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-    } else {
-      const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-      while (__hip_atomic_load(gen, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == g) {
-        __builtin_amdgcn_s_sleep(1);
-        if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-          ok = 0;
-          break;
-        }
+    const uint32_t lane = threadIdx.x;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    for (uint32_t base = 0; base < G; base += 256) {
+      uint32_t* f[4];
+      bool live[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t w = base + lane + 64 * i;
+        live[i] = w < G;
+        f[i] = arrive + (live[i] ? w : 0) * kFlagStride;
+      }
+      for (;;) {
+        bool done = true;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (live[i]) {
+            const uint32_t v = __hip_atomic_load(f[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            if ((int32_t)(v - epoch) < 0) done = false;
+          }
+        if (done) break;
+        if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = 0; break; }
         if (__builtin_amdgcn_s_memrealtime() - t0 > deadline) {
           __hip_atomic_store((uint32_t*)(ka.ws + kHdrAbortStage), stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(abort, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ok = 0;
           break;
         }
       }
-      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      if (!ok) break;
     }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
+    // release everyone (a timed-out master still releases: the abort word stops them)
+    for (uint32_t w = lane; w < G; w += 64)
+      __hip_atomic_store(release + w * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t all_ok = __builtin_amdgcn_readfirstlane(ok) & (uint32_t)__all(ok);
+    if (lane == 0) s_ok = all_ok;
+  } else if (bid != 0 && threadIdx.x == 0) {
+    uint32_t ok = 1;
+    uint32_t* f = release + bid * kFlagStride;
+    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
+    while ((int32_t)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - epoch) < 0) {
+      if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = 0; break; }
+      if (__builtin_amdgcn_s_memrealtime() - t0 > deadline) {
+        __hip_atomic_store((uint32_t*)(ka.ws + kHdrAbortStage), stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        ok = 0;
+        break;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     s_ok = ok;
   }
   __syncthreads();
@@ -937,28 +974,42 @@ DEV uint32_t hash32(uint32_t x) {
   return x;
 }
 
+// Copy a stage blob into LDS (all threads; 16-byte chunks).
+DEV void stage_blob_to_lds(const uint8_t* plan, const DStage& st, uint8_t* lds) {
+  const u32x4* src = (const u32x4*)(plan + st.blob_off);
+  u32x4* dst = (u32x4*)lds;
+  for (uint32_t i = threadIdx.x; i < st.blob_bytes / 16; i += kBlock) dst[i] = src[i];
+}
+
 }  // namespace
 
 __global__ __launch_bounds__(kBlock, 2) void tk_persistent(KArgs) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t planbuf[kPlanLds];
   // Read the argument block in place (the kernarg segment) so the base-pointer
   // table is indexed in memory rather than copied into private storage.
   const KArgs& ka = *(const KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  Plan pl;
-  pl.h = (const DHeader*)ka.plan;
-  pl.stages = (const DStage*)(ka.plan + pl.h->off_stages);
-  pl.tasks = (const DTask*)(ka.plan + pl.h->off_tasks);
-  pl.views = (const DView*)(ka.plan + pl.h->off_views);
-  pl.ins = (const DIns*)(ka.plan + pl.h->off_ins);
-  const uint32_t n_stages = pl.h->n_stages;
+  const DHeader* h = (const DHeader*)ka.plan;
+  const DStage* stages = (const DStage*)(ka.plan + h->off_stages);
+  const uint32_t n_stages = h->n_stages;
   const uint64_t deadline = ka.deadline_ticks ? ka.deadline_ticks : 400000000ull;  // 4 s at 100 MHz
   if (*(volatile uint32_t*)(ka.ws + kHdrAbort) != 0u) return;  // a previous launch on this workspace aborted
+  const uint32_t epoch0 = *(volatile uint32_t*)(ka.ws + kHdrEpoch);
+  if (n_stages == 0) return;
+  DStage st = stages[0];
+  if (st.blob_bytes <= kPlanLds) stage_blob_to_lds(ka.plan, st, planbuf);
+  __syncthreads();
   for (uint32_t s = 0; s < n_stages; ++s) {
-    const DStage st = pl.stages[s];
+    const bool in_lds = st.blob_bytes <= kPlanLds;
+    const uint8_t* blob = in_lds ? planbuf : ka.plan + st.blob_off;
+    Plan pl;
+    pl.tasks = (const DTask*)blob;
+    pl.views = (const DView*)(blob + st.off_views);
+    pl.ins = (const DIns*)(blob + st.off_ins);
     uint32_t ti = 0;
     for (uint32_t item = blockIdx.x; item < st.n_items; item += gridDim.x) {
-      while (ti + 1 < st.n_tasks && item >= pl.tasks[st.task_first + ti + 1].item_begin) ++ti;
-      const DTask t = pl.tasks[st.task_first + ti];
+      while (ti + 1 < st.n_tasks && item >= pl.tasks[ti + 1].item_begin) ++ti;
+      const DTask t = pl.tasks[ti];
       if (ka.flags & K_STAGGER) {
         uint32_t n = hash32(ka.stagger_seed ^ (blockIdx.x * 0x9e3779b9u) ^ (item * 0x85ebca6bu) ^ s) % 48u;
         for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
@@ -966,12 +1017,21 @@ __global__ __launch_bounds__(kBlock, 2) void tk_persistent(KArgs) {
       run_item(ka, pl, t, item - t.item_begin, smem);
     }
     if (s + 1 < n_stages) {
+      // stage the next stage's descriptors while the barrier completes
+      __syncthreads();
+      st = stages[s + 1];
+      if (st.blob_bytes <= kPlanLds) stage_blob_to_lds(ka.plan, st, planbuf);
       const bool stamp = (ka.flags & K_TIMESTAMPS) && blockIdx.x == 0 && threadIdx.x == 0 && s < kMaxTimedStages;
       if (stamp) ((uint64_t*)(ka.ws + kHdrStamps))[2 * s] = __builtin_amdgcn_s_memrealtime();
-      if (!grid_barrier(ka, s, deadline)) return;
+      if (!grid_barrier(ka, epoch0 + s + 1, s, deadline)) return;
       if (stamp) ((uint64_t*)(ka.ws + kHdrStamps))[2 * s + 1] = __builtin_amdgcn_s_memrealtime();
     }
   }
+  // The next launch on this workspace continues the epoch sequence.  Every
+  // workgroup has read the base before the first barrier, which this
+  // workgroup has passed.
+  if (n_stages > 1 && blockIdx.x == 0 && threadIdx.x == 0)
+    *(volatile uint32_t*)(ka.ws + kHdrEpoch) = epoch0 + n_stages - 1;
 }
 
 __global__ void tk_zero_header(uint8_t* ws, uint32_t bytes) {

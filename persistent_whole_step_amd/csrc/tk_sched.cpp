@@ -1618,54 +1618,89 @@ struct Builder {
       stages.push_back(stage_tasks[L]);
       descs.push_back(stage_desc[L]);
     }
+    // Per stage: tasks, then the views and instructions they use, re-indexed
+    // locally so the stage blob is self-contained.
     std::vector<DStage> ds;
-    std::vector<DTask> dt;
+    std::vector<std::vector<uint8_t>> blobs;
     int max_items = 0;
+    size_t n_tasks_total = 0;
     std::ostringstream dump;
     for (size_t s = 0; s < stages.size(); ++s) {
-      DStage d{};
-      d.task_first = (uint32_t)dt.size();
-      d.n_tasks = (uint32_t)stages[s].size();
+      std::vector<DTask> tk;
+      std::vector<DView> sv;
+      std::vector<DIns> si;
+      std::map<uint32_t, uint16_t> vmap;
+      auto mapv = [&](uint32_t g) -> uint16_t {
+        auto it = vmap.find(g);
+        if (it != vmap.end()) return it->second;
+        uint16_t l = (uint16_t)sv.size();
+        vmap[g] = l;
+        sv.push_back(views.at(g));
+        return l;
+      };
+      auto mapcode = [&](uint32_t first, uint32_t len) -> uint32_t {
+        uint32_t at = (uint32_t)si.size();
+        for (uint32_t i = 0; i < len; ++i) {
+          DIns d = ins.at(first + i);
+          if (d.src == SRC_VIEW || d.op == VM_STORE) d.arg = mapv(d.arg);
+          si.push_back(d);
+        }
+        return at;
+      };
       uint32_t items = 0;
       dump << "stage " << s << ":\n";
       for (size_t t = 0; t < stages[s].size(); ++t) {
         DTask task = stages[s][t];
         task.item_begin = items;
         items += task.n_items;
-        dt.push_back(task);
+        if (task.kind == T_GEMM_MFMA || task.kind == T_GEMM_SIMT || task.kind == T_GEMV_Q8) {
+          task.va = mapv(task.va);
+          task.vb = mapv(task.vb);
+          if (task.kind == T_GEMV_Q8) task.vs = mapv(task.vs);
+        }
+        task.expr_first = task.expr_len ? mapcode(task.expr_first, task.expr_len) : 0;
+        task.fin_first = task.fin_len ? mapcode(task.fin_first, task.fin_len) : 0;
+        tk.push_back(task);
         dump << "  " << kind_name(task.kind) << " items=" << task.n_items << " : " << descs[s][t] << "\n";
       }
+      DStage d{};
+      d.n_tasks = (uint32_t)tk.size();
       d.n_items = items;
-      max_items = std::max<int>(max_items, (int)items);
+      d.n_views = (uint32_t)sv.size();
+      d.n_ins = (uint32_t)si.size();
+      d.off_views = (uint32_t)align_up(tk.size() * sizeof(DTask), 16);
+      d.off_ins = (uint32_t)align_up(d.off_views + sv.size() * sizeof(DView), 16);
+      d.blob_bytes = (uint32_t)align_up(d.off_ins + si.size() * sizeof(DIns), 16);
+      std::vector<uint8_t> blob(d.blob_bytes, 0);
+      if (!tk.empty()) std::memcpy(blob.data(), tk.data(), tk.size() * sizeof(DTask));
+      if (!sv.empty()) std::memcpy(blob.data() + d.off_views, sv.data(), sv.size() * sizeof(DView));
+      if (!si.empty()) std::memcpy(blob.data() + d.off_ins, si.data(), si.size() * sizeof(DIns));
+      blobs.push_back(blob);
       ds.push_back(d);
+      max_items = std::max<int>(max_items, (int)items);
+      n_tasks_total += tk.size();
     }
     dump << "workspace: " << kHeaderBytes << " header + " << arena_bytes << " arena bytes\n";
     for (auto& kv : arena_off) dump << "  arena " << kv.first << " @" << kv.second << "\n";
     for (auto& kv : bound) dump << "  bound " << kv.first << " -> out[" << kv.second << "]\n";
     for (auto& kv : direct) dump << "  direct in-place out[" << kv.first << "] -> in[" << kv.second << "]\n";
-    // serialize
+    // serialize: header | stage table | blobs
     DHeader h{};
     h.magic = kPlanMagic;
     h.n_stages = (uint32_t)ds.size();
-    h.n_tasks = (uint32_t)dt.size();
-    h.n_views = (uint32_t)views.size();
-    h.n_ins = (uint32_t)ins.size();
-    uint32_t off = (uint32_t)align_up(sizeof(DHeader), 64);
-    h.off_stages = off;
-    off = (uint32_t)align_up(off + ds.size() * sizeof(DStage), 64);
-    h.off_tasks = off;
-    off = (uint32_t)align_up(off + dt.size() * sizeof(DTask), 64);
-    h.off_views = off;
-    off = (uint32_t)align_up(off + views.size() * sizeof(DView), 64);
-    h.off_ins = off;
-    off = (uint32_t)align_up(off + ins.size() * sizeof(DIns), 64);
+    h.off_stages = (uint32_t)align_up(sizeof(DHeader), 64);
+    uint32_t off = (uint32_t)align_up(h.off_stages + ds.size() * sizeof(DStage), 64);
+    for (size_t s = 0; s < ds.size(); ++s) {
+      ds[s].blob_off = off;
+      off = (uint32_t)align_up(off + ds[s].blob_bytes, 64);
+      h.max_blob = std::max(h.max_blob, ds[s].blob_bytes);
+    }
     h.bytes = off;
     pl.bytes.assign(off, 0);
     std::memcpy(pl.bytes.data(), &h, sizeof(h));
     if (!ds.empty()) std::memcpy(pl.bytes.data() + h.off_stages, ds.data(), ds.size() * sizeof(DStage));
-    if (!dt.empty()) std::memcpy(pl.bytes.data() + h.off_tasks, dt.data(), dt.size() * sizeof(DTask));
-    if (!views.empty()) std::memcpy(pl.bytes.data() + h.off_views, views.data(), views.size() * sizeof(DView));
-    if (!ins.empty()) std::memcpy(pl.bytes.data() + h.off_ins, ins.data(), ins.size() * sizeof(DIns));
+    for (size_t s = 0; s < ds.size(); ++s)
+      if (!blobs[s].empty()) std::memcpy(pl.bytes.data() + ds[s].blob_off, blobs[s].data(), blobs[s].size());
     pl.n_stages = (int)ds.size();
     pl.max_items = max_items;
     pl.workspace_bytes = kHeaderBytes + align_up(arena_bytes, kAlign);
@@ -1676,7 +1711,7 @@ struct Builder {
     s.workspace_bytes = pl.workspace_bytes;
     s.n_stages = (int32_t)ds.size();
     s.grid_barriers = std::max(0, (int32_t)ds.size() - 1);
-    s.n_tasks = (int32_t)dt.size();
+    s.n_tasks = (int32_t)n_tasks_total;
     s.inlined_ops = (int32_t)inlined.size();
     int mat = 0, fe = 0, se = 0, fu = 0;
     for (auto& e : sched) {
