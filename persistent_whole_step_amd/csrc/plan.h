@@ -1,6 +1,6 @@
 // Device-resident plan of one compiled whole-step program.
 //
-// The host scheduler (tk_compile.cpp) turns a program into a list of stages;
+// The host scheduler (tk_sched.cpp) turns a program into a list of stages;
 // the persistent kernel (tk_device.hip) walks the stages, runs every work item
 // of a stage, and separates consecutive stages with one grid barrier.  This
 // header is the contract between the two: plain structs, no pointers (bases are
@@ -21,20 +21,21 @@ constexpr int kBlock = 256;         // threads per workgroup (4 wave64)
 constexpr int kMaxBases = 240;      // pointer slots per launch (inputs, outputs, workspace)
 constexpr int kMaxDims = 4;         // iteration dims after collapsing
 constexpr int kMaxSlots = 4;        // saved values in the expression machine
-constexpr uint32_t kPlanLds = 8192;        // LDS bytes for the current stage's descriptors
+constexpr uint32_t kPlanLds = 16384;       // LDS bytes for the current stage's descriptors (every stage blob fits)
 constexpr uint32_t kMaxGrid = 1024;        // workgroups per launch (barrier flag slots)
 constexpr uint32_t kFlagStride = 16;       // u32 words between two workgroups' flags (64 B)
 constexpr uint32_t kHdrArrive = 16384;     // u32 [kMaxGrid * kFlagStride] arrival epochs
 constexpr uint32_t kHdrRelease = kHdrArrive + kMaxGrid * kFlagStride * 4;  // u32 release epochs
 constexpr uint32_t kHeaderBytes = kHdrRelease + kMaxGrid * kFlagStride * 4;  // 147456: header size
-constexpr uint32_t kMaxTimedStages = 480;
+constexpr uint32_t kMaxTimedStages = 400;
 
 // Workspace header layout (bytes).  Each word sits on its own 64-byte line.
 constexpr uint32_t kHdrEpoch = 0;      // last barrier epoch of the previous launch on this workspace
 constexpr uint32_t kHdrGen = 64;       // (unused)
 constexpr uint32_t kHdrAbort = 128;    // nonzero: a barrier timed out; the launch stopped
 constexpr uint32_t kHdrAbortStage = 192;
-constexpr uint32_t kHdrStamps = 1024;  // optional: u64 [stage][2] arrival/departure ticks of workgroup 0
+constexpr uint32_t kHdrStamps = 1024;  // optional: u64 [stage][4] of workgroup 0: stage start, items done,
+                                       // barrier entry, barrier exit (100 MHz ticks)
 
 // Addressing of one operand over a task's iteration space: element
 // (c0..c3) lives at bases[base] + (offset + sum c_i * stride[i]) * size(dtype).

@@ -423,7 +423,7 @@ tk_status tk_set_debug(tk_program* p, int32_t timestamps, uint32_t stagger_seed,
 
 tk_status tk_read_timestamps(const tk_program* p, const tk_tensor* ws, void* stream, uint64_t* out, size_t n) {
   if (!p || !ws || !out) return fail(TK_E_ARG, "NULL argument");
-  size_t want = std::min<size_t>(n, 2 * (size_t)std::min<int>(p->plan.n_stages, (int)kMaxTimedStages));
+  size_t want = std::min<size_t>(n, 4 * (size_t)std::min<int>(p->plan.n_stages, (int)kMaxTimedStages));
   hipError_t e = hipStreamSynchronize((hipStream_t)stream);
   if (e == hipSuccess) e = hipMemcpy(out, (uint8_t*)ws->data + kHdrStamps, want * 8, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "timestamp read");

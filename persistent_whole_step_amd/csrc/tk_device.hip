@@ -4,11 +4,14 @@
 // the plan's stages, takes the stage's work items round-robin
 // (item = blockIdx.x + i * gridDim.x), and all workgroups meet at a
 // global-memory grid barrier between stages.  This is the execution model of
-// the trainkernel generator (codegen.py `_Generator.generate`: operators in
-// topological order separated by `mk_grid_sync`; the device helpers of
-// `_CUDA_PREAMBLE`), re-designed as an interpreter of a device-resident plan:
-//   * pointwise work and every epilogue run on a small accumulator machine over
-//     chunks of 8 consecutive elements per lane (vector loads/stores);
+// the trainkernel generator (trainkernel wheel, codegen.py: operators emitted
+// in topological order with a grid sync between dependent ones, and the device
+// helpers of its CUDA preamble), re-designed as an interpreter of a
+// device-resident plan:
+//   * pointwise work and every epilogue run on one expression machine that is
+//     compiled into the kernel exactly once; each task kind feeds it batches of
+//     16 elements per thread (two 8-wide chunks, or sixteen single elements)
+//     through LDS, so the code every stage runs stays small;
 //   * contractions with bf16/f16 operands run on MFMA 32x32x16 tiles with
 //     LDS double buffering; other dtypes use an fp32-FMA tile whose per-output
 //     accumulation is sequential in k;
@@ -16,6 +19,9 @@
 //     the 64 lanes of a wave;
 //   * reductions sum fixed partitions in a fixed order (deterministic, every
 //     element covered).
+// Every pointer into device memory carries the global address space and every
+// LDS access the local one, so a wait for LDS never waits for global traffic
+// (generic "flat" accesses count against both wait counters).
 // Built with -ffp-contract=off: no implicit fused multiply-adds, so pointwise
 // results equal IEEE binary32 step by step.
 #include <hip/hip_runtime.h>
@@ -26,16 +32,28 @@
 using namespace tkplan;
 
 #define DEV __device__ __forceinline__
+#define GLOBAL __attribute__((address_space(1)))
+#define LDS __attribute__((address_space(3)))
 
 namespace {
 
 constexpr int kSmemBytes = 2 * 2 * 128 * 72 * 2;  // A and B tiles, double buffered (73728 B)
+constexpr int kVmElems = 16;                       // elements per thread per machine batch
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// Workgroup-shared storage.
+__shared__ __attribute__((aligned(16))) uint8_t g_smem[kSmemBytes];  // GEMM staging / C tile / scratch
+__shared__ __attribute__((aligned(16))) uint8_t g_plan[kPlanLds];    // current stage's descriptors
+__shared__ float g_xv[kVmElems * kBlock];     // machine exchange: values   [element][thread]
+__shared__ uint32_t g_xe[kVmElems * kBlock];  // machine exchange: first linear element of each chunk
+
+DEV LDS float& xv(int j) { return ((LDS float*)g_xv)[j * kBlock + threadIdx.x]; }
+DEV LDS uint32_t& xe(int q) { return ((LDS uint32_t*)g_xe)[q * kBlock + threadIdx.x]; }
 
 // ------------------------------------------------------------ conversions --
 
@@ -59,34 +77,192 @@ DEV uint32_t f32_to_f16_bits(float f) {
   return (uint32_t)__builtin_bit_cast(uint16_t, v);
 }
 
-DEV float round_to(float x, uint32_t dt) {
-  if (dt == DT_BF16) return bf16_bits_to_f32(f32_to_bf16_bits(x));
-  if (dt == DT_F16) return f16_bits_to_f32(f32_to_f16_bits(x));
-  return x;
-}
+DEV float half_bits_to_f32(uint32_t h, bool bf) { return bf ? bf16_bits_to_f32(h) : f16_bits_to_f32(h); }
+DEV uint32_t f32_to_half_bits(float f, bool bf) { return bf ? f32_to_bf16_bits(f) : f32_to_f16_bits(f); }
 
 DEV uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+DEV int64_t uniform64(int64_t v) {
+  const uint64_t u = (uint64_t)v;
+  return (int64_t)(((uint64_t)uniform((uint32_t)(u >> 32)) << 32) | uniform((uint32_t)u));
+}
 
+template <class T>
+DEV bool aligned16(const GLOBAL T* p) {
+  return ((uintptr_t)p & 15) == 0;
+}
+
+// ------------------------------------------------------- launch context --
+// The argument block is read once per launch: scalars into registers, the
+// base-pointer table into LDS.  Later reads never go back to the kernel
+// argument segment.
+__shared__ uint64_t g_bases[kMaxBases];
+
+struct Ctx {
+  GLOBAL uint8_t* ws;          // workspace: header, then arena
+  const GLOBAL uint8_t* plan;  // device-resident plan
+  uint32_t flags;              // K_* debug switches
+  uint32_t stagger_seed;
+};
+
+DEV GLOBAL uint8_t* base_ptr(const Ctx&, uint32_t base) {
+  return (GLOBAL uint8_t*)uniform64((int64_t)((const LDS uint64_t*)g_bases)[base]);
+}
 // ------------------------------------------------------- element access --
 
-DEV const uint8_t* base_ptr(const KArgs& ka, uint32_t base) { return (const uint8_t*)ka.bases[base]; }
+DEV GLOBAL float* ws_f32(const Ctx& ka, uint64_t off) { return (GLOBAL float*)(ka.ws + off); }
 
-DEV float load_elem(const uint8_t* p, uint32_t dt, int64_t idx) {
-  switch (dt) {
-    case DT_F32: return ((const float*)p)[idx];
-    case DT_BF16: return bf16_bits_to_f32(((const uint16_t*)p)[idx]);
-    case DT_F16: return f16_bits_to_f32(((const uint16_t*)p)[idx]);
-    default: return (float)((const int8_t*)p)[idx];
+DEV float load_elem(const GLOBAL uint8_t* p, uint32_t dt, int64_t idx) {
+  if (dt == DT_F32) return ((const GLOBAL float*)p)[idx];
+  if (dt == DT_I8) return (float)((const GLOBAL int8_t*)p)[idx];
+  return half_bits_to_f32(((const GLOBAL uint16_t*)p)[idx], dt == DT_BF16);
+}
+
+// W consecutive elements (stride s) starting at element idx.  Unit-stride
+// aligned chunks use 16-byte loads; stride 0 loads once and broadcasts.
+template <int W>
+DEV void load_chunk(const GLOBAL uint8_t* p, uint32_t dt, int64_t idx, int64_t s, float (&x)[W]) {
+  if (dt == DT_F32) {
+    const GLOBAL float* q = (const GLOBAL float*)p + idx;
+    if (W == 8 && s == 1 && aligned16(q)) {
+      const u32x4 r0 = *(const GLOBAL u32x4*)q, r1 = *(const GLOBAL u32x4*)(q + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        x[j] = __uint_as_float(r0[j]);
+        x[4 + j] = __uint_as_float(r1[j]);
+      }
+    } else if (W == 8 && s == 0) {
+      const float a = q[0];
+#pragma unroll
+      for (int j = 0; j < W; ++j) x[j] = a;
+    } else {
+#pragma unroll
+      for (int j = 0; j < W; ++j) x[j] = q[j * s];
+    }
+  } else if (dt == DT_I8) {
+    const GLOBAL int8_t* q = (const GLOBAL int8_t*)p + idx;
+#pragma unroll
+    for (int j = 0; j < W; ++j) x[j] = (float)q[j * s];
+  } else {
+    const GLOBAL uint16_t* q = (const GLOBAL uint16_t*)p + idx;
+    uint32_t h[W];
+    if (W == 8 && s == 1 && aligned16(q)) {
+      const u32x4 r = *(const GLOBAL u32x4*)q;
+#pragma unroll
+      for (int j = 0; j < W / 2; ++j) {
+        h[2 * j] = r[j] & 0xffffu;
+        h[2 * j + 1] = r[j] >> 16;
+      }
+    } else if (W == 8 && s == 0) {
+      const uint32_t a = q[0];
+#pragma unroll
+      for (int j = 0; j < W; ++j) h[j] = a;
+    } else {
+#pragma unroll
+      for (int j = 0; j < W; ++j) h[j] = q[j * s];
+    }
+    const bool bf = dt == DT_BF16;
+#pragma unroll
+    for (int j = 0; j < W; ++j) x[j] = half_bits_to_f32(h[j], bf);
   }
 }
 
-DEV void store_elem(uint8_t* p, uint32_t dt, int64_t idx, float v) {
-  switch (dt) {
-    case DT_F32: ((float*)p)[idx] = v; break;
-    case DT_BF16: ((uint16_t*)p)[idx] = (uint16_t)f32_to_bf16_bits(v); break;
-    case DT_F16: ((uint16_t*)p)[idx] = (uint16_t)f32_to_f16_bits(v); break;
-    default: break;
+template <int W>
+DEV void store_chunk(GLOBAL uint8_t* p, uint32_t dt, int64_t idx, int64_t s, const float (&x)[W]) {
+  if (dt == DT_F32) {
+    GLOBAL float* q = (GLOBAL float*)p + idx;
+    if (W == 8 && s == 1 && aligned16(q)) {
+      u32x4 r0, r1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        r0[j] = __float_as_uint(x[j]);
+        r1[j] = __float_as_uint(x[4 + j]);
+      }
+      *(GLOBAL u32x4*)q = r0;
+      *(GLOBAL u32x4*)(q + 4) = r1;
+    } else {
+#pragma unroll
+      for (int j = 0; j < W; ++j) q[j * s] = x[j];
+    }
+  } else if (dt != DT_I8) {
+    GLOBAL uint16_t* q = (GLOBAL uint16_t*)p + idx;
+    const bool bf = dt == DT_BF16;
+    uint32_t h[W];
+#pragma unroll
+    for (int j = 0; j < W; ++j) h[j] = f32_to_half_bits(x[j], bf);
+    if (W == 8 && s == 1 && aligned16(q)) {
+      u32x4 r;
+#pragma unroll
+      for (int j = 0; j < W / 2; ++j) r[j] = h[2 * j] | (h[2 * j + 1] << 16);
+      *(GLOBAL u32x4*)q = r;
+    } else {
+#pragma unroll
+      for (int j = 0; j < W; ++j) q[j * s] = (uint16_t)h[j];
+    }
   }
+}
+
+DEV void unravel4(uint32_t e, const uint32_t (&dims)[kMaxDims], uint32_t nd, uint32_t (&c)[kMaxDims]) {
+#pragma unroll
+  for (int d = kMaxDims - 1; d >= 0; --d) {
+    if ((uint32_t)d >= nd) {
+      c[d] = 0;
+    } else {
+      c[d] = e % dims[d];
+      e /= dims[d];
+    }
+  }
+}
+
+// ------------------------------------------------------ debug trace --
+// With K_TIMESTAMPS, lane 0 of workgroup 0 also records up to kTraceLen
+// fine-grained timestamps of the current launch into the workspace header.
+constexpr uint32_t kTraceOff = 14336;
+constexpr uint32_t kTraceLen = 64;
+
+DEV void trace_stamp(const Ctx& ka, uint32_t tag) {
+  if (!(ka.flags & K_TIMESTAMPS) || blockIdx.x != 0 || threadIdx.x != 0) return;
+  __shared__ uint32_t s_trace_n;  // entries written by this launch (reset at launch start)
+  if (tag == 0xffffffffu) {
+    s_trace_n = 0;
+    return;
+  }
+  const uint32_t i = s_trace_n;
+  if (i >= kTraceLen) return;
+  GLOBAL uint64_t* ent = (GLOBAL uint64_t*)(ka.ws + kTraceOff + 8) + 2 * i;
+  ent[0] = tag;
+  ent[1] = __builtin_amdgcn_s_memrealtime();
+  s_trace_n = i + 1;
+  *(GLOBAL uint32_t*)(ka.ws + kTraceOff) = i + 1;
+}
+
+// ------------------------------------------------------ plan access (LDS) --
+
+// A task's descriptor with every word made wave-uniform (scalar registers).
+DEV DTask load_task(uint32_t i) {
+  constexpr int N = sizeof(DTask) / 4;
+  static_assert(sizeof(DTask) % 4 == 0, "DTask words");
+  const LDS uint32_t* w = (const LDS uint32_t*)(g_plan + i * sizeof(DTask));
+  struct Words {
+    uint32_t u[N];
+  } r;
+#pragma unroll
+  for (int k = 0; k < N; ++k) r.u[k] = uniform(w[k]);
+  return __builtin_bit_cast(DTask, r);
+}
+
+DEV uint32_t task_item_begin(uint32_t i) {
+  return uniform(((const LDS DTask*)g_plan)[i].item_begin);
+}
+
+DEV DView load_view(uint32_t off) {
+  const LDS DView& v = *(const LDS DView*)(g_plan + off);
+  DView r;
+  r.offset = uniform64(v.offset);
+#pragma unroll
+  for (int d = 0; d < kMaxDims; ++d) r.stride[d] = uniform64(v.stride[d]);
+  r.base = (uint16_t)uniform(v.base);
+  r.dtype = (uint8_t)uniform(v.dtype);
+  return r;
 }
 
 // Element index of a view at coordinates c (dims past the task's rank have
@@ -102,365 +278,251 @@ DEV int64_t inner_stride(const DView& v, uint32_t nd) {
   return nd <= 1 ? v.stride[0] : nd == 2 ? v.stride[1] : nd == 3 ? v.stride[2] : v.stride[3];
 }
 
-// Load W consecutive (along the innermost iteration dim) elements of a view.
-template <int W>
-DEV void load_view(const KArgs& ka, const DView& v, const uint32_t (&c)[kMaxDims], uint32_t nd, float (&x)[W]) {
-  const uint8_t* p = base_ptr(ka, v.base);
-  const int64_t idx = view_index(v, c);
-  const int64_t s = inner_stride(v, nd);
-  const uint32_t dt = v.dtype;
-  if (W == 1) {
-    x[0] = load_elem(p, dt, idx);
-    return;
-  }
-  if (s == 0) {
-    float a = load_elem(p, dt, idx);
-#pragma unroll
-    for (int j = 0; j < W; ++j) x[j] = a;
-    return;
-  }
-  if (s == 1) {
-    if (dt == DT_BF16 || dt == DT_F16) {
-      const uint16_t* q = (const uint16_t*)p + idx;
-      if (((uintptr_t)q & 15) == 0) {
-        u32x4 r = *(const u32x4*)q;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t lo = r[j] & 0xffffu, hi = r[j] >> 16;
-          x[2 * j] = dt == DT_BF16 ? bf16_bits_to_f32(lo) : f16_bits_to_f32(lo);
-          x[2 * j + 1] = dt == DT_BF16 ? bf16_bits_to_f32(hi) : f16_bits_to_f32(hi);
-        }
-        return;
-      }
-    } else if (dt == DT_F32) {
-      const float* q = (const float*)p + idx;
-      if (((uintptr_t)q & 15) == 0) {
-        u32x4 r0 = *(const u32x4*)q;
-        u32x4 r1 = *(const u32x4*)(q + 4);
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          x[j] = __uint_as_float(r0[j]);
-          x[4 + j] = __uint_as_float(r1[j]);
-        }
-        return;
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < W; ++j) x[j] = load_elem(p, dt, idx + (int64_t)j * s);
-}
-
-template <int W>
-DEV void store_view(const KArgs& ka, const DView& v, const uint32_t (&c)[kMaxDims], uint32_t nd, const float (&x)[W]) {
-  uint8_t* p = (uint8_t*)ka.bases[v.base];
-  const int64_t idx = view_index(v, c);
-  const int64_t s = inner_stride(v, nd);
-  const uint32_t dt = v.dtype;
-  if (W == 8 && s == 1) {
-    if (dt == DT_BF16 || dt == DT_F16) {
-      uint16_t* q = (uint16_t*)p + idx;
-      if (((uintptr_t)q & 15) == 0) {
-        u32x4 r;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          uint32_t lo = dt == DT_BF16 ? f32_to_bf16_bits(x[2 * j]) : f32_to_f16_bits(x[2 * j]);
-          uint32_t hi = dt == DT_BF16 ? f32_to_bf16_bits(x[2 * j + 1]) : f32_to_f16_bits(x[2 * j + 1]);
-          r[j] = lo | (hi << 16);
-        }
-        *(u32x4*)q = r;
-        return;
-      }
-    } else if (dt == DT_F32) {
-      float* q = (float*)p + idx;
-      if (((uintptr_t)q & 15) == 0) {
-        u32x4 r0, r1;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          r0[j] = __float_as_uint(x[j]);
-          r1[j] = __float_as_uint(x[4 + j]);
-        }
-        *(u32x4*)q = r0;
-        *(u32x4*)(q + 4) = r1;
-        return;
-      }
-    }
-  }
-#pragma unroll
-  for (int j = 0; j < W; ++j) store_elem(p, dt, idx + (int64_t)j * s, x[j]);
-}
-
 // ------------------------------------------------------ expression machine --
 
-// The current stage's descriptors (in LDS when the stage blob fits).
-struct Plan {
-  const DTask* tasks;
-  const DView* views;
-  const DIns* ins;
+// One batch for the machine: a program over an iteration space.
+struct Batch {
+  uint32_t ins;         // byte offset (in the LDS plan) of the first instruction
+  uint32_t n;           // instructions
+  uint32_t width;       // 8: two 8-wide chunks per thread; 1: sixteen single elements
+  uint32_t nd;
+  uint32_t dims[kMaxDims];
+  uint32_t accumulate;  // reductions: add the results into the thread's sums
 };
 
-template <int W>
-struct Slots {
-  float s0[W], s1[W], s2[W], s3[W];
-  DEV void get(uint32_t k, float (&x)[W]) const {
-    switch (k) {
-      case 0:
+// Run a program on C chunks of W elements (C * W == 16).  Chunk q starts at
+// linear element xe(q) of the iteration space and covers W consecutive
+// elements along its last dim; chunks whose bit in `live` is clear touch no
+// memory.  The accumulators start from and end in the exchange values.  The
+// loads of all chunks of one instruction are issued before any is used, so an
+// instruction costs one memory latency, not one per element.
+template <int W, int C>
+DEV void vm_run(const Ctx& ka, const Batch& b, uint32_t views_off, uint32_t live) {
+  float acc[C][W];
+  uint32_t c[C][kMaxDims];
 #pragma unroll
-        for (int j = 0; j < W; ++j) x[j] = s0[j];
-        break;
-      case 1:
+  for (int q = 0; q < C; ++q) {
+    unravel4(xe(q), b.dims, b.nd, c[q]);
 #pragma unroll
-        for (int j = 0; j < W; ++j) x[j] = s1[j];
-        break;
-      case 2:
-#pragma unroll
-        for (int j = 0; j < W; ++j) x[j] = s2[j];
-        break;
-      default:
-#pragma unroll
-        for (int j = 0; j < W; ++j) x[j] = s3[j];
-        break;
-    }
+    for (int j = 0; j < W; ++j) acc[q][j] = xv(q * W + j);
   }
-  DEV void set(uint32_t k, const float (&x)[W]) {
-    switch (k) {
-      case 0:
+  float s0[C][W], s1[C][W], s2[C][W], s3[C][W];
+  for (uint32_t pc = 0; pc < b.n; ++pc) {
+    const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + b.ins + pc * sizeof(DIns));
+    const uint32_t w0 = uniform(iw[0]), w1 = uniform(iw[1]);
+    const float a = __uint_as_float(uniform(iw[2])), sv = __uint_as_float(uniform(iw[3]));
+    const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff, rnd = (w0 >> 16) & 0xff, rev = w0 >> 24;
+    const uint32_t arg = w1 & 0xffff;
+    float x[C][W];
+    if (src == SRC_VIEW || op == VM_STORE) {
+      const DView v = load_view(views_off + arg * sizeof(DView));
+      const int64_t s = inner_stride(v, b.nd);
+      const uint32_t dt = v.dtype;
+      GLOBAL uint8_t* p = base_ptr(ka, v.base);
+      if (op == VM_STORE) {
 #pragma unroll
-        for (int j = 0; j < W; ++j) s0[j] = x[j];
-        break;
-      case 1:
+        for (int q = 0; q < C; ++q)
+          if (live & (1u << q)) store_chunk<W>(p, dt, view_index(v, c[q]), s, acc[q]);
+        continue;
+      }
 #pragma unroll
-        for (int j = 0; j < W; ++j) s1[j] = x[j];
-        break;
-      case 2:
+      for (int q = 0; q < C; ++q) {
+        if (live & (1u << q)) {
+          load_chunk<W>(p, dt, view_index(v, c[q]), s, x[q]);
+        } else {
 #pragma unroll
-        for (int j = 0; j < W; ++j) s2[j] = x[j];
-        break;
-      default:
-#pragma unroll
-        for (int j = 0; j < W; ++j) s3[j] = x[j];
-        break;
-    }
-  }
-};
-
-// Run `n` instructions on the accumulator `acc` at chunk coordinates `c`.
-template <int W>
-DEV void vm_run(const KArgs& ka, const Plan& pl, uint32_t first, uint32_t n, const uint32_t (&c)[kMaxDims],
-                uint32_t nd, float (&acc)[W]) {
-  Slots<W> sl;
-  for (uint32_t pc = 0; pc < n; ++pc) {
-    const DIns in = pl.ins[first + pc];
-    const uint32_t op = uniform(in.op), src = uniform(in.src), rnd = uniform(in.rnd), rev = uniform(in.rev);
-    const uint32_t arg = uniform(in.arg);
-    float x[W];
-    if (src == SRC_VIEW) {
-      load_view<W>(ka, pl.views[arg], c, nd, x);
-    } else if (src == SRC_SCALAR) {
-#pragma unroll
-      for (int j = 0; j < W; ++j) x[j] = in.s;
-    } else if (src == SRC_SLOT) {
-      sl.get(arg, x);
-    } else {
-#pragma unroll
-      for (int j = 0; j < W; ++j) x[j] = 0.0f;
-    }
-    const float a = in.a;
-    switch (op) {
-      case VM_LOAD:
-#pragma unroll
-        for (int j = 0; j < W; ++j) acc[j] = x[j];
-        break;
-      case VM_ADD:
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-          if (rev) { float t = a * acc[j]; acc[j] = x[j] + t; }
-          else { float t = a * x[j]; acc[j] = acc[j] + t; }
+          for (int j = 0; j < W; ++j) x[q][j] = 0.0f;
         }
+      }
+    } else if (src == SRC_SLOT) {
+#pragma unroll
+      for (int q = 0; q < C; ++q)
+#pragma unroll
+        for (int j = 0; j < W; ++j)
+          x[q][j] = arg == 0 ? s0[q][j] : arg == 1 ? s1[q][j] : arg == 2 ? s2[q][j] : s3[q][j];
+    } else {
+      const float k = src == SRC_SCALAR ? sv : 0.0f;
+#pragma unroll
+      for (int q = 0; q < C; ++q)
+#pragma unroll
+        for (int j = 0; j < W; ++j) x[q][j] = k;
+    }
+#define TK_EACH(expr)                             \
+  _Pragma("unroll") for (int q = 0; q < C; ++q)   \
+  _Pragma("unroll") for (int j = 0; j < W; ++j) { \
+    float& y = acc[q][j];                         \
+    const float o = x[q][j];                      \
+    (void)o;                                      \
+    expr;                                         \
+  }
+    switch (op) {
+      case VM_LOAD: TK_EACH(y = o) break;
+      case VM_ADD:
+        if (rev) { TK_EACH(float t = a * y; y = o + t) }
+        else { TK_EACH(float t = a * o; y = y + t) }
         break;
       case VM_SUB:
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-          if (rev) { float t = a * acc[j]; acc[j] = x[j] - t; }
-          else { float t = a * x[j]; acc[j] = acc[j] - t; }
-        }
+        if (rev) { TK_EACH(float t = a * y; y = o - t) }
+        else { TK_EACH(float t = a * o; y = y - t) }
         break;
-      case VM_MUL:
-#pragma unroll
-        for (int j = 0; j < W; ++j) acc[j] = rev ? x[j] * acc[j] : acc[j] * x[j];
-        break;
+      case VM_MUL: TK_EACH(y = y * o) break;
       case VM_DIV:
-#pragma unroll
-        for (int j = 0; j < W; ++j) acc[j] = rev ? x[j] / acc[j] : acc[j] / x[j];
+        if (rev) { TK_EACH(y = o / y) }
+        else { TK_EACH(y = y / o) }
         break;
-      case VM_NEG:
-#pragma unroll
-        for (int j = 0; j < W; ++j) acc[j] = -acc[j];
-        break;
-      case VM_RELU:
-#pragma unroll
-        for (int j = 0; j < W; ++j) acc[j] = acc[j] < 0.0f ? 0.0f : acc[j];
-        break;
-      case VM_SQUARE:
-#pragma unroll
-        for (int j = 0; j < W; ++j) acc[j] = acc[j] * acc[j];
-        break;
-      case VM_POW:
-#pragma unroll
-        for (int j = 0; j < W; ++j) acc[j] = powf(acc[j], a);
-        break;
+      case VM_NEG: TK_EACH(y = -y) break;
+      case VM_RELU: TK_EACH(y = y < 0.0f ? 0.0f : y) break;
+      case VM_SQUARE: TK_EACH(y = y * y) break;
+      case VM_POW: TK_EACH(y = powf(y, a)) break;
       case VM_TB:
-#pragma unroll
-        for (int j = 0; j < W; ++j) {
-          if (rev) acc[j] = acc[j] <= a ? 0.0f : x[j];
-          else acc[j] = x[j] <= a ? 0.0f : acc[j];
-        }
+        if (rev) { TK_EACH(y = y <= a ? 0.0f : o) }
+        else { TK_EACH(y = o <= a ? 0.0f : y) }
         break;
       case VM_SAVE:
-        sl.set(arg, acc);
+        TK_EACH(s0[q][j] = arg == 0 ? y : s0[q][j]; s1[q][j] = arg == 1 ? y : s1[q][j];
+                s2[q][j] = arg == 2 ? y : s2[q][j]; s3[q][j] = arg == 3 ? y : s3[q][j])
         break;
-      case VM_STORE:
-        store_view<W>(ka, pl.views[arg], c, nd, acc);
-        break;
-      case VM_SCALE:
-#pragma unroll
-        for (int j = 0; j < W; ++j) acc[j] = a * acc[j];
-        break;
-      case VM_ZERO:
-#pragma unroll
-        for (int j = 0; j < W; ++j) acc[j] = 0.0f;
-        break;
-      default:
-        break;
+      case VM_SCALE: TK_EACH(y = a * y) break;
+      case VM_ZERO: TK_EACH(y = 0.0f) break;
+      default: break;
     }
-    if (rnd != RND_NONE) {
+#undef TK_EACH
+    if (rnd == DT_BF16) {
 #pragma unroll
-      for (int j = 0; j < W; ++j) acc[j] = round_to(acc[j], rnd);
+      for (int q = 0; q < C; ++q)
+#pragma unroll
+        for (int j = 0; j < W; ++j) acc[q][j] = bf16_bits_to_f32(f32_to_bf16_bits(acc[q][j]));
+    } else if (rnd == DT_F16) {
+#pragma unroll
+      for (int q = 0; q < C; ++q)
+#pragma unroll
+        for (int j = 0; j < W; ++j) acc[q][j] = f16_bits_to_f32(f32_to_f16_bits(acc[q][j]));
     }
   }
+#pragma unroll
+  for (int q = 0; q < C; ++q)
+#pragma unroll
+    for (int j = 0; j < W; ++j) xv(q * W + j) = acc[q][j];
 }
 
-DEV void unravel(uint32_t e, const DTask& t, uint32_t nd, uint32_t (&c)[kMaxDims]) {
-#pragma unroll
-  for (int d = kMaxDims - 1; d >= 0; --d) {
-    if ((uint32_t)d >= nd) {
-      c[d] = 0;
-    } else {
-      const uint32_t n = t.dims[d];
-      c[d] = e % n;
-      e /= n;
-    }
-  }
-}
+// ------------------------------------------------------------ work items --
+// Every work item runs as: an optional prologue (a contraction's main loop,
+// a GEMV's dot products), then batches b = 0, 1, ... each filled by the task
+// kind, run on the machine and consumed by the task kind, until the kind
+// reports no further batch.  Batch decisions are uniform across the workgroup.
 
-// ------------------------------------------------------------- elementwise --
+// Per-item state carried across batches.
+struct ItemState {
+  uint32_t m0, n0, split_index;  // contraction tile origin / split-K part
+  int bm, bn;                    // contraction tile size
+  float acc;                     // reductions: this thread's running sum
+  float acc8[8];
+};
 
-template <int W>
-__device__ __noinline__ void run_ew(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item) {
-  const uint32_t nd = t.ndim;
-  uint32_t numel = 1;
-#pragma unroll
-  for (int d = 0; d < kMaxDims; ++d) numel *= t.dims[d];  // unused dims are 1
-  const uint32_t base = item * 2048u;
-  if (W == 8) {
-    const uint32_t e = base + threadIdx.x * 8u;
-    if (e < numel) {
-      uint32_t c[kMaxDims];
-      unravel(e, t, nd, c);
-      float acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      vm_run<8>(ka, pl, t.expr_first, t.expr_len, c, nd, acc);
-    }
-  } else {
-    for (uint32_t j = 0; j < 8; ++j) {
-      const uint32_t e = base + j * 256u + threadIdx.x;
-      if (e < numel) {
-        uint32_t c[kMaxDims];
-        unravel(e, t, nd, c);
-        float acc[1] = {0};
-        vm_run<1>(ka, pl, t.expr_first, t.expr_len, c, nd, acc);
-      }
-    }
-  }
-}
-
-// Epilogue over a tile held in LDS as fp32 [BM][BN + 4].
-template <int W>
-DEV void tile_epilogue(const KArgs& ka, const Plan& pl, const DTask& t, const float* ctile, int BM, int BN,
-                       uint32_t m0, uint32_t n0, uint32_t split_index) {
-  const int pitch = BN + 4;
-  const int cpr = BN / W;  // chunks per row
-  const int nchunks = BM * cpr;
-  const bool partial = (t.flags & F_PARTIAL) != 0;
-  for (int q = threadIdx.x; q < nchunks; q += kBlock) {
-    const int r = q / cpr, cc = (q % cpr) * W;
-    const uint32_t row = m0 + r, col = n0 + cc;
-    if (row >= t.m || col >= t.n) continue;
-    float acc[W];
-#pragma unroll
-    for (int j = 0; j < W; ++j) acc[j] = ctile[r * pitch + cc + j];
-    if (partial) {
-      float* P = (float*)(ka.ws + t.scratch) + ((uint64_t)split_index * t.m + row) * t.n + col;
-#pragma unroll
-      for (int j = 0; j < W; ++j) P[j] = acc[j];
-      continue;
-    }
-    uint32_t c[kMaxDims] = {row, col, 0, 0};
-    vm_run<W>(ka, pl, t.expr_first, t.expr_len, c, 2, acc);
-  }
+// Tile index for work item `local` of a contraction: the eight XCDs take
+// workgroups round-robin, so items with equal local % 8 share an XCD; give
+// each such class a contiguous run of tiles (row-major), which share operand
+// panels in that XCD's L2.
+DEV uint32_t xcd_tile(uint32_t local, uint32_t tiles) {
+  if (tiles % 8 != 0) return local;
+  return (local % 8) * (tiles / 8) + local / 8;
 }
 
 // ------------------------------------------------------ fp32-FMA contraction --
-// 64x64 output tile, 256 threads, each thread a 4x4 block; K staged 16 deep.
-// Each output accumulates acc = fma(a_k, b_k, acc) for k = 0, 1, ... in order.
+// 64x64 output tile, 256 threads, each thread a 4x4 block; K staged 32 deep in
+// a double-buffered LDS ring, the next slice's loads issued before the current
+// slice is consumed.  Each output accumulates acc = fma(a_k, b_k, acc) for
+// k = 0, 1, ... in order.
 
-__device__ __noinline__ void run_gemm_simt(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item, uint8_t* smem) {
-  const uint32_t tm = item / t.tiles_n, tn = item % t.tiles_n;
+DEV void simt_load(const GLOBAL uint8_t* p, const DView& v, bool mn_contig, bool is_a, uint32_t r0, uint32_t rmax,
+                   uint32_t k0, uint32_t kmax, float (&reg)[8]) {
+  const int64_t s_r = is_a ? v.stride[0] : v.stride[1], s_k = is_a ? v.stride[1] : v.stride[0];
+  const uint32_t dt = v.dtype;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = threadIdx.x + i * kBlock;  // 0 .. 2047 over a 64 x 32 slice
+    const int r = mn_contig ? q % 64 : q / 32, kk = mn_contig ? q / 64 : q % 32;
+    const uint32_t gr = r0 + r, gk = k0 + kk;
+    const bool ok = gr < rmax && gk < kmax;
+    const int64_t idx = v.offset + (int64_t)(ok ? gr : 0) * s_r + (int64_t)(ok ? gk : 0) * s_k;
+    const float val = load_elem(p, dt, idx);
+    reg[i] = ok ? val : 0.0f;
+  }
+}
+
+DEV void simt_store(LDS float* s, bool mn_contig, const float (&reg)[8]) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int q = threadIdx.x + i * kBlock;
+    const int r = mn_contig ? q % 64 : q / 32, kk = mn_contig ? q / 64 : q % 32;
+    s[kk * 68 + r] = reg[i];
+  }
+}
+
+DEV void gemm_simt(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
+  const uint32_t tile = xcd_tile(item, t.tiles_m * t.tiles_n);
+  const uint32_t tm = tile / t.tiles_n, tn = tile % t.tiles_n;
   const uint32_t m0 = tm * 64, n0 = tn * 64;
-  float* As = (float*)smem;              // [16][64 + 4]
-  float* Bs = As + 16 * 68;              // [16][64 + 4]
-  const DView A = pl.views[t.va], B = pl.views[t.vb];
-  const uint8_t* pa = base_ptr(ka, A.base);
-  const uint8_t* pb = base_ptr(ka, B.base);
+  LDS float* As0 = (LDS float*)g_smem;
+  LDS float* As1 = As0 + 32 * 68;
+  LDS float* Bs0 = As0 + 2 * 32 * 68;
+  LDS float* Bs1 = As0 + 3 * 32 * 68;
+  const DView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
+  const GLOBAL uint8_t* pa = base_ptr(ka, A.base);
+  const GLOBAL uint8_t* pb = base_ptr(ka, B.base);
+  const bool a_mc = A.stride[0] == 1 && A.stride[1] != 1;  // A unit-stride along m
+  const bool b_nc = B.stride[1] == 1;                      // B unit-stride along n
   const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
   float acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (uint32_t k0 = 0; k0 < t.k; k0 += 16) {
-    for (int p = threadIdx.x; p < 1024; p += kBlock) {
-      const int kk = p % 16, mm = p / 16;  // A: 64 rows x 16 k
-      const uint32_t gm = m0 + mm, gk = k0 + kk;
-      As[kk * 68 + mm] = (gm < t.m && gk < t.k) ? load_elem(pa, A.dtype, A.offset + (int64_t)gm * A.stride[0] + (int64_t)gk * A.stride[1]) : 0.0f;
-      const int nn = p % 64, kb = p / 64;  // B: 16 k x 64 cols
-      const uint32_t gn = n0 + nn, gkb = k0 + kb;
-      Bs[kb * 68 + nn] = (gn < t.n && gkb < t.k) ? load_elem(pb, B.dtype, B.offset + (int64_t)gkb * B.stride[0] + (int64_t)gn * B.stride[1]) : 0.0f;
+  const uint32_t nk = (t.k + 31) / 32;
+  float ra[8], rb[8];
+  if (nk > 0) {
+    simt_load(pa, A, a_mc, true, m0, t.m, 0, t.k, ra);
+    simt_load(pb, B, b_nc, false, n0, t.n, 0, t.k, rb);
+    simt_store(As0, a_mc, ra);
+    simt_store(Bs0, b_nc, rb);
+  }
+  __syncthreads();
+  for (uint32_t kt = 0; kt < nk; ++kt) {
+    const bool odd = kt & 1;
+    if (kt + 1 < nk) {
+      simt_load(pa, A, a_mc, true, m0, t.m, (kt + 1) * 32, t.k, ra);
+      simt_load(pb, B, b_nc, false, n0, t.n, (kt + 1) * 32, t.k, rb);
     }
-    __syncthreads();
-    const uint32_t kend = t.k - k0 < 16 ? t.k - k0 : 16;
+    const LDS float* as = odd ? As1 : As0;
+    const LDS float* bs = odd ? Bs1 : Bs0;
+    const uint32_t kend = t.k - kt * 32 < 32 ? t.k - kt * 32 : 32;
     for (uint32_t kk = 0; kk < kend; ++kk) {
       float a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) a[i] = As[kk * 68 + ty * 4 + i];
+      for (int i = 0; i < 4; ++i) a[i] = as[kk * 68 + ty * 4 + i];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) b[j] = Bs[kk * 68 + tx * 4 + j];
+      for (int j = 0; j < 4; ++j) b[j] = bs[kk * 68 + tx * 4 + j];
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
     }
+    if (kt + 1 < nk) {
+      simt_store(odd ? As0 : As1, a_mc, ra);
+      simt_store(odd ? Bs0 : Bs1, b_nc, rb);
+    }
     __syncthreads();
   }
-  float* C = (float*)smem;  // [64][68]
+  LDS float* C = (LDS float*)g_smem;  // [64][68]
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) C[(ty * 4 + i) * 68 + tx * 4 + j] = acc[i][j];
-  __syncthreads();
-  if (t.width == 8)
-    tile_epilogue<8>(ka, pl, t, C, 64, 64, m0, n0, 0);
-  else
-    tile_epilogue<1>(ka, pl, t, C, 64, 64, m0, n0, 0);
-  __syncthreads();
+  st.m0 = m0;
+  st.n0 = n0;
+  st.bm = 64;
+  st.bn = 64;
+  st.split_index = 0;
 }
 
 // ------------------------------------------------------- MFMA contraction --
@@ -468,112 +530,142 @@ __device__ __noinline__ void run_gemm_simt(const KArgs& ka, const Plan& pl, cons
 // (BM/2) x (BN/2) block of 32x32 MFMA accumulators.  Both operands are staged
 // in LDS k-contiguous ([row][k], pitch 72 elements): an operand stored with
 // unit stride along M/N is transposed in registers on its way to LDS so every
-// global read stays 16 bytes wide and coalesced.
+// global read stays 16 bytes wide and coalesced.  On the fast path (interior
+// tile, whole 64-deep slices, 16-byte aligned rows) the global loads of slice
+// k+1 are issued into registers before slice k is multiplied and written to
+// the other LDS buffer afterwards; other tiles stage element by element.
 
 constexpr int kBK = 64;
 constexpr int kPitch = kBK + 8;
 
-// Stage rows [r0, r0 + R) x k [k0, k0 + 64) of an operand whose element (r, k)
-// lives at p[off + r * sr + k * sk] into lds[r][k] (bf16/f16 bits).
+// Per-thread loads of one operand: N = R/32 16-byte loads per 64-deep slice.
+// kc: unit stride along k (16-byte chunks along k); otherwise unit stride
+// along rows (blocks of R/32 k-rows x 8 rows, transposed when committed).
 template <int R>
-DEV void stage_operand(const uint8_t* p, int64_t off, int64_t sr, int64_t sk, uint32_t r0, uint32_t rmax, uint32_t k0,
-                       uint32_t kmax, uint16_t* lds) {
-  const uint16_t* q = (const uint16_t*)p;
-  if (sk == 1) {
-    // 16-byte chunks along k: R * 8 chunks
+struct FastOp {
+  static constexpr int N = R / 32;
+  const GLOBAL uint16_t* ptr[N];
+  int64_t kstep;
+  bool kc;
+  DEV void init(bool kcontig, const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0,
+                uint32_t k0) {
+    kc = kcontig;
+    if (kc) {
 #pragma unroll
-    for (int i = 0; i < R / 32; ++i) {
-      const int ch = threadIdx.x + i * kBlock;
-      const int r = ch / 8, kq = (ch % 8) * 8;
-      const uint32_t gr = r0 + r, gk = k0 + kq;
-      const int64_t idx = off + (int64_t)gr * sr + gk;
-      u32x4 v;
-      if (gr < rmax && gk + 8 <= kmax && (((uintptr_t)(q + idx)) & 15) == 0) {
-        v = *(const u32x4*)(q + idx);
-      } else {
-        uint32_t e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = (gr < rmax && gk + j < kmax) ? q[idx + j] : 0u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = e[2 * j] | (e[2 * j + 1] << 16);
+      for (int i = 0; i < N; ++i) {
+        const int ch = threadIdx.x + i * kBlock;
+        ptr[i] = q + off + (int64_t)(r0 + ch / 8) * sr + k0 + (ch % 8) * 8;
       }
-      *(u32x4*)(lds + r * kPitch + kq) = v;
+      kstep = kBK;
+    } else {
+      const int rb = threadIdx.x % (R / 8), kb = threadIdx.x / (R / 8);
+#pragma unroll
+      for (int i = 0; i < N; ++i) ptr[i] = q + off + (int64_t)(k0 + kb * N + i) * sk + r0 + rb * 8;
+      kstep = (int64_t)kBK * sk;
     }
-  } else if (sr == 1) {
-    // unit stride along rows: blocks of KB k-rows x 8 rows, transposed in registers
-    constexpr int KB = R / 32;  // 4 for R = 128, 2 for R = 64
-    const int rb = threadIdx.x % (R / 8), kb = threadIdx.x / (R / 8);
-    const uint32_t gr = r0 + rb * 8, gk = k0 + kb * KB;
-    uint32_t w[KB][4];
+  }
+  DEV void load(uint32_t slice, u32x4 (&v)[N]) const {
 #pragma unroll
-    for (int kr = 0; kr < KB; ++kr) {
-      const int64_t idx = off + (int64_t)(gk + kr) * sk + gr;
-      if (gk + kr < kmax && gr + 8 <= rmax && (((uintptr_t)(q + idx)) & 15) == 0) {
-        u32x4 v = *(const u32x4*)(q + idx);
+    for (int i = 0; i < N; ++i) v[i] = *(const GLOBAL u32x4*)(ptr[i] + (int64_t)slice * kstep);
+  }
+  DEV void commit(const u32x4 (&v)[N], LDS uint16_t* lds) const {
+    if (kc) {
 #pragma unroll
-        for (int j = 0; j < 4; ++j) w[kr][j] = v[j];
-      } else {
-        uint32_t e[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) e[j] = (gk + kr < kmax && gr + j < rmax) ? q[idx + j] : 0u;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) w[kr][j] = e[2 * j] | (e[2 * j + 1] << 16);
+      for (int i = 0; i < N; ++i) {
+        const int ch = threadIdx.x + i * kBlock;
+        *(LDS u32x4*)(lds + (ch / 8) * kPitch + (ch % 8) * 8) = v[i];
       }
-    }
-    // row rb*8 + 2j takes the low halves, row rb*8 + 2j + 1 the high halves
+    } else {
+      const int rb = threadIdx.x % (R / 8), kb = threadIdx.x / (R / 8);
+      // row rb*8 + 2j takes the low halves, row rb*8 + 2j + 1 the high halves
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      uint32_t lo[KB / 2], hi[KB / 2];
+      for (int j = 0; j < 4; ++j) {
+        uint32_t lo[N / 2], hi[N / 2];
 #pragma unroll
-      for (int h = 0; h < KB / 2; ++h) {
-        lo[h] = (w[2 * h][j] & 0xffffu) | (w[2 * h + 1][j] << 16);
-        hi[h] = (w[2 * h][j] >> 16) | (w[2 * h + 1][j] & 0xffff0000u);
-      }
-      uint16_t* d0 = lds + (rb * 8 + 2 * j) * kPitch + kb * KB;
-      uint16_t* d1 = d0 + kPitch;
-      if (KB == 4) {
-        u32x2 a = {lo[0], lo[1]}, b = {hi[0], hi[1]};
-        *(u32x2*)d0 = a;
-        *(u32x2*)d1 = b;
-      } else {
-        *(uint32_t*)d0 = lo[0];
-        *(uint32_t*)d1 = hi[0];
+        for (int h = 0; h < N / 2; ++h) {
+          lo[h] = (v[2 * h][j] & 0xffffu) | (v[2 * h + 1][j] << 16);
+          hi[h] = (v[2 * h][j] >> 16) | (v[2 * h + 1][j] & 0xffff0000u);
+        }
+        LDS uint16_t* d0 = lds + (rb * 8 + 2 * j) * kPitch + kb * N;
+        LDS uint16_t* d1 = d0 + kPitch;
+        if (N == 4) {
+          *(LDS u32x2*)d0 = u32x2{lo[0], lo[1]};
+          *(LDS u32x2*)d1 = u32x2{hi[0], hi[1]};
+        } else {
+          *(LDS uint32_t*)d0 = lo[0];
+          *(LDS uint32_t*)d1 = hi[0];
+        }
       }
     }
-  } else {
-    // general strides: element by element
-    for (int p = threadIdx.x; p < R * kBK; p += kBlock) {
-      const int r = p / kBK, kk = p % kBK;
-      const uint32_t gr = r0 + r, gk = k0 + kk;
-      lds[r * kPitch + kk] = (gr < rmax && gk < kmax) ? q[off + (int64_t)gr * sr + (int64_t)gk * sk] : (uint16_t)0;
+  }
+};
+
+// General operand path: element by element straight into LDS, zero outside.
+template <int R>
+DEV void slow_stage(const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0, uint32_t rmax,
+                    uint32_t k0, uint32_t kmax, LDS uint16_t* lds) {
+  // consecutive threads walk the operand's unit-stride dimension when it has one
+  const bool kfast = sk == 1 || sr != 1;
+  for (int p = threadIdx.x; p < R * kBK; p += kBlock) {
+    const int r = kfast ? p / kBK : p % R, kk = kfast ? p % kBK : p / R;
+    const uint32_t gr = r0 + r, gk = k0 + kk;
+    const bool ok = gr < rmax && gk < kmax;
+    const uint16_t v = q[off + (int64_t)(ok ? gr : 0) * sr + (int64_t)(ok ? gk : 0) * sk];
+    lds[r * kPitch + kk] = ok ? v : (uint16_t)0;
+  }
+}
+
+DEV f32x16 mfma32(bool bf16, u32x4 a, u32x4 b, f32x16 c) {
+  if (bf16)
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                   0, 0);
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
+                                                0);
+}
+
+// One 64-deep K slice from LDS into the wave's accumulators.
+template <int BM, int BN>
+DEV void mfma_slice(bool bf16, const LDS uint16_t* sa, const LDS uint16_t* sb, f32x16 (&acc)[BM / 64][BN / 64]) {
+  constexpr int FM = BM / 64, FN = BN / 64;
+  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wm = wave / 2, wn = wave % 2;
+  const LDS uint16_t* a_t = sa + (wm * (BM / 2) + (lane % 32)) * kPitch + 8 * (lane / 32);
+  const LDS uint16_t* b_t = sb + (wn * (BN / 2) + (lane % 32)) * kPitch + 8 * (lane / 32);
+#pragma unroll
+  for (int kk = 0; kk < kBK; kk += 16) {
+    u32x4 af[FM], bfr[FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) af[i] = *(const LDS u32x4*)(a_t + i * 32 * kPitch + kk);
+#pragma unroll
+    for (int j = 0; j < FN; ++j) bfr[j] = *(const LDS u32x4*)(b_t + j * 32 * kPitch + kk);
+    if (bf16) {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(true, af[i], bfr[j], acc[i][j]);
+    } else {
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(false, af[i], bfr[j], acc[i][j]);
     }
   }
 }
 
-template <bool BF16>
-DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
-  if constexpr (BF16) {
-    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
-  } else {
-    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
-  }
-}
-
-template <bool BF16, int BM, int BN>
-__device__ __noinline__ void run_gemm_mfma(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item, uint8_t* smem) {
+template <int BM, int BN>
+DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
   constexpr int FM = BM / 64, FN = BN / 64;  // 32x32 blocks per wave along m / n
   const uint32_t tiles = t.tiles_m * t.tiles_n;
   const uint32_t split_index = item / tiles;
-  const uint32_t tile = item % tiles;
+  const uint32_t tile = xcd_tile(item % tiles, tiles);
   const uint32_t tm = tile / t.tiles_n, tn = tile % t.tiles_n;
   const uint32_t m0 = tm * BM, n0 = tn * BN;
   const uint32_t kbeg = split_index * t.kchunk;
   const uint32_t kend = (kbeg + t.kchunk < t.k) ? kbeg + t.kchunk : t.k;
-  const DView A = pl.views[t.va], B = pl.views[t.vb];
-  const uint8_t* pa = base_ptr(ka, A.base);
-  const uint8_t* pb = base_ptr(ka, B.base);
-  uint16_t* sa[2] = {(uint16_t*)smem, (uint16_t*)smem + BM * kPitch};
-  uint16_t* sb[2] = {(uint16_t*)smem + 2 * BM * kPitch, (uint16_t*)smem + 2 * BM * kPitch + BN * kPitch};
+  const DView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
+  const bool bf16 = A.dtype == DT_BF16;
+  const GLOBAL uint16_t* pa = (const GLOBAL uint16_t*)base_ptr(ka, A.base);
+  const GLOBAL uint16_t* pb = (const GLOBAL uint16_t*)base_ptr(ka, B.base);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int wm = wave / 2, wn = wave % 2;
   f32x16 acc[FM][FN];
@@ -584,37 +676,70 @@ __device__ __noinline__ void run_gemm_mfma(const KArgs& ka, const Plan& pl, cons
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   const uint32_t nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
-  if (nk > 0) {
-    stage_operand<BM>(pa, A.offset, A.stride[0], A.stride[1], m0, t.m, kbeg, kend, sa[0]);
-    // B's element (n, k) lives at off + k * stride[0] + n * stride[1]
-    stage_operand<BN>(pb, B.offset, B.stride[1], B.stride[0], n0, t.n, kbeg, kend, sb[0]);
-  }
-  __syncthreads();
-  for (uint32_t kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    if (kt + 1 < nk) {
-      const uint32_t k1 = kbeg + (kt + 1) * kBK;
-      stage_operand<BM>(pa, A.offset, A.stride[0], A.stride[1], m0, t.m, k1, kend, sa[cur ^ 1]);
-      stage_operand<BN>(pb, B.offset, B.stride[1], B.stride[0], n0, t.n, k1, kend, sb[cur ^ 1]);
+  LDS uint16_t* sa0 = (LDS uint16_t*)g_smem;
+  LDS uint16_t* sa1 = sa0 + BM * kPitch;
+  LDS uint16_t* sb0 = sa0 + 2 * BM * kPitch;
+  LDS uint16_t* sb1 = sb0 + BN * kPitch;
+  // A's element (m, k) at off + m * stride[0] + k * stride[1];
+  // B's element (n, k) at off + k * stride[0] + n * stride[1]
+  const bool full_k = (kend - kbeg) % kBK == 0;
+  const bool a_kc = A.stride[1] == 1, a_rc = !a_kc && A.stride[0] == 1;
+  const bool b_kc = B.stride[0] == 1, b_rc = !b_kc && B.stride[1] == 1;
+  const int64_t a_other = a_kc ? A.stride[0] : A.stride[1], b_other = b_kc ? B.stride[1] : B.stride[0];
+  const bool a_ok = m0 + BM <= t.m && (a_kc || a_rc) && aligned16(pa) && (A.offset & 7) == 0 && (a_other & 7) == 0;
+  const bool b_ok = n0 + BN <= t.n && (b_kc || b_rc) && aligned16(pb) && (B.offset & 7) == 0 && (b_other & 7) == 0;
+  if (nk > 0 && full_k && a_ok && b_ok) {
+    // D slices of global loads in flight in registers; LDS double buffer.
+    // Slice k is committed to buffer k % 2, then (after a workgroup barrier)
+    // its register set takes the loads of slice k + D and the MFMAs read the
+    // buffer.  Buffer k % 2 was last read by slice k - 2, which every wave
+    // finished before the barrier of slice k - 1.
+    constexpr int D = BM == 64 ? 4 : 3;
+    FastOp<BM> fa;
+    FastOp<BN> fb;
+    fa.init(a_kc, pa, A.offset, A.stride[0], A.stride[1], m0, kbeg);
+    fb.init(b_kc, pb, B.offset, B.stride[1], B.stride[0], n0, kbeg);
+    // Loads are unconditional (past the last slice they repeat it): the
+    // compiler can then count exactly which loads each commit must wait for.
+    u32x4 ra[D][FastOp<BM>::N], rb[D][FastOp<BN>::N];
+    const uint32_t last = nk - 1;
+#pragma unroll
+    for (int d = 0; d < D; ++d) {
+      const uint32_t sl = (uint32_t)d < last ? (uint32_t)d : last;
+      fa.load(sl, ra[d]);
+      fb.load(sl, rb[d]);
     }
-    const uint16_t* a_t = sa[cur] + (wm * (BM / 2) + (lane % 32)) * kPitch + 8 * (lane / 32);
-    const uint16_t* b_t = sb[cur] + (wn * (BN / 2) + (lane % 32)) * kPitch + 8 * (lane / 32);
+    for (uint32_t k0 = 0; k0 < nk; k0 += D) {
 #pragma unroll
-    for (int kk = 0; kk < kBK; kk += 16) {
-      u32x4 af[FM], bfr[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) af[i] = *(const u32x4*)(a_t + i * 32 * kPitch + kk);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) bfr[j] = *(const u32x4*)(b_t + j * 32 * kPitch + kk);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<BF16>(af[i], bfr[j], acc[i][j]);
+      for (int d = 0; d < D; ++d) {
+        const uint32_t k = k0 + d;
+        const bool act = k < nk;  // uniform; false only in the last group
+        LDS uint16_t* sa = (k & 1) ? sa1 : sa0;
+        LDS uint16_t* sb = (k & 1) ? sb1 : sb0;
+        if (act) {
+          fa.commit(ra[d], sa);
+          fb.commit(rb[d], sb);
+        }
+        __syncthreads();
+        const uint32_t nx = k + D < last ? k + D : last;
+        fa.load(nx, ra[d]);
+        fb.load(nx, rb[d]);
+        if (act) mfma_slice<BM, BN>(bf16, sa, sb, acc);
+      }
     }
-    __syncthreads();
+    __syncthreads();  // every wave is done with the staging buffers (the C tile reuses them)
+  } else {
+    for (uint32_t kt = 0; kt < nk; ++kt) {
+      const uint32_t k0 = kbeg + kt * kBK;
+      slow_stage<BM>(pa, A.offset, A.stride[0], A.stride[1], m0, t.m, k0, kend, sa0);
+      slow_stage<BN>(pb, B.offset, B.stride[1], B.stride[0], n0, t.n, k0, kend, sb0);
+      __syncthreads();
+      mfma_slice<BM, BN>(bf16, sa0, sb0, acc);
+      __syncthreads();
+    }
   }
   // accumulators -> LDS tile [BM][BN + 4]
-  float* C = (float*)smem;
+  LDS float* C = (LDS float*)g_smem;
   const int pitch = BN + 4;
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -626,37 +751,18 @@ __device__ __noinline__ void run_gemm_mfma(const KArgs& ka, const Plan& pl, cons
         const int col = wn * (BN / 2) + j * 32 + (lane % 32);
         C[row * pitch + col] = acc[i][j][r];
       }
-  __syncthreads();
-  if (t.width == 8)
-    tile_epilogue<8>(ka, pl, t, C, BM, BN, m0, n0, split_index);
-  else
-    tile_epilogue<1>(ka, pl, t, C, BM, BN, m0, n0, split_index);
-  __syncthreads();
-}
-
-// Split-K combine: sum the partial tiles in split order, then the epilogue.
-template <int W>
-__device__ __noinline__ void run_gemm_reduce(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item) {
-  const uint64_t total = (uint64_t)t.m * t.n;
-  const float* P = (const float*)(ka.ws + t.scratch);
-  for (uint32_t j8 = 0; j8 < (W == 8 ? 1u : 8u); ++j8) {
-    const uint64_t e = (uint64_t)item * 2048u + (W == 8 ? threadIdx.x * 8u : j8 * 256u + threadIdx.x);
-    if (e >= total) continue;
-    const uint32_t row = (uint32_t)(e / t.n), col = (uint32_t)(e % t.n);
-    float acc[W];
-#pragma unroll
-    for (int j = 0; j < W; ++j) acc[j] = P[e + j];
-    for (uint32_t s = 1; s < t.split; ++s)
-#pragma unroll
-      for (int j = 0; j < W; ++j) acc[j] = acc[j] + P[s * total + e + j];
-    uint32_t c[kMaxDims] = {row, col, 0, 0};
-    vm_run<W>(ka, pl, t.expr_first, t.expr_len, c, 2, acc);
-  }
+  st.m0 = m0;
+  st.n0 = n0;
+  st.bm = BM;
+  st.bn = BN;
+  st.split_index = split_index;
 }
 
 // ------------------------------------------------------ int8-weight GEMV --
 // 16 output rows per work item, 4 per wave; each lane takes 16-wide K chunks
-// (k = 16 * lane + 1024 * j).  w = fl(q * s) then acc = fma(x, w, acc).
+// (k = 16 * lane + 1024 * j).  All weight loads of a wave's 4 rows for up to
+// 4096 columns are issued before any is used.  w = fl(q * s), then
+// acc = fma(x, w, acc).  Leaves the 16 row sums in LDS.
 
 DEV float wave_sum(float v) {
 #pragma unroll
@@ -664,80 +770,84 @@ DEV float wave_sum(float v) {
   return v;
 }
 
-__device__ __noinline__ void run_gemv_q8(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item, uint8_t* smem) {
-  const DView X = pl.views[t.va], Q = pl.views[t.vb], S = pl.views[t.vs];
-  const uint8_t* px = base_ptr(ka, X.base);
-  const int8_t* pq = (const int8_t*)base_ptr(ka, Q.base);
-  const float* ps = (const float*)base_ptr(ka, S.base);
+constexpr uint32_t kGemvRed = kSmemBytes - 64;  // byte offset of the 16 row sums
+
+DEV void gemv_q8(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
+  const DView X = load_view(views_off + t.va * sizeof(DView)), Q = load_view(views_off + t.vb * sizeof(DView)),
+              S = load_view(views_off + t.vs * sizeof(DView));
+  const GLOBAL uint8_t* px = base_ptr(ka, X.base);
+  const GLOBAL int8_t* pq = (const GLOBAL int8_t*)base_ptr(ka, Q.base);
+  const GLOBAL float* ps = (const GLOBAL float*)base_ptr(ka, S.base);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const uint32_t K = t.k;
-  // The activation row, widened to fp32, staged once per item in LDS.
-  float* xs = (float*)smem;
+  LDS float* xs = (LDS float*)g_smem;
   const bool staged = (uint64_t)K * 4 + 64 <= (uint64_t)kSmemBytes;
-  if (staged) {
-    for (uint32_t k = threadIdx.x; k < K; k += kBlock)
-      xs[k] = load_elem(px, X.dtype, X.offset + (int64_t)k * X.stride[1]);
-    __syncthreads();
-  }
-  float* red = (float*)(smem + kSmemBytes - 64);
-  for (int r = 0; r < 4; ++r) {
-    const uint32_t row = item * 16 + wave * 4 + r;
-    float acc = 0.0f;
-    if (row < t.n) {
+  const uint32_t row0 = item * 16 + wave * 4;
+  const bool vec = staged && Q.stride[1] == 1;
+  constexpr int NC = 4;  // chunks per lane per pass (4096 columns)
+  float acc[4] = {0, 0, 0, 0};
+  for (uint32_t kpass = 0; kpass < K; kpass += 1024 * NC) {
+    u32x4 qv[4][NC];
+    float sv[4][NC];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const uint32_t row = row0 + r;
       const int64_t qrow = Q.offset + (int64_t)row * Q.stride[0];
       const int64_t srow = S.offset + (int64_t)row * S.stride[0];
-      for (uint32_t kc = lane * 16; kc < K; kc += 1024) {
-        // a 16-wide chunk starting at a multiple of 16 lies inside one 32-block
-        const float sv = ps[srow + (int64_t)(kc / 32) * S.stride[1]];
-        const int64_t qidx = qrow + (int64_t)kc * Q.stride[1];
-        if (staged && Q.stride[1] == 1 && kc + 16 <= K && (((uintptr_t)(pq + qidx)) & 15) == 0) {
-          const u32x4 v = *(const u32x4*)(pq + qidx);
 #pragma unroll
-          for (int j = 0; j < 16; ++j) {
-            const int32_t qj = (int32_t)(v[j / 4] << (24 - 8 * (j % 4))) >> 24;
-            const float w = (float)qj * sv;
-            acc = __builtin_fmaf(xs[kc + j], w, acc);
-          }
+      for (int j = 0; j < NC; ++j) {
+        const uint32_t kc = kpass + 1024 * j + lane * 16;
+        const bool ok = row < t.n && kc < K;
+        const int64_t qidx = qrow + (int64_t)kc * Q.stride[1];
+        if (ok && vec && kc + 16 <= K && aligned16(pq + qidx)) {
+          qv[r][j] = *(const GLOBAL u32x4*)(pq + qidx);
         } else {
-          for (uint32_t j = 0; j < 16 && kc + j < K; ++j) {
-            const float xj = staged ? xs[kc + j] : load_elem(px, X.dtype, X.offset + (int64_t)(kc + j) * X.stride[1]);
-            const float w = (float)pq[qidx + (int64_t)j * Q.stride[1]] * sv;
-            acc = __builtin_fmaf(xj, w, acc);
-          }
+          uint32_t w[4] = {0, 0, 0, 0};
+          for (int e = 0; e < 16; ++e)
+            if (ok && kc + e < K) w[e / 4] |= ((uint32_t)(uint8_t)pq[qidx + (int64_t)e * Q.stride[1]]) << (8 * (e % 4));
+          qv[r][j] = u32x4{w[0], w[1], w[2], w[3]};
+        }
+        // a 16-wide chunk starting at a multiple of 16 lies inside one 32-block
+        sv[r][j] = ok ? ps[srow + (int64_t)(kc / 32) * S.stride[1]] : 0.0f;
+      }
+    }
+    if (kpass == 0 && staged) {
+      for (uint32_t k = threadIdx.x; k < K; k += kBlock)
+        xs[k] = load_elem(px, X.dtype, X.offset + (int64_t)k * X.stride[1]);
+      __syncthreads();
+    }
+#pragma unroll
+    for (int j = 0; j < NC; ++j) {
+      const uint32_t kc = kpass + 1024 * j + lane * 16;
+      if (kc >= K) continue;
+      float xk[16];
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        xk[e] = (kc + e < K) ? (staged ? xs[kc + e] : load_elem(px, X.dtype, X.offset + (int64_t)(kc + e) * X.stride[1]))
+                             : 0.0f;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int32_t qj = (int32_t)(qv[r][j][e / 4] << (24 - 8 * (e % 4))) >> 24;
+          const float w = (float)qj * sv[r][j];
+          acc[r] = __builtin_fmaf(xk[e], w, acc[r]);
         }
       }
     }
-    acc = wave_sum(acc);
-    if (lane == 0) red[wave * 4 + r] = acc;
   }
-  __syncthreads();
-  const uint32_t rb = item * 16;
-  if (t.width == 8) {
-    if (threadIdx.x < 2) {
-      const uint32_t col = rb + threadIdx.x * 8;
-      if (col < t.n) {
-        float v[8];
+  LDS float* red = (LDS float*)(g_smem + kGemvRed);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) v[j] = red[threadIdx.x * 8 + j];
-        uint32_t c[kMaxDims] = {0, col, 0, 0};
-        vm_run<8>(ka, pl, t.expr_first, t.expr_len, c, 2, v);
-      }
-    }
-  } else if (threadIdx.x < 16) {
-    const uint32_t col = rb + threadIdx.x;
-    if (col < t.n) {
-      float v[1] = {red[threadIdx.x]};
-      uint32_t c[kMaxDims] = {0, col, 0, 0};
-      vm_run<1>(ka, pl, t.expr_first, t.expr_len, c, 2, v);
-    }
+  for (int r = 0; r < 4; ++r) {
+    const float s = wave_sum(acc[r]);
+    if (lane == 0) red[wave * 4 + r] = s;
   }
   __syncthreads();
 }
 
-// -------------------------------------------------------------- reductions --
-
 // Block-wide sum in a fixed order: wave butterflies, then waves 0..3 in order.
-DEV float block_sum(float v, float* scratch) {
+DEV float block_sum(float v) {
+  LDS float* scratch = (LDS float*)g_smem;
   v = wave_sum(v);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   if (lane == 0) scratch[wave] = v;
@@ -747,159 +857,337 @@ DEV float block_sum(float v, float* scratch) {
   return s;
 }
 
-// Reduce the trailing part of the iteration space: item = row * parts + part.
-template <int W>
-__device__ __noinline__ void run_red_rows(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item, uint8_t* smem) {
-  const uint32_t row = item / t.split, part = item % t.split;
-  const uint32_t R = t.k;
-  const uint32_t kb = part * t.kchunk;
-  const uint32_t ke = (kb + t.kchunk < R) ? kb + t.kchunk : R;
-  const uint32_t nd = t.ndim;
-  float s = 0.0f;
-  for (uint32_t kk = kb + threadIdx.x * W; kk < ke; kk += kBlock * W) {
-    const uint32_t e = row * R + kk;
-    uint32_t c[kMaxDims];
-    unravel(e, t, nd, c);
-    float acc[W];
-#pragma unroll
-    for (int j = 0; j < W; ++j) acc[j] = 0.0f;
-    vm_run<W>(ka, pl, t.expr_first, t.expr_len, c, nd, acc);
-#pragma unroll
-    for (int j = 0; j < W; ++j) s = s + acc[j];
-  }
-  const float total = block_sum(s, (float*)smem);
-  if (threadIdx.x == 0) {
-    if (t.flags & F_PARTIAL) {
-      ((float*)(ka.ws + t.scratch))[(uint64_t)row * t.split + part] = total;
-    } else {
-      float v[1] = {total};
-      uint32_t c[kMaxDims] = {row, 0, 0, 0};
-      vm_run<1>(ka, pl, t.fin_first, t.fin_len, c, 1, v);
-    }
-  }
+// -------------------------------------------------------------- batches --
+
+DEV void set_dims(Batch& b, uint32_t d0, uint32_t d1, uint32_t nd) {
+  b.dims[0] = d0;
+  b.dims[1] = d1;
+  b.dims[2] = 1;
+  b.dims[3] = 1;
+  b.nd = nd;
 }
 
-// Reduce the leading part: item = colblock * parts + part; 32 column chunks x
-// 8 row lanes per workgroup, rows summed lane-strided then across lanes in order.
-template <int W>
-__device__ __noinline__ void run_red_cols(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item, uint8_t* smem) {
-  const uint32_t cb = item / t.split, part = item % t.split;
-  const uint32_t cols = t.m, R = t.k;
-  const uint32_t cc = threadIdx.x % 32, rl = threadIdx.x / 32;
-  const uint32_t col = cb * 32 * W + cc * W;
-  const uint32_t rb = part * t.kchunk;
-  const uint32_t re = (rb + t.kchunk < R) ? rb + t.kchunk : R;
-  const uint32_t nd = t.ndim;
-  float s[W];
-#pragma unroll
-  for (int j = 0; j < W; ++j) s[j] = 0.0f;
-  if (col < cols) {
-    for (uint32_t r = rb + rl; r < re; r += 8) {
-      const uint32_t e = r * cols + col;
-      uint32_t c[kMaxDims];
-      unravel(e, t, nd, c);
-      float acc[W];
-#pragma unroll
-      for (int j = 0; j < W; ++j) acc[j] = 0.0f;
-      vm_run<W>(ka, pl, t.expr_first, t.expr_len, c, nd, acc);
-#pragma unroll
-      for (int j = 0; j < W; ++j) s[j] = s[j] + acc[j];
-    }
-  }
-  float* red = (float*)smem;  // [8][32 * W]
-#pragma unroll
-  for (int j = 0; j < W; ++j) red[rl * 32 * W + cc * W + j] = s[j];
-  __syncthreads();
-  if (rl == 0 && col < cols) {
-    float tot[W];
-#pragma unroll
-    for (int j = 0; j < W; ++j) {
-      float a = red[cc * W + j];
-      for (int q = 1; q < 8; ++q) a = a + red[q * 32 * W + cc * W + j];
-      tot[j] = a;
-    }
-    if (t.flags & F_PARTIAL) {
-      float* P = (float*)(ka.ws + t.scratch) + (uint64_t)part * cols + col;
-#pragma unroll
-      for (int j = 0; j < W; ++j) P[j] = tot[j];
-    } else {
-      uint32_t c[kMaxDims] = {col, 0, 0, 0};
-      vm_run<W>(ka, pl, t.fin_first, t.fin_len, c, 1, tot);
-    }
-  }
-  __syncthreads();
+DEV void expr_batch(Batch& b, const DTask& t, uint32_t ins_off) {
+  b.ins = ins_off + t.expr_first * sizeof(DIns);
+  b.n = t.expr_len;
+  b.width = t.width == 8 ? 8 : 1;
+  b.accumulate = 0;
 }
 
-__device__ __noinline__ void run_red_final(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item) {
-  const uint32_t row = item * kBlock + threadIdx.x;
-  if (row >= t.m) return;
-  const float* P = (const float*)(ka.ws + t.scratch);
-  float a = 0.0f;
-  for (uint32_t p = 0; p < t.split; ++p) a = a + (t.tile ? P[(uint64_t)p * t.m + row] : P[(uint64_t)row * t.split + p]);
-  float v[1] = {a};
-  uint32_t c[kMaxDims] = {row, 0, 0, 0};
-  vm_run<1>(ka, pl, t.fin_first, t.fin_len, c, 1, v);
+DEV void task_space(Batch& b, const DTask& t) {
+  b.nd = t.ndim;
+#pragma unroll
+  for (int d = 0; d < kMaxDims; ++d) b.dims[d] = t.dims[d];
 }
 
-// -------------------------------------------------------------- dispatch --
+DEV void fin_batch(Batch& b, const DTask& t, uint32_t ins_off, uint32_t width) {
+  b.ins = ins_off + t.fin_first * sizeof(DIns);
+  b.n = t.fin_len;
+  b.width = width;
+  b.accumulate = 0;
+  set_dims(b, t.m, 1, 1);
+}
 
-DEV void run_item(const KArgs& ka, const Plan& pl, const DTask& t, uint32_t item, uint8_t* smem) {
+// Fill batch `bi` of a work item: set up the program and the exchange, and
+// set this thread's live-chunk mask.  Returns false when the item has no
+// batch `bi` (uniform across the workgroup).
+DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, uint32_t bi, ItemState& st, Batch& b,
+              uint32_t& live) {
+  live = 0;
+  const int W = t.width == 8 ? 8 : 1, C = kVmElems / W;
   switch (t.kind) {
-    case T_EW:
-      if (t.width == 8) run_ew<8>(ka, pl, t, item);
-      else run_ew<1>(ka, pl, t, item);
-      break;
-    case T_GEMM_SIMT:
-      run_gemm_simt(ka, pl, t, item, smem);
-      break;
-    case T_GEMM_MFMA: {
-      const bool bf = pl.views[t.va].dtype == DT_BF16;
-      if (t.tile == 0) {
-        if (bf) run_gemm_mfma<true, 128, 128>(ka, pl, t, item, smem);
-        else run_gemm_mfma<false, 128, 128>(ka, pl, t, item, smem);
-      } else {
-        if (bf) run_gemm_mfma<true, 64, 64>(ka, pl, t, item, smem);
-        else run_gemm_mfma<false, 64, 64>(ka, pl, t, item, smem);
+    case T_EW: {
+      // 4096 consecutive elements per item: two 8-wide chunks or sixteen singles per thread
+      if (bi > 0) return false;
+      expr_batch(b, t, ins_off);
+      task_space(b, t);
+      const uint32_t numel = t.dims[0] * t.dims[1] * t.dims[2] * t.dims[3];  // unused dims are 1
+      const uint32_t base = item * 4096u;
+      for (int q = 0; q < C; ++q) {
+        const uint32_t e = W == 8 ? base + q * 2048u + threadIdx.x * 8u : base + q * 256u + threadIdx.x;
+        xe(q) = e < numel ? e : 0;
+        live |= (e < numel ? 1u : 0u) << q;
       }
-      break;
+      for (int j = 0; j < kVmElems; ++j) xv(j) = 0.0f;
+      return true;
     }
-    case T_GEMM_REDUCE:
-      if (t.width == 8) run_gemm_reduce<8>(ka, pl, t, item);
-      else run_gemm_reduce<1>(ka, pl, t, item);
+    case T_GEMM_MFMA:
+    case T_GEMM_SIMT: {
+      // epilogue over the fp32 tile in LDS ([bm][bn + 4]), 16 elements per
+      // thread per batch; split-K partial tiles are written out instead
+      const int pitch = st.bn + 4;
+      const int cpr = st.bn / W;  // chunks per row
+      const int nchunks = st.bm * cpr;
+      const int q0 = (int)bi * kBlock * C;
+      if (q0 >= nchunks) return false;
+      expr_batch(b, t, ins_off);
+      set_dims(b, t.m, t.n, 2);
+      const LDS float* ctile = (const LDS float*)g_smem;
+      const bool partial = (t.flags & F_PARTIAL) != 0;
+      GLOBAL float* P = ws_f32(ka, t.scratch) + (uint64_t)st.split_index * t.m * t.n;
+      for (int q = 0; q < C; ++q) {
+        const int qq = q0 + q * kBlock + (int)threadIdx.x;
+        const int r = qq / cpr, cc = (qq % cpr) * W;
+        const uint32_t row = st.m0 + r, col = st.n0 + cc;
+        const bool ok = qq < nchunks && row < t.m && col < t.n;
+        const uint32_t e = ok ? row * t.n + col : 0;
+        if (partial) {
+          if (ok)
+            for (int j = 0; j < W; ++j) P[e + j] = ctile[r * pitch + cc + j];
+          continue;
+        }
+        live |= (ok ? 1u : 0u) << q;
+        xe(q) = e;
+        for (int j = 0; j < W; ++j) xv(q * W + j) = qq < nchunks ? ctile[r * pitch + cc + j] : 0.0f;
+      }
+      return true;
+    }
+    case T_GEMM_REDUCE: {
+      // split-K combine: partial tiles summed in split order, then the epilogue
+      if (bi > 0) return false;
+      expr_batch(b, t, ins_off);
+      set_dims(b, t.m, t.n, 2);
+      const uint64_t total = (uint64_t)t.m * t.n;
+      const GLOBAL float* P = ws_f32(ka, t.scratch);
+      for (int q = 0; q < C; ++q) {
+        const uint64_t e = (uint64_t)item * 4096u + (W == 8 ? q * 2048u + threadIdx.x * 8u : q * 256u + threadIdx.x);
+        const bool ok = e < total;
+        live |= (ok ? 1u : 0u) << q;
+        xe(q) = ok ? (uint32_t)e : 0;
+        for (int j = 0; j < W; ++j) {
+          float a = ok ? P[e + j] : 0.0f;
+          for (uint32_t s = 1; s < t.split; ++s) a = a + (ok ? P[s * total + e + j] : 0.0f);
+          xv(q * W + j) = a;
+        }
+      }
+      return true;
+    }
+    case T_GEMV_Q8: {
+      // epilogue over the 16 row sums: threads 0..1 take 8-wide chunks (or
+      // thread 0 sixteen singles)
+      if (bi > 0) return false;
+      expr_batch(b, t, ins_off);
+      set_dims(b, 1, t.n, 2);
+      const LDS float* red = (const LDS float*)(g_smem + kGemvRed);
+      const uint32_t rb = item * 16;
+      if (threadIdx.x < (W == 8 ? 2u : 1u)) {
+        for (int q = 0; q < C; ++q) {
+          const uint32_t col = rb + (W == 8 ? threadIdx.x * 8 : q);
+          const bool ok = (W == 8 ? q == 0 : true) && col < t.n;
+          live |= (ok ? 1u : 0u) << q;
+          xe(q) = ok ? col : 0;
+          for (int j = 0; j < W; ++j) xv(q * W + j) = red[W == 8 ? threadIdx.x * 8 + j : q];
+        }
+      }
+      return true;
+    }
+    case T_RED_ROWS: {
+      // item = row * parts + part; thread t takes chunks t, t + 256, ... of
+      // its part; the batch after the last sums over the block and finishes
+      const uint32_t row = item / t.split, part = item % t.split;
+      const uint32_t R = t.k;
+      const uint32_t kb = part * t.kchunk;
+      const uint32_t ke = (kb + t.kchunk < R) ? kb + t.kchunk : R;
+      const uint32_t per = kBlock * W * C;
+      const uint32_t nb = ke > kb ? (ke - kb + per - 1) / per : 0;
+      if (bi < nb) {
+        expr_batch(b, t, ins_off);
+        task_space(b, t);
+        b.accumulate = 1;
+        const uint32_t k0 = kb + bi * per + threadIdx.x * W;
+        for (int q = 0; q < C; ++q) {
+          const uint32_t kk = k0 + q * kBlock * W;
+          const bool ok = kk < ke;
+          live |= (ok ? 1u : 0u) << q;
+          xe(q) = row * R + (ok ? kk : kb);
+        }
+        for (int j = 0; j < kVmElems; ++j) xv(j) = 0.0f;
+        return true;
+      }
+      if (bi > nb) return false;
+      const float total = block_sum(st.acc);
+      fin_batch(b, t, ins_off, 1);
+      if (threadIdx.x == 0) {
+        if (t.flags & F_PARTIAL) {
+          ws_f32(ka, t.scratch)[(uint64_t)row * t.split + part] = total;
+        } else {
+          live = 1;
+          xe(0) = row;
+          xv(0) = total;
+        }
+      }
+      return true;
+    }
+    case T_RED_COLS: {
+      // item = colblock * parts + part; 32 column chunks x 8 row lanes; rows
+      // taken lane-strided, then summed across lanes in order
+      const uint32_t cb = item / t.split, part = item % t.split;
+      const uint32_t cols = t.m, R = t.k;
+      const uint32_t cc = threadIdx.x % 32, rl = threadIdx.x / 32;
+      const uint32_t col = cb * 32 * W + cc * W;
+      const uint32_t rb = part * t.kchunk;
+      const uint32_t re = (rb + t.kchunk < R) ? rb + t.kchunk : R;
+      const uint32_t per = 8 * C;
+      const uint32_t nb = re > rb ? (re - rb + per - 1) / per : 0;
+      if (bi < nb) {
+        expr_batch(b, t, ins_off);
+        task_space(b, t);
+        b.accumulate = 1;
+        const uint32_t r0 = rb + bi * per + rl;
+        for (int q = 0; q < C; ++q) {
+          const uint32_t r = r0 + 8 * q;
+          const bool ok = r < re && col < cols;
+          live |= (ok ? 1u : 0u) << q;
+          xe(q) = (ok ? r : rb) * cols + (col < cols ? col : 0);
+        }
+        for (int j = 0; j < kVmElems; ++j) xv(j) = 0.0f;
+        return true;
+      }
+      if (bi > nb) return false;
+      LDS float* red = (LDS float*)g_smem;  // [8][32 * W]
+      for (int j = 0; j < W; ++j) red[rl * 32 * W + cc * W + j] = st.acc8[j];
+      __syncthreads();
+      fin_batch(b, t, ins_off, W);
+      if (rl == 0 && col < cols) {
+        float tot[8];
+        for (int j = 0; j < W; ++j) {
+          float a = red[cc * W + j];
+          for (int q = 1; q < 8; ++q) a = a + red[q * 32 * W + cc * W + j];
+          tot[j] = a;
+        }
+        if (t.flags & F_PARTIAL) {
+          GLOBAL float* P = ws_f32(ka, t.scratch) + (uint64_t)part * cols + col;
+          for (int j = 0; j < W; ++j) P[j] = tot[j];
+        } else {
+          // finishing program over `cols` outputs: one 8-wide chunk or one element
+          live = 1;
+          xe(0) = col;
+          for (int j = 0; j < W; ++j) xv(j) = tot[j];
+        }
+      }
+      return true;
+    }
+    case T_RED_FINAL: {
+      // one thread per output: parts summed in order, eight loads in flight
+      if (bi > 0) return false;
+      fin_batch(b, t, ins_off, 1);
+      const GLOBAL float* P = ws_f32(ka, t.scratch);
+      const bool cols_layout = (t.tile & 1) != 0;  // [parts][rows] instead of [rows][parts]
+      const uint32_t row = item * kBlock + threadIdx.x;
+      if (row < t.m) {
+        float a = 0.0f;
+        for (uint32_t p0 = 0; p0 < t.split; p0 += 8) {
+          float v8[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            const uint32_t p = p0 + i;
+            v8[i] = p < t.split ? (cols_layout ? P[(uint64_t)p * t.m + row] : P[(uint64_t)row * t.split + p]) : 0.0f;
+          }
+#pragma unroll
+          for (int i = 0; i < 8; ++i)
+            if (p0 + i < t.split) a = a + v8[i];
+        }
+        live = 1;
+        xe(0) = row;
+        xv(0) = a;
+      }
+      return true;
+    }
+    default:
+      return false;
+  }
+}
+
+// After a summing batch: a reduction adds the machine's results into the
+// thread's running sums (chunk by chunk, elements in order).
+DEV void consume(const DTask& t, const Batch& b, uint32_t live, ItemState& st) {
+  if (!b.accumulate) return;
+  const int W = t.width == 8 ? 8 : 1, C = kVmElems / W;
+  if (t.kind == T_RED_ROWS) {
+    for (int q = 0; q < C; ++q)
+      if (live & (1u << q))
+        for (int j = 0; j < W; ++j) st.acc = st.acc + xv(q * W + j);
+  } else {
+    for (int q = 0; q < C; ++q)
+      if (live & (1u << q))
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < W) st.acc8[j] = st.acc8[j] + xv(q * W + j);
+  }
+}
+
+// A stage record from the plan (wave-uniform).
+DEV DStage load_stage(const GLOBAL uint8_t* stages, uint32_t s) {
+  constexpr int N = sizeof(DStage) / 4;
+  const GLOBAL uint32_t* w = (const GLOBAL uint32_t*)(stages + s * sizeof(DStage));
+  struct Words {
+    uint32_t u[N];
+  } r;
+#pragma unroll
+  for (int k = 0; k < N; ++k) r.u[k] = uniform(w[k]);
+  return __builtin_bit_cast(DStage, r);
+}
+
+// One work item: prologue, then batches through the machine.
+DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item) {
+  ItemState st;
+  st.m0 = st.n0 = st.split_index = 0;
+  st.bm = st.bn = 0;
+  st.acc = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) st.acc8[j] = 0.0f;
+  switch (t.kind) {
+    case T_GEMM_SIMT:
+      gemm_simt(ka, t, sd.off_views, item, st);
+      __syncthreads();
+      break;
+    case T_GEMM_MFMA:
+      if (t.tile == 0)
+        gemm_mfma<128, 128>(ka, t, sd.off_views, item, st);
+      else
+        gemm_mfma<64, 64>(ka, t, sd.off_views, item, st);
+      __syncthreads();
       break;
     case T_GEMV_Q8:
-      run_gemv_q8(ka, pl, t, item, smem);
-      break;
-    case T_RED_ROWS:
-      if (t.width == 8) run_red_rows<8>(ka, pl, t, item, smem);
-      else run_red_rows<1>(ka, pl, t, item, smem);
-      break;
-    case T_RED_COLS:
-      if (t.width == 8) run_red_cols<8>(ka, pl, t, item, smem);
-      else run_red_cols<1>(ka, pl, t, item, smem);
-      break;
-    case T_RED_FINAL:
-      run_red_final(ka, pl, t, item);
+      gemv_q8(ka, t, sd.off_views, item);
       break;
     default:
       break;
   }
+  trace_stamp(ka, 0x300);
+  for (uint32_t bi = 0;; ++bi) {
+    Batch b;
+    uint32_t live;
+    if (!fill(ka, t, sd.off_ins, item, bi, st, b, live)) break;
+    if (live) {
+      if (b.width == 8)
+        vm_run<8, 2>(ka, b, sd.off_views, live);
+      else
+        vm_run<1, 16>(ka, b, sd.off_views, live);
+    }
+    consume(t, b, live, st);
+    trace_stamp(ka, 0x400 + bi);
+  }
+  // the next item may overwrite the LDS tile and scratch
+  __syncthreads();
 }
 
-// Grid barrier with per-workgroup flags.  Arrival: every wave waits for its
-// own stores, the workgroup meets, one lane publishes (agent-scope release)
-// and writes its arrival flag = epoch.  The first wave of workgroup 0 polls
-// all arrival flags (4 per lane, loads issued together), then acquires and
-// writes every workgroup's release flag; each other workgroup polls its own
-// release flag and acquires.  No two workgroups spin on one address.  Epochs
-// grow monotonically across launches on a workspace (the base is kept in the
+// Grid barrier with per-workgroup flags.
+//
+// Arrival: thread 0 of each workgroup releases its writes (agent-scope fence)
+// and stores the epoch into its own arrival flag (64-byte line).  Workgroup 0's
+// first wave polls all arrival flags (4 per lane, in flight together), then
+// writes every release flag.  Other workgroups poll only their own release
+// flag, so no line is contended by more than two agents.  Epochs grow
+// monotonically across launches on a workspace (the base is kept in the
 // header), so flags never need resetting.  Every spin is bounded by the
 // deadline; a timeout sets the abort word, which every spinner also watches.
-DEV bool grid_barrier(const KArgs& ka, uint32_t epoch, uint32_t stage, uint64_t deadline) {
+DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline) {
   __shared__ uint32_t s_ok;
-  uint32_t* arrive = (uint32_t*)(ka.ws + kHdrArrive);
-  uint32_t* release = (uint32_t*)(ka.ws + kHdrRelease);
-  uint32_t* abort = (uint32_t*)(ka.ws + kHdrAbort);
+  GLOBAL uint32_t* arrive = (GLOBAL uint32_t*)(ka.ws + kHdrArrive);
+  GLOBAL uint32_t* release = (GLOBAL uint32_t*)(ka.ws + kHdrRelease);
+  GLOBAL uint32_t* abort = (GLOBAL uint32_t*)(ka.ws + kHdrAbort);
+  GLOBAL uint32_t* abort_stage = (GLOBAL uint32_t*)(ka.ws + kHdrAbortStage);
   const uint32_t G = gridDim.x, bid = blockIdx.x;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -912,7 +1200,7 @@ DEV bool grid_barrier(const KArgs& ka, uint32_t epoch, uint32_t stage, uint64_t 
     const uint32_t lane = threadIdx.x;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     for (uint32_t base = 0; base < G; base += 256) {
-      uint32_t* f[4];
+      GLOBAL uint32_t* f[4];
       bool live[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -929,9 +1217,12 @@ DEV bool grid_barrier(const KArgs& ka, uint32_t epoch, uint32_t stage, uint64_t 
             if ((int32_t)(v - epoch) < 0) done = false;
           }
         if (done) break;
-        if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = 0; break; }
+        if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+          ok = 0;
+          break;
+        }
         if (__builtin_amdgcn_s_memrealtime() - t0 > deadline) {
-          __hip_atomic_store((uint32_t*)(ka.ws + kHdrAbortStage), stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          __hip_atomic_store(abort_stage, stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           __hip_atomic_store(abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
           ok = 0;
           break;
@@ -947,12 +1238,15 @@ DEV bool grid_barrier(const KArgs& ka, uint32_t epoch, uint32_t stage, uint64_t 
     if (lane == 0) s_ok = all_ok;
   } else if (bid != 0 && threadIdx.x == 0) {
     uint32_t ok = 1;
-    uint32_t* f = release + bid * kFlagStride;
+    GLOBAL uint32_t* f = release + bid * kFlagStride;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
     while ((int32_t)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - epoch) < 0) {
-      if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) { ok = 0; break; }
+      if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
+        ok = 0;
+        break;
+      }
       if (__builtin_amdgcn_s_memrealtime() - t0 > deadline) {
-        __hip_atomic_store((uint32_t*)(ka.ws + kHdrAbortStage), stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(abort_stage, stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         ok = 0;
         break;
@@ -974,64 +1268,73 @@ DEV uint32_t hash32(uint32_t x) {
   return x;
 }
 
-// Copy a stage blob into LDS (all threads; 16-byte chunks).
-DEV void stage_blob_to_lds(const uint8_t* plan, const DStage& st, uint8_t* lds) {
-  const u32x4* src = (const u32x4*)(plan + st.blob_off);
-  u32x4* dst = (u32x4*)lds;
-  for (uint32_t i = threadIdx.x; i < st.blob_bytes / 16; i += kBlock) dst[i] = src[i];
+// Copy a stage blob into LDS (all threads; 16-byte chunks).  The scheduler
+// keeps every stage blob within kPlanLds bytes.
+DEV void stage_blob_to_lds(const GLOBAL uint8_t* plan, const DStage& st) {
+  const GLOBAL u32x4* src = (const GLOBAL u32x4*)(plan + st.blob_off);
+  LDS u32x4* dst = (LDS u32x4*)g_plan;
+  const uint32_t n = (st.blob_bytes < kPlanLds ? st.blob_bytes : kPlanLds) / 16;
+  for (uint32_t i = threadIdx.x; i < n; i += kBlock) dst[i] = src[i];
 }
 
 }  // namespace
 
-__global__ __launch_bounds__(kBlock, 2) void tk_persistent(KArgs) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[kSmemBytes];
-  __shared__ __attribute__((aligned(16))) uint8_t planbuf[kPlanLds];
-  // Read the argument block in place (the kernarg segment) so the base-pointer
-  // table is indexed in memory rather than copied into private storage.
-  const KArgs& ka = *(const KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
-  const DHeader* h = (const DHeader*)ka.plan;
-  const DStage* stages = (const DStage*)(ka.plan + h->off_stages);
+__global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
+  // The argument block stays in the kernel argument segment (read in place, so
+  // the base table is never copied into private memory); it is read once here.
+  const KArgs& kargs = *(const KArgs*)__builtin_amdgcn_kernarg_segment_ptr();
+  Ctx ka;
+  ka.ws = (GLOBAL uint8_t*)uniform64((int64_t)kargs.ws);
+  ka.plan = (const GLOBAL uint8_t*)uniform64((int64_t)kargs.plan);
+  ka.flags = uniform(kargs.flags);
+  ka.stagger_seed = uniform(kargs.stagger_seed);
+  const uint32_t n_bases = kargs.n_bases < (uint32_t)kMaxBases ? kargs.n_bases : (uint32_t)kMaxBases;
+  for (uint32_t i = threadIdx.x; i < n_bases; i += kBlock) ((LDS uint64_t*)g_bases)[i] = (uint64_t)kargs.bases[i];
+  const uint64_t deadline = kargs.deadline_ticks ? kargs.deadline_ticks : 400000000ull;  // 4 s at 100 MHz
+  const GLOBAL DHeader* h = (const GLOBAL DHeader*)ka.plan;
+  const GLOBAL uint8_t* stages = ka.plan + h->off_stages;
   const uint32_t n_stages = h->n_stages;
-  const uint64_t deadline = ka.deadline_ticks ? ka.deadline_ticks : 400000000ull;  // 4 s at 100 MHz
-  if (*(volatile uint32_t*)(ka.ws + kHdrAbort) != 0u) return;  // a previous launch on this workspace aborted
-  const uint32_t epoch0 = *(volatile uint32_t*)(ka.ws + kHdrEpoch);
+  if (*(volatile GLOBAL uint32_t*)(ka.ws + kHdrAbort) != 0u) return;  // a previous launch on this workspace aborted
+  const uint32_t epoch0 = *(volatile GLOBAL uint32_t*)(ka.ws + kHdrEpoch);
   if (n_stages == 0) return;
-  DStage st = stages[0];
-  if (st.blob_bytes <= kPlanLds) stage_blob_to_lds(ka.plan, st, planbuf);
+  DStage sd = load_stage(stages, 0);
+  stage_blob_to_lds(ka.plan, sd);
   __syncthreads();
+  if ((ka.flags & K_TIMESTAMPS) && blockIdx.x == 0 && threadIdx.x == 0)
+    ((GLOBAL uint64_t*)(ka.ws + kHdrStamps))[0] = __builtin_amdgcn_s_memrealtime();
+  trace_stamp(ka, 0xffffffffu);
   for (uint32_t s = 0; s < n_stages; ++s) {
-    const bool in_lds = st.blob_bytes <= kPlanLds;
-    const uint8_t* blob = in_lds ? planbuf : ka.plan + st.blob_off;
-    Plan pl;
-    pl.tasks = (const DTask*)blob;
-    pl.views = (const DView*)(blob + st.off_views);
-    pl.ins = (const DIns*)(blob + st.off_ins);
     uint32_t ti = 0;
-    for (uint32_t item = blockIdx.x; item < st.n_items; item += gridDim.x) {
-      while (ti + 1 < st.n_tasks && item >= pl.tasks[ti + 1].item_begin) ++ti;
-      const DTask t = pl.tasks[ti];
+    for (uint32_t item = blockIdx.x; item < sd.n_items; item += gridDim.x) {
+      while (ti + 1 < sd.n_tasks && item >= task_item_begin(ti + 1)) ++ti;
+      const DTask t = load_task(ti);
       if (ka.flags & K_STAGGER) {
         uint32_t n = hash32(ka.stagger_seed ^ (blockIdx.x * 0x9e3779b9u) ^ (item * 0x85ebca6bu) ^ s) % 48u;
         for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
       }
-      run_item(ka, pl, t, item - t.item_begin, smem);
+      trace_stamp(ka, 0x1000 + s);
+      run_item(ka, t, sd, item - t.item_begin);
+      trace_stamp(ka, 0x2000 + s);
     }
     if (s + 1 < n_stages) {
-      // stage the next stage's descriptors while the barrier completes
-      __syncthreads();
-      st = stages[s + 1];
-      if (st.blob_bytes <= kPlanLds) stage_blob_to_lds(ka.plan, st, planbuf);
       const bool stamp = (ka.flags & K_TIMESTAMPS) && blockIdx.x == 0 && threadIdx.x == 0 && s < kMaxTimedStages;
-      if (stamp) ((uint64_t*)(ka.ws + kHdrStamps))[2 * s] = __builtin_amdgcn_s_memrealtime();
+      GLOBAL uint64_t* stamps = (GLOBAL uint64_t*)(ka.ws + kHdrStamps) + 4 * s;
+      if (stamp) stamps[1] = __builtin_amdgcn_s_memrealtime();
+      // stage the next stage's descriptors while the barrier completes (every
+      // thread of this workgroup is past its last read of the current blob)
+      sd = load_stage(stages, s + 1);
+      stage_blob_to_lds(ka.plan, sd);
+      if (stamp) stamps[2] = __builtin_amdgcn_s_memrealtime();
       if (!grid_barrier(ka, epoch0 + s + 1, s, deadline)) return;
-      if (stamp) ((uint64_t*)(ka.ws + kHdrStamps))[2 * s + 1] = __builtin_amdgcn_s_memrealtime();
+      if (stamp) stamps[3] = __builtin_amdgcn_s_memrealtime();
+      if (stamp && s + 1 < kMaxTimedStages) stamps[4] = stamps[3];
     }
   }
   // The next launch on this workspace continues the epoch sequence.  Every
   // workgroup has read the base before the first barrier, which this
   // workgroup has passed.
   if (n_stages > 1 && blockIdx.x == 0 && threadIdx.x == 0)
-    *(volatile uint32_t*)(ka.ws + kHdrEpoch) = epoch0 + n_stages - 1;
+    *(volatile GLOBAL uint32_t*)(ka.ws + kHdrEpoch) = epoch0 + n_stages - 1;
 }
 
 __global__ void tk_zero_header(uint8_t* ws, uint32_t bytes) {

@@ -1071,7 +1071,8 @@ struct Builder {
     return t;
   }
 
-  static uint32_t ew_items(int64_t numel) { return (uint32_t)std::max<int64_t>(1, (numel + 2047) / 2048); }
+  // Elementwise work item: 4096 elements (16 per thread).
+  static uint32_t ew_items(int64_t numel) { return (uint32_t)std::max<int64_t>(1, (numel + 4095) / 4096); }
 
   void emit_pointwise(const Entry& e) {
     const Op& o2 = op(e.op);
@@ -1620,12 +1621,16 @@ struct Builder {
     }
     // Per stage: tasks, then the views and instructions they use, re-indexed
     // locally so the stage blob is self-contained.
-    std::vector<DStage> ds;
-    std::vector<std::vector<uint8_t>> blobs;
-    int max_items = 0;
-    size_t n_tasks_total = 0;
-    std::ostringstream dump;
-    for (size_t s = 0; s < stages.size(); ++s) {
+    // A stage blob is staged whole in LDS by every workgroup; a level whose
+    // descriptors exceed that buffer runs as several consecutive stages
+    // (tasks of one level are independent, so any split is valid).
+    struct Enc {
+      DStage d;
+      std::vector<uint8_t> blob;
+      std::string dump;
+      uint32_t items;
+    };
+    auto encode_group = [&](const std::vector<DTask>& group, const std::vector<std::string>& gdesc) -> Enc {
       std::vector<DTask> tk;
       std::vector<DView> sv;
       std::vector<DIns> si;
@@ -1647,12 +1652,13 @@ struct Builder {
         }
         return at;
       };
-      uint32_t items = 0;
-      dump << "stage " << s << ":\n";
-      for (size_t t = 0; t < stages[s].size(); ++t) {
-        DTask task = stages[s][t];
-        task.item_begin = items;
-        items += task.n_items;
+      Enc e;
+      e.items = 0;
+      std::ostringstream gd;
+      for (size_t t = 0; t < group.size(); ++t) {
+        DTask task = group[t];
+        task.item_begin = e.items;
+        e.items += task.n_items;
         if (task.kind == T_GEMM_MFMA || task.kind == T_GEMM_SIMT || task.kind == T_GEMV_Q8) {
           task.va = mapv(task.va);
           task.vb = mapv(task.vb);
@@ -1661,24 +1667,54 @@ struct Builder {
         task.expr_first = task.expr_len ? mapcode(task.expr_first, task.expr_len) : 0;
         task.fin_first = task.fin_len ? mapcode(task.fin_first, task.fin_len) : 0;
         tk.push_back(task);
-        dump << "  " << kind_name(task.kind) << " items=" << task.n_items << " : " << descs[s][t] << "\n";
+        gd << "  " << kind_name(task.kind) << " items=" << task.n_items << " : " << gdesc[t] << "\n";
       }
-      DStage d{};
+      DStage& d = e.d;
+      d = DStage{};
       d.n_tasks = (uint32_t)tk.size();
-      d.n_items = items;
+      d.n_items = e.items;
       d.n_views = (uint32_t)sv.size();
       d.n_ins = (uint32_t)si.size();
       d.off_views = (uint32_t)align_up(tk.size() * sizeof(DTask), 16);
       d.off_ins = (uint32_t)align_up(d.off_views + sv.size() * sizeof(DView), 16);
       d.blob_bytes = (uint32_t)align_up(d.off_ins + si.size() * sizeof(DIns), 16);
-      std::vector<uint8_t> blob(d.blob_bytes, 0);
-      if (!tk.empty()) std::memcpy(blob.data(), tk.data(), tk.size() * sizeof(DTask));
-      if (!sv.empty()) std::memcpy(blob.data() + d.off_views, sv.data(), sv.size() * sizeof(DView));
-      if (!si.empty()) std::memcpy(blob.data() + d.off_ins, si.data(), si.size() * sizeof(DIns));
-      blobs.push_back(blob);
-      ds.push_back(d);
-      max_items = std::max<int>(max_items, (int)items);
-      n_tasks_total += tk.size();
+      e.blob.assign(d.blob_bytes, 0);
+      if (!tk.empty()) std::memcpy(e.blob.data(), tk.data(), tk.size() * sizeof(DTask));
+      if (!sv.empty()) std::memcpy(e.blob.data() + d.off_views, sv.data(), sv.size() * sizeof(DView));
+      if (!si.empty()) std::memcpy(e.blob.data() + d.off_ins, si.data(), si.size() * sizeof(DIns));
+      e.dump = gd.str();
+      return e;
+    };
+    std::vector<Enc> enc;
+    for (size_t s = 0; s < stages.size(); ++s) {
+      std::vector<DTask> group;
+      std::vector<std::string> gdesc;
+      for (size_t t = 0; t < stages[s].size(); ++t) {
+        group.push_back(stages[s][t]);
+        gdesc.push_back(descs[s][t]);
+        if (encode_group(group, gdesc).d.blob_bytes <= kPlanLds) continue;
+        if (group.size() == 1)
+          raise(TK_E_UNSUPPORTED, "descriptors of one task exceed the " + std::to_string(kPlanLds) + "-byte stage buffer: " +
+                                      descs[s][t]);
+        group.pop_back();
+        gdesc.pop_back();
+        enc.push_back(encode_group(group, gdesc));
+        group = {stages[s][t]};
+        gdesc = {descs[s][t]};
+      }
+      if (!group.empty()) enc.push_back(encode_group(group, gdesc));
+    }
+    std::vector<DStage> ds;
+    std::vector<std::vector<uint8_t>> blobs;
+    int max_items = 0;
+    size_t n_tasks_total = 0;
+    std::ostringstream dump;
+    for (size_t s = 0; s < enc.size(); ++s) {
+      dump << "stage " << s << ":\n" << enc[s].dump;
+      ds.push_back(enc[s].d);
+      blobs.push_back(enc[s].blob);
+      max_items = std::max<int>(max_items, (int)enc[s].items);
+      n_tasks_total += enc[s].d.n_tasks;
     }
     dump << "workspace: " << kHeaderBytes << " header + " << arena_bytes << " arena bytes\n";
     for (auto& kv : arena_off) dump << "  arena " << kv.first << " @" << kv.second << "\n";

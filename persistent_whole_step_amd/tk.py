@@ -313,7 +313,7 @@ class Program:
         return bool(a.value), s.value
 
     def read_timestamps(self, workspace, stream=None):
-        n = 2 * self.query()["n_stages"]
+        n = 4 * self.query()["n_stages"]
         ws = describe(workspace)
         ws.dtype = TK_I8
         arr = (ctypes.c_uint64 * max(1, n))()
