@@ -63,7 +63,7 @@ class Runner:
     def __init__(self, name: str, seed0: int = 0, **opts):
         import torch
         from persistent_whole_step_amd import programs, tk
-        from tests.parity import to_torch
+        to_torch = tk.tensor_from_storage
         self.name = name
         self.cfg = programs.CONFIGS[name]
         self.prog = programs.build(self.cfg)

@@ -117,6 +117,28 @@ def _torch_dtype_code(t) -> int:
     return m[t.dtype]
 
 
+def tensor_from_storage(a, dt: str, device="cuda:0"):
+    """Device tensor holding numpy storage `a` of program dtype `dt` (bf16 is
+    carried as uint16 bit patterns).  Argument marshalling only."""
+    import numpy as np
+    import torch
+    if dt == "bf16":
+        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
+    else:
+        t = torch.from_numpy(np.ascontiguousarray(a))
+    return t.to(device)
+
+
+def storage_from_tensor(t, dt: str):
+    """Host numpy storage of a tensor of program dtype `dt` (bf16 as uint16)."""
+    import numpy as np
+    import torch
+    t = t.detach().cpu()
+    if dt == "bf16":
+        return t.view(torch.int16).numpy().view(np.uint16).copy()
+    return t.numpy().copy()
+
+
 def describe(t) -> TkTensor:
     """A tk_tensor for a torch tensor (storage extent used for aliasing)."""
     d = TkTensor()

@@ -31,20 +31,13 @@ def torch_dtype(dt):
 
 
 def to_torch(a: np.ndarray, dt: str, device="cuda:0"):
-    import torch
-    if dt == "bf16":
-        t = torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16)
-    else:
-        t = torch.from_numpy(np.ascontiguousarray(a))
-    return t.to(device)
+    from persistent_whole_step_amd import tk
+    return tk.tensor_from_storage(a, dt, device)
 
 
 def to_numpy(t, dt: str) -> np.ndarray:
-    import torch
-    t = t.detach().cpu()
-    if dt == "bf16":
-        return t.view(torch.int16).numpy().view(np.uint16).copy()
-    return t.numpy().copy()
+    from persistent_whole_step_amd import tk
+    return tk.storage_from_tensor(t, dt)
 
 
 def f32_of(a: np.ndarray, dt: str) -> np.ndarray:
