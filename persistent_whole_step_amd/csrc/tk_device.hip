@@ -528,15 +528,21 @@ DEV void gemm_simt(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
 // ------------------------------------------------------- MFMA contraction --
 // Tile BM x BN, K staged 64 deep; 4 waves in a 2x2 grid, each wave a
 // (BM/2) x (BN/2) block of 32x32 MFMA accumulators.  Both operands are staged
-// in LDS k-contiguous ([row][k], pitch 72 elements): an operand stored with
-// unit stride along M/N is transposed in registers on its way to LDS so every
-// global read stays 16 bytes wide and coalesced.  On the fast path (interior
-// tile, whole 64-deep slices, 16-byte aligned rows) the global loads of slice
-// k+1 are issued into registers before slice k is multiplied and written to
-// the other LDS buffer afterwards; other tiles stage element by element.
+// in LDS k-contiguous, [row][64 k] in 128-byte rows of eight 16-byte chunks,
+// chunk c of row r stored at position c ^ ((r ^ (r >> 3)) & 7).  The swizzle
+// spreads every access pattern of the loop over all banks: the 16-byte
+// stores of a k-contiguous operand, the 4/8-byte stores of an operand
+// transposed in registers (unit stride along M/N, loaded 16 bytes wide along
+// its rows), and the 16-byte fragment reads of the MFMAs.  On the fast path
+// (interior tile, whole 64-deep slices, 16-byte aligned rows) the global
+// loads of D slices are in flight in registers ahead of the MFMAs; other
+// tiles stage element by element.
 
 constexpr int kBK = 64;
-constexpr int kPitch = kBK + 8;
+constexpr int kPitch = kBK;  // halfs per staged row
+
+// Element offset (in halfs) of (row, 16-byte chunk c) in a staged operand.
+DEV int swz(int row, int c) { return row * kPitch + ((c ^ ((row ^ (row >> 3)) & 7)) << 3); }
 
 // Per-thread loads of one operand: N = R/32 16-byte loads per 64-deep slice.
 // kc: unit stride along k (16-byte chunks along k); otherwise unit stride
@@ -573,11 +579,13 @@ struct FastOp {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
         const int ch = threadIdx.x + i * kBlock;
-        *(LDS u32x4*)(lds + (ch / 8) * kPitch + (ch % 8) * 8) = v[i];
+        *(LDS u32x4*)(lds + swz(ch / 8, ch % 8)) = v[i];
       }
     } else {
-      const int rb = threadIdx.x % (R / 8), kb = threadIdx.x / (R / 8);
+      // thread (rb, kb) holds rows rb*8 .. rb*8+7 at k = kb*N .. kb*N+N-1;
       // row rb*8 + 2j takes the low halves, row rb*8 + 2j + 1 the high halves
+      const int rb = threadIdx.x % (R / 8), kb = threadIdx.x / (R / 8);
+      const int c = (kb * N) / 8, e = (kb * N) % 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         uint32_t lo[N / 2], hi[N / 2];
@@ -586,8 +594,9 @@ struct FastOp {
           lo[h] = (v[2 * h][j] & 0xffffu) | (v[2 * h + 1][j] << 16);
           hi[h] = (v[2 * h][j] >> 16) | (v[2 * h + 1][j] & 0xffff0000u);
         }
-        LDS uint16_t* d0 = lds + (rb * 8 + 2 * j) * kPitch + kb * N;
-        LDS uint16_t* d1 = d0 + kPitch;
+        const int r0 = rb * 8 + 2 * j;
+        LDS uint16_t* d0 = lds + swz(r0, c) + e;
+        LDS uint16_t* d1 = lds + swz(r0 + 1, c) + e;
         if (N == 4) {
           *(LDS u32x2*)d0 = u32x2{lo[0], lo[1]};
           *(LDS u32x2*)d1 = u32x2{hi[0], hi[1]};
@@ -611,12 +620,13 @@ DEV void slow_stage(const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t s
     const uint32_t gr = r0 + r, gk = k0 + kk;
     const bool ok = gr < rmax && gk < kmax;
     const uint16_t v = q[off + (int64_t)(ok ? gr : 0) * sr + (int64_t)(ok ? gk : 0) * sk];
-    lds[r * kPitch + kk] = ok ? v : (uint16_t)0;
+    lds[swz(r, kk / 8) + kk % 8] = ok ? v : (uint16_t)0;
   }
 }
 
-DEV f32x16 mfma32(bool bf16, u32x4 a, u32x4 b, f32x16 c) {
-  if (bf16)
+template <bool BF16>
+DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
+  if (BF16)
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                    0, 0);
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a), __builtin_bit_cast(f16x8, b), c, 0, 0,
@@ -624,35 +634,29 @@ DEV f32x16 mfma32(bool bf16, u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // One 64-deep K slice from LDS into the wave's accumulators.
-template <int BM, int BN>
-DEV void mfma_slice(bool bf16, const LDS uint16_t* sa, const LDS uint16_t* sb, f32x16 (&acc)[BM / 64][BN / 64]) {
+template <int BM, int BN, bool BF16>
+DEV void mfma_slice(const LDS uint16_t* sa, const LDS uint16_t* sb, f32x16 (&acc)[BM / 64][BN / 64]) {
   constexpr int FM = BM / 64, FN = BN / 64;
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
   const int wm = wave / 2, wn = wave % 2;
-  const LDS uint16_t* a_t = sa + (wm * (BM / 2) + (lane % 32)) * kPitch + 8 * (lane / 32);
-  const LDS uint16_t* b_t = sb + (wn * (BN / 2) + (lane % 32)) * kPitch + 8 * (lane / 32);
+  const int ra = wm * (BM / 2) + (lane % 32), rbw = wn * (BN / 2) + (lane % 32), ch = lane / 32;
 #pragma unroll
   for (int kk = 0; kk < kBK; kk += 16) {
     u32x4 af[FM], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *(const LDS u32x4*)(a_t + i * 32 * kPitch + kk);
+    for (int i = 0; i < FM; ++i) af[i] = *(const LDS u32x4*)(sa + swz(ra + i * 32, kk / 8 + ch));
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[j] = *(const LDS u32x4*)(b_t + j * 32 * kPitch + kk);
-    if (bf16) {
+    for (int j = 0; j < FN; ++j) bfr[j] = *(const LDS u32x4*)(sb + swz(rbw + j * 32, kk / 8 + ch));
 #pragma unroll
-      for (int i = 0; i < FM; ++i)
+    for (int i = 0; i < FM; ++i)
 #pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(true, af[i], bfr[j], acc[i][j]);
-    } else {
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32(false, af[i], bfr[j], acc[i][j]);
-    }
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<BF16>(af[i], bfr[j], acc[i][j]);
   }
 }
 
-template <int BM, int BN>
+// BF16: operand dtype (bf16, else f16), a template parameter so the MFMA
+// accumulators never change registers between the two instruction forms.
+template <int BM, int BN, bool BF16>
 DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
   constexpr int FM = BM / 64, FN = BN / 64;  // 32x32 blocks per wave along m / n
   const uint32_t tiles = t.tiles_m * t.tiles_n;
@@ -663,7 +667,6 @@ DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
   const uint32_t kbeg = split_index * t.kchunk;
   const uint32_t kend = (kbeg + t.kchunk < t.k) ? kbeg + t.kchunk : t.k;
   const DView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
-  const bool bf16 = A.dtype == DT_BF16;
   const GLOBAL uint16_t* pa = (const GLOBAL uint16_t*)base_ptr(ka, A.base);
   const GLOBAL uint16_t* pb = (const GLOBAL uint16_t*)base_ptr(ka, B.base);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -724,7 +727,7 @@ DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
         const uint32_t nx = k + D < last ? k + D : last;
         fa.load(nx, ra[d]);
         fb.load(nx, rb[d]);
-        if (act) mfma_slice<BM, BN>(bf16, sa, sb, acc);
+        if (act) mfma_slice<BM, BN, BF16>(sa, sb, acc);
       }
     }
     __syncthreads();  // every wave is done with the staging buffers (the C tile reuses them)
@@ -734,7 +737,7 @@ DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
       slow_stage<BM>(pa, A.offset, A.stride[0], A.stride[1], m0, t.m, k0, kend, sa0);
       slow_stage<BN>(pb, B.offset, B.stride[1], B.stride[0], n0, t.n, k0, kend, sb0);
       __syncthreads();
-      mfma_slice<BM, BN>(bf16, sa0, sb0, acc);
+      mfma_slice<BM, BN, BF16>(sa0, sb0, acc);
       __syncthreads();
     }
   }
@@ -1141,13 +1144,23 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
       gemm_simt(ka, t, sd.off_views, item, st);
       __syncthreads();
       break;
-    case T_GEMM_MFMA:
-      if (t.tile == 0)
-        gemm_mfma<128, 128>(ka, t, sd.off_views, item, st);
-      else
-        gemm_mfma<64, 64>(ka, t, sd.off_views, item, st);
+    case T_GEMM_MFMA: {
+      // the operand dtype is the A view's (both operands share it)
+      const bool bf16 = uniform(((const LDS DView*)(g_plan + sd.off_views + t.va * sizeof(DView)))->dtype) == DT_BF16;
+      if (t.tile == 0) {
+        if (bf16)
+          gemm_mfma<128, 128, true>(ka, t, sd.off_views, item, st);
+        else
+          gemm_mfma<128, 128, false>(ka, t, sd.off_views, item, st);
+      } else {
+        if (bf16)
+          gemm_mfma<64, 64, true>(ka, t, sd.off_views, item, st);
+        else
+          gemm_mfma<64, 64, false>(ka, t, sd.off_views, item, st);
+      }
       __syncthreads();
       break;
+    }
     case T_GEMV_Q8:
       gemv_q8(ka, t, sd.off_views, item);
       break;
