@@ -113,6 +113,8 @@ struct DTask {
   uint32_t fin_first;  // reductions: the finishing program (mean, rounding, store)
   uint32_t fin_len;
   uint32_t dims[kMaxDims];  // iteration shape (elementwise / reduction source / GEMM output [m, n])
+  uint32_t dmul[kMaxDims];  // division by dims[d] (d >= 1): q = (t + ((e - t) >> min(l,1))) >> max(l-1,0),
+  uint8_t dsh[kMaxDims];    //   t = mulhi(dmul[d], e), l = dsh[d] = ceil(log2 dims[d])  (Granlund-Montgomery)
   uint32_t m, n, k;         // contraction sizes; reductions: rows/cols and reduced size
   uint32_t split;           // split-K parts / reduction parts
   uint32_t kchunk;          // K elements per split part / rows per reduction part
@@ -122,6 +124,7 @@ struct DTask {
   float count;              // mean divisor
   uint32_t pad2;
 };
+static_assert(sizeof(DTask) % 8 == 0, "DTask layout");
 
 // A stage's descriptors form one contiguous blob in the plan:
 // [DTask x n_tasks][DView x n_views][DIns x n_ins], indices local to the blob,

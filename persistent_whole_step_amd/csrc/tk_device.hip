@@ -59,12 +59,11 @@ DEV LDS uint32_t& xe(int q) { return ((LDS uint32_t*)g_xe)[q * kBlock + threadId
 
 DEV float bf16_bits_to_f32(uint32_t h) { return __uint_as_float(h << 16); }
 
-// float -> bf16 with round-to-nearest-even; NaN stays a quiet NaN.
+// float -> bf16 with round-to-nearest-even (v_cvt_pk_bf16_f32; NaN stays
+// NaN, subnormals kept).
 DEV uint32_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return u >> 16;
+  const __bf16 h = (__bf16)f;
+  return (uint32_t)__builtin_bit_cast(uint16_t, h);
 }
 
 DEV float f16_bits_to_f32(uint32_t h) {
@@ -117,100 +116,135 @@ DEV float load_elem(const GLOBAL uint8_t* p, uint32_t dt, int64_t idx) {
   return half_bits_to_f32(((const GLOBAL uint16_t*)p)[idx], dt == DT_BF16);
 }
 
-// W consecutive elements (stride s) starting at element idx.  Unit-stride
-// aligned chunks use 16-byte loads; stride 0 loads once and broadcasts.
-template <int W>
-DEV void load_chunk(const GLOBAL uint8_t* p, uint32_t dt, int64_t idx, int64_t s, float (&x)[W]) {
+// Loads of all C chunks of one view operand, issued before any is used.
+// vec (uniform): unit inner stride, 16-byte aligned base, and every chunk
+// start 16-byte aligned, so each 8-wide chunk is one (bf16/f16) or two (f32)
+// 16-byte loads.  Every index must address an element of the view (dead
+// chunks point at its first element).
+template <int W, int C>
+DEV void load_chunks(const GLOBAL uint8_t* p, uint32_t dt, bool vec, int32_t s, const int32_t (&idx)[C],
+                     float (&x)[C][W]) {
   if (dt == DT_F32) {
-    const GLOBAL float* q = (const GLOBAL float*)p + idx;
-    if (W == 8 && s == 1 && aligned16(q)) {
-      const u32x4 r0 = *(const GLOBAL u32x4*)q, r1 = *(const GLOBAL u32x4*)(q + 4);
+    const GLOBAL float* q = (const GLOBAL float*)p;
+    if (W == 8 && vec) {
+      u32x4 r[C][2];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        x[j] = __uint_as_float(r0[j]);
-        x[4 + j] = __uint_as_float(r1[j]);
+      for (int c = 0; c < C; ++c) {
+        r[c][0] = *(const GLOBAL u32x4*)(q + idx[c]);
+        r[c][1] = *(const GLOBAL u32x4*)(q + idx[c] + 4);
       }
-    } else if (W == 8 && s == 0) {
-      const float a = q[0];
 #pragma unroll
-      for (int j = 0; j < W; ++j) x[j] = a;
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < W; ++j) x[c][j] = __uint_as_float(r[c][j / 4][j % 4]);
+    } else if (W == 8 && s == 0) {
+      float r[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) r[c] = q[idx[c]];
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < W; ++j) x[c][j] = r[c];
     } else {
 #pragma unroll
-      for (int j = 0; j < W; ++j) x[j] = q[j * s];
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < W; ++j) x[c][j] = q[idx[c] + j * s];
     }
   } else if (dt == DT_I8) {
-    const GLOBAL int8_t* q = (const GLOBAL int8_t*)p + idx;
+    const GLOBAL int8_t* q = (const GLOBAL int8_t*)p;
+    int32_t r[C][W];
 #pragma unroll
-    for (int j = 0; j < W; ++j) x[j] = (float)q[j * s];
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < W; ++j) r[c][j] = q[idx[c] + j * s];
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < W; ++j) x[c][j] = (float)r[c][j];
   } else {
-    const GLOBAL uint16_t* q = (const GLOBAL uint16_t*)p + idx;
-    uint32_t h[W];
-    if (W == 8 && s == 1 && aligned16(q)) {
-      const u32x4 r = *(const GLOBAL u32x4*)q;
+    const GLOBAL uint16_t* q = (const GLOBAL uint16_t*)p;
+    const bool bf = dt == DT_BF16;
+    uint32_t h[C][W];
+    if (W == 8 && vec) {
+      u32x4 r[C];
 #pragma unroll
-      for (int j = 0; j < W / 2; ++j) {
-        h[2 * j] = r[j] & 0xffffu;
-        h[2 * j + 1] = r[j] >> 16;
-      }
+      for (int c = 0; c < C; ++c) r[c] = *(const GLOBAL u32x4*)(q + idx[c]);
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < W; ++j) h[c][j] = (j & 1) ? r[c][j / 2] >> 16 : r[c][j / 2] & 0xffffu;
     } else if (W == 8 && s == 0) {
-      const uint32_t a = q[0];
+      uint32_t r[C];
 #pragma unroll
-      for (int j = 0; j < W; ++j) h[j] = a;
+      for (int c = 0; c < C; ++c) r[c] = q[idx[c]];
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+#pragma unroll
+        for (int j = 0; j < W; ++j) h[c][j] = r[c];
     } else {
 #pragma unroll
-      for (int j = 0; j < W; ++j) h[j] = q[j * s];
-    }
-    const bool bf = dt == DT_BF16;
+      for (int c = 0; c < C; ++c)
 #pragma unroll
-    for (int j = 0; j < W; ++j) x[j] = half_bits_to_f32(h[j], bf);
+        for (int j = 0; j < W; ++j) h[c][j] = q[idx[c] + j * s];
+    }
+#pragma unroll
+    for (int c = 0; c < C; ++c)
+#pragma unroll
+      for (int j = 0; j < W; ++j) x[c][j] = half_bits_to_f32(h[c][j], bf);
   }
 }
 
-template <int W>
-DEV void store_chunk(GLOBAL uint8_t* p, uint32_t dt, int64_t idx, int64_t s, const float (&x)[W]) {
+// Stores of the live chunks (bit q of `live`), converted to the view's dtype.
+template <int W, int C>
+DEV void store_chunks(GLOBAL uint8_t* p, uint32_t dt, bool vec, int32_t s, const int32_t (&idx)[C], uint32_t live,
+                      const float (&x)[C][W]) {
   if (dt == DT_F32) {
-    GLOBAL float* q = (GLOBAL float*)p + idx;
-    if (W == 8 && s == 1 && aligned16(q)) {
-      u32x4 r0, r1;
+    GLOBAL float* q = (GLOBAL float*)p;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        r0[j] = __float_as_uint(x[j]);
-        r1[j] = __float_as_uint(x[4 + j]);
+    for (int c = 0; c < C; ++c) {
+      if (!(live & (1u << c))) continue;
+      if (W == 8 && vec) {
+        u32x4 r0, r1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          r0[j] = __float_as_uint(x[c][j]);
+          r1[j] = __float_as_uint(x[c][4 + j]);
+        }
+        *(GLOBAL u32x4*)(q + idx[c]) = r0;
+        *(GLOBAL u32x4*)(q + idx[c] + 4) = r1;
+      } else {
+#pragma unroll
+        for (int j = 0; j < W; ++j) q[idx[c] + j * s] = x[c][j];
       }
-      *(GLOBAL u32x4*)q = r0;
-      *(GLOBAL u32x4*)(q + 4) = r1;
-    } else {
-#pragma unroll
-      for (int j = 0; j < W; ++j) q[j * s] = x[j];
     }
   } else if (dt != DT_I8) {
-    GLOBAL uint16_t* q = (GLOBAL uint16_t*)p + idx;
+    GLOBAL uint16_t* q = (GLOBAL uint16_t*)p;
     const bool bf = dt == DT_BF16;
-    uint32_t h[W];
 #pragma unroll
-    for (int j = 0; j < W; ++j) h[j] = f32_to_half_bits(x[j], bf);
-    if (W == 8 && s == 1 && aligned16(q)) {
-      u32x4 r;
+    for (int c = 0; c < C; ++c) {
+      if (!(live & (1u << c))) continue;
+      uint32_t h[W];
 #pragma unroll
-      for (int j = 0; j < W / 2; ++j) r[j] = h[2 * j] | (h[2 * j + 1] << 16);
-      *(GLOBAL u32x4*)q = r;
-    } else {
+      for (int j = 0; j < W; ++j) h[j] = f32_to_half_bits(x[c][j], bf);
+      if (W == 8 && vec) {
+        u32x4 r;
 #pragma unroll
-      for (int j = 0; j < W; ++j) q[j * s] = (uint16_t)h[j];
+        for (int j = 0; j < W / 2; ++j) r[j] = h[2 * j] | (h[2 * j + 1] << 16);
+        *(GLOBAL u32x4*)(q + idx[c]) = r;
+      } else {
+#pragma unroll
+        for (int j = 0; j < W; ++j) q[idx[c] + j * s] = (uint16_t)h[j];
+      }
     }
   }
 }
 
-DEV void unravel4(uint32_t e, const uint32_t (&dims)[kMaxDims], uint32_t nd, uint32_t (&c)[kMaxDims]) {
-#pragma unroll
-  for (int d = kMaxDims - 1; d >= 0; --d) {
-    if ((uint32_t)d >= nd) {
-      c[d] = 0;
-    } else {
-      c[d] = e % dims[d];
-      e /= dims[d];
-    }
-  }
+// e / d for the divisor constants (m, l) the host computed for d.
+DEV uint32_t udiv(uint32_t e, uint32_t m, uint32_t l) {
+  const uint32_t t = __umulhi(m, e);
+  const uint32_t sh1 = l ? 1u : 0u, sh2 = l ? l - 1u : 0u;
+  return (t + ((e - t) >> sh1)) >> sh2;
 }
 
 // ------------------------------------------------------ debug trace --
@@ -254,27 +288,36 @@ DEV uint32_t task_item_begin(uint32_t i) {
   return uniform(((const LDS DTask*)g_plan)[i].item_begin);
 }
 
-DEV DView load_view(uint32_t off) {
+// A view with 32-bit offset and strides (the compiler rejects programs whose
+// views or workspace address 2^31 elements or more), in scalar registers.
+struct VView {
+  int32_t offset;
+  int32_t stride[kMaxDims];
+  uint32_t base;
+  uint32_t dtype;
+};
+
+DEV VView load_view(uint32_t off) {
   const LDS DView& v = *(const LDS DView*)(g_plan + off);
-  DView r;
-  r.offset = uniform64(v.offset);
+  VView r;
+  r.offset = (int32_t)uniform((uint32_t)v.offset);
 #pragma unroll
-  for (int d = 0; d < kMaxDims; ++d) r.stride[d] = uniform64(v.stride[d]);
-  r.base = (uint16_t)uniform(v.base);
-  r.dtype = (uint8_t)uniform(v.dtype);
+  for (int d = 0; d < kMaxDims; ++d) r.stride[d] = (int32_t)uniform((uint32_t)v.stride[d]);
+  r.base = uniform(v.base);
+  r.dtype = uniform(v.dtype);
   return r;
 }
 
 // Element index of a view at coordinates c (dims past the task's rank have
 // coordinate 0 and stride 0).
-DEV int64_t view_index(const DView& v, const uint32_t (&c)[kMaxDims]) {
-  int64_t idx = v.offset;
+DEV int32_t view_index(const VView& v, const uint32_t (&c)[kMaxDims]) {
+  int32_t idx = v.offset;
 #pragma unroll
-  for (int d = 0; d < kMaxDims; ++d) idx += (int64_t)c[d] * v.stride[d];
+  for (int d = 0; d < kMaxDims; ++d) idx += (int32_t)c[d] * v.stride[d];
   return idx;
 }
 
-DEV int64_t inner_stride(const DView& v, uint32_t nd) {
+DEV int32_t inner_stride(const VView& v, uint32_t nd) {
   return nd <= 1 ? v.stride[0] : nd == 2 ? v.stride[1] : nd == 3 ? v.stride[2] : v.stride[3];
 }
 
@@ -287,8 +330,24 @@ struct Batch {
   uint32_t width;       // 8: two 8-wide chunks per thread; 1: sixteen single elements
   uint32_t nd;
   uint32_t dims[kMaxDims];
+  uint32_t dmul[kMaxDims], dsh[kMaxDims];  // division constants for dims[1..nd-1]
   uint32_t accumulate;  // reductions: add the results into the thread's sums
 };
+
+// Coordinates of linear element e of the batch's iteration space (row-major).
+DEV void unravel(uint32_t e, const Batch& b, uint32_t (&c)[kMaxDims]) {
+#pragma unroll
+  for (int d = kMaxDims - 1; d >= 1; --d) {
+    if ((uint32_t)d < b.nd) {
+      const uint32_t q = udiv(e, b.dmul[d], b.dsh[d]);
+      c[d] = e - q * b.dims[d];
+      e = q;
+    } else {
+      c[d] = 0;
+    }
+  }
+  c[0] = e;
+}
 
 // Run a program on C chunks of W elements (C * W == 16).  Chunk q starts at
 // linear element xe(q) of the iteration space and covers W consecutive
@@ -302,7 +361,7 @@ DEV void vm_run(const Ctx& ka, const Batch& b, uint32_t views_off, uint32_t live
   uint32_t c[C][kMaxDims];
 #pragma unroll
   for (int q = 0; q < C; ++q) {
-    unravel4(xe(q), b.dims, b.nd, c[q]);
+    unravel(xe(q), b, c[q]);
 #pragma unroll
     for (int j = 0; j < W; ++j) acc[q][j] = xv(q * W + j);
   }
@@ -315,25 +374,26 @@ DEV void vm_run(const Ctx& ka, const Batch& b, uint32_t views_off, uint32_t live
     const uint32_t arg = w1 & 0xffff;
     float x[C][W];
     if (src == SRC_VIEW || op == VM_STORE) {
-      const DView v = load_view(views_off + arg * sizeof(DView));
-      const int64_t s = inner_stride(v, b.nd);
+      const VView v = load_view(views_off + arg * sizeof(DView));
+      const int32_t s = inner_stride(v, b.nd);
       const uint32_t dt = v.dtype;
       GLOBAL uint8_t* p = base_ptr(ka, v.base);
-      if (op == VM_STORE) {
+      // 16-byte chunk accesses: unit inner stride, aligned base, and offset and
+      // outer strides multiples of the elements per 16 bytes (chunk starts lie
+      // at multiples of 8 along the inner dim)
+      const int32_t epc = dt == DT_F32 ? 4 : 8;
+      bool vec = W == 8 && s == 1 && dt != DT_I8 && ((uintptr_t)p & 15) == 0 && v.offset % epc == 0;
 #pragma unroll
-        for (int q = 0; q < C; ++q)
-          if (live & (1u << q)) store_chunk<W>(p, dt, view_index(v, c[q]), s, acc[q]);
+      for (int d = 0; d + 1 < kMaxDims; ++d)
+        if ((uint32_t)d + 1 < b.nd) vec = vec && v.stride[d] % epc == 0;
+      int32_t idx[C];
+#pragma unroll
+      for (int q = 0; q < C; ++q) idx[q] = view_index(v, c[q]);
+      if (op == VM_STORE) {
+        store_chunks<W, C>(p, dt, vec, s, idx, live, acc);
         continue;
       }
-#pragma unroll
-      for (int q = 0; q < C; ++q) {
-        if (live & (1u << q)) {
-          load_chunk<W>(p, dt, view_index(v, c[q]), s, x[q]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < W; ++j) x[q][j] = 0.0f;
-        }
-      }
+      load_chunks<W, C>(p, dt, vec, s, idx, x);
     } else if (src == SRC_SLOT) {
 #pragma unroll
       for (int q = 0; q < C; ++q)
@@ -434,7 +494,7 @@ DEV uint32_t xcd_tile(uint32_t local, uint32_t tiles) {
 // slice is consumed.  Each output accumulates acc = fma(a_k, b_k, acc) for
 // k = 0, 1, ... in order.
 
-DEV void simt_load(const GLOBAL uint8_t* p, const DView& v, bool mn_contig, bool is_a, uint32_t r0, uint32_t rmax,
+DEV void simt_load(const GLOBAL uint8_t* p, const VView& v, bool mn_contig, bool is_a, uint32_t r0, uint32_t rmax,
                    uint32_t k0, uint32_t kmax, float (&reg)[8]) {
   const int64_t s_r = is_a ? v.stride[0] : v.stride[1], s_k = is_a ? v.stride[1] : v.stride[0];
   const uint32_t dt = v.dtype;
@@ -467,7 +527,7 @@ DEV void gemm_simt(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
   LDS float* As1 = As0 + 32 * 68;
   LDS float* Bs0 = As0 + 2 * 32 * 68;
   LDS float* Bs1 = As0 + 3 * 32 * 68;
-  const DView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
+  const VView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
   const GLOBAL uint8_t* pa = base_ptr(ka, A.base);
   const GLOBAL uint8_t* pb = base_ptr(ka, B.base);
   const bool a_mc = A.stride[0] == 1 && A.stride[1] != 1;  // A unit-stride along m
@@ -666,7 +726,7 @@ DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
   const uint32_t m0 = tm * BM, n0 = tn * BN;
   const uint32_t kbeg = split_index * t.kchunk;
   const uint32_t kend = (kbeg + t.kchunk < t.k) ? kbeg + t.kchunk : t.k;
-  const DView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
+  const VView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
   const GLOBAL uint16_t* pa = (const GLOBAL uint16_t*)base_ptr(ka, A.base);
   const GLOBAL uint16_t* pb = (const GLOBAL uint16_t*)base_ptr(ka, B.base);
   const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
@@ -776,7 +836,7 @@ DEV float wave_sum(float v) {
 constexpr uint32_t kGemvRed = kSmemBytes - 64;  // byte offset of the 16 row sums
 
 DEV void gemv_q8(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
-  const DView X = load_view(views_off + t.va * sizeof(DView)), Q = load_view(views_off + t.vb * sizeof(DView)),
+  const VView X = load_view(views_off + t.va * sizeof(DView)), Q = load_view(views_off + t.vb * sizeof(DView)),
               S = load_view(views_off + t.vs * sizeof(DView));
   const GLOBAL uint8_t* px = base_ptr(ka, X.base);
   const GLOBAL int8_t* pq = (const GLOBAL int8_t*)base_ptr(ka, Q.base);
@@ -862,12 +922,15 @@ DEV float block_sum(float v) {
 
 // -------------------------------------------------------------- batches --
 
-DEV void set_dims(Batch& b, uint32_t d0, uint32_t d1, uint32_t nd) {
+DEV void set_1d(Batch& b, uint32_t d0) {
   b.dims[0] = d0;
-  b.dims[1] = d1;
-  b.dims[2] = 1;
-  b.dims[3] = 1;
-  b.nd = nd;
+#pragma unroll
+  for (int d = 1; d < kMaxDims; ++d) {
+    b.dims[d] = 1;
+    b.dmul[d] = 1;
+    b.dsh[d] = 0;
+  }
+  b.nd = 1;
 }
 
 DEV void expr_batch(Batch& b, const DTask& t, uint32_t ins_off) {
@@ -880,7 +943,11 @@ DEV void expr_batch(Batch& b, const DTask& t, uint32_t ins_off) {
 DEV void task_space(Batch& b, const DTask& t) {
   b.nd = t.ndim;
 #pragma unroll
-  for (int d = 0; d < kMaxDims; ++d) b.dims[d] = t.dims[d];
+  for (int d = 0; d < kMaxDims; ++d) {
+    b.dims[d] = t.dims[d];
+    b.dmul[d] = t.dmul[d];
+    b.dsh[d] = t.dsh[d];
+  }
 }
 
 DEV void fin_batch(Batch& b, const DTask& t, uint32_t ins_off, uint32_t width) {
@@ -888,7 +955,7 @@ DEV void fin_batch(Batch& b, const DTask& t, uint32_t ins_off, uint32_t width) {
   b.n = t.fin_len;
   b.width = width;
   b.accumulate = 0;
-  set_dims(b, t.m, 1, 1);
+  set_1d(b, t.m);
 }
 
 // Fill batch `bi` of a work item: set up the program and the exchange, and
@@ -897,6 +964,10 @@ DEV void fin_batch(Batch& b, const DTask& t, uint32_t ins_off, uint32_t width) {
 DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, uint32_t bi, ItemState& st, Batch& b,
               uint32_t& live) {
   live = 0;
+  // every chunk index must address the iteration space: dead chunks read
+  // element 0 (the machine loads every chunk, and stores only live ones)
+#pragma unroll
+  for (int q = 0; q < kVmElems; ++q) xe(q) = 0;
   const int W = t.width == 8 ? 8 : 1, C = kVmElems / W;
   switch (t.kind) {
     case T_EW: {
@@ -924,7 +995,7 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
       const int q0 = (int)bi * kBlock * C;
       if (q0 >= nchunks) return false;
       expr_batch(b, t, ins_off);
-      set_dims(b, t.m, t.n, 2);
+      task_space(b, t);
       const LDS float* ctile = (const LDS float*)g_smem;
       const bool partial = (t.flags & F_PARTIAL) != 0;
       GLOBAL float* P = ws_f32(ka, t.scratch) + (uint64_t)st.split_index * t.m * t.n;
@@ -949,7 +1020,7 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
       // split-K combine: partial tiles summed in split order, then the epilogue
       if (bi > 0) return false;
       expr_batch(b, t, ins_off);
-      set_dims(b, t.m, t.n, 2);
+      task_space(b, t);
       const uint64_t total = (uint64_t)t.m * t.n;
       const GLOBAL float* P = ws_f32(ka, t.scratch);
       for (int q = 0; q < C; ++q) {
@@ -970,7 +1041,7 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
       // thread 0 sixteen singles)
       if (bi > 0) return false;
       expr_batch(b, t, ins_off);
-      set_dims(b, 1, t.n, 2);
+      task_space(b, t);
       const LDS float* red = (const LDS float*)(g_smem + kGemvRed);
       const uint32_t rb = item * 16;
       if (threadIdx.x < (W == 8 ? 2u : 1u)) {

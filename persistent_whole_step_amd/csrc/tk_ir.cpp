@@ -131,6 +131,15 @@ void check_spec(const Spec& s) {
     if (d < 0) raise(TK_E_STRIDE, "invalid static shape or stride in " + s.buf);
   if (s.offset < 0) raise(TK_E_STRIDE, "negative offset in " + s.buf);
   if (s.numel() > (int64_t)0x7fffffff) raise(TK_E_UNSUPPORTED, "tensor above 2^31 elements: " + s.buf);
+  // element indices are 32-bit on the device
+  if (s.numel() > 0) {
+    int64_t hi = s.offset;
+    for (size_t i = 0; i < s.shape.size(); ++i) {
+      if (s.strides[i] > (int64_t)0x7fffffff) raise(TK_E_UNSUPPORTED, "stride above 2^31 elements in " + s.buf);
+      hi += (s.shape[i] - 1) * s.strides[i];
+      if (hi > (int64_t)0x7fffffff) raise(TK_E_UNSUPPORTED, "view addresses beyond 2^31 elements: " + s.buf);
+    }
+  }
 }
 
 // Largest element index a view can address (-1 when empty).

@@ -1071,6 +1071,24 @@ struct Builder {
     return t;
   }
 
+  // Constants for dividing 32-bit unsigned values by dims[d] (d >= 1) with a
+  // multiply-high and shifts, exact for every dividend below 2^32
+  // (Granlund and Montgomery, "Division by invariant integers using
+  // multiplication", 1994, figure 4.1).
+  static void set_divisors(DTask& t) {
+    for (int d = 0; d < kMaxDims; ++d) {
+      t.dmul[d] = 0;
+      t.dsh[d] = 0;
+    }
+    for (int d = 1; d < (int)t.ndim && d < kMaxDims; ++d) {
+      const uint64_t dv = t.dims[d] ? t.dims[d] : 1;
+      uint32_t l = 0;
+      while ((1ull << l) < dv) ++l;
+      t.dmul[d] = (uint32_t)(((1ull << 32) * ((1ull << l) - dv)) / dv + 1);
+      t.dsh[d] = (uint8_t)l;
+    }
+  }
+
   // Elementwise work item: 4096 elements (16 per thread).
   static uint32_t ew_items(int64_t numel) { return (uint32_t)std::max<int64_t>(1, (numel + 4095) / 4096); }
 
@@ -1657,6 +1675,7 @@ struct Builder {
       std::ostringstream gd;
       for (size_t t = 0; t < group.size(); ++t) {
         DTask task = group[t];
+        set_divisors(task);
         task.item_begin = e.items;
         e.items += task.n_items;
         if (task.kind == T_GEMM_MFMA || task.kind == T_GEMM_SIMT || task.kind == T_GEMV_Q8) {
@@ -1740,6 +1759,9 @@ struct Builder {
     pl.n_stages = (int)ds.size();
     pl.max_items = max_items;
     pl.workspace_bytes = kHeaderBytes + align_up(arena_bytes, kAlign);
+    // arena views address the workspace with 32-bit element indices
+    if (pl.workspace_bytes > (uint64_t)0x7fffffff)
+      raise(TK_E_UNSUPPORTED, "workspace above 2 GiB (" + std::to_string(pl.workspace_bytes) + " bytes)");
     pl.dump = dump.str();
     // statistics
     tk_stats& s = pl.stats;

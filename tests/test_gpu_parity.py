@@ -82,6 +82,44 @@ def test_pointwise_special_values(oracle_mod):
         parity.assert_bitexact(g, w, s.dtype, s.buf)
 
 
+def _cast_patterns() -> np.ndarray:
+    """fp32 bit patterns around every rounding decision of bf16 and fp16: all
+    exponents, mantissas at and next to the halfway points (both parities of
+    the kept bit), subnormals, zeros, infinities and NaNs."""
+    exps = np.arange(256, dtype=np.uint32) << 23
+    lows = []
+    for keep in (16, 13):  # bf16 keeps the top 16 bits; fp16 rounds at mantissa bit 13 (normal range)
+        half = 1 << (keep - 1)
+        for hi in (0, 1, 2, 3, 0x3FF, 0x7F):  # kept-bit parities and saturating mantissas
+            base = (hi << keep) & 0x7FFFFF
+            for d in (-1, 0, 1):
+                lows.append((base + half + d) & 0x7FFFFF)
+        lows += [0, 0x7FFFFF, 1]
+    low = np.array(lows, np.uint32)
+    bits = (exps[:, None] | low[None, :]).ravel()
+    bits = np.concatenate([bits, bits | np.uint32(0x80000000)])
+    # fp16 subnormal range: exponents 102..112 with dense mantissas
+    rng = np.random.default_rng(7)
+    sub = (rng.integers(102, 113, 4096).astype(np.uint32) << 23) | rng.integers(0, 1 << 23, 4096).astype(np.uint32)
+    bits = np.concatenate([bits, sub, np.array([0x7FC00001, 0xFF800000, 0x7F800000, 0x7F7FFFFF, 0x477FF000,
+                                                0x477FEFFF, 0x33000000, 0x33000001], np.uint32)])
+    return bits.view(np.float32)
+
+
+def test_cast_rounding_bit_patterns(oracle_mod):
+    say("cast rounding bit patterns")
+    x = _cast_patterns()
+    p = Program()
+    xi = p.input("x", "f32", x.shape)
+    p.output(p.op("cast", [xi], "bf16"))
+    p.output(p.op("cast", [xi], "f16"))
+    p.output(p.op("relu", [xi], "bf16"))
+    want = oracle_mod.run(p.text(), [x])
+    got, _ = parity.gpu_run(p, [x])
+    for g, w, s in zip(got, want, p.outputs):
+        parity.assert_bitexact(g, w, s.dtype, s.buf)
+
+
 def test_views_broadcast_and_output_copies(oracle_mod):
     say("views / broadcast / copies")
     rng = np.random.default_rng(3)
