@@ -230,6 +230,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-barrier", action="store_true")
+    ap.add_argument("--launch-mode", type=int, default=1, choices=(0, 1),
+                    help="0: cooperative launch; 1: ordinary launch of the co-resident grid (default)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py: this build runs on one GPU; the multi-GPU path is design only (see DESIGN.md)",
@@ -243,7 +245,7 @@ def main():
     tk.lib()
 
     log(f"[bench] workload {args.config}: compiling")
-    r = Runner(args.config)
+    r = Runner(args.config, launch_mode=args.launch_mode)
     log(f"[bench] {args.config}: stages={r.stats['n_stages']} grid={r.stats['grid_size']}; timing {args.steps} steps")
     wall, ev_ms = r.time_steps(args.steps, args.warmup)
     kms = r.kernel_ms()
@@ -265,7 +267,8 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.config], "batch": r.cfg.get("batch"), "dims": r.cfg.get("dims"),
                    "lr": r.cfg.get("lr"), "parallelism": "single-gpu", "resident_batches": 4,
                    "stages": r.stats["n_stages"], "grid_barriers": r.stats["grid_barriers"],
-                   "grid": r.stats["grid_size"]},
+                   "grid": r.stats["grid_size"],
+                   "launch": "ordinary, co-resident grid" if args.launch_mode == 1 else "cooperative"},
         "event_ms_per_step": round(ev_ms / args.steps, 5),
         "kernel_ms": round(kms, 5),
         "roofline": roofline(args.config, r.cfg, r.prog, kms, traffic_for(args.config)),
@@ -277,7 +280,7 @@ def main():
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.config]:
         log(f"[bench] other workload {name}")
-        o = Runner(name)
+        o = Runner(name, launch_mode=args.launch_mode)
         w, _ = o.time_steps(args.other_steps, 10)
         k = o.kernel_ms(20)
         rf = roofline(name, o.cfg, o.prog, k, traffic_for(name))

@@ -79,7 +79,14 @@ typedef struct {
   int32_t gemm_split_k;        /* 0: automatic; else force split-K parts for MFMA GEMMs */
   int32_t force_grid;          /* 0: automatic; else launch exactly this many workgroups
                                   (clamped to the co-resident capacity) */
-  int32_t reserved[4];
+  int32_t launch_mode;         /* 0 (default): cooperative launch (co-residency guaranteed by
+                                  the runtime, or the launch fails).  1: ordinary launch of a
+                                  grid the compiler sized to be co-resident on an idle device
+                                  (occupancy x CUs); avoids the runtime's serialization of
+                                  cooperative launches.  If other work keeps a CU busy, the
+                                  grid barrier's bounded wait turns a stall into an abort
+                                  (tk_workspace_status), never a hang. */
+  int32_t reserved[3];
 } tk_options;
 
 /* Plan and kernel statistics (pages: `GeneratedKernel` and `resource_usage`). */

@@ -15,6 +15,7 @@
 using namespace tkplan;
 
 hipError_t tk_device_launch(const KArgs& ka, int grid, hipStream_t stream);
+hipError_t tk_device_launch_resident(const KArgs& ka, int grid, hipStream_t stream);
 hipError_t tk_device_occupancy(int* blocks_per_cu);
 hipError_t tk_device_attributes(hipFuncAttributes* attr);
 hipError_t tk_device_zero_header(uint8_t* ws, hipStream_t stream);
@@ -202,6 +203,7 @@ tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int3
       return fail(TK_E_ARG, "gemm_split_k must be 0, 1, 2, 4 or 8");
     if (o.num_cus < 0) return fail(TK_E_ARG, "num_cus must not be negative");
     if (o.force_grid < 0) return fail(TK_E_ARG, "force_grid must not be negative");
+    if (o.launch_mode != 0 && o.launch_mode != 1) return fail(TK_E_ARG, "launch_mode must be 0 or 1");
     so.blocks_per_cu = o.blocks_per_cu;
     so.max_blocks = o.max_blocks;
     so.fuse_pointwise = o.fuse_pointwise != 0;
@@ -211,6 +213,7 @@ tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int3
     so.fuse_updates = o.fuse_updates != 0;
     so.barrier_every_op = o.barrier_every_op != 0;
     so.gemm_split_k = o.gemm_split_k;
+    so.launch_mode = o.launch_mode;
     so.num_cus = o.num_cus > 0 ? o.num_cus : 256;
     int occupancy = 0;
     hipFuncAttributes attr{};
@@ -393,9 +396,10 @@ tk_status tk_run_into(const tk_program* p, const tk_tensor* inputs, size_t n_in,
     int cur = 0;
     hipGetDevice(&cur);
     if (cur != p->device) hipSetDevice(p->device);
-    hipError_t e = tk_device_launch(ka, p->grid, (hipStream_t)stream);
+    hipError_t e = p->opts.launch_mode == 1 ? tk_device_launch_resident(ka, p->grid, (hipStream_t)stream)
+                                             : tk_device_launch(ka, p->grid, (hipStream_t)stream);
     if (cur != p->device) hipSetDevice(cur);
-    if (e != hipSuccess) return hip_fail(e, "cooperative launch");
+    if (e != hipSuccess) return hip_fail(e, p->opts.launch_mode == 1 ? "launch" : "cooperative launch");
     return TK_OK;
   })
 }

@@ -52,8 +52,8 @@ __shared__ __attribute__((aligned(16))) uint8_t g_plan[kPlanLds];    // current 
 __shared__ float g_xv[kVmElems * kBlock];     // machine exchange: values   [element][thread]
 __shared__ uint32_t g_xe[kVmElems * kBlock];  // machine exchange: first linear element of each chunk
 
-DEV LDS float& xv(int j) { return ((LDS float*)g_xv)[j * kBlock + threadIdx.x]; }
-DEV LDS uint32_t& xe(int q) { return ((LDS uint32_t*)g_xe)[q * kBlock + threadIdx.x]; }
+DEV LDS float& xv(uint32_t tid, int j) { return ((LDS float*)g_xv)[j * kBlock + tid]; }
+DEV LDS uint32_t& xe(uint32_t tid, int q) { return ((LDS uint32_t*)g_xe)[q * kBlock + tid]; }
 
 // ------------------------------------------------------------ conversions --
 
@@ -350,20 +350,20 @@ DEV void unravel(uint32_t e, const Batch& b, uint32_t (&c)[kMaxDims]) {
 }
 
 // Run a program on C chunks of W elements (C * W == 16).  Chunk q starts at
-// linear element xe(q) of the iteration space and covers W consecutive
+// linear element xe(tid, q) of the iteration space and covers W consecutive
 // elements along its last dim; chunks whose bit in `live` is clear touch no
 // memory.  The accumulators start from and end in the exchange values.  The
 // loads of all chunks of one instruction are issued before any is used, so an
 // instruction costs one memory latency, not one per element.
 template <int W, int C>
-DEV void vm_run(const Ctx& ka, const Batch& b, uint32_t views_off, uint32_t live) {
+DEV void vm_run(uint32_t tid, const Ctx& ka, const Batch& b, uint32_t views_off, uint32_t live) {
   float acc[C][W];
   uint32_t c[C][kMaxDims];
 #pragma unroll
   for (int q = 0; q < C; ++q) {
-    unravel(xe(q), b, c[q]);
+    unravel(xe(tid, q), b, c[q]);
 #pragma unroll
-    for (int j = 0; j < W; ++j) acc[q][j] = xv(q * W + j);
+    for (int j = 0; j < W; ++j) acc[q][j] = xv(tid, q * W + j);
   }
   float s0[C][W], s1[C][W], s2[C][W], s3[C][W];
   for (uint32_t pc = 0; pc < b.n; ++pc) {
@@ -462,7 +462,7 @@ DEV void vm_run(const Ctx& ka, const Batch& b, uint32_t views_off, uint32_t live
 #pragma unroll
   for (int q = 0; q < C; ++q)
 #pragma unroll
-    for (int j = 0; j < W; ++j) xv(q * W + j) = acc[q][j];
+    for (int j = 0; j < W; ++j) xv(tid, q * W + j) = acc[q][j];
 }
 
 // ------------------------------------------------------------ work items --
@@ -494,13 +494,13 @@ DEV uint32_t xcd_tile(uint32_t local, uint32_t tiles) {
 // slice is consumed.  Each output accumulates acc = fma(a_k, b_k, acc) for
 // k = 0, 1, ... in order.
 
-DEV void simt_load(const GLOBAL uint8_t* p, const VView& v, bool mn_contig, bool is_a, uint32_t r0, uint32_t rmax,
+DEV void simt_load(uint32_t tid, const GLOBAL uint8_t* p, const VView& v, bool mn_contig, bool is_a, uint32_t r0, uint32_t rmax,
                    uint32_t k0, uint32_t kmax, float (&reg)[8]) {
   const int64_t s_r = is_a ? v.stride[0] : v.stride[1], s_k = is_a ? v.stride[1] : v.stride[0];
   const uint32_t dt = v.dtype;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int q = threadIdx.x + i * kBlock;  // 0 .. 2047 over a 64 x 32 slice
+    const int q = tid + i * kBlock;  // 0 .. 2047 over a 64 x 32 slice
     const int r = mn_contig ? q % 64 : q / 32, kk = mn_contig ? q / 64 : q % 32;
     const uint32_t gr = r0 + r, gk = k0 + kk;
     const bool ok = gr < rmax && gk < kmax;
@@ -510,16 +510,16 @@ DEV void simt_load(const GLOBAL uint8_t* p, const VView& v, bool mn_contig, bool
   }
 }
 
-DEV void simt_store(LDS float* s, bool mn_contig, const float (&reg)[8]) {
+DEV void simt_store(uint32_t tid, LDS float* s, bool mn_contig, const float (&reg)[8]) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const int q = threadIdx.x + i * kBlock;
+    const int q = tid + i * kBlock;
     const int r = mn_contig ? q % 64 : q / 32, kk = mn_contig ? q / 64 : q % 32;
     s[kk * 68 + r] = reg[i];
   }
 }
 
-DEV void gemm_simt(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
+DEV void gemm_simt(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
   const uint32_t tile = xcd_tile(item, t.tiles_m * t.tiles_n);
   const uint32_t tm = tile / t.tiles_n, tn = tile % t.tiles_n;
   const uint32_t m0 = tm * 64, n0 = tn * 64;
@@ -532,7 +532,7 @@ DEV void gemm_simt(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
   const GLOBAL uint8_t* pb = base_ptr(ka, B.base);
   const bool a_mc = A.stride[0] == 1 && A.stride[1] != 1;  // A unit-stride along m
   const bool b_nc = B.stride[1] == 1;                      // B unit-stride along n
-  const int tx = threadIdx.x % 16, ty = threadIdx.x / 16;
+  const int tx = tid % 16, ty = tid / 16;
   float acc[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
@@ -541,17 +541,17 @@ DEV void gemm_simt(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
   const uint32_t nk = (t.k + 31) / 32;
   float ra[8], rb[8];
   if (nk > 0) {
-    simt_load(pa, A, a_mc, true, m0, t.m, 0, t.k, ra);
-    simt_load(pb, B, b_nc, false, n0, t.n, 0, t.k, rb);
-    simt_store(As0, a_mc, ra);
-    simt_store(Bs0, b_nc, rb);
+    simt_load(tid, pa, A, a_mc, true, m0, t.m, 0, t.k, ra);
+    simt_load(tid, pb, B, b_nc, false, n0, t.n, 0, t.k, rb);
+    simt_store(tid, As0, a_mc, ra);
+    simt_store(tid, Bs0, b_nc, rb);
   }
   __syncthreads();
   for (uint32_t kt = 0; kt < nk; ++kt) {
     const bool odd = kt & 1;
     if (kt + 1 < nk) {
-      simt_load(pa, A, a_mc, true, m0, t.m, (kt + 1) * 32, t.k, ra);
-      simt_load(pb, B, b_nc, false, n0, t.n, (kt + 1) * 32, t.k, rb);
+      simt_load(tid, pa, A, a_mc, true, m0, t.m, (kt + 1) * 32, t.k, ra);
+      simt_load(tid, pb, B, b_nc, false, n0, t.n, (kt + 1) * 32, t.k, rb);
     }
     const LDS float* as = odd ? As1 : As0;
     const LDS float* bs = odd ? Bs1 : Bs0;
@@ -568,8 +568,8 @@ DEV void gemm_simt(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
         for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
     }
     if (kt + 1 < nk) {
-      simt_store(odd ? As0 : As1, a_mc, ra);
-      simt_store(odd ? Bs0 : Bs1, b_nc, rb);
+      simt_store(tid, odd ? As0 : As1, a_mc, ra);
+      simt_store(tid, odd ? Bs0 : Bs1, b_nc, rb);
     }
     __syncthreads();
   }
@@ -613,18 +613,20 @@ struct FastOp {
   const GLOBAL uint16_t* ptr[N];
   int64_t kstep;
   bool kc;
-  DEV void init(bool kcontig, const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0,
+  uint32_t tid;
+  DEV void init(uint32_t tid_, bool kcontig, const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0,
                 uint32_t k0) {
+    tid = tid_;
     kc = kcontig;
     if (kc) {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        const int ch = threadIdx.x + i * kBlock;
+        const int ch = tid + i * kBlock;
         ptr[i] = q + off + (int64_t)(r0 + ch / 8) * sr + k0 + (ch % 8) * 8;
       }
       kstep = kBK;
     } else {
-      const int rb = threadIdx.x % (R / 8), kb = threadIdx.x / (R / 8);
+      const int rb = tid % (R / 8), kb = tid / (R / 8);
 #pragma unroll
       for (int i = 0; i < N; ++i) ptr[i] = q + off + (int64_t)(k0 + kb * N + i) * sk + r0 + rb * 8;
       kstep = (int64_t)kBK * sk;
@@ -638,13 +640,13 @@ struct FastOp {
     if (kc) {
 #pragma unroll
       for (int i = 0; i < N; ++i) {
-        const int ch = threadIdx.x + i * kBlock;
+        const int ch = tid + i * kBlock;
         *(LDS u32x4*)(lds + swz(ch / 8, ch % 8)) = v[i];
       }
     } else {
       // thread (rb, kb) holds rows rb*8 .. rb*8+7 at k = kb*N .. kb*N+N-1;
       // row rb*8 + 2j takes the low halves, row rb*8 + 2j + 1 the high halves
-      const int rb = threadIdx.x % (R / 8), kb = threadIdx.x / (R / 8);
+      const int rb = tid % (R / 8), kb = tid / (R / 8);
       const int c = (kb * N) / 8, e = (kb * N) % 8;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -671,11 +673,11 @@ struct FastOp {
 
 // General operand path: element by element straight into LDS, zero outside.
 template <int R>
-DEV void slow_stage(const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0, uint32_t rmax,
+DEV void slow_stage(uint32_t tid, const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0, uint32_t rmax,
                     uint32_t k0, uint32_t kmax, LDS uint16_t* lds) {
   // consecutive threads walk the operand's unit-stride dimension when it has one
   const bool kfast = sk == 1 || sr != 1;
-  for (int p = threadIdx.x; p < R * kBK; p += kBlock) {
+  for (int p = tid; p < R * kBK; p += kBlock) {
     const int r = kfast ? p / kBK : p % R, kk = kfast ? p % kBK : p / R;
     const uint32_t gr = r0 + r, gk = k0 + kk;
     const bool ok = gr < rmax && gk < kmax;
@@ -695,9 +697,9 @@ DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 
 // One 64-deep K slice from LDS into the wave's accumulators.
 template <int BM, int BN, bool BF16>
-DEV void mfma_slice(const LDS uint16_t* sa, const LDS uint16_t* sb, f32x16 (&acc)[BM / 64][BN / 64]) {
+DEV void mfma_slice(uint32_t tid, const LDS uint16_t* sa, const LDS uint16_t* sb, f32x16 (&acc)[BM / 64][BN / 64]) {
   constexpr int FM = BM / 64, FN = BN / 64;
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wave = tid / 64, lane = tid % 64;
   const int wm = wave / 2, wn = wave % 2;
   const int ra = wm * (BM / 2) + (lane % 32), rbw = wn * (BN / 2) + (lane % 32), ch = lane / 32;
 #pragma unroll
@@ -717,7 +719,7 @@ DEV void mfma_slice(const LDS uint16_t* sa, const LDS uint16_t* sb, f32x16 (&acc
 // BF16: operand dtype (bf16, else f16), a template parameter so the MFMA
 // accumulators never change registers between the two instruction forms.
 template <int BM, int BN, bool BF16>
-DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
+DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
   constexpr int FM = BM / 64, FN = BN / 64;  // 32x32 blocks per wave along m / n
   const uint32_t tiles = t.tiles_m * t.tiles_n;
   const uint32_t split_index = item / tiles;
@@ -729,7 +731,7 @@ DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
   const VView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
   const GLOBAL uint16_t* pa = (const GLOBAL uint16_t*)base_ptr(ka, A.base);
   const GLOBAL uint16_t* pb = (const GLOBAL uint16_t*)base_ptr(ka, B.base);
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wave = tid / 64, lane = tid % 64;
   const int wm = wave / 2, wn = wave % 2;
   f32x16 acc[FM][FN];
 #pragma unroll
@@ -760,8 +762,8 @@ DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
     constexpr int D = BM == 64 ? 4 : 3;
     FastOp<BM> fa;
     FastOp<BN> fb;
-    fa.init(a_kc, pa, A.offset, A.stride[0], A.stride[1], m0, kbeg);
-    fb.init(b_kc, pb, B.offset, B.stride[1], B.stride[0], n0, kbeg);
+    fa.init(tid, a_kc, pa, A.offset, A.stride[0], A.stride[1], m0, kbeg);
+    fb.init(tid, b_kc, pb, B.offset, B.stride[1], B.stride[0], n0, kbeg);
     // Loads are unconditional (past the last slice they repeat it): the
     // compiler can then count exactly which loads each commit must wait for.
     u32x4 ra[D][FastOp<BM>::N], rb[D][FastOp<BN>::N];
@@ -787,17 +789,17 @@ DEV void gemm_mfma(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t i
         const uint32_t nx = k + D < last ? k + D : last;
         fa.load(nx, ra[d]);
         fb.load(nx, rb[d]);
-        if (act) mfma_slice<BM, BN, BF16>(sa, sb, acc);
+        if (act) mfma_slice<BM, BN, BF16>(tid, sa, sb, acc);
       }
     }
     __syncthreads();  // every wave is done with the staging buffers (the C tile reuses them)
   } else {
     for (uint32_t kt = 0; kt < nk; ++kt) {
       const uint32_t k0 = kbeg + kt * kBK;
-      slow_stage<BM>(pa, A.offset, A.stride[0], A.stride[1], m0, t.m, k0, kend, sa0);
-      slow_stage<BN>(pb, B.offset, B.stride[1], B.stride[0], n0, t.n, k0, kend, sb0);
+      slow_stage<BM>(tid, pa, A.offset, A.stride[0], A.stride[1], m0, t.m, k0, kend, sa0);
+      slow_stage<BN>(tid, pb, B.offset, B.stride[1], B.stride[0], n0, t.n, k0, kend, sb0);
       __syncthreads();
-      mfma_slice<BM, BN, BF16>(sa0, sb0, acc);
+      mfma_slice<BM, BN, BF16>(tid, sa0, sb0, acc);
       __syncthreads();
     }
   }
@@ -835,13 +837,13 @@ DEV float wave_sum(float v) {
 
 constexpr uint32_t kGemvRed = kSmemBytes - 64;  // byte offset of the 16 row sums
 
-DEV void gemv_q8(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
+DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
   const VView X = load_view(views_off + t.va * sizeof(DView)), Q = load_view(views_off + t.vb * sizeof(DView)),
               S = load_view(views_off + t.vs * sizeof(DView));
   const GLOBAL uint8_t* px = base_ptr(ka, X.base);
   const GLOBAL int8_t* pq = (const GLOBAL int8_t*)base_ptr(ka, Q.base);
   const GLOBAL float* ps = (const GLOBAL float*)base_ptr(ka, S.base);
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wave = tid / 64, lane = tid % 64;
   const uint32_t K = t.k;
   LDS float* xs = (LDS float*)g_smem;
   const bool staged = (uint64_t)K * 4 + 64 <= (uint64_t)kSmemBytes;
@@ -875,7 +877,7 @@ DEV void gemv_q8(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ite
       }
     }
     if (kpass == 0 && staged) {
-      for (uint32_t k = threadIdx.x; k < K; k += kBlock)
+      for (uint32_t k = tid; k < K; k += kBlock)
         xs[k] = load_elem(px, X.dtype, X.offset + (int64_t)k * X.stride[1]);
       __syncthreads();
     }
@@ -909,10 +911,10 @@ DEV void gemv_q8(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ite
 }
 
 // Block-wide sum in a fixed order: wave butterflies, then waves 0..3 in order.
-DEV float block_sum(float v) {
+DEV float block_sum(uint32_t tid, float v) {
   LDS float* scratch = (LDS float*)g_smem;
   v = wave_sum(v);
-  const int wave = threadIdx.x / 64, lane = threadIdx.x % 64;
+  const int wave = tid / 64, lane = tid % 64;
   if (lane == 0) scratch[wave] = v;
   __syncthreads();
   float s = ((scratch[0] + scratch[1]) + scratch[2]) + scratch[3];
@@ -961,13 +963,13 @@ DEV void fin_batch(Batch& b, const DTask& t, uint32_t ins_off, uint32_t width) {
 // Fill batch `bi` of a work item: set up the program and the exchange, and
 // set this thread's live-chunk mask.  Returns false when the item has no
 // batch `bi` (uniform across the workgroup).
-DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, uint32_t bi, ItemState& st, Batch& b,
+DEV bool fill(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, uint32_t bi, ItemState& st, Batch& b,
               uint32_t& live) {
   live = 0;
   // every chunk index must address the iteration space: dead chunks read
   // element 0 (the machine loads every chunk, and stores only live ones)
 #pragma unroll
-  for (int q = 0; q < kVmElems; ++q) xe(q) = 0;
+  for (int q = 0; q < kVmElems; ++q) xe(tid, q) = 0;
   const int W = t.width == 8 ? 8 : 1, C = kVmElems / W;
   switch (t.kind) {
     case T_EW: {
@@ -978,11 +980,11 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
       const uint32_t numel = t.dims[0] * t.dims[1] * t.dims[2] * t.dims[3];  // unused dims are 1
       const uint32_t base = item * 4096u;
       for (int q = 0; q < C; ++q) {
-        const uint32_t e = W == 8 ? base + q * 2048u + threadIdx.x * 8u : base + q * 256u + threadIdx.x;
-        xe(q) = e < numel ? e : 0;
+        const uint32_t e = W == 8 ? base + q * 2048u + tid * 8u : base + q * 256u + tid;
+        xe(tid, q) = e < numel ? e : 0;
         live |= (e < numel ? 1u : 0u) << q;
       }
-      for (int j = 0; j < kVmElems; ++j) xv(j) = 0.0f;
+      for (int j = 0; j < kVmElems; ++j) xv(tid, j) = 0.0f;
       return true;
     }
     case T_GEMM_MFMA:
@@ -1000,7 +1002,7 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
       const bool partial = (t.flags & F_PARTIAL) != 0;
       GLOBAL float* P = ws_f32(ka, t.scratch) + (uint64_t)st.split_index * t.m * t.n;
       for (int q = 0; q < C; ++q) {
-        const int qq = q0 + q * kBlock + (int)threadIdx.x;
+        const int qq = q0 + q * kBlock + (int)tid;
         const int r = qq / cpr, cc = (qq % cpr) * W;
         const uint32_t row = st.m0 + r, col = st.n0 + cc;
         const bool ok = qq < nchunks && row < t.m && col < t.n;
@@ -1011,8 +1013,8 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
           continue;
         }
         live |= (ok ? 1u : 0u) << q;
-        xe(q) = e;
-        for (int j = 0; j < W; ++j) xv(q * W + j) = qq < nchunks ? ctile[r * pitch + cc + j] : 0.0f;
+        xe(tid, q) = e;
+        for (int j = 0; j < W; ++j) xv(tid, q * W + j) = qq < nchunks ? ctile[r * pitch + cc + j] : 0.0f;
       }
       return true;
     }
@@ -1024,14 +1026,14 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
       const uint64_t total = (uint64_t)t.m * t.n;
       const GLOBAL float* P = ws_f32(ka, t.scratch);
       for (int q = 0; q < C; ++q) {
-        const uint64_t e = (uint64_t)item * 4096u + (W == 8 ? q * 2048u + threadIdx.x * 8u : q * 256u + threadIdx.x);
+        const uint64_t e = (uint64_t)item * 4096u + (W == 8 ? q * 2048u + tid * 8u : q * 256u + tid);
         const bool ok = e < total;
         live |= (ok ? 1u : 0u) << q;
-        xe(q) = ok ? (uint32_t)e : 0;
+        xe(tid, q) = ok ? (uint32_t)e : 0;
         for (int j = 0; j < W; ++j) {
           float a = ok ? P[e + j] : 0.0f;
           for (uint32_t s = 1; s < t.split; ++s) a = a + (ok ? P[s * total + e + j] : 0.0f);
-          xv(q * W + j) = a;
+          xv(tid, q * W + j) = a;
         }
       }
       return true;
@@ -1044,13 +1046,13 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
       task_space(b, t);
       const LDS float* red = (const LDS float*)(g_smem + kGemvRed);
       const uint32_t rb = item * 16;
-      if (threadIdx.x < (W == 8 ? 2u : 1u)) {
+      if (tid < (W == 8 ? 2u : 1u)) {
         for (int q = 0; q < C; ++q) {
-          const uint32_t col = rb + (W == 8 ? threadIdx.x * 8 : q);
+          const uint32_t col = rb + (W == 8 ? tid * 8 : q);
           const bool ok = (W == 8 ? q == 0 : true) && col < t.n;
           live |= (ok ? 1u : 0u) << q;
-          xe(q) = ok ? col : 0;
-          for (int j = 0; j < W; ++j) xv(q * W + j) = red[W == 8 ? threadIdx.x * 8 + j : q];
+          xe(tid, q) = ok ? col : 0;
+          for (int j = 0; j < W; ++j) xv(tid, q * W + j) = red[W == 8 ? tid * 8 + j : q];
         }
       }
       return true;
@@ -1068,26 +1070,26 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
         expr_batch(b, t, ins_off);
         task_space(b, t);
         b.accumulate = 1;
-        const uint32_t k0 = kb + bi * per + threadIdx.x * W;
+        const uint32_t k0 = kb + bi * per + tid * W;
         for (int q = 0; q < C; ++q) {
           const uint32_t kk = k0 + q * kBlock * W;
           const bool ok = kk < ke;
           live |= (ok ? 1u : 0u) << q;
-          xe(q) = row * R + (ok ? kk : kb);
+          xe(tid, q) = row * R + (ok ? kk : kb);
         }
-        for (int j = 0; j < kVmElems; ++j) xv(j) = 0.0f;
+        for (int j = 0; j < kVmElems; ++j) xv(tid, j) = 0.0f;
         return true;
       }
       if (bi > nb) return false;
-      const float total = block_sum(st.acc);
+      const float total = block_sum(tid, st.acc);
       fin_batch(b, t, ins_off, 1);
-      if (threadIdx.x == 0) {
+      if (tid == 0) {
         if (t.flags & F_PARTIAL) {
           ws_f32(ka, t.scratch)[(uint64_t)row * t.split + part] = total;
         } else {
           live = 1;
-          xe(0) = row;
-          xv(0) = total;
+          xe(tid, 0) = row;
+          xv(tid, 0) = total;
         }
       }
       return true;
@@ -1097,7 +1099,7 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
       // taken lane-strided, then summed across lanes in order
       const uint32_t cb = item / t.split, part = item % t.split;
       const uint32_t cols = t.m, R = t.k;
-      const uint32_t cc = threadIdx.x % 32, rl = threadIdx.x / 32;
+      const uint32_t cc = tid % 32, rl = tid / 32;
       const uint32_t col = cb * 32 * W + cc * W;
       const uint32_t rb = part * t.kchunk;
       const uint32_t re = (rb + t.kchunk < R) ? rb + t.kchunk : R;
@@ -1112,9 +1114,9 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
           const uint32_t r = r0 + 8 * q;
           const bool ok = r < re && col < cols;
           live |= (ok ? 1u : 0u) << q;
-          xe(q) = (ok ? r : rb) * cols + (col < cols ? col : 0);
+          xe(tid, q) = (ok ? r : rb) * cols + (col < cols ? col : 0);
         }
-        for (int j = 0; j < kVmElems; ++j) xv(j) = 0.0f;
+        for (int j = 0; j < kVmElems; ++j) xv(tid, j) = 0.0f;
         return true;
       }
       if (bi > nb) return false;
@@ -1135,8 +1137,8 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
         } else {
           // finishing program over `cols` outputs: one 8-wide chunk or one element
           live = 1;
-          xe(0) = col;
-          for (int j = 0; j < W; ++j) xv(j) = tot[j];
+          xe(tid, 0) = col;
+          for (int j = 0; j < W; ++j) xv(tid, j) = tot[j];
         }
       }
       return true;
@@ -1147,7 +1149,7 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
       fin_batch(b, t, ins_off, 1);
       const GLOBAL float* P = ws_f32(ka, t.scratch);
       const bool cols_layout = (t.tile & 1) != 0;  // [parts][rows] instead of [rows][parts]
-      const uint32_t row = item * kBlock + threadIdx.x;
+      const uint32_t row = item * kBlock + tid;
       if (row < t.m) {
         float a = 0.0f;
         for (uint32_t p0 = 0; p0 < t.split; p0 += 8) {
@@ -1162,8 +1164,8 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
             if (p0 + i < t.split) a = a + v8[i];
         }
         live = 1;
-        xe(0) = row;
-        xv(0) = a;
+        xe(tid, 0) = row;
+        xv(tid, 0) = a;
       }
       return true;
     }
@@ -1174,19 +1176,19 @@ DEV bool fill(const Ctx& ka, const DTask& t, uint32_t ins_off, uint32_t item, ui
 
 // After a summing batch: a reduction adds the machine's results into the
 // thread's running sums (chunk by chunk, elements in order).
-DEV void consume(const DTask& t, const Batch& b, uint32_t live, ItemState& st) {
+DEV void consume(uint32_t tid, const DTask& t, const Batch& b, uint32_t live, ItemState& st) {
   if (!b.accumulate) return;
   const int W = t.width == 8 ? 8 : 1, C = kVmElems / W;
   if (t.kind == T_RED_ROWS) {
     for (int q = 0; q < C; ++q)
       if (live & (1u << q))
-        for (int j = 0; j < W; ++j) st.acc = st.acc + xv(q * W + j);
+        for (int j = 0; j < W; ++j) st.acc = st.acc + xv(tid, q * W + j);
   } else {
     for (int q = 0; q < C; ++q)
       if (live & (1u << q))
 #pragma unroll
         for (int j = 0; j < 8; ++j)
-          if (j < W) st.acc8[j] = st.acc8[j] + xv(q * W + j);
+          if (j < W) st.acc8[j] = st.acc8[j] + xv(tid, q * W + j);
   }
 }
 
@@ -1204,6 +1206,12 @@ DEV DStage load_stage(const GLOBAL uint8_t* stages, uint32_t s) {
 
 // One work item: prologue, then batches through the machine.
 DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item) {
+  // The thread index passes through an empty asm once per item, so values
+  // derived from it (LDS addresses, tile offsets) are computed per item
+  // instead of being hoisted out of the stage loop and held in registers
+  // for the whole launch.
+  uint32_t tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   ItemState st;
   st.m0 = st.n0 = st.split_index = 0;
   st.bm = st.bn = 0;
@@ -1212,7 +1220,7 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
   for (int j = 0; j < 8; ++j) st.acc8[j] = 0.0f;
   switch (t.kind) {
     case T_GEMM_SIMT:
-      gemm_simt(ka, t, sd.off_views, item, st);
+      gemm_simt(tid, ka, t, sd.off_views, item, st);
       __syncthreads();
       break;
     case T_GEMM_MFMA: {
@@ -1220,20 +1228,20 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
       const bool bf16 = uniform(((const LDS DView*)(g_plan + sd.off_views + t.va * sizeof(DView)))->dtype) == DT_BF16;
       if (t.tile == 0) {
         if (bf16)
-          gemm_mfma<128, 128, true>(ka, t, sd.off_views, item, st);
+          gemm_mfma<128, 128, true>(tid, ka, t, sd.off_views, item, st);
         else
-          gemm_mfma<128, 128, false>(ka, t, sd.off_views, item, st);
+          gemm_mfma<128, 128, false>(tid, ka, t, sd.off_views, item, st);
       } else {
         if (bf16)
-          gemm_mfma<64, 64, true>(ka, t, sd.off_views, item, st);
+          gemm_mfma<64, 64, true>(tid, ka, t, sd.off_views, item, st);
         else
-          gemm_mfma<64, 64, false>(ka, t, sd.off_views, item, st);
+          gemm_mfma<64, 64, false>(tid, ka, t, sd.off_views, item, st);
       }
       __syncthreads();
       break;
     }
     case T_GEMV_Q8:
-      gemv_q8(ka, t, sd.off_views, item);
+      gemv_q8(tid, ka, t, sd.off_views, item);
       break;
     default:
       break;
@@ -1242,14 +1250,14 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
   for (uint32_t bi = 0;; ++bi) {
     Batch b;
     uint32_t live;
-    if (!fill(ka, t, sd.off_ins, item, bi, st, b, live)) break;
+    if (!fill(tid, ka, t, sd.off_ins, item, bi, st, b, live)) break;
     if (live) {
       if (b.width == 8)
-        vm_run<8, 2>(ka, b, sd.off_views, live);
+        vm_run<8, 2>(tid, ka, b, sd.off_views, live);
       else
-        vm_run<1, 16>(ka, b, sd.off_views, live);
+        vm_run<1, 16>(tid, ka, b, sd.off_views, live);
     }
-    consume(t, b, live, st);
+    consume(tid, t, b, live, st);
     trace_stamp(ka, 0x400 + bi);
   }
   // the next item may overwrite the LDS tile and scratch
@@ -1429,6 +1437,13 @@ __global__ void tk_zero_header(uint8_t* ws, uint32_t bytes) {
 hipError_t tk_device_launch(const KArgs& ka, int grid, hipStream_t stream) {
   void* args[] = {(void*)&ka};
   return hipLaunchCooperativeKernel((const void*)tk_persistent, dim3(grid), dim3(kBlock), args, 0, stream);
+}
+
+// Ordinary launch of a grid the compiler sized to be co-resident (occupancy x
+// CUs); the barrier's bounded wait covers a device shared with other work.
+hipError_t tk_device_launch_resident(const KArgs& ka, int grid, hipStream_t stream) {
+  hipLaunchKernelGGL(tk_persistent, dim3(grid), dim3(kBlock), 0, stream, ka);
+  return hipGetLastError();
 }
 
 hipError_t tk_device_occupancy(int* blocks_per_cu) {

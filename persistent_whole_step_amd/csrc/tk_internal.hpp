@@ -83,6 +83,7 @@ struct Options {
   bool barrier_every_op = false;
   int num_cus = 256;
   int gemm_split_k = 0;
+  int launch_mode = 0;  // 0 cooperative, 1 ordinary launch of a co-resident grid
 };
 
 // Compiled plan: device bytes plus host-side description for queries/dumps.

@@ -227,7 +227,20 @@ struct Builder {
       std::set<std::string> returned;
       for (auto& d : derived)
         if (output_bufs.count(d)) returned.insert(d);
+      // Addition of this design: a derived value read by an op outside the
+      // candidate chain is also written by the tile (to its usual home), so
+      // the pointwise stage that would recompute it from the stored root
+      // disappears; later readers see the same value in the same place.
+      std::set<std::string> chain_outs;
+      for (int c : chain) chain_outs.insert(op(c).out.buf);
+      std::set<std::string> escaping;
+      for (auto& d : derived) {
+        if (returned.count(d)) continue;
+        for (int u : users[d])
+          if (!chain_outs.count(op(u).out.buf)) escaping.insert(d);
+      }
       std::set<std::string> needed = returned;
+      needed.insert(escaping.begin(), escaping.end());
       for (auto it = chain.rbegin(); it != chain.rend(); ++it)
         if (needed.count(op(*it).out.buf))
           for (auto& a : op(*it).args)
@@ -238,11 +251,12 @@ struct Builder {
       std::set<std::string> dkept;
       for (auto& d : derived)
         if (needed.count(d)) dkept.insert(d);
-      if (returned.empty()) continue;
+      if (returned.empty() && escaping.empty()) continue;
       bool ok = true;
-      // every reader of a non-returned derived value must be inside the tile
+      // every reader of a kept value that is neither returned nor stored must
+      // be inside the tile
       for (auto& d : dkept) {
-        if (returned.count(d)) continue;
+        if (returned.count(d) || escaping.count(d)) continue;
         for (int u : users[d])
           if (!dkept.count(op(u).out.buf)) ok = false;
       }
@@ -369,6 +383,19 @@ struct Builder {
     for (size_t i = 0; i < sched.size(); ++i) sched[i].order = (int)i;
   }
 
+  // Whether a side-epilogue value is written to storage: it is returned, or
+  // an op outside the tile reads it.
+  bool side_stored(const Entry& e, int c) const {
+    const std::string& b = op(c).out.buf;
+    if (output_bufs.count(b)) return true;
+    auto it = users.find(b);
+    if (it == users.end()) return false;
+    const std::set<std::string> inside = internal_bufs(e);
+    for (int u : it->second)
+      if (!inside.count(op(u).out.buf)) return true;
+    return false;
+  }
+
   // Values an entry writes to storage.
   std::vector<std::string> written(const Entry& e) const {
     std::vector<std::string> w;
@@ -376,7 +403,7 @@ struct Builder {
     if (!e.side.empty()) {
       if (!e.discard_root) w.push_back(op(e.op).out.buf);
       for (int c : e.side)
-        if (output_bufs.count(op(c).out.buf)) w.push_back(op(c).out.buf);
+        if (side_stored(e, c)) w.push_back(op(c).out.buf);
       return w;
     }
     w.push_back(final_buf(e));
@@ -1246,7 +1273,7 @@ struct Builder {
         Node n = op_node(cx, c, map);
         emit(code, n, next + 1);
         const std::string& ob = op(c).out.buf;
-        if (output_bufs.count(ob)) emit_store(code, cx, ob, map);
+        if (side_stored(e, c)) emit_store(code, cx, ob, map);
         if (i + 1 < e.side.size()) {
           DIns s2{};
           s2.op = VM_SAVE;

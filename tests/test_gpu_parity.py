@@ -291,6 +291,21 @@ def test_fused_equals_unfused(name):
         parity.assert_bitexact(a, b, s.dtype, s.buf)
 
 
+@pytest.mark.parametrize("name", ["c2s", "c5s"])
+def test_ordinary_launch_matches_cooperative(name):
+    """launch_mode=1 (ordinary launch of the co-resident grid) runs the same
+    kernel on the same plan: outputs are bit-identical to the cooperative
+    launch, and no barrier aborts."""
+    cfg = SMALL[name]
+    say("launch modes", name)
+    base = programs.build(cfg)
+    ins = programs.inputs_for(cfg, 2)
+    o1, _ = parity.gpu_run(base, [a.copy() for a in ins], launch_mode=0)
+    o2, p2 = parity.gpu_run(base, [a.copy() for a in ins], launch_mode=1)
+    for a, b, s in zip(o1, o2, base.outputs):
+        parity.assert_bitexact(a, b, s.dtype, s.buf)
+
+
 def test_c1_end_to_end_close_to_oracle(oracle_mod):
     cfg = SMALL["c1"]
     say("c1 end to end")

@@ -46,11 +46,32 @@ def test_mlp_schedule_decisions():
     p = programs.build(programs.CONFIGS["c1"])
     q = tk.compile(p.text(), device=-1).query()
     # addmm + sub(d) chain, gm + threshold_backward chain: two epilogue fusions;
-    # every weight update folds into its gradient tile; pow is inlined into mean
+    # the first layer's relu is written by its addmm tile (side epilogue: both
+    # the pre-activation and the activation are read later); every weight
+    # update folds into its gradient tile; pow is inlined into mean
     assert q["fused_epilogues"] == 2
+    assert q["side_epilogues"] == 1
     assert q["fused_updates"] == 2
     assert q["inlined_ops"] == 1
-    assert q["n_stages"] == 7
+    assert q["n_stages"] == 6
+
+
+def test_side_epilogue_stores_values_read_later():
+    # h = a@b is read later (by threshold_backward) and so is r = relu(h): the
+    # tile writes both, and no separate pointwise stage remains
+    p = Program()
+    a = p.input("a", "f32", (8, 8))
+    b = p.input("b", "f32", (8, 8))
+    g = p.input("g", "f32", (8, 8))
+    h = p.op("mm", [a, b], "f32", (8, 8))
+    r = p.op("relu", [h], "f32")
+    m = p.op("mm", [r, b], "f32", (8, 8))
+    t = p.op("threshold_backward", [g, h], "f32", threshold=0.0)
+    p.output(m)
+    p.output(t)
+    q = tk.compile(p.text(), device=-1).query()
+    assert q["side_epilogues"] == 1
+    assert q["n_stages"] == 2
 
 
 def test_fusion_stops_at_returned_values():
