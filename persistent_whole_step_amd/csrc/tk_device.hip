@@ -37,7 +37,14 @@ using namespace tkplan;
 
 namespace {
 
-constexpr int kSmemBytes = 2 * 2 * 128 * 72 * 2;  // A and B tiles, double buffered (73728 B)
+// Workgroup LDS arena (104 KB).  A contraction's operand ring uses up to
+// 96 KB during its main loop; afterwards the fp32 C tile (at most 128 x 132
+// floats) takes the bottom and the machine exchange the top 32 KB.  Every
+// other task uses the bottom 72 KB for staging or scratch.
+constexpr int kArenaBytes = 106496;
+constexpr int kSmemBytes = 73728;        // staging / scratch region below the exchange
+constexpr int kXvOff = kSmemBytes;       // machine exchange: values
+constexpr int kXeOff = kSmemBytes + 16384;
 constexpr int kVmElems = 16;                       // elements per thread per machine batch
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -47,13 +54,13 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 // Workgroup-shared storage.
-__shared__ __attribute__((aligned(16))) uint8_t g_smem[kSmemBytes];  // GEMM staging / C tile / scratch
+__shared__ __attribute__((aligned(16))) uint8_t g_smem[kArenaBytes];  // see kArenaBytes
 __shared__ __attribute__((aligned(16))) uint8_t g_plan[kPlanLds];    // current stage's descriptors
-__shared__ float g_xv[kVmElems * kBlock];     // machine exchange: values   [element][thread]
-__shared__ uint32_t g_xe[kVmElems * kBlock];  // machine exchange: first linear element of each chunk
-
-DEV LDS float& xv(uint32_t tid, int j) { return ((LDS float*)g_xv)[j * kBlock + tid]; }
-DEV LDS uint32_t& xe(uint32_t tid, int q) { return ((LDS uint32_t*)g_xe)[q * kBlock + tid]; }
+// Machine exchange (in the arena's top 32 KB): values [element][thread] and
+// the first linear element of each chunk [chunk][thread].
+DEV LDS float& xv(uint32_t tid, int j) { return ((LDS float*)(g_smem + kXvOff))[j * kBlock + tid]; }
+DEV LDS uint32_t& xe(uint32_t tid, int q) { return ((LDS uint32_t*)(g_smem + kXeOff))[q * kBlock + tid]; }
+static_assert(kXeOff + kVmElems * kBlock * 4 == kArenaBytes, "arena layout");
 
 // ------------------------------------------------------------ conversions --
 
@@ -587,94 +594,92 @@ DEV void gemm_simt(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
 
 // ------------------------------------------------------- MFMA contraction --
 // Tile BM x BN, K staged 64 deep; 4 waves in a 2x2 grid, each wave a
-// (BM/2) x (BN/2) block of 32x32 MFMA accumulators.  Both operands are staged
-// in LDS k-contiguous, [row][64 k] in 128-byte rows of eight 16-byte chunks,
-// chunk c of row r stored at position c ^ ((r ^ (r >> 3)) & 7).  The swizzle
-// spreads every access pattern of the loop over all banks: the 16-byte
-// stores of a k-contiguous operand, the 4/8-byte stores of an operand
-// transposed in registers (unit stride along M/N, loaded 16 bytes wide along
-// its rows), and the 16-byte fragment reads of the MFMAs.  On the fast path
-// (interior tile, whole 64-deep slices, 16-byte aligned rows) the global
-// loads of D slices are in flight in registers ahead of the MFMAs; other
-// tiles stage element by element.
+// (BM/2) x (BN/2) block of 32x32 MFMA accumulators.
+//
+// Fast path (interior tile, whole 64-deep slices, 16-byte aligned rows):
+// operands go from global memory straight into LDS (global_load_lds, 16
+// bytes per lane; each wave instruction fills one contiguous 1 KB block, the
+// lane's source address choosing what lands where), in a ring of S stages
+// with S - 1 slices in flight.  An operand with unit stride along k is staged
+// as [row][64 k] (128-byte rows, 16-byte chunk c of row r at position
+// c ^ ((r ^ r>>3) & 7)) and read with 16-byte fragment loads.  An operand
+// with unit stride along M/N is staged as it lies, [k][rows] (chunk c of k-row
+// k at c ^ kswz(k)), and read with ds_read_b64_tr_b16: lane i of each 16-lane
+// group addresses k-row kbase + i/4, columns nbase + 4(i%4), and receives the
+// four k values of column nbase + (its lane within the group), so two reads
+// give the 8 k values of an MFMA fragment.  Both swizzles keep every access
+// pattern at most two-way per bank.  Other tiles stage element by element in
+// the k-major layout.
 
 constexpr int kBK = 64;
-constexpr int kPitch = kBK;  // halfs per staged row
+constexpr int kPitch = kBK;  // halfs per k-major staged row
 
-// Element offset (in halfs) of (row, 16-byte chunk c) in a staged operand.
+// Element offset (in halfs) of (row, 16-byte chunk c) in a k-major operand.
 DEV int swz(int row, int c) { return row * kPitch + ((c ^ ((row ^ (row >> 3)) & 7)) << 3); }
 
-// Per-thread loads of one operand: N = R/32 16-byte loads per 64-deep slice.
-// kc: unit stride along k (16-byte chunks along k); otherwise unit stride
-// along rows (blocks of R/32 k-rows x 8 rows, transposed when committed).
+// Chunk position swizzle of k-row k in a row-major ([k][R]) operand.
 template <int R>
-struct FastOp {
-  static constexpr int N = R / 32;
-  const GLOBAL uint16_t* ptr[N];
-  int64_t kstep;
-  bool kc;
-  uint32_t tid;
-  DEV void init(uint32_t tid_, bool kcontig, const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0,
+DEV int kswz(int k) {
+  if (R == 128) return ((k & 3) << 2) ^ (((k >> 3) & 1) << 1);
+  return (((k >> 1) & 1) << 2) ^ (((k >> 3) & 1) << 1);
+}
+
+// Wait until at most N vector-memory operations of this wave are in flight
+// (gfx9 s_waitcnt encoding; expcnt and lgkmcnt left at their maxima).
+template <int N>
+DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// Direct-to-LDS staging of one operand: R tile rows x 64 k per slice, R/8 KB,
+// R/32 blocks of 1 KB per wave.
+template <int R>
+struct DirectOp {
+  static constexpr int NB = R / 32;
+  const GLOBAL uint8_t* src[NB];  // this lane's source for slice 0, per block
+  int64_t kstep;                  // bytes from one slice to the next
+  uint32_t wave;
+  DEV void init(uint32_t tid, bool kc, const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0,
                 uint32_t k0) {
-    tid = tid_;
-    kc = kcontig;
-    if (kc) {
+    wave = uniform(tid / 64);  // the LDS destination (M0) must be wave-uniform
+    const int lane = tid % 64;
 #pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int ch = tid + i * kBlock;
-        ptr[i] = q + off + (int64_t)(r0 + ch / 8) * sr + k0 + (ch % 8) * 8;
+    for (int i = 0; i < NB; ++i) {
+      const int b = (int)wave + 4 * i;  // block index
+      if (kc) {
+        // block b: rows 8b .. 8b+7; lane -> (row, position); load the chunk the swizzle puts there
+        const int r = 8 * b + lane / 8, p = lane % 8;
+        const int c = p ^ ((r ^ (r >> 3)) & 7);
+        src[i] = (const GLOBAL uint8_t*)(q + off + (int64_t)(r0 + r) * sr + k0 + c * 8);
+      } else {
+        // block b: k-rows b*(512/R) ..; R/8 chunks per k-row
+        constexpr int cpr = R / 8;
+        const int k = b * (512 / R) + lane / cpr, p = lane % cpr;
+        const int c = p ^ kswz<R>(k);
+        src[i] = (const GLOBAL uint8_t*)(q + off + (int64_t)(k0 + k) * sk + r0 + c * 8);
       }
-      kstep = kBK;
-    } else {
-      const int rb = tid % (R / 8), kb = tid / (R / 8);
-#pragma unroll
-      for (int i = 0; i < N; ++i) ptr[i] = q + off + (int64_t)(k0 + kb * N + i) * sk + r0 + rb * 8;
-      kstep = (int64_t)kBK * sk;
     }
+    kstep = kc ? (int64_t)kBK * 2 : (int64_t)kBK * sk * 2;
   }
-  DEV void load(uint32_t slice, u32x4 (&v)[N]) const {
+  // Issue the loads of `slice` into the operand region at LDS byte offset `lds`.
+  // Written as inline asm so the compiler does not order every later LDS read
+  // behind these writes (it cannot tell the ring stages apart); the main loop
+  // waits for them explicitly (vmcnt) and with a workgroup barrier.
+  DEV void issue(uint32_t slice, uint32_t lds) const {
+    const uint32_t base = (uint32_t)(uintptr_t)(LDS uint8_t*)g_smem + lds + wave * 1024;
 #pragma unroll
-    for (int i = 0; i < N; ++i) v[i] = *(const GLOBAL u32x4*)(ptr[i] + (int64_t)slice * kstep);
-  }
-  DEV void commit(const u32x4 (&v)[N], LDS uint16_t* lds) const {
-    if (kc) {
-#pragma unroll
-      for (int i = 0; i < N; ++i) {
-        const int ch = tid + i * kBlock;
-        *(LDS u32x4*)(lds + swz(ch / 8, ch % 8)) = v[i];
-      }
-    } else {
-      // thread (rb, kb) holds rows rb*8 .. rb*8+7 at k = kb*N .. kb*N+N-1;
-      // row rb*8 + 2j takes the low halves, row rb*8 + 2j + 1 the high halves
-      const int rb = tid % (R / 8), kb = tid / (R / 8);
-      const int c = (kb * N) / 8, e = (kb * N) % 8;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        uint32_t lo[N / 2], hi[N / 2];
-#pragma unroll
-        for (int h = 0; h < N / 2; ++h) {
-          lo[h] = (v[2 * h][j] & 0xffffu) | (v[2 * h + 1][j] << 16);
-          hi[h] = (v[2 * h][j] >> 16) | (v[2 * h + 1][j] & 0xffff0000u);
-        }
-        const int r0 = rb * 8 + 2 * j;
-        LDS uint16_t* d0 = lds + swz(r0, c) + e;
-        LDS uint16_t* d1 = lds + swz(r0 + 1, c) + e;
-        if (N == 4) {
-          *(LDS u32x2*)d0 = u32x2{lo[0], lo[1]};
-          *(LDS u32x2*)d1 = u32x2{hi[0], hi[1]};
-        } else {
-          *(LDS uint32_t*)d0 = lo[0];
-          *(LDS uint32_t*)d1 = hi[0];
-        }
-      }
+    for (int i = 0; i < NB; ++i) {
+      const GLOBAL uint8_t* g = src[i] + (int64_t)slice * kstep;
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(base + 4096 * i) : "m0");
     }
   }
 };
 
-// General operand path: element by element straight into LDS, zero outside.
+// General operand path: element by element into the k-major layout, zero outside.
 template <int R>
-DEV void slow_stage(uint32_t tid, const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0, uint32_t rmax,
-                    uint32_t k0, uint32_t kmax, LDS uint16_t* lds) {
+DEV void slow_stage(uint32_t tid, const GLOBAL uint16_t* q, int64_t off, int64_t sr, int64_t sk, uint32_t r0,
+                    uint32_t rmax, uint32_t k0, uint32_t kmax, LDS uint16_t* lds) {
   // consecutive threads walk the operand's unit-stride dimension when it has one
   const bool kfast = sk == 1 || sr != 1;
   for (int p = tid; p < R * kBK; p += kBlock) {
@@ -695,20 +700,41 @@ DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                 0);
 }
 
-// One 64-deep K slice from LDS into the wave's accumulators.
+// MFMA fragment of `row0 + lane%32` (rows of an R-row operand), k = kk + 8*(lane/32) .. +7.
+template <int R>
+DEV u32x4 frag(uint32_t tid, const LDS uint16_t* s, bool kmajor, int row0, int kk) {
+  const int lane = tid % 64;
+  if (kmajor) return *(const LDS u32x4*)(s + swz(row0 + lane % 32, kk / 8 + lane / 32));
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const int g = lane / 16, i = lane % 16;
+  const int n = row0 + 16 * (g % 2) + 4 * (i % 4);
+  const int k1 = kk + 8 * (g / 2) + i / 4, k2 = k1 + 4;
+  const int c = n / 8, e = n % 8;
+  const v4s r1 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS v4s*)(s + k1 * R + ((c ^ kswz<R>(k1)) << 3) + e));
+  const v4s r2 = __builtin_amdgcn_ds_read_tr16_b64_v4i16((LDS v4s*)(s + k2 * R + ((c ^ kswz<R>(k2)) << 3) + e));
+  u32x4 v;
+  v[0] = (uint32_t)(uint16_t)r1[0] | ((uint32_t)(uint16_t)r1[1] << 16);
+  v[1] = (uint32_t)(uint16_t)r1[2] | ((uint32_t)(uint16_t)r1[3] << 16);
+  v[2] = (uint32_t)(uint16_t)r2[0] | ((uint32_t)(uint16_t)r2[1] << 16);
+  v[3] = (uint32_t)(uint16_t)r2[2] | ((uint32_t)(uint16_t)r2[3] << 16);
+  return v;
+}
+
+// One 64-deep K slice from LDS into the wave's accumulators.  a_km / b_km:
+// operand staged k-major (else row-major, read transposed).
 template <int BM, int BN, bool BF16>
-DEV void mfma_slice(uint32_t tid, const LDS uint16_t* sa, const LDS uint16_t* sb, f32x16 (&acc)[BM / 64][BN / 64]) {
+DEV void mfma_slice(uint32_t tid, const LDS uint16_t* sa, const LDS uint16_t* sb, bool a_km, bool b_km,
+                    f32x16 (&acc)[BM / 64][BN / 64]) {
   constexpr int FM = BM / 64, FN = BN / 64;
-  const int wave = tid / 64, lane = tid % 64;
+  const int wave = tid / 64;
   const int wm = wave / 2, wn = wave % 2;
-  const int ra = wm * (BM / 2) + (lane % 32), rbw = wn * (BN / 2) + (lane % 32), ch = lane / 32;
 #pragma unroll
   for (int kk = 0; kk < kBK; kk += 16) {
     u32x4 af[FM], bfr[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = *(const LDS u32x4*)(sa + swz(ra + i * 32, kk / 8 + ch));
+    for (int i = 0; i < FM; ++i) af[i] = frag<BM>(tid, sa, a_km, wm * (BM / 2) + i * 32, kk);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[j] = *(const LDS u32x4*)(sb + swz(rbw + j * 32, kk / 8 + ch));
+    for (int j = 0; j < FN; ++j) bfr[j] = frag<BN>(tid, sb, b_km, wn * (BN / 2) + j * 32, kk);
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -721,6 +747,10 @@ DEV void mfma_slice(uint32_t tid, const LDS uint16_t* sa, const LDS uint16_t* sb
 template <int BM, int BN, bool BF16>
 DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
   constexpr int FM = BM / 64, FN = BN / 64;  // 32x32 blocks per wave along m / n
+  constexpr int S = BM == 128 ? 3 : 4;       // ring stages (S * (BM + BN) * 128 bytes <= 96 KB)
+  constexpr int SA = BM * kBK * 2, SB = BN * kBK * 2;
+  constexpr int LPS = BM / 32 + BN / 32;     // direct loads per wave per slice
+  static_assert(S * (SA + SB) <= 98304, "operand ring exceeds the arena");
   const uint32_t tiles = t.tiles_m * t.tiles_n;
   const uint32_t split_index = item / tiles;
   const uint32_t tile = xcd_tile(item % tiles, tiles);
@@ -741,10 +771,6 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
   const uint32_t nk = kend > kbeg ? (kend - kbeg + kBK - 1) / kBK : 0;
-  LDS uint16_t* sa0 = (LDS uint16_t*)g_smem;
-  LDS uint16_t* sa1 = sa0 + BM * kPitch;
-  LDS uint16_t* sb0 = sa0 + 2 * BM * kPitch;
-  LDS uint16_t* sb1 = sb0 + BN * kPitch;
   // A's element (m, k) at off + m * stride[0] + k * stride[1];
   // B's element (n, k) at off + k * stride[0] + n * stride[1]
   const bool full_k = (kend - kbeg) % kBK == 0;
@@ -754,52 +780,44 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
   const bool a_ok = m0 + BM <= t.m && (a_kc || a_rc) && aligned16(pa) && (A.offset & 7) == 0 && (a_other & 7) == 0;
   const bool b_ok = n0 + BN <= t.n && (b_kc || b_rc) && aligned16(pb) && (B.offset & 7) == 0 && (b_other & 7) == 0;
   if (nk > 0 && full_k && a_ok && b_ok) {
-    // D slices of global loads in flight in registers; LDS double buffer.
-    // Slice k is committed to buffer k % 2, then (after a workgroup barrier)
-    // its register set takes the loads of slice k + D and the MFMAs read the
-    // buffer.  Buffer k % 2 was last read by slice k - 2, which every wave
-    // finished before the barrier of slice k - 1.
-    constexpr int D = BM == 64 ? 4 : 3;
-    FastOp<BM> fa;
-    FastOp<BN> fb;
-    fa.init(tid, a_kc, pa, A.offset, A.stride[0], A.stride[1], m0, kbeg);
-    fb.init(tid, b_kc, pb, B.offset, B.stride[1], B.stride[0], n0, kbeg);
-    // Loads are unconditional (past the last slice they repeat it): the
-    // compiler can then count exactly which loads each commit must wait for.
-    u32x4 ra[D][FastOp<BM>::N], rb[D][FastOp<BN>::N];
+    DirectOp<BM> da;
+    DirectOp<BN> db;
+    da.init(tid, a_kc, pa, A.offset, A.stride[0], A.stride[1], m0, kbeg);
+    db.init(tid, b_kc, pb, B.offset, B.stride[1], B.stride[0], n0, kbeg);
     const uint32_t last = nk - 1;
+    // slices 0 .. S-2 in flight (past the last slice, loads repeat it into a
+    // stage that is not read again)
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const uint32_t sl = (uint32_t)d < last ? (uint32_t)d : last;
-      fa.load(sl, ra[d]);
-      fb.load(sl, rb[d]);
+    for (int s = 0; s < S - 1; ++s) {
+      const uint32_t sl = (uint32_t)s < last ? (uint32_t)s : last;
+      da.issue(sl, s * (SA + SB));
+      db.issue(sl, s * (SA + SB) + SA);
     }
-    for (uint32_t k0 = 0; k0 < nk; k0 += D) {
-#pragma unroll
-      for (int d = 0; d < D; ++d) {
-        const uint32_t k = k0 + d;
-        const bool act = k < nk;  // uniform; false only in the last group
-        LDS uint16_t* sa = (k & 1) ? sa1 : sa0;
-        LDS uint16_t* sb = (k & 1) ? sb1 : sb0;
-        if (act) {
-          fa.commit(ra[d], sa);
-          fb.commit(rb[d], sb);
-        }
-        __syncthreads();
-        const uint32_t nx = k + D < last ? k + D : last;
-        fa.load(nx, ra[d]);
-        fb.load(nx, rb[d]);
-        if (act) mfma_slice<BM, BN, BF16>(tid, sa, sb, acc);
-      }
+    for (uint32_t k = 0; k < nk; ++k) {
+      // this wave's loads of slice k have landed once at most the S-2 younger
+      // slices are in flight; the barrier then covers every wave's loads and
+      // every wave's last read of stage (k-1) % S, which the next issue refills
+      wait_vmcnt<(S - 2) * LPS>();
+      __syncthreads();
+      const uint32_t nx = k + S - 1 < last ? k + S - 1 : last;
+      const uint32_t ns = (k + S - 1) % S;
+      da.issue(nx, ns * (SA + SB));
+      db.issue(nx, ns * (SA + SB) + SA);
+      const uint32_t cs = (k % S) * (SA + SB);
+      mfma_slice<BM, BN, BF16>(tid, (const LDS uint16_t*)(g_smem + cs), (const LDS uint16_t*)(g_smem + cs + SA), a_kc,
+                               b_kc, acc);
     }
-    __syncthreads();  // every wave is done with the staging buffers (the C tile reuses them)
+    wait_vmcnt<0>();  // no load may still be writing the arena
+    __syncthreads();  // every wave is done with the ring (the C tile reuses it)
   } else {
+    LDS uint16_t* sa0 = (LDS uint16_t*)g_smem;
+    LDS uint16_t* sb0 = (LDS uint16_t*)(g_smem + SA);
     for (uint32_t kt = 0; kt < nk; ++kt) {
       const uint32_t k0 = kbeg + kt * kBK;
       slow_stage<BM>(tid, pa, A.offset, A.stride[0], A.stride[1], m0, t.m, k0, kend, sa0);
       slow_stage<BN>(tid, pb, B.offset, B.stride[1], B.stride[0], n0, t.n, k0, kend, sb0);
       __syncthreads();
-      mfma_slice<BM, BN, BF16>(tid, sa0, sb0, acc);
+      mfma_slice<BM, BN, BF16>(tid, sa0, sb0, true, true, acc);
       __syncthreads();
     }
   }
