@@ -122,7 +122,7 @@ struct DTask {
   uint16_t va, vb, vs, vx;  // operand views (A, B, scale, extra)
   uint64_t scratch;         // byte offset of fp32 partials in the workspace
   float count;              // mean divisor
-  uint32_t pad2;
+  uint32_t group_m;         // contractions: tile rows per group of the tile order (see the kernel)
 };
 static_assert(sizeof(DTask) % 8 == 0, "DTask layout");
 

@@ -495,6 +495,17 @@ DEV uint32_t xcd_tile(uint32_t local, uint32_t tiles) {
   return (local % 8) * (tiles / 8) + local / 8;
 }
 
+// Tile coordinates of tile-order index `tile`: group-major, group_m tile rows
+// per group, column by column within a group (group_m divides tiles_m), so a
+// run of consecutive indices covers a compact block of the output.
+DEV void tile_coords(const DTask& t, uint32_t tile, uint32_t& tm, uint32_t& tn) {
+  const uint32_t gm = t.group_m > 1 ? t.group_m : 1;
+  const uint32_t gsz = gm * t.tiles_n;
+  const uint32_t g = tile / gsz, r = tile % gsz;
+  tm = g * gm + r % gm;
+  tn = r / gm;
+}
+
 // ------------------------------------------------------ fp32-FMA contraction --
 // 64x64 output tile, 256 threads, each thread a 4x4 block; K staged 32 deep in
 // a double-buffered LDS ring, the next slice's loads issued before the current
@@ -528,7 +539,8 @@ DEV void simt_store(uint32_t tid, LDS float* s, bool mn_contig, const float (&re
 
 DEV void gemm_simt(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
   const uint32_t tile = xcd_tile(item, t.tiles_m * t.tiles_n);
-  const uint32_t tm = tile / t.tiles_n, tn = tile % t.tiles_n;
+  uint32_t tm, tn;
+  tile_coords(t, tile, tm, tn);
   const uint32_t m0 = tm * 64, n0 = tn * 64;
   LDS float* As0 = (LDS float*)g_smem;
   LDS float* As1 = As0 + 32 * 68;
@@ -754,7 +766,8 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
   const uint32_t tiles = t.tiles_m * t.tiles_n;
   const uint32_t split_index = item / tiles;
   const uint32_t tile = xcd_tile(item % tiles, tiles);
-  const uint32_t tm = tile / t.tiles_n, tn = tile % t.tiles_n;
+  uint32_t tm, tn;
+  tile_coords(t, tile, tm, tn);
   const uint32_t m0 = tm * BM, n0 = tn * BN;
   const uint32_t kbeg = split_index * t.kchunk;
   const uint32_t kend = (kbeg + t.kchunk < t.k) ? kbeg + t.kchunk : t.k;

@@ -1343,6 +1343,24 @@ struct Builder {
     t.tiles_m = g.tm;
     t.tiles_n = g.tn;
     t.width = (n % 8 == 0) ? 8 : 1;
+    // Tile order: the kernel gives each XCD a contiguous run of tiles/8 tiles
+    // (when the count divides by 8); in group-major order (group_m tile rows
+    // at a time, column by column) such a run is a group_m x (run/group_m)
+    // block, whose operand panels the XCD's L2 shares.  Choose the block that
+    // touches the fewest panels.
+    t.group_m = 1;
+    {
+      const uint64_t tiles = (uint64_t)g.tm * g.tn;
+      const uint64_t run = tiles % 8 == 0 ? tiles / 8 : tiles;
+      uint64_t best = run + 1;
+      for (uint64_t d = 1; d <= g.tm; ++d) {
+        if (g.tm % d || run % d || run / d > g.tn) continue;
+        if (d + run / d < best) {
+          best = d + run / d;
+          t.group_m = (uint32_t)d;
+        }
+      }
+    }
     // operand views go first in this task's view block
     std::vector<DView> ops;
     if (g.kind == T_GEMV_Q8) {
