@@ -1035,7 +1035,11 @@ struct Builder {
     if (c.colform) {
       c.kind = T_RED_COLS;
       for (int d = 0; d < rank; ++d) c.perm.push_back(d);
-      int64_t parts = std::min<int64_t>(64, std::max<int64_t>(1, (rr + 127) / 128));
+      // 32 rows per part: a work item is at most two machine batches (8 row
+      // lanes x 2 rows per batch for 8-wide chunks), so parts run in parallel
+      // across workgroups instead of in sequence within one
+      // (up to 64 rows stay one part: a combine stage would cost more)
+      int64_t parts = rr <= 64 ? 1 : std::min<int64_t>(64, (rr + 31) / 32);
       int64_t kc = (rr + parts - 1) / parts;
       parts = (rr + kc - 1) / std::max<int64_t>(1, kc);
       c.parts = (uint32_t)std::max<int64_t>(1, parts);
