@@ -350,7 +350,43 @@ def compile(text: str, device: int = 0, opts: TkOptions | None = None, **kw) -> 
     h = ctypes.c_void_p()
     raw = text.encode()
     _check(lib().tk_compile(raw, len(raw), ctypes.byref(opts), int(device), ctypes.byref(h)))
-    return Program(h, text, device)
+    prog = Program(h, text, device)
+    prog.launch_mode = int(opts.launch_mode)
+    return prog
+
+
+class StepGraph:
+    """A captured sequence of whole-step launches, replayed as one unit.
+
+    The steady-state loop of the runtime page's graph-replayed benchmark (README,
+    Benchmark section: state feedback over resident batches): one launch per
+    (inputs, buffers) variant, captured once on a private stream, then replayed
+    any number of times.  Parameters updated in place feed the next replay.
+    Every variant's tensors must stay alive and unmoved while the graph exists.
+    The program must use launch_mode=1 (ordinary launches are capturable;
+    cooperative ones are not), and its workspace must be initialised before
+    capture (tk_allocate does it).  Nothing in a step clears memory with a
+    memset node."""
+
+    def __init__(self, program: "Program", variants):
+        import torch
+        if getattr(program, "launch_mode", 0) != 1:
+            raise ValueError("tk: graph capture needs a program compiled with launch_mode=1")
+        self.program = program
+        self.variants = list(variants)
+        self._graph = torch.cuda.CUDAGraph()
+        torch.cuda.synchronize()
+        with torch.cuda.graph(self._graph):
+            for ins, bufs in self.variants:
+                program.run_into(*ins, buffers=bufs)
+
+    def replay(self):
+        """Enqueue every captured step on the current stream."""
+        self._graph.replay()
+
+    @property
+    def steps(self) -> int:
+        return len(self.variants)
 
 
 def validate_fake(prog: Program, inputs, outputs, workspace):

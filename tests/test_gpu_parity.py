@@ -306,6 +306,49 @@ def test_ordinary_launch_matches_cooperative(name):
         parity.assert_bitexact(a, b, s.dtype, s.buf)
 
 
+def test_graph_replay_matches_eager_steps():
+    """Four steps over four resident batches, captured once and replayed three
+    times with eager work and synchronisations in between, give after every
+    replay exactly the parameters and loss of the same twelve steps run
+    eagerly (state feedback through the in-place updates)."""
+    import torch
+    from persistent_whole_step_amd import tk
+    cfg = SMALL["c2s"]
+    say("graph replay c2s")
+    prog = programs.build(cfg)
+    p = tk.compile(prog.text(), device=0, launch_mode=1)
+    base = programs.inputs_for(cfg, 3)
+    batches = [programs.inputs_for(cfg, 10 + j)[:2] for j in range(4)]
+
+    def state():
+        params = [parity.to_torch(a, s.dtype) for a, s in zip(base[2:], prog.inputs[2:])]
+        xs = [[parity.to_torch(b[0], prog.inputs[0].dtype), parity.to_torch(b[1], prog.inputs[1].dtype)]
+              for b in batches]
+        bufs = p.allocate(*(xs[0] + params))
+        variants = [(x + params, tk.ExecutionBuffers(
+            tuple(params[p._inplace_map()[s] - 2] if s in p._inplace_map() else o
+                  for s, o in enumerate(bufs.outputs)), bufs.workspace)) for x in xs]
+        return params, variants
+
+    e_params, e_vars = state()
+    g_params, g_vars = state()
+    graph = tk.StepGraph(p, g_vars)
+    junk = torch.zeros(1 << 20, device="cuda:0")
+    for rep in range(3):
+        for ins, bufs in e_vars:
+            p.run_into(*ins, buffers=bufs)
+        graph.replay()
+        junk.add_(1.0)  # eager work of the program's own between replays
+        torch.cuda.synchronize()
+        for a, b, s in zip(e_params, g_params, prog.inputs[2:]):
+            parity.assert_bitexact(parity.to_numpy(b, s.dtype), parity.to_numpy(a, s.dtype), s.dtype, s.buf)
+        le = parity.to_numpy(e_vars[-1][1].outputs[0], prog.outputs[0].dtype)
+        lg = parity.to_numpy(g_vars[-1][1].outputs[0], prog.outputs[0].dtype)
+        parity.assert_bitexact(lg, le, prog.outputs[0].dtype, "loss")
+    aborted, _ = p.workspace_status(g_vars[0][1].workspace)
+    assert not aborted
+
+
 def test_c1_end_to_end_close_to_oracle(oracle_mod):
     cfg = SMALL["c1"]
     say("c1 end to end")
