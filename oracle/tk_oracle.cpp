@@ -434,6 +434,7 @@ struct Interp {
     if (c == "div") return arg(0) / arg(1);
     if (c == "neg") return -arg(0);
     if (c == "relu") { T x = arg(0); return x < (T)0 ? (T)0 : x; }
+    if (c == "sqrt") return std::sqrt(arg(0));  // IEEE: correctly rounded in the evaluation type
     if (c == "pow") {
       T e = op.args.size() > 1 ? arg(1) : attr("exponent", 2.0f);
       T x = arg(0);
@@ -458,11 +459,12 @@ struct Interp {
   }
 
   void run_pointwise(const Op& op, Value<T>& out) {
-    static const char* known[] = {"add", "sub", "mul", "div", "neg", "relu", "pow", "threshold_backward", "full", "cast"};
+    static const char* known[] = {"add", "sub", "mul", "div", "neg", "relu", "pow", "threshold_backward", "full", "cast",
+                                  "sqrt"};
     bool ok = false;
     for (const char* k : known) ok = ok || op.opcode == k;
     if (!ok) fail("unsupported pointwise operation " + op.opcode);
-    static const char* unary[] = {"neg", "relu", "cast"};
+    static const char* unary[] = {"neg", "relu", "cast", "sqrt"};
     for (const char* k : unary)
       if (op.opcode == k && op.args.size() != 1) fail(op.opcode + " takes one operand");
     if ((op.opcode == "add" || op.opcode == "sub" || op.opcode == "mul" || op.opcode == "div" ||

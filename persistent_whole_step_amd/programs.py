@@ -35,7 +35,7 @@ from dataclasses import dataclass, field
 
 import numpy as np
 
-POINTWISE = ("add", "sub", "mul", "div", "neg", "relu", "pow", "threshold_backward", "full", "cast")
+POINTWISE = ("add", "sub", "mul", "div", "neg", "relu", "pow", "threshold_backward", "full", "cast", "sqrt")
 CONTRACTIONS = ("mm", "addmm", "mm_q8", "addmm_q8")
 REDUCTIONS = ("sum", "mean")
 
@@ -176,18 +176,103 @@ class Program:
 
 
 # ---------------------------------------------------------------------------
+# Parameter updates.
+# ---------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class AdamW:
+    """Adam with decoupled weight decay (Loshchilov and Hutter), the optimizer
+    the trainkernel README's roadmap names next after SGD.
+
+    Hyper-parameters are static scalars of the program.  The step-dependent
+    bias corrections are not: they enter as two one-element float32 inputs,
+    ``c1 = 1/(1 - beta1^t)`` and ``c2 = 1/(1 - beta2^t)``, so one compiled
+    program serves every step t (the caller recomputes them per step)."""
+    beta1: float = 0.9
+    beta2: float = 0.999
+    eps: float = 1e-8
+    weight_decay: float = 1e-2
+
+    def corrections(self, t: int):
+        """(c1, c2) for step t >= 1, each rounded once to float32."""
+        if t < 1:
+            raise ValueError("AdamW steps count from 1")
+        return f32(1.0 / (1.0 - self.beta1 ** t)), f32(1.0 / (1.0 - self.beta2 ** t))
+
+
+def adamw_update(p: Program, w: Spec, g: Spec, m: Spec, v: Spec, c1: Spec, c2: Spec,
+                 lr: float, opt: AdamW, name: str):
+    """One parameter's AdamW update, written as pointwise ops evaluated in
+    float32 (states m and v are float32; the gradient is widened on read):
+
+        w_d = w * (1 - lr*wd)                 decoupled decay, applied first
+        m'  = beta1*m + (1-beta1)*g
+        v'  = beta2*v + (1-beta2)*(g*g)
+        w'  = w_d - lr * (m'*c1) / (sqrt(v'*c2) + eps)    rounded to w's dtype
+
+    Returns (w', m', v')."""
+    sh = w.shape
+    one = lambda s: s.view(sh, (0,) * len(sh))  # broadcast a one-element input
+    wd = p.op("mul", [w, f32(1.0 - lr * opt.weight_decay)], "f32", sh, name=f"{name}_decayed")
+    m1 = p.op("mul", [m, f32(opt.beta1)], "f32", sh, name=f"{name}_m_decay")
+    mn = p.op("add", [m1, g], "f32", sh, name=f"{name}_m_new", alpha=f32(1.0 - opt.beta1))
+    gg = p.op("mul", [g, g], "f32", sh, name=f"{name}_g_sq")
+    v1 = p.op("mul", [v, f32(opt.beta2)], "f32", sh, name=f"{name}_v_decay")
+    vn = p.op("add", [v1, gg], "f32", sh, name=f"{name}_v_new", alpha=f32(1.0 - opt.beta2))
+    mh = p.op("mul", [mn, one(c1)], "f32", sh, name=f"{name}_m_hat")
+    vh = p.op("mul", [vn, one(c2)], "f32", sh, name=f"{name}_v_hat")
+    rt = p.op("sqrt", [vh], "f32", sh, name=f"{name}_v_root")
+    dn = p.op("add", [rt, f32(opt.eps)], "f32", sh, name=f"{name}_denom")
+    u = p.op("div", [mh, dn], "f32", sh, name=f"{name}_step")
+    wn = p.op("sub", [wd, u], w.dtype, sh, name=f"{name}_new", alpha=f32(lr))
+    return wn, mn, vn
+
+
+def _update(p: Program, weights, biases, loss, dtype: str, lr: float, optimizer, return_grads: bool):
+    """Append the parameter update and the outputs: loss, then (W_i', b_i') per
+    layer in place of W_i, b_i, then with AdamW (m', v') of W1, b1, W2, ... in
+    place of their states, then the gradients when asked for.  AdamW adds the
+    inputs m and v (float32, parameter-shaped) per parameter in the same order,
+    then c1 and c2."""
+    pairs = [x for wb in zip(weights, biases) for x in wb]
+    new, states = [], []
+    if optimizer is None:
+        for w, g, nm in pairs:
+            new.append(p.op("sub", [w, g], dtype, name=f"{nm}_new", alpha=lr))
+    else:
+        mv = [(p.input(f"m_{nm}", "f32", w.shape), p.input(f"v_{nm}", "f32", w.shape)) for w, _, nm in pairs]
+        c1 = p.input("c1", "f32", (1,))
+        c2 = p.input("c2", "f32", (1,))
+        for (w, g, nm), (m, v) in zip(pairs, mv):
+            wn, mn, vn = adamw_update(p, w, g, m, v, c1, c2, lr, optimizer, nm)
+            new.append(wn)
+            states.append((mn, m, vn, v))
+    if loss is not None:
+        p.output(loss)
+    for (w, _, _), wn in zip(pairs, new):
+        p.output(wn, inplace_of=w)
+    for mn, m, vn, v in states:
+        p.output(mn, inplace_of=m)
+        p.output(vn, inplace_of=v)
+    if return_grads:
+        for _, g, _ in pairs:
+            p.output(g)
+
+
+# ---------------------------------------------------------------------------
 # Canonical whole-step programs (forward, MSE loss, explicit backward, SGD).
 # ---------------------------------------------------------------------------
 
 def mlp_step(dims, batch: int, dtype: str, lr: float, with_loss: bool = True,
-             return_grads: bool = False) -> Program:
+             return_grads: bool = False, optimizer: "AdamW | None" = None) -> Program:
     """L-layer MLP, ReLU between layers, MSE loss against t, full backward and an
     in-place SGD update of every weight and bias.  Inputs: x, t, W1, b1, ...
 
     The backward is written out op by op: gW_i = a_{i-1}^T g_i (transposed view),
     gb_i = sum over the batch, g_{i-1} = threshold_backward(g_i W_i^T, h_{i-1}, 0);
     MSE's gradient is (h_L - t) times fl32(2/(B*d_L)).  Updates use
-    ``sub(W, gW, alpha=lr)`` and are returned in place of their inputs.
+    ``sub(W, gW, alpha=lr)`` and are returned in place of their inputs; with an
+    ``AdamW`` optimizer the update is the one ``adamw_update`` writes out.
     """
     L = len(dims) - 1
     p = Program()
@@ -216,24 +301,14 @@ def mlp_step(dims, batch: int, dtype: str, lr: float, with_loss: bool = True,
         if i > 0:
             gm = p.op("mm", [g, W[i].T], dtype, (batch, dims[i]), name=f"gm{i}")
             g = p.op("threshold_backward", [gm, h[i - 1]], dtype, name=f"g{i}", threshold=0.0)
-    newW, newb = [], []
-    for i in range(L):
-        newW.append(p.op("sub", [W[i], gW[i]], dtype, name=f"W{i + 1}_new", alpha=lr))
-        newb.append(p.op("sub", [b[i], gb[i]], dtype, name=f"b{i + 1}_new", alpha=lr))
-    if loss is not None:
-        p.output(loss)
-    for i in range(L):
-        p.output(newW[i], inplace_of=W[i])
-        p.output(newb[i], inplace_of=b[i])
-    if return_grads:
-        for i in range(L):
-            p.output(gW[i])
-            p.output(gb[i])
+    _update(p, [(W[i], gW[i], f"W{i + 1}") for i in range(L)], [(b[i], gb[i], f"b{i + 1}") for i in range(L)],
+            loss, dtype, lr, optimizer, return_grads)
     return p
 
 
 def residual_step(width: int, layers: int, batch: int, dtype: str, lr: float,
-                  with_loss: bool = True, return_grads: bool = False) -> Program:
+                  with_loss: bool = True, return_grads: bool = False,
+                  optimizer: "AdamW | None" = None) -> Program:
     """h_i = h_{i-1} + relu(addmm(b_i, h_{i-1}, W_i)), MSE of h_L against t (no
     extra head weight), full backward, in-place SGD.  Inputs: x, t, W1, b1, ..."""
     p = Program()
@@ -263,19 +338,8 @@ def residual_step(width: int, layers: int, batch: int, dtype: str, lr: float,
         if i > 0:
             gm = p.op("mm", [gz, W[i].T], dtype, (batch, width), name=f"gm{i}")
             g = p.op("add", [g, gm], dtype, name=f"g{i}")
-    newW, newb = [], []
-    for i in range(layers):
-        newW.append(p.op("sub", [W[i], gW[i]], dtype, name=f"W{i + 1}_new", alpha=lr))
-        newb.append(p.op("sub", [b[i], gb[i]], dtype, name=f"b{i + 1}_new", alpha=lr))
-    if loss is not None:
-        p.output(loss)
-    for i in range(layers):
-        p.output(newW[i], inplace_of=W[i])
-        p.output(newb[i], inplace_of=b[i])
-    if return_grads:
-        for i in range(layers):
-            p.output(gW[i])
-            p.output(gb[i])
+    _update(p, [(W[i], gW[i], f"W{i + 1}") for i in range(layers)],
+            [(b[i], gb[i], f"b{i + 1}") for i in range(layers)], loss, dtype, lr, optimizer, return_grads)
     return p
 
 
@@ -309,6 +373,9 @@ CONFIGS = {
 
 def build(cfg: dict, **variant) -> Program:
     kind = cfg["kind"]
+    opt = cfg.get("optimizer")
+    if opt is not None:
+        variant.setdefault("optimizer", opt)
     if kind == "mlp":
         return mlp_step(cfg["dims"], cfg["batch"], cfg["dtype"], cfg["lr"], **variant)
     if kind == "residual":
@@ -321,10 +388,19 @@ def build(cfg: dict, **variant) -> Program:
 def inputs_for(cfg: dict, seed: int):
     from . import synth
     kind = cfg["kind"]
+    opt = cfg.get("optimizer")
     if kind == "mlp":
-        return synth.mlp_inputs(seed, cfg["dims"], cfg["batch"], cfg["dtype"])
-    if kind == "residual":
-        return synth.residual_inputs(seed, cfg["width"], cfg["layers"], cfg["batch"], cfg["dtype"])
+        base = synth.mlp_inputs(seed, cfg["dims"], cfg["batch"], cfg["dtype"])
+    elif kind == "residual":
+        base = synth.residual_inputs(seed, cfg["width"], cfg["layers"], cfg["batch"], cfg["dtype"])
+    else:
+        base = None
+    if base is not None:
+        if opt is None:
+            return base
+        c1, c2 = opt.corrections(cfg.get("adam_t", 10))
+        return (base + synth.adamw_state(seed + 1, [a.shape for a in base[2:]])
+                + [np.array([c1], np.float32), np.array([c2], np.float32)])
     if kind == "gemv":
         return synth.gemv_q8_inputs(seed, cfg["k"], cfg["n"], cfg["layers"])
     raise ValueError(kind)

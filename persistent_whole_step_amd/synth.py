@@ -88,6 +88,19 @@ def gemv_q8_inputs(seed: int, k: int, n: int, layers: int, block: int = 32):
     return out
 
 
+def adamw_state(seed: int, shapes):
+    """Optimizer state part-way through training, float32: per shape, in
+    order, m ~ N(0, 1e-6) then v = u^2 with u ~ N(0, 1e-6) (non-negative, as
+    a running mean of squares is)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = []
+    for sh in shapes:
+        out.append(normal(rng, sh, 1e-6, "f32"))
+        u = rng.normal(0.0, 1e-3, size=sh)
+        out.append(np.ascontiguousarray(u * u).astype(np.float32))
+    return out
+
+
 def random_tensor(rng: np.random.Generator, shape, dtype: str, scale: float = 1.0) -> np.ndarray:
     """Generic N(0, scale^2) tensor (int8: uniform integers) for small test programs."""
     if dtype == "i8":
