@@ -68,6 +68,7 @@ enum VmOp : uint8_t {
   VM_STORE,      // view[arg] = acc (converted to the view's dtype)
   VM_SCALE,      // acc = a * acc (addmm alpha)
   VM_ZERO,       // acc = 0
+  VM_SQRT,       // acc = sqrt(acc), correctly rounded
 };
 enum VmSrc : uint8_t { SRC_NONE = 0, SRC_VIEW = 1, SRC_SCALAR = 2, SRC_SLOT = 3 };
 constexpr uint8_t RND_NONE = 0xff;

@@ -451,6 +451,7 @@ DEV void vm_run(uint32_t tid, const Ctx& ka, const Batch& b, uint32_t views_off,
         break;
       case VM_SCALE: TK_EACH(y = a * y) break;
       case VM_ZERO: TK_EACH(y = 0.0f) break;
+      case VM_SQRT: TK_EACH(y = sqrtf(y)) break;
       default: break;
     }
 #undef TK_EACH

@@ -262,7 +262,7 @@ void validate_program(const Program& p) {
       if (v.shape[i] != 1 && v.shape[i] != out[off + i]) raise(TK_E_SHAPE, "incompatible broadcast dimensions");
   };
   static const std::set<std::string> pointwise = {"add", "sub", "mul", "div", "neg", "relu", "pow",
-                                                  "threshold_backward", "full", "cast"};
+                                                  "threshold_backward", "full", "cast", "sqrt"};
   for (auto& op : p.ops) {
     check_spec(op.out);
     if (op.out.dtype == DT_I8) raise(TK_E_DTYPE, "operations produce float values only: " + op.name);
@@ -276,7 +276,7 @@ void validate_program(const Program& p) {
       const_cast<Op&>(op).cls = OC_POINTWISE;
       for (auto& a : op.args)
         if (!a.scalar) check_broadcast(a.spec, op.out.shape);
-      if ((c == "neg" || c == "relu" || c == "cast") && n != 1) raise(TK_E_ARG, c + " takes one operand");
+      if ((c == "neg" || c == "relu" || c == "cast" || c == "sqrt") && n != 1) raise(TK_E_ARG, c + " takes one operand");
       if ((c == "add" || c == "sub" || c == "mul" || c == "div" || c == "threshold_backward") && n != 2)
         raise(TK_E_ARG, c + " takes two operands");
       if (c == "pow") {

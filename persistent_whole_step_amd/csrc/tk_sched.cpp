@@ -86,7 +86,7 @@ struct Entry {            // one scheduled (materialized) unit
   std::vector<std::string> reads_vals;    // materialized values read
   std::set<std::string> reads_inputs;     // input buffers read (through inline)
   std::set<std::string> writes_vals;      // values written
-  int writes_input = -1;                  // input index written (direct in-place / commit)
+  std::vector<int> writes_inputs;         // input indices written (direct in-place / commit)
   int order = 0;
 };
 
@@ -195,10 +195,41 @@ struct Builder {
     }
   }
 
+  // A value computed by pointwise ops from inputs and scalars alone: any task
+  // can evaluate (or read) it, whatever its place in program order.
+  bool input_pure(const std::string& b) const {
+    if (is_input(b)) return true;
+    const int j = prod(b);
+    if (j < 0 || op(j).cls != OC_POINTWISE || output_bufs.count(b)) return false;
+    for (auto& a : op(j).args)
+      if (!a.scalar && !input_pure(a.spec.buf)) return false;
+    return true;
+  }
+
+  // Whether a view can be read over the flattened output space of a
+  // reduction root (rank other than one): the root's own shape, contiguous,
+  // or one element broadcast.
+  static bool flattenable(const Spec& s, const std::vector<int64_t>& shape) {
+    return (s.shape == shape && s.contiguous()) || s.numel() == 1 ||
+           std::all_of(s.strides.begin(), s.strides.end(), [](int64_t v) { return v == 0; });
+  }
+
+  // Pass 2 ("side epilogues"): a contraction tile or a reduction's finishing
+  // program also evaluates pointwise descendants of its result over the same
+  // index space and writes those that are returned or read elsewhere.
+  // Additions of this design: a derived value read by an op outside the tile
+  // is written too (to its usual home), so the pointwise stage that would
+  // recompute it disappears; reductions are roots as well as contractions;
+  // returned in-place values (parameter and optimizer-state updates) may be
+  // descendants, committed directly when the in-place proof holds; operands
+  // that are pure functions of inputs may come later in program order.
   void pass2() {
     for (int mi = 0; mi < (int)P.ops.size(); ++mi) {
       const Op& mm = op(mi);
-      if (!is_contraction(mi) || fused.count(mi) || skip.count(mi)) continue;
+      const bool red = mm.cls == OC_REDUCE;
+      if ((!is_contraction(mi) && !red) || fused.count(mi) || skip.count(mi)) continue;
+      const std::vector<int64_t>& rshape = mm.out.shape;
+      const bool flat = red && rshape.size() != 1;
       std::set<std::string> known = {mm.out.buf};
       std::vector<int> chain;
       for (int j = mi + 1; j < (int)P.ops.size(); ++j) {
@@ -208,14 +239,16 @@ struct Builder {
         for (auto& a : nx.args)
           if (!a.scalar && known.count(a.spec.buf)) touches = true;
         if (!touches) continue;
-        if (nx.out.shape != mm.out.shape || aliased.count(nx.out.buf)) continue;
+        if (nx.out.shape != rshape) continue;
+        if (aliased.count(nx.out.buf) && !O.fuse_updates) continue;
         bool ok = true;
         for (auto& a : nx.args) {
           if (a.scalar) continue;
           if (known.count(a.spec.buf)) {
-            if (!identity_view(a.spec, mm.out.shape)) ok = false;
-          } else if (prod(a.spec.buf) >= mi) {
-            ok = false;
+            if (!identity_view(a.spec, rshape)) ok = false;
+          } else {
+            if (prod(a.spec.buf) >= mi && !input_pure(a.spec.buf)) ok = false;
+            if (flat && !flattenable(a.spec, rshape)) ok = false;
           }
         }
         if (!ok) continue;
@@ -227,10 +260,6 @@ struct Builder {
       std::set<std::string> returned;
       for (auto& d : derived)
         if (output_bufs.count(d)) returned.insert(d);
-      // Addition of this design: a derived value read by an op outside the
-      // candidate chain is also written by the tile (to its usual home), so
-      // the pointwise stage that would recompute it from the stored root
-      // disappears; later readers see the same value in the same place.
       std::set<std::string> chain_outs;
       for (int c : chain) chain_outs.insert(op(c).out.buf);
       std::set<std::string> escaping;
@@ -261,7 +290,9 @@ struct Builder {
           if (!dkept.count(op(u).out.buf)) ok = false;
       }
       // returned values must be bindable straight into their output buffer
+      // (in-place values are committed directly or staged instead)
       for (auto& r : returned) {
+        if (aliased.count(r)) continue;
         bool bindable = false;
         for (int s = 0; s < n_out; ++s) {
           const Spec& o2 = P.outputs[s];
@@ -271,7 +302,6 @@ struct Builder {
         }
         if (!bindable) ok = false;
       }
-      if ((int)kept.size() + 1 > kMaxSlots - 1) ok = false;  // slot budget of the tile program
       if (!ok) continue;
       Entry e;
       e.op = mi;
@@ -280,36 +310,163 @@ struct Builder {
       for (int u : users[mm.out.buf])
         if (!dkept.count(op(u).out.buf)) root_only_chain = false;
       e.discard_root = root_only_chain;
+      // the side program must fit the machine's slots
+      std::set<std::string> ext;
+      for (int j = 0; j < (int)P.ops.size(); ++j)
+        if (!skip.count(j) && !dkept.count(op(j).out.buf) && inlinable(j)) ext.insert(op(j).out.buf);
+      if (!plan_side(e, ext).ok) continue;
       fused[mi] = e;
       for (int c : kept) skip.insert(c);
     }
   }
 
+  // ------------------------------------------------------- side programs --
+  // A side program runs after the root value (a tile's or a reduction's
+  // result) is in the accumulator.  A side value that is not stored and has
+  // exactly one reader among the side ops is expanded into that reader's
+  // expression; the others are evaluated in program order, stored when
+  // written to storage, and held in a slot while later side ops read them.
+  struct SidePlan {
+    std::vector<int> evals;               // side ops evaluated in turn
+    std::set<std::string> expanded;       // side values expanded into their reader
+    std::map<std::string, int> slot;      // held value -> slot
+    std::vector<int> temp_base;           // per eval: first slot free for temporaries
+    std::map<int, int> pos;               // side op -> eval index where its value is computed
+    int slots = 0;                        // slots used, temporaries included
+    bool ok = true;
+  };
+
+  // Temporaries an operand's expression needs (Sethi-Ullman numbering for the
+  // accumulator machine); `simple` when it is one load.
+  int need_arg(const Arg& a, const std::set<std::string>& held, const std::set<std::string>& expand,
+               const std::set<std::string>& inl, bool& simple) const {
+    simple = true;
+    if (a.scalar || held.count(a.spec.buf)) return 0;
+    if (expand.count(a.spec.buf) || inl.count(a.spec.buf)) {
+      simple = false;
+      return need_op(prod(a.spec.buf), held, expand, inl);
+    }
+    return 0;
+  }
+  int need_op(int j, const std::set<std::string>& held, const std::set<std::string>& expand,
+              const std::set<std::string>& inl) const {
+    const Op& o2 = op(j);
+    if (o2.opcode == "full" || o2.args.empty()) return 0;
+    bool sx = true, sy = true;
+    const int nx = need_arg(o2.args[0], held, expand, inl, sx);
+    const bool binary = o2.opcode == "add" || o2.opcode == "sub" || o2.opcode == "mul" || o2.opcode == "div" ||
+                        o2.opcode == "threshold_backward";
+    if (!binary) return nx;
+    const int ny = need_arg(o2.args[1], held, expand, inl, sy);
+    if (sy) return nx;
+    if (sx) return ny;
+    return ny > nx ? std::max(ny, 1 + nx) : std::max(nx, 1 + ny);
+  }
+
+  // Held values (root and evaluated side values) an expression reads.
+  void held_refs(int j, const std::set<std::string>& expand, const std::set<std::string>& inl,
+                 const std::set<std::string>& holdable, std::set<std::string>& out) const {
+    for (auto& a : op(j).args) {
+      if (a.scalar) continue;
+      const std::string& b = a.spec.buf;
+      if (holdable.count(b))
+        out.insert(b);
+      else if (expand.count(b) || inl.count(b))
+        held_refs(prod(b), expand, inl, holdable, out);
+    }
+  }
+
+  SidePlan plan_side(const Entry& e, const std::set<std::string>& inl) const {
+    SidePlan sp;
+    const std::string root = op(e.op).out.buf;
+    std::map<std::string, int> readers;
+    for (int c : e.side)
+      for (auto& a : op(c).args)
+        if (!a.scalar) readers[a.spec.buf]++;
+    for (int c : e.side) {
+      const std::string& b = op(c).out.buf;
+      if (!side_stored(e, c) && readers[b] == 1)
+        sp.expanded.insert(b);
+      else
+        sp.evals.push_back(c);
+    }
+    std::set<std::string> holdable = {root};
+    for (int c : sp.evals) holdable.insert(op(c).out.buf);
+    std::map<std::string, int> last_use;
+    std::vector<std::set<std::string>> refs(sp.evals.size());
+    for (size_t i = 0; i < sp.evals.size(); ++i) {
+      held_refs(sp.evals[i], sp.expanded, inl, holdable, refs[i]);
+      for (auto& v : refs[i]) last_use[v] = (int)i;
+    }
+    // where each expanded value is computed: inside its reader's evaluation
+    std::function<int(const std::string&)> at = [&](const std::string& b) -> int {
+      for (size_t i = 0; i < sp.evals.size(); ++i)
+        if (op(sp.evals[i]).out.buf == b) return (int)i;
+      for (int c : e.side)
+        for (auto& a : op(c).args)
+          if (!a.scalar && a.spec.buf == b) return at(op(c).out.buf);
+      return (int)sp.evals.size();
+    };
+    for (int c : e.side) sp.pos[c] = at(op(c).out.buf);
+    std::map<int, std::string> live;  // slot -> value
+    if (last_use.count(root)) {
+      live[0] = root;
+      sp.slot[root] = 0;
+      sp.slots = 1;
+    }
+    for (size_t i = 0; i < sp.evals.size(); ++i) {
+      std::set<std::string> held;
+      for (auto& kv : live) held.insert(kv.second);
+      const int base = live.empty() ? 0 : live.rbegin()->first + 1;
+      sp.temp_base.push_back(base);
+      sp.slots = std::max(sp.slots, base + need_op(sp.evals[i], held, sp.expanded, inl));
+      for (auto it = live.begin(); it != live.end();)
+        it = last_use[it->second] <= (int)i ? live.erase(it) : std::next(it);
+      const std::string& b = op(sp.evals[i]).out.buf;
+      if (last_use.count(b) && last_use[b] > (int)i) {
+        int s = 0;
+        while (live.count(s)) ++s;
+        live[s] = b;
+        sp.slot[b] = s;
+        sp.slots = std::max(sp.slots, s + 1);
+      }
+    }
+    sp.ok = sp.slots <= kMaxSlots;
+    return sp;
+  }
+
   // ---------------------------------------------------------- inlining --
+  // Whether a pointwise value may be recomputed inside its one reader (or,
+  // for casts of inputs, inside every reader).
+  bool inlinable(int j) const {
+    const Op& o2 = op(j);
+    if (!O.fuse_pointwise || o2.cls != OC_POINTWISE) return false;
+    if (output_bufs.count(o2.out.buf)) return false;
+    bool input_cast = O.inline_input_casts && o2.opcode == "cast" && !o2.args[0].scalar && is_input(o2.args[0].spec.buf);
+    auto rc = refcount.find(o2.out.buf);
+    if (!((rc != refcount.end() && rc->second == 1) || input_cast)) return false;
+    // Readers must see the value through an identity view and must not be
+    // contraction operands (the matrix loaders read storage).
+    auto us = users.find(o2.out.buf);
+    if (us == users.end()) return true;
+    for (int u : us->second) {
+      const Op& uo = op(u);
+      for (size_t ai = 0; ai < uo.args.size(); ++ai) {
+        const Arg& a = uo.args[ai];
+        if (a.scalar || a.spec.buf != o2.out.buf) continue;
+        if (!identity_view(a.spec, o2.out.shape)) return false;
+        if (uo.cls == OC_MM || uo.cls == OC_MM_Q8)
+          if (!(uo.has_bias() && ai == 0)) return false;
+      }
+    }
+    return true;
+  }
+
   void choose_inline() {
     for (int j = 0; j < (int)P.ops.size(); ++j) {
-      const Op& o2 = op(j);
-      if (!O.fuse_pointwise || o2.cls != OC_POINTWISE || skip.count(j)) continue;
-      if (output_bufs.count(o2.out.buf)) continue;
-      bool input_cast = O.inline_input_casts && o2.opcode == "cast" && !o2.args[0].scalar && is_input(o2.args[0].spec.buf);
-      if (!(refcount[o2.out.buf] == 1 || input_cast)) continue;
-      // Readers must see the value through an identity view and must not be
-      // contraction operands (the matrix loaders read storage).
-      bool ok = true;
-      for (int u : users[o2.out.buf]) {
-        const Op& uo = op(u);
-        for (size_t ai = 0; ai < uo.args.size(); ++ai) {
-          const Arg& a = uo.args[ai];
-          if (a.scalar || a.spec.buf != o2.out.buf) continue;
-          if (!identity_view(a.spec, o2.out.shape)) ok = false;
-          if (uo.cls == OC_MM || uo.cls == OC_MM_Q8)
-            if (!(uo.has_bias() && ai == 0)) ok = false;
-        }
-      }
-      if (ok) {
-        inlined.insert(j);
-        inlined_bufs.insert(o2.out.buf);
-      }
+      if (skip.count(j) || !inlinable(j)) continue;
+      inlined.insert(j);
+      inlined_bufs.insert(op(j).out.buf);
     }
   }
 
@@ -370,17 +527,62 @@ struct Builder {
     return op(e.op).out.buf;
   }
 
+  // Whether an entry's side ops write a returned in-place value.
+  bool writes_aliased(const Entry& e) const {
+    for (int c : e.side)
+      if (aliased.count(op(c).out.buf)) return true;
+    return false;
+  }
+
   void build_schedule() {
+    // An entry whose side ops update state in place takes the place of its
+    // last side op in program order (after the readers of the old state), as
+    // the update it absorbs would have.
+    std::map<int, std::vector<Entry>> at;
     for (int j = 0; j < (int)P.ops.size(); ++j) {
       if (fused.count(j)) {
-        sched.push_back(fused[j]);
+        const Entry& f = fused[j];
+        int place = j;
+        if (writes_aliased(f))
+          for (int c : f.side) place = std::max(place, c);
+        at[place].push_back(f);
       } else if (!skip.count(j) && !inlined.count(j)) {
         Entry e;
         e.op = j;
-        sched.push_back(e);
+        at[j].push_back(e);
       }
     }
+    for (auto& kv : at)
+      for (auto& e : kv.second) sched.push_back(e);
     for (size_t i = 0; i < sched.size(); ++i) sched[i].order = (int)i;
+  }
+
+  // Whether entry i reads, directly or through other entries, a value that
+  // entry w writes.
+  bool depends_on(int i, int w) const {
+    std::map<std::string, int> writer;
+    for (size_t k = 0; k < sched.size(); ++k)
+      for (auto& v : written(sched[k])) writer[v] = (int)k;
+    std::vector<int> stack = {i};
+    std::set<int> seen;
+    while (!stack.empty()) {
+      const int k = stack.back();
+      stack.pop_back();
+      if (!seen.insert(k).second) continue;
+      const auto internal = internal_bufs(sched[k]);
+      for (auto* a : entry_args(sched[k])) {
+        if (a->scalar || internal.count(a->spec.buf)) continue;
+        std::vector<std::string> rv;
+        root_values(a->spec, rv);
+        for (auto& v : rv) {
+          auto it = writer.find(v);
+          if (it == writer.end()) continue;
+          if (it->second == w) return true;
+          stack.push_back(it->second);
+        }
+      }
+    }
+    return false;
   }
 
   // Whether a side-epilogue value is written to storage: it is returned, or
@@ -422,7 +624,12 @@ struct Builder {
           if (w == out.buf) owner = (int)i;
       if (owner < 0) continue;
       const Entry& e = sched[owner];
-      if (e.kind != 0 || op(e.op).cls != OC_POINTWISE || !e.chain.empty() || !e.side.empty()) continue;
+      if (e.kind != 0) continue;
+      const bool plain = op(e.op).cls == OC_POINTWISE && e.chain.empty() && e.side.empty();
+      int writer_op = -1;
+      for (int c : e.side)
+        if (op(c).out.buf == out.buf) writer_op = c;
+      if (!plain && writer_op < 0) continue;
       if (output_count[out.buf] != 1) continue;
       if (out.offset != 0 || !out.contiguous()) continue;
       bool named = false;
@@ -435,8 +642,29 @@ struct Builder {
           if (!a->scalar && raw_inputs(a->spec).count(target)) later = true;
       if (later) continue;
       bool ident = true;
-      for (auto& a : op(e.op).args)
-        if (!a.scalar && !identity_access(a.spec, target, out.shape)) ident = false;
+      if (plain) {
+        for (auto& a : op(e.op).args)
+          if (!a.scalar && !identity_access(a.spec, target, out.shape)) ident = false;
+      } else {
+        // The root's own operands never see the target; side ops read it
+        // element for element, and none after the one that overwrites it.
+        for (auto& a : op(e.op).args)
+          if (!a.scalar && raw_inputs(a.spec).count(target)) ident = false;
+        const SidePlan sp = plan_side(e, inlined_bufs);
+        for (int c : e.side)
+          for (auto& a : op(c).args) {
+            if (a.scalar || !raw_inputs(a.spec).count(target)) continue;
+            if (!identity_access(a.spec, target, out.shape) || sp.pos.at(c) > sp.pos.at(writer_op)) ident = false;
+          }
+        // and no earlier reader of the target waits for this entry's values
+        for (size_t i = 0; ident && i < sched.size(); ++i) {
+          if ((int)i == owner) continue;
+          bool reads = false;
+          for (auto* a : entry_args(sched[i]))
+            if (!a->scalar && raw_inputs(a->spec).count(target)) reads = true;
+          if (reads && depends_on((int)i, owner)) ident = false;
+        }
+      }
       if (!ident) continue;
       direct[slot] = tidx;
     }
@@ -516,7 +744,7 @@ struct Builder {
     // every returned side-epilogue value must be bound (pass 2 checked bindability)
     for (auto& e : sched)
       for (int c : e.side)
-        if (output_bufs.count(op(c).out.buf) && !bound.count(op(c).out.buf))
+        if (output_bufs.count(op(c).out.buf) && !aliased.count(op(c).out.buf) && !bound.count(op(c).out.buf))
           raise(TK_E_UNSUPPORTED, "internal: side epilogue without a direct output binding");
   }
 
@@ -528,7 +756,7 @@ struct Builder {
         Entry c;
         c.kind = 2;
         c.slot = s;
-        c.writes_input = P.inplace.at(s);
+        c.writes_inputs = {P.inplace.at(s)};
         sched.push_back(c);
         continue;
       }
@@ -555,8 +783,9 @@ struct Builder {
           e.reads_inputs.insert(r.begin(), r.end());
         }
         for (auto& w : written(e)) e.writes_vals.insert(w);
+        e.writes_inputs.clear();
         for (auto& kv : direct)
-          if (e.writes_vals.count(P.outputs[kv.first].buf)) e.writes_input = kv.second;
+          if (e.writes_vals.count(P.outputs[kv.first].buf)) e.writes_inputs.push_back(kv.second);
       } else {
         const Spec& o2 = P.outputs[e.slot];
         if (is_input(o2.buf))
@@ -583,8 +812,8 @@ struct Builder {
           if (it == writer.end()) raise(TK_E_ARG, "internal: value '" + v + "' has no writer");
           if ((size_t)it->second != i) L = std::max(L, sched[it->second].avail() + 1);
         }
-        if (e.writes_input >= 0) {
-          const std::string& t = P.inputs[e.writes_input].buf;
+        for (int wi : e.writes_inputs) {
+          const std::string& t = P.inputs[wi].buf;
           for (size_t r = 0; r < sched.size(); ++r)
             if (r != i && sched[r].reads_inputs.count(t)) L = std::max(L, sched[r].avail() + 1);
         }
@@ -703,7 +932,19 @@ struct Builder {
     std::vector<int64_t> space;  // task iteration shape (uncollapsed)
     std::vector<DView> vtab;     // views over `space` (uncollapsed, rank = space.size())
     std::map<std::string, int> slot_of;  // tile values held in slots
+    std::set<std::string> expand;        // side values expanded into their reader
+    const std::vector<int64_t>* flat = nullptr;  // read views over this shape flattened to 1-D
   };
+
+  // A view as read over a flattened 1-D task space (see flattenable).
+  static Spec flat_view(const Spec& s, const std::vector<int64_t>& shape) {
+    Spec f = s;
+    int64_t n = 1;
+    for (auto d : shape) n *= d;
+    f.shape = {n};
+    f.strides = {(s.shape == shape && s.contiguous() && s.numel() != 1) ? 1 : 0};
+    return f;
+  }
 
   // A view of stored data over the task space: dims map[i] of the reading
   // op's space go to task dims (or -1: broadcast to coordinate 0).
@@ -754,7 +995,7 @@ struct Builder {
       n.slot = sl->second;
       return n;
     }
-    if (inlined_bufs.count(a.spec.buf)) {
+    if (cx.expand.count(a.spec.buf) || inlined_bufs.count(a.spec.buf)) {
       // identity view of the producer: its dims align with the view's dims
       std::vector<int> pm(a.spec.shape.size());
       const size_t r = a.spec.shape.size(), R = map.size();
@@ -763,7 +1004,8 @@ struct Builder {
     }
     n.kind = Node::LEAF;
     n.view = (int)cx.vtab.size();
-    cx.vtab.push_back(lift(a.spec, map, storage_of(a.spec.buf), cx.space.size()));
+    const Spec v = cx.flat ? flat_view(a.spec, *cx.flat) : a.spec;
+    cx.vtab.push_back(lift(v, map, storage_of(a.spec.buf), cx.space.size()));
     return n;
   }
 
@@ -777,6 +1019,22 @@ struct Builder {
   }
 
   static bool simple(const Node& n) { return n.kind != Node::OP; }
+
+  // Temporaries the accumulator machine needs for a node (Sethi-Ullman).
+  int node_need(const Node& n) const {
+    if (simple(n)) return 0;
+    const Op& o2 = op(n.op);
+    if (o2.opcode == "full" || n.kids.empty()) return 0;
+    const bool binary = o2.opcode == "add" || o2.opcode == "sub" || o2.opcode == "mul" || o2.opcode == "div" ||
+                        o2.opcode == "threshold_backward";
+    const int nx = node_need(n.kids[0]);
+    if (!binary) return nx;
+    const Node &x = n.kids[0], &y = n.kids[1];
+    const int ny = node_need(y);
+    if (simple(y)) return nx;
+    if (simple(x)) return ny;
+    return ny > nx ? std::max(ny, 1 + nx) : std::max(nx, 1 + ny);
+  }
 
   void emit_load(std::vector<DIns>& code, const Node& n) {
     DIns d{};
@@ -826,6 +1084,7 @@ struct Builder {
     }
     if (c == "neg") return unary(VM_NEG, 0);
     if (c == "relu") return unary(VM_RELU, 0);
+    if (c == "sqrt") return unary(VM_SQRT, 0);
     if (c == "cast") {
       emit(code, n.kids[0], free_slot);
       if (rnd != RND_NONE) {
@@ -862,24 +1121,27 @@ struct Builder {
       set_src(d, x);
       d.rev = 1;
     } else {
+      // both operands are expressions: the one needing more temporaries
+      // goes first, the other is computed while it waits in a slot
       if (free_slot >= kMaxSlots) raise(TK_E_UNSUPPORTED, "expression too deep for the tile program");
-      emit(code, x, free_slot);
+      const bool y_first = node_need(y) > node_need(x);
+      emit(code, y_first ? y : x, free_slot);
       DIns sv{};
       sv.op = VM_SAVE;
       sv.arg = (uint16_t)free_slot;
       sv.rnd = RND_NONE;
       code.push_back(sv);
-      emit(code, y, free_slot + 1);
+      emit(code, y_first ? x : y, free_slot + 1);
       d.src = SRC_SLOT;
       d.arg = (uint16_t)free_slot;
-      d.rev = 1;
+      d.rev = y_first ? 0 : 1;
     }
     code.push_back(d);
   }
 
   void emit_store(std::vector<DIns>& code, ExprCtx& cx, const std::string& buf, const std::vector<int>& map) {
     const Spec& pv = op(prod(buf)).out;
-    Spec s = pv;  // contiguous view of the value itself
+    Spec s = cx.flat ? flat_view(pv, *cx.flat) : pv;  // contiguous view of the value itself
     DIns st{};
     st.op = VM_STORE;
     st.rnd = RND_NONE;
@@ -1263,30 +1525,7 @@ struct Builder {
       code.push_back(s);
     }
     if (!e.side.empty()) {
-      // root in slot 0; each descendant computed from tile values
-      DIns sv{};
-      sv.op = VM_SAVE;
-      sv.arg = 0;
-      sv.rnd = RND_NONE;
-      code.push_back(sv);
-      cx.slot_of[mm.out.buf] = 0;
-      if (!e.discard_root) emit_store(code, cx, mm.out.buf, map);
-      int next = 1;
-      for (size_t i = 0; i < e.side.size(); ++i) {
-        int c = e.side[i];
-        Node n = op_node(cx, c, map);
-        emit(code, n, next + 1);
-        const std::string& ob = op(c).out.buf;
-        if (side_stored(e, c)) emit_store(code, cx, ob, map);
-        if (i + 1 < e.side.size()) {
-          DIns s2{};
-          s2.op = VM_SAVE;
-          s2.arg = (uint16_t)next;
-          s2.rnd = RND_NONE;
-          code.push_back(s2);
-          cx.slot_of[ob] = next++;
-        }
-      }
+      emit_side_program(e, cx, code, map);
       return;
     }
     std::string cur = mm.out.buf;
@@ -1304,6 +1543,39 @@ struct Builder {
     }
     cx.slot_of.clear();
     emit_store(code, cx, cur, map);
+  }
+
+  // The root value is in the accumulator: hold it if side ops read it, store
+  // it unless discarded, then evaluate the side ops as plan_side laid out.
+  void emit_side_program(const Entry& e, ExprCtx& cx, std::vector<DIns>& code, const std::vector<int>& map) {
+    const std::string& root = op(e.op).out.buf;
+    const SidePlan sp = plan_side(e, inlined_bufs);
+    if (!sp.ok) raise(TK_E_UNSUPPORTED, "internal: side program of " + op(e.op).name + " exceeds the slot budget");
+    cx.expand = sp.expanded;
+    auto save = [&](int slot) {
+      DIns sv{};
+      sv.op = VM_SAVE;
+      sv.arg = (uint16_t)slot;
+      sv.rnd = RND_NONE;
+      code.push_back(sv);
+    };
+    if (sp.slot.count(root)) {
+      save(0);
+      cx.slot_of[root] = 0;
+    }
+    if (!e.discard_root) emit_store(code, cx, root, map);
+    for (size_t i = 0; i < sp.evals.size(); ++i) {
+      const int c = sp.evals[i];
+      Node n = op_node(cx, c, map);
+      emit(code, n, sp.temp_base[i]);
+      const std::string& ob = op(c).out.buf;
+      if (side_stored(e, c)) emit_store(code, cx, ob, map);
+      auto it = sp.slot.find(ob);
+      if (it != sp.slot.end()) {
+        save(it->second);
+        cx.slot_of[ob] = it->second;
+      }
+    }
   }
 
   DView operand_view(const Spec& s, int d0, int d1) {
@@ -1508,7 +1780,12 @@ struct Builder {
       s.rnd = r.out.dtype;
       fin.push_back(s);
     }
-    {
+    if (!e.side.empty()) {
+      // side ops over the outputs, addressed as one flat index
+      if (r.out.shape.size() != 1) fx.flat = &r.out.shape;
+      emit_side_program(e, fx, fin, {0});
+      for (size_t v = 0; v < fx.vtab.size(); ++v) fx.vtab[v].stride[0] = vstride_full[v][0];
+    } else {
       Spec flat = r.out;
       flat.shape = {rc.rows};
       flat.strides = {1};
@@ -1537,6 +1814,11 @@ struct Builder {
     t.k = (uint32_t)rc.R;
     if (r.opcode == "mean") t.flags |= F_MEAN;
     std::string desc = r.name + " (" + r.opcode + " " + std::to_string(rc.rows) + " outputs over " + std::to_string(rc.R) + ")";
+    if (!e.side.empty()) {
+      desc += " +side";
+      for (int c : e.side) desc += " " + op(c).name;
+      if (e.discard_root) desc += " (root discarded)";
+    }
     if (rc.kind == T_RED_COLS) {
       t.width = (rc.rows % 8 == 0) ? 8 : 1;
       const uint32_t cols_per_item = 32u * t.width;
@@ -1599,7 +1881,8 @@ struct Builder {
       for (auto& t : e.reads_inputs) rd.push_back({input_idx[t], 0, ~0ull});
       for (auto& w : e.writes_vals) wr.push_back(value_region(w));
       if (e.kind != 0) wr.push_back({space_of(n_in + e.slot), 0, ~0ull});
-      if (e.kind == 2) wr.push_back({e.writes_input, 0, ~0ull});
+      if (e.kind == 2)
+        for (int wi : e.writes_inputs) wr.push_back({wi, 0, ~0ull});
       const std::string nm = e.kind == 0 ? op(e.op).name : ("out[" + std::to_string(e.slot) + "]");
       if (e.two_phase) {
         // phase 1 reads the operands and writes fp32 partials; phase 2 reads
@@ -1825,8 +2108,18 @@ struct Builder {
       if (e.kind != 0) continue;
       mat++;
       if (!e.chain.empty() && !e.update) fe++;
-      if (!e.side.empty()) se++;
       if (e.update) fu++;
+      // side programs: those writing other values than in-place updates count
+      // as side epilogues, each directly committed update as a fused update
+      bool other = false;
+      for (int c : e.side) {
+        const std::string& b = op(c).out.buf;
+        if (!aliased.count(b) && side_stored(e, c)) other = true;
+        if (aliased.count(b))
+          for (auto& kv : direct)
+            if (P.outputs[kv.first].buf == b) fu++;
+      }
+      if (other) se++;
     }
     s.materialized_ops = mat;
     s.fused_epilogues = fe;

@@ -259,6 +259,12 @@ SMALL = {
     "c3s": dict(kind="gemv", k=1024, n=1024, layers=3),
     "c4s": dict(kind="mlp", dims=(256, 384, 256, 128), batch=160, dtype="bf16", lr=1e-4),
     "c5s": dict(kind="residual", width=256, layers=4, batch=96, dtype="f16", lr=1e-4),
+    # AdamW in place of SGD: two float32 states per parameter, updated in place
+    "c1a": dict(programs.CONFIGS["c1"], optimizer=programs.AdamW()),
+    "c2sa": dict(kind="mlp", dims=(192, 320, 256, 48), batch=96, dtype="bf16", lr=1e-3,
+                 optimizer=programs.AdamW(), adam_t=5),
+    "c5sa": dict(kind="residual", width=256, layers=4, batch=96, dtype="f16", lr=1e-4,
+                 optimizer=programs.AdamW(weight_decay=0.1), adam_t=2),
 }
 
 

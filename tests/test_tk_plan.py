@@ -42,18 +42,80 @@ def test_plan_only_compile_of_workloads(name):
     assert "stage 0:" in prog.dump()
 
 
+@pytest.mark.parametrize("name", ["c1", "c2", "c4", "c5"])
+def test_plan_only_compile_with_adamw(name):
+    cfg = dict(programs.CONFIGS[name], optimizer=programs.AdamW())
+    p = programs.build(cfg)
+    q = tk.compile(p.text(), device=-1).query()
+    # parameter, first and second moment of every parameter committed in place
+    assert len(p.inplace) == len(p.inputs) - 4  # inputs: x, t, params, (m, v) per param, c1, c2
+    assert q["direct_state_commits"] == len(p.inplace)
+    assert q["staged_commits"] == 0
+    assert q["grid_barriers"] == q["n_stages"] - 1
+
+
 def test_mlp_schedule_decisions():
     p = programs.build(programs.CONFIGS["c1"])
     q = tk.compile(p.text(), device=-1).query()
     # addmm + sub(d) chain, gm + threshold_backward chain: two epilogue fusions;
     # the first layer's relu is written by its addmm tile (side epilogue: both
     # the pre-activation and the activation are read later); every weight
-    # update folds into its gradient tile; pow is inlined into mean
+    # update folds into its gradient tile and every bias update into the
+    # finishing program of its batch sum; pow is inlined into mean
     assert q["fused_epilogues"] == 2
     assert q["side_epilogues"] == 1
-    assert q["fused_updates"] == 2
+    assert q["fused_updates"] == 4
     assert q["inlined_ops"] == 1
-    assert q["n_stages"] == 6
+    assert q["n_stages"] == 5
+
+
+def test_adamw_update_folds_like_sgd():
+    # the whole AdamW update (two states and the parameter, all in place) is
+    # evaluated by the gradient's tile or the bias sum's finishing program:
+    # the step keeps SGD's stage count
+    for name in ("c1", "c2"):
+        sgd = tk.compile(programs.build(programs.CONFIGS[name]).text(), device=-1).query()
+        p = programs.build(dict(programs.CONFIGS[name], optimizer=programs.AdamW()))
+        q = tk.compile(p.text(), device=-1).query()
+        assert q["n_stages"] == sgd["n_stages"]
+        assert q["fused_updates"] == len(p.inplace) == 3 * sgd["fused_updates"]
+        assert q["materialized_ops"] == sgd["materialized_ops"]
+
+
+def _tile_update(later_read: bool):
+    p = Program()
+    a = p.input("a", "f32", (8, 8))
+    b = p.input("b", "f32", (8, 8))
+    W = p.input("W", "f32", (8, 8))
+    g = p.op("mm", [a, b], "f32", (8, 8))
+    Wn = p.op("sub", [W, g], "f32", alpha=0.5)
+    if later_read:
+        # reads the old W after the update in program order, from the same tile
+        y = p.op("mul", [W, g], "f32")
+        p.output(y)
+    p.output(Wn, inplace_of=W)
+    return p
+
+
+def test_tile_update_commits_directly():
+    q = tk.compile(_tile_update(False).text(), device=-1).query()
+    assert q["direct_state_commits"] == 1 and q["fused_updates"] == 1 and q["n_stages"] == 1
+
+
+def test_tile_update_staged_when_tile_reads_target_after_store():
+    q = tk.compile(_tile_update(True).text(), device=-1).query()
+    assert q["direct_state_commits"] == 0 and q["staged_commits"] == 1
+
+
+def test_tile_update_staged_when_contraction_reads_target():
+    # the tile's own operand is the target: the update cannot overwrite it
+    p = Program()
+    a = p.input("a", "f32", (8, 8))
+    W = p.input("W", "f32", (8, 8))
+    g = p.op("mm", [a, W], "f32", (8, 8))
+    p.output(p.op("sub", [W, g], "f32", alpha=0.5), inplace_of=W)
+    q = tk.compile(p.text(), device=-1).query()
+    assert q["direct_state_commits"] == 0 and q["staged_commits"] == 1
 
 
 def test_side_epilogue_stores_values_read_later():
