@@ -7,9 +7,9 @@ benchmark set: the default workload is the 3-layer bf16 MLP (batch 256,
 512 -> 1024 -> 1024 -> 64, lr 1e-3).  Inputs are seeded synthetic tensors
 already resident in HBM; parameters are updated in place every step (state
 feedback) and the (x, target) batch rotates over 4 resident batches.  The
-other workloads (2-layer fp32 MLP, int8-weight GEMV stack rotating 3 weight
-sets, 4096-wide bf16 MLP, 16-layer fp16 residual MLP) are timed briefly and
-reported under "others".
+other workloads (2-layer fp32 MLP, the default MLP with AdamW in place of
+SGD, int8-weight GEMV stack rotating 3 weight sets, 4096-wide bf16 MLP,
+16-layer fp16 residual MLP) are timed briefly and reported under "others".
 
 Prints one JSON line on stdout.  --gpus N with N > 1 is refused: this
 build runs on one GPU.
@@ -35,7 +35,17 @@ WORKLOAD_NAMES = {
     "c3": "gemv8-int8w-bf16x-4096x4096",
     "c4": "mlp3-bf16-b1024-4096-4096-4096-1024",
     "c5": "resmlp16-fp16-b512-w2048",
+    "c2a": "mlp3-bf16-b256-512-1024-1024-64-adamw",
 }
+
+
+def config(name: str) -> dict:
+    """The workload's configuration; c2a is C2 with AdamW (defaults 0.9,
+    0.999, 1e-8, weight decay 1e-2) in place of SGD, at step t = 10."""
+    from persistent_whole_step_amd import programs
+    if name == "c2a":
+        return dict(programs.CONFIGS["c2"], optimizer=programs.AdamW(), adam_t=10)
+    return programs.CONFIGS[name]
 
 
 def log(*a):
@@ -65,7 +75,7 @@ class Runner:
         from persistent_whole_step_amd import programs, tk
         to_torch = tk.tensor_from_storage
         self.name = name
-        self.cfg = programs.CONFIGS[name]
+        self.cfg = config(name)
         self.prog = programs.build(self.cfg)
         self.p = tk.compile(self.prog.text(), device=0, **opts)
         self.stats = self.p.query()
@@ -228,7 +238,7 @@ def cpu_baseline(name: str, seconds: float):
     """The oracle, as it stands, on the same workload: whole steps until `seconds` pass."""
     from oracle import oracle
     from persistent_whole_step_amd import programs
-    cfg = programs.CONFIGS[name]
+    cfg = config(name)
     prog = programs.build(cfg)
     text = prog.text()
     ins = programs.inputs_for(cfg, 0)
@@ -250,7 +260,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--others", default="c1,c3,c4,c5", help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--others", default="c1,c2a,c3,c4,c5", help="comma list of extra workloads ('' for none)")
     ap.add_argument("--other-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")

@@ -86,7 +86,8 @@ typedef struct {
                                   cooperative launches.  If other work keeps a CU busy, the
                                   grid barrier's bounded wait turns a stall into an abort
                                   (tk_workspace_status), never a hang. */
-  int32_t reserved[3];
+  int32_t gemm_tile;           /* 0: automatic; 1: force 128x128 MFMA tiles; 2: force 64x64 */
+  int32_t reserved[2];
 } tk_options;
 
 /* Plan and kernel statistics (pages: `GeneratedKernel` and `resource_usage`). */

@@ -880,32 +880,60 @@ DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off
   LDS float* xs = (LDS float*)g_smem;
   const bool staged = (uint64_t)K * 4 + 64 <= (uint64_t)kSmemBytes;
   const uint32_t row0 = item * 16 + wave * 4;
-  const bool vec = staged && Q.stride[1] == 1;
+  // Fast form (uniform per task): contiguous int8 rows, 16-byte aligned
+  // chunk starts, K a multiple of 16.  Every load is then issued
+  // unconditionally from a clamped in-bounds address, so all sixteen chunks
+  // of a lane are in flight at once; lanes past the end mask the weights
+  // when they use them.
+  const bool fast = staged && Q.stride[1] == 1 && K % 16 == 0 && (Q.offset & 15) == 0 && (Q.stride[0] & 15) == 0 &&
+                    aligned16(pq);
   constexpr int NC = 4;  // chunks per lane per pass (4096 columns)
   float acc[4] = {0, 0, 0, 0};
   for (uint32_t kpass = 0; kpass < K; kpass += 1024 * NC) {
     u32x4 qv[4][NC];
     float sv[4][NC];
+    uint32_t okm = 0;  // bit r * NC + j: chunk (r, j) exists
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const uint32_t row = row0 + r;
-      const int64_t qrow = Q.offset + (int64_t)row * Q.stride[0];
-      const int64_t srow = S.offset + (int64_t)row * S.stride[0];
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const uint32_t kc = kpass + 1024 * j + lane * 16;
-        const bool ok = row < t.n && kc < K;
-        const int64_t qidx = qrow + (int64_t)kc * Q.stride[1];
-        if (ok && vec && kc + 16 <= K && aligned16(pq + qidx)) {
-          qv[r][j] = *(const GLOBAL u32x4*)(pq + qidx);
-        } else {
+        okm |= (row < t.n && kc < K ? 1u : 0u) << (r * NC + j);
+      }
+    }
+    if (fast) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t row = row0 + r < t.n ? row0 + r : 0;
+        const int64_t qrow = Q.offset + (int64_t)row * Q.stride[0];
+        const int64_t srow = S.offset + (int64_t)row * S.stride[0];
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          const uint32_t kc0 = kpass + 1024 * j + lane * 16;
+          const uint32_t kc = kc0 < K ? kc0 : 0;
+          qv[r][j] = *(const GLOBAL u32x4*)(pq + qrow + kc);
+          // a 16-wide chunk starting at a multiple of 16 lies inside one 32-block
+          sv[r][j] = ps[srow + (int64_t)(kc / 32) * S.stride[1]];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const uint32_t row = row0 + r;
+        const int64_t qrow = Q.offset + (int64_t)row * Q.stride[0];
+        const int64_t srow = S.offset + (int64_t)row * S.stride[0];
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          const uint32_t kc = kpass + 1024 * j + lane * 16;
+          const bool ok = (okm >> (r * NC + j)) & 1u;
+          const int64_t qidx = qrow + (int64_t)kc * Q.stride[1];
           uint32_t w[4] = {0, 0, 0, 0};
           for (int e = 0; e < 16; ++e)
             if (ok && kc + e < K) w[e / 4] |= ((uint32_t)(uint8_t)pq[qidx + (int64_t)e * Q.stride[1]]) << (8 * (e % 4));
           qv[r][j] = u32x4{w[0], w[1], w[2], w[3]};
+          sv[r][j] = ok ? ps[srow + (int64_t)(kc / 32) * S.stride[1]] : 0.0f;
         }
-        // a 16-wide chunk starting at a multiple of 16 lies inside one 32-block
-        sv[r][j] = ok ? ps[srow + (int64_t)(kc / 32) * S.stride[1]] : 0.0f;
       }
     }
     if (kpass == 0 && staged) {
@@ -922,14 +950,23 @@ DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off
       for (int e = 0; e < 16; ++e)
         xk[e] = (kc + e < K) ? (staged ? xs[kc + e] : load_elem(px, X.dtype, X.offset + (int64_t)(kc + e) * X.stride[1]))
                              : 0.0f;
+      // q = b - 128 with b = q ^ 0x80 an unsigned byte (converted by the
+      // byte-select conversions), so the chunk's dot product is
+      // sum(x b) - 128 sum(x), scaled once by the block scale
+      float xsum = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) xsum = xsum + xk[e];
+      const float xoff = 128.0f * xsum;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
+        float d = 0.0f;
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int32_t qj = (int32_t)(qv[r][j][e / 4] << (24 - 8 * (e % 4))) >> 24;
-          const float w = (float)qj * sv[r][j];
-          acc[r] = __builtin_fmaf(xk[e], w, acc[r]);
+        for (int w4 = 0; w4 < 4; ++w4) {
+          const uint32_t u = qv[r][j][w4] ^ 0x80808080u;
+#pragma unroll
+          for (int by = 0; by < 4; ++by) d = __builtin_fmaf(xk[4 * w4 + by], (float)((u >> (8 * by)) & 0xffu), d);
         }
+        acc[r] = __builtin_fmaf(sv[r][j], d - xoff, acc[r]);
       }
     }
   }
@@ -1181,6 +1218,21 @@ DEV bool fill(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, uin
       fin_batch(b, t, ins_off, 1);
       const GLOBAL float* P = ws_f32(ka, t.scratch);
       const bool cols_layout = (t.tile & 1) != 0;  // [parts][rows] instead of [rows][parts]
+      if (t.flags & F_ROWWG) {
+        // output `item`: thread t sums parts t, t + 256, ... in order, then a
+        // fixed-order block sum
+        const uint32_t r = item;
+        float a = 0.0f;
+        for (uint32_t p = tid; p < t.split; p += kBlock)
+          a = a + (cols_layout ? P[(uint64_t)p * t.m + r] : P[(uint64_t)r * t.split + p]);
+        const float total = block_sum(tid, a);
+        if (tid == 0) {
+          live = 1;
+          xe(tid, 0) = r;
+          xv(tid, 0) = total;
+        }
+        return true;
+      }
       const uint32_t row = item * kBlock + tid;
       if (row < t.m) {
         float a = 0.0f;

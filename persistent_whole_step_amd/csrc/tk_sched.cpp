@@ -1197,7 +1197,49 @@ struct Builder {
     if (views.size() > 65000) raise(TK_E_UNSUPPORTED, "too many operand views");
     return first;
   }
+  // Value-preserving clean-up of a program: an identity scale (1 * acc, no
+  // rounding) goes, a reload of the slot just saved goes (the accumulator
+  // still holds it), and a save nobody reads before the slot is overwritten
+  // goes.  Every instruction the machine runs costs a dispatch.
+  static void peephole(std::vector<DIns>& code) {
+    for (bool changed = true; changed;) {
+      changed = false;
+      for (size_t i = 0; i < code.size(); ++i) {
+        const DIns& d = code[i];
+        if (d.op == VM_SCALE && d.a == 1.0f && d.rnd == RND_NONE && d.src == SRC_NONE) {
+          code.erase(code.begin() + i);
+          changed = true;
+          break;
+        }
+        if (d.op == VM_SAVE && i + 1 < code.size()) {
+          const DIns& n = code[i + 1];
+          if (n.op == VM_LOAD && n.src == SRC_SLOT && n.arg == d.arg && n.rnd == RND_NONE) {
+            code.erase(code.begin() + i + 1);
+            changed = true;
+            break;
+          }
+        }
+        if (d.op == VM_SAVE) {
+          bool read = false;
+          for (size_t j = i + 1; j < code.size(); ++j) {
+            if (code[j].src == SRC_SLOT && code[j].arg == d.arg && code[j].op != VM_SAVE && code[j].op != VM_STORE) {
+              read = true;
+              break;
+            }
+            if (code[j].op == VM_SAVE && code[j].arg == d.arg) break;
+          }
+          if (!read) {
+            code.erase(code.begin() + i);
+            changed = true;
+            break;
+          }
+        }
+      }
+    }
+  }
+
   uint32_t commit_code(std::vector<DIns>& code, uint32_t view_base) {
+    peephole(code);
     uint32_t first = (uint32_t)ins.size();
     for (auto d : code) {
       if (d.src == SRC_VIEW || d.op == VM_STORE) d.arg = (uint16_t)(d.arg + view_base);
@@ -1237,6 +1279,7 @@ struct Builder {
     const int tiles[2][2] = {{128, 128}, {64, 64}};
     const double eff[2] = {1.0, 0.55};
     for (int t = 0; t < 2; ++t) {
+      if (O.gemm_tile > 0 && t != O.gemm_tile - 1) continue;
       const int bm = tiles[t][0], bn = tiles[t][1];
       const int64_t tm = (m + bm - 1) / bm, tn = (n + bn - 1) / bn;
       for (int S : {1, 2, 4, 8}) {
@@ -1842,6 +1885,12 @@ struct Builder {
       f.flags = t.flags & F_MEAN;
       f.tile = rc.kind == T_RED_COLS ? 1 : 0;  // partial layout: [parts][rows] (cols) or [rows][parts]
       f.n_items = (uint32_t)((rc.rows + kBlock - 1) / kBlock);
+      if (rc.rows <= 32 && rc.parts >= 32) {
+        // few outputs over many parts: a workgroup per output loads the parts
+        // at once instead of one thread walking them
+        f.flags |= F_ROWWG;
+        f.n_items = (uint32_t)rc.rows;
+      }
       put(e.level + 1, f, desc + " [combine]");
     } else {
       put(e.level, t, desc);

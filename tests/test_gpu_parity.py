@@ -145,7 +145,9 @@ def test_views_broadcast_and_output_copies(oracle_mod):
 @pytest.mark.parametrize("shape,dims,op", [
     ((64, 10), [0], "sum"), ((256, 1024), [0], "sum"), ((1000, 37), [0], "sum"),
     ((640,), None, "mean"), ((300000,), None, "sum"), ((512, 2048), None, "mean"),
-    ((7, 9, 11), [1], "sum"), ((6, 5, 4), [-1, 0], "mean"), ((0, 4), [0], "sum"), ((129, 3), [1], "sum")])
+    ((7, 9, 11), [1], "sum"), ((6, 5, 4), [-1, 0], "mean"), ((0, 4), [0], "sum"), ((129, 3), [1], "sum"),
+    # few outputs over many partials: the combine runs a workgroup per output
+    ((4, 300000), [1], "sum"), ((100000, 8), [0], "mean")])
 def test_reductions(oracle_mod, shape, dims, op):
     say("reduction", shape, dims, op)
     rng = np.random.default_rng(5)
