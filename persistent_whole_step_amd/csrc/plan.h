@@ -20,7 +20,7 @@ enum DType : uint8_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_I8 = 3 };
 constexpr int kBlock = 256;         // threads per workgroup (4 wave64)
 constexpr int kMaxBases = 240;      // pointer slots per launch (inputs, outputs, workspace)
 constexpr int kMaxDims = 4;         // iteration dims after collapsing
-constexpr int kMaxSlots = 4;        // saved values in the expression machine
+constexpr int kMaxSlots = 3;        // saved values in the expression machine (LDS-resident)
 constexpr uint32_t kPlanLds = 16384;       // LDS bytes for the current stage's descriptors (every stage blob fits)
 constexpr uint32_t kMaxGrid = 1024;        // workgroups per launch (barrier flag slots)
 constexpr uint32_t kFlagStride = 16;       // u32 words between two workgroups' flags (64 B)

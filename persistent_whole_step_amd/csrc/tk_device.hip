@@ -60,6 +60,17 @@ __shared__ __attribute__((aligned(16))) uint8_t g_plan[kPlanLds];    // current 
 // the first linear element of each chunk [chunk][thread].
 DEV LDS float& xv(uint32_t tid, int j) { return ((LDS float*)(g_smem + kXvOff))[j * kBlock + tid]; }
 DEV LDS uint32_t& xe(uint32_t tid, int q) { return ((LDS uint32_t*)(g_smem + kXeOff))[q * kBlock + tid]; }
+// Slots of the expression machine live in LDS, laid out like the exchange
+// (element j of thread t at j * kBlock + t, so each thread touches only its
+// own words): slot 0 reuses the value exchange and slot 1 the index exchange
+// (both are read at the start of a batch and rewritten only at its end),
+// slot 2 has a region of its own.  Holding them in registers made every join
+// of the interpreter loop copy them.
+__shared__ __attribute__((aligned(16))) float g_slot2[kVmElems * kBlock];
+static_assert(kMaxSlots == 3, "three LDS slots");
+DEV LDS float* slot_base(uint32_t k) {
+  return k == 0 ? (LDS float*)(g_smem + kXvOff) : k == 1 ? (LDS float*)(g_smem + kXeOff) : (LDS float*)g_slot2;
+}
 static_assert(kXeOff + kVmElems * kBlock * 4 == kArenaBytes, "arena layout");
 
 // ------------------------------------------------------------ conversions --
@@ -372,7 +383,6 @@ DEV void vm_run(uint32_t tid, const Ctx& ka, const Batch& b, uint32_t views_off,
 #pragma unroll
     for (int j = 0; j < W; ++j) acc[q][j] = xv(tid, q * W + j);
   }
-  float s0[C][W], s1[C][W], s2[C][W], s3[C][W];
   for (uint32_t pc = 0; pc < b.n; ++pc) {
     const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + b.ins + pc * sizeof(DIns));
     const uint32_t w0 = uniform(iw[0]), w1 = uniform(iw[1]);
@@ -402,11 +412,11 @@ DEV void vm_run(uint32_t tid, const Ctx& ka, const Batch& b, uint32_t views_off,
       }
       load_chunks<W, C>(p, dt, vec, s, idx, x);
     } else if (src == SRC_SLOT) {
+      const LDS float* sb = slot_base(arg);
 #pragma unroll
       for (int q = 0; q < C; ++q)
 #pragma unroll
-        for (int j = 0; j < W; ++j)
-          x[q][j] = arg == 0 ? s0[q][j] : arg == 1 ? s1[q][j] : arg == 2 ? s2[q][j] : s3[q][j];
+        for (int j = 0; j < W; ++j) x[q][j] = sb[(q * W + j) * kBlock + tid];
     } else {
       const float k = src == SRC_SCALAR ? sv : 0.0f;
 #pragma unroll
@@ -445,10 +455,11 @@ DEV void vm_run(uint32_t tid, const Ctx& ka, const Batch& b, uint32_t views_off,
         if (rev) { TK_EACH(y = y <= a ? 0.0f : o) }
         else { TK_EACH(y = o <= a ? 0.0f : y) }
         break;
-      case VM_SAVE:
-        TK_EACH(s0[q][j] = arg == 0 ? y : s0[q][j]; s1[q][j] = arg == 1 ? y : s1[q][j];
-                s2[q][j] = arg == 2 ? y : s2[q][j]; s3[q][j] = arg == 3 ? y : s3[q][j])
+      case VM_SAVE: {
+        LDS float* sb = slot_base(arg);
+        TK_EACH(sb[(q * W + j) * kBlock + tid] = y)
         break;
+      }
       case VM_SCALE: TK_EACH(y = a * y) break;
       case VM_ZERO: TK_EACH(y = 0.0f) break;
       case VM_SQRT: TK_EACH(y = sqrtf(y)) break;

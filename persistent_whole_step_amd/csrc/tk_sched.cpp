@@ -330,7 +330,7 @@ struct Builder {
     std::vector<int> evals;               // side ops evaluated in turn
     std::set<std::string> expanded;       // side values expanded into their reader
     std::map<std::string, int> slot;      // held value -> slot
-    std::vector<int> temp_base;           // per eval: first slot free for temporaries
+    std::vector<uint32_t> busy;           // per eval: slots holding values during it
     std::map<int, int> pos;               // side op -> eval index where its value is computed
     int slots = 0;                        // slots used, temporaries included
     bool ok = true;
@@ -416,10 +416,18 @@ struct Builder {
     }
     for (size_t i = 0; i < sp.evals.size(); ++i) {
       std::set<std::string> held;
-      for (auto& kv : live) held.insert(kv.second);
-      const int base = live.empty() ? 0 : live.rbegin()->first + 1;
-      sp.temp_base.push_back(base);
-      sp.slots = std::max(sp.slots, base + need_op(sp.evals[i], held, sp.expanded, inl));
+      uint32_t mask = 0;
+      for (auto& kv : live) {
+        held.insert(kv.second);
+        mask |= 1u << kv.first;
+      }
+      sp.busy.push_back(mask);
+      // temporaries take the lowest free slots: the highest one in use
+      int top = 0, need = need_op(sp.evals[i], held, sp.expanded, inl);
+      for (int k = 0; need > 0 || (mask >> k); ++k)
+        if (mask & (1u << k)) top = k + 1;
+        else if (need > 0) { --need; top = k + 1; }
+      sp.slots = std::max(sp.slots, top);
       for (auto it = live.begin(); it != live.end();)
         it = last_use[it->second] <= (int)i ? live.erase(it) : std::next(it);
       const std::string& b = op(sp.evals[i]).out.buf;
@@ -1057,7 +1065,15 @@ struct Builder {
   }
 
   // Emit code leaving the node's value (rounded to its dtype) in the accumulator.
-  void emit(std::vector<DIns>& code, const Node& n, int free_slot) {
+  // `busy`: slots holding values that must survive; temporaries take the
+  // lowest free slots.
+  static int lowest_free(uint32_t busy) {
+    int k = 0;
+    while (busy & (1u << k)) ++k;
+    return k;
+  }
+
+  void emit(std::vector<DIns>& code, const Node& n, uint32_t busy) {
     if (simple(n)) {
       emit_load(code, n);
       return;
@@ -1068,7 +1084,7 @@ struct Builder {
     DIns d{};
     d.rnd = rnd;
     auto unary = [&](uint8_t vop, float a) {
-      emit(code, n.kids[0], free_slot);
+      emit(code, n.kids[0], busy);
       d.op = vop;
       d.a = a;
       d.src = SRC_NONE;
@@ -1086,7 +1102,7 @@ struct Builder {
     if (c == "relu") return unary(VM_RELU, 0);
     if (c == "sqrt") return unary(VM_SQRT, 0);
     if (c == "cast") {
-      emit(code, n.kids[0], free_slot);
+      emit(code, n.kids[0], busy);
       if (rnd != RND_NONE) {
         DIns r{};
         r.op = VM_SCALE;  // 1 * x is exact; the instruction carries the rounding
@@ -1113,27 +1129,28 @@ struct Builder {
     d.op = vop;
     d.a = a;
     if (simple(y)) {
-      emit(code, x, free_slot);
+      emit(code, x, busy);
       set_src(d, y);
       d.rev = 0;
     } else if (simple(x)) {
-      emit(code, y, free_slot);
+      emit(code, y, busy);
       set_src(d, x);
       d.rev = 1;
     } else {
       // both operands are expressions: the one needing more temporaries
       // goes first, the other is computed while it waits in a slot
-      if (free_slot >= kMaxSlots) raise(TK_E_UNSUPPORTED, "expression too deep for the tile program");
+      const int t = lowest_free(busy);
+      if (t >= kMaxSlots) raise(TK_E_UNSUPPORTED, "expression too deep for the tile program");
       const bool y_first = node_need(y) > node_need(x);
-      emit(code, y_first ? y : x, free_slot);
+      emit(code, y_first ? y : x, busy);
       DIns sv{};
       sv.op = VM_SAVE;
-      sv.arg = (uint16_t)free_slot;
+      sv.arg = (uint16_t)t;
       sv.rnd = RND_NONE;
       code.push_back(sv);
-      emit(code, y_first ? x : y, free_slot + 1);
+      emit(code, y_first ? x : y, busy | (1u << t));
       d.src = SRC_SLOT;
-      d.arg = (uint16_t)free_slot;
+      d.arg = (uint16_t)t;
       d.rev = y_first ? 0 : 1;
     }
     code.push_back(d);
@@ -1437,7 +1454,7 @@ struct Builder {
     for (size_t d = 0; d < map.size(); ++d) map[d] = (int)d;
     Node root = op_node(cx, e.op, map);
     std::vector<DIns> code;
-    emit(code, root, 0);
+    emit(code, root, 0u);
     emit_store(code, cx, o2.out.buf, map);
     auto dims = collapse(cx);
     DTask t = blank(T_EW);
@@ -1523,7 +1540,7 @@ struct Builder {
         code.push_back(s);
       } else if (alpha == 0.0f) {
         Node b = operand_node(cx, mm.args[0], map);
-        emit(code, b, 1);
+        emit(code, b, 1u);
         DIns s{};
         s.op = VM_SCALE;
         s.a = beta;
@@ -1549,7 +1566,7 @@ struct Builder {
           sv.arg = 0;
           sv.rnd = RND_NONE;
           code.push_back(sv);
-          emit(code, b, 1);  // bias expression
+          emit(code, b, 1u);  // bias expression
           DIns ad{};
           ad.op = VM_ADD;  // acc(bias) ; slot0 + beta*acc
           ad.a = beta;
@@ -1581,7 +1598,7 @@ struct Builder {
       cx.slot_of.clear();
       cx.slot_of[cur] = 0;
       Node n = op_node(cx, c, map);
-      emit(code, n, 1);
+      emit(code, n, 1u);
       cur = op(c).out.buf;
     }
     cx.slot_of.clear();
@@ -1610,7 +1627,7 @@ struct Builder {
     for (size_t i = 0; i < sp.evals.size(); ++i) {
       const int c = sp.evals[i];
       Node n = op_node(cx, c, map);
-      emit(code, n, sp.temp_base[i]);
+      emit(code, n, sp.busy[i]);
       const std::string& ob = op(c).out.buf;
       if (side_stored(e, c)) emit_store(code, cx, ob, map);
       auto it = sp.slot.find(ob);
@@ -1752,7 +1769,7 @@ struct Builder {
     for (size_t i = 0; i < rc.perm.size(); ++i) map[rc.perm[i]] = (int)i;
     Node src = operand_node(cx, r.args[0], map);
     std::vector<DIns> code;
-    emit(code, src, 0);
+    emit(code, src, 0u);
     // collapse kept and reduced parts separately
     std::vector<int64_t> dims;
     {
