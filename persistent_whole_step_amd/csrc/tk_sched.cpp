@@ -1236,6 +1236,44 @@ struct Builder {
             break;
           }
         }
+      }
+      if (changed) continue;
+      // Slots whose value the accumulator still holds: a save makes its slot
+      // equal to it, stores leave it alone, anything else changes it.
+      uint32_t acc_eq = 0;
+      for (size_t i = 0; i < code.size() && !changed; ++i) {
+        DIns& d = code[i];
+        const bool slot_equal = d.src == SRC_SLOT && d.arg < 32 && (acc_eq >> d.arg) & 1u;
+        if (d.op == VM_LOAD && slot_equal && d.rnd == RND_NONE) {
+          // reloading what the accumulator holds
+          code.erase(code.begin() + i);
+          changed = true;
+        } else if (d.op == VM_LOAD && d.rnd == RND_NONE && (d.src == SRC_VIEW || d.src == SRC_SCALAR) &&
+                   i + 1 < code.size()) {
+          // load v ; op slot  ==>  op v with the operands' roles swapped,
+          // when the slot's value is still in the accumulator
+          DIns& n = code[i + 1];
+          const bool binary = n.op == VM_ADD || n.op == VM_SUB || n.op == VM_MUL || n.op == VM_DIV || n.op == VM_TB;
+          if (binary && n.src == SRC_SLOT && n.arg < 32 && ((acc_eq >> n.arg) & 1u)) {
+            DIns r = n;
+            r.src = d.src;
+            r.arg = d.arg;
+            r.s = d.s;
+            r.rev = n.op == VM_MUL ? 0 : (n.rev ? 0 : 1);
+            code[i] = r;
+            code.erase(code.begin() + i + 1);
+            changed = true;
+          }
+        }
+        if (changed) break;
+        if (d.op == VM_SAVE)
+          acc_eq |= 1u << d.arg;
+        else if (d.op != VM_STORE)
+          acc_eq = 0;
+      }
+      if (changed) continue;
+      for (size_t i = 0; i < code.size(); ++i) {
+        const DIns& d = code[i];
         if (d.op == VM_SAVE) {
           bool read = false;
           for (size_t j = i + 1; j < code.size(); ++j) {
@@ -2019,6 +2057,23 @@ struct Builder {
     return encode();
   }
 
+  // One machine instruction as text (plan dumps).
+  static std::string ins_text(const DIns& d) {
+    static const char* names[] = {"?", "load", "add", "sub", "mul", "div", "neg", "relu", "square", "pow", "tb",
+                                  "save", "store", "scale", "zero", "sqrt"};
+    std::ostringstream o;
+    o << (d.op < sizeof(names) / sizeof(names[0]) ? names[d.op] : "?");
+    if (d.op == VM_STORE) o << "(v" << d.arg << ")";
+    else if (d.op == VM_SAVE) o << "(s" << d.arg << ")";
+    else if (d.src == SRC_VIEW) o << "(v" << d.arg << ")";
+    else if (d.src == SRC_SLOT) o << "(s" << d.arg << ")";
+    else if (d.src == SRC_SCALAR) o << "(" << d.s << ")";
+    if (d.rev) o << "'";
+    if (d.rnd == DT_BF16) o << ">bf16";
+    else if (d.rnd == DT_F16) o << ">f16";
+    return o.str();
+  }
+
   Plan encode() {
     Plan pl;
     pl.n_in = n_in;
@@ -2085,6 +2140,14 @@ struct Builder {
         task.fin_first = task.fin_len ? mapcode(task.fin_first, task.fin_len) : 0;
         tk.push_back(task);
         gd << "  " << kind_name(task.kind) << " items=" << task.n_items << " : " << gdesc[t] << "\n";
+        auto prog = [&](const char* what, uint32_t first, uint32_t len) {
+          if (!len) return;
+          gd << "    | " << what << ":";
+          for (uint32_t i = 0; i < len; ++i) gd << " " << ins_text(si.at(first + i));
+          gd << "\n";
+        };
+        prog("code", task.expr_first, task.expr_len);
+        prog("finish", task.fin_first, task.fin_len);
       }
       DStage& d = e.d;
       d = DStage{};
