@@ -227,13 +227,25 @@ struct Builder {
     for (int mi = 0; mi < (int)P.ops.size(); ++mi) {
       const Op& mm = op(mi);
       const bool red = mm.cls == OC_REDUCE;
-      if ((!is_contraction(mi) && !red) || fused.count(mi) || skip.count(mi)) continue;
+      if ((!is_contraction(mi) && !red) || skip.count(mi)) continue;
+      // a pass-1 chain is extended when more descendants can join it (the
+      // chain's links become side ops)
+      const bool from_pass1 = fused.count(mi) && !fused[mi].chain.empty() && fused[mi].side.empty();
+      if (fused.count(mi) && !from_pass1) continue;
       const std::vector<int64_t>& rshape = mm.out.shape;
       const bool flat = red && rshape.size() != 1;
       std::set<std::string> known = {mm.out.buf};
       std::vector<int> chain;
+      std::set<int> seeded;
+      if (from_pass1)
+        for (int c : fused[mi].chain) {
+          chain.push_back(c);
+          seeded.insert(c);
+          known.insert(op(c).out.buf);
+        }
       for (int j = mi + 1; j < (int)P.ops.size(); ++j) {
         const Op& nx = op(j);
+        if (seeded.count(j)) continue;
         if (nx.cls != OC_POINTWISE || skip.count(j)) continue;
         bool touches = false;
         for (auto& a : nx.args)
@@ -255,6 +267,8 @@ struct Builder {
         chain.push_back(j);
         known.insert(nx.out.buf);
       }
+      if (from_pass1 && chain.size() == seeded.size()) continue;  // nothing to add
+      std::sort(chain.begin(), chain.end());
       std::set<std::string> derived = known;
       derived.erase(mm.out.buf);
       std::set<std::string> returned;
@@ -315,6 +329,11 @@ struct Builder {
       for (int j = 0; j < (int)P.ops.size(); ++j)
         if (!skip.count(j) && !dkept.count(op(j).out.buf) && inlinable(j)) ext.insert(op(j).out.buf);
       if (!plan_side(e, ext).ok) continue;
+      // a replaced pass-1 entry must still compute every link it owned
+      bool covers = true;
+      for (int c : seeded)
+        if (std::find(kept.begin(), kept.end(), c) == kept.end()) covers = false;
+      if (!covers) continue;
       fused[mi] = e;
       for (int c : kept) skip.insert(c);
     }
