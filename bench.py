@@ -36,6 +36,7 @@ WORKLOAD_NAMES = {
     "c4": "mlp3-bf16-b1024-4096-4096-4096-1024",
     "c5": "resmlp16-fp16-b512-w2048",
     "c2a": "mlp3-bf16-b256-512-1024-1024-64-adamw",
+    "c3r4": "gemv8-int8w-bf16x-4x4096x4096",
 }
 
 
@@ -45,6 +46,8 @@ def config(name: str) -> dict:
     from persistent_whole_step_amd import programs
     if name == "c2a":
         return dict(programs.CONFIGS["c2"], optimizer=programs.AdamW(), adam_t=10)
+    if name == "c3r4":
+        return dict(programs.CONFIGS["c3"], rows=4)
     return programs.CONFIGS[name]
 
 
@@ -62,9 +65,9 @@ def source_hash() -> str:
 
 
 def gemv_bytes(cfg) -> int:
-    k, n, L = cfg["k"], cfg["n"], cfg["layers"]
+    k, n, L, m = cfg["k"], cfg["n"], cfg["layers"], cfg.get("rows", 1)
     nb = (k + 31) // 32
-    return L * (n * k + n * nb * 4 + n * 4 + k * 2 + n * 2)
+    return L * (n * k + n * nb * 4 + n * 4 + m * k * 2 + m * n * 2)
 
 
 class Runner:
@@ -260,7 +263,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--others", default="c1,c2a,c3,c4,c5", help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--others", default="c1,c2a,c3,c3r4,c4,c5", help="comma list of extra workloads ('' for none)")
     ap.add_argument("--other-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")

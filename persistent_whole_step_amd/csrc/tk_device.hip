@@ -878,9 +878,13 @@ DEV float wave_sum(float v) {
   return v;
 }
 
-constexpr uint32_t kGemvRed = kSmemBytes - 64;  // byte offset of the 16 row sums
+constexpr uint32_t kGemvRed = kSmemBytes - 64 * kGemvRows;  // byte offset of the [rows][16] output sums
 
-DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
+// Split-K GEMV slab: output columns cb*16 .. +16 (rows of the int8 weight q,
+// four per wave) for activation rows r0 .. r0+R-1.  Each lane takes 16-wide
+// K chunks; the weight chunks are loaded once and serve all R rows.
+template <int R>
+DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t cb, uint32_t r0) {
   const VView X = load_view(views_off + t.va * sizeof(DView)), Q = load_view(views_off + t.vb * sizeof(DView)),
               S = load_view(views_off + t.vs * sizeof(DView));
   const GLOBAL uint8_t* px = base_ptr(ka, X.base);
@@ -888,9 +892,9 @@ DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off
   const GLOBAL float* ps = (const GLOBAL float*)base_ptr(ka, S.base);
   const int wave = tid / 64, lane = tid % 64;
   const uint32_t K = t.k;
-  LDS float* xs = (LDS float*)g_smem;
-  const bool staged = (uint64_t)K * 4 + 64 <= (uint64_t)kSmemBytes;
-  const uint32_t row0 = item * 16 + wave * 4;
+  LDS float* xs = (LDS float*)g_smem;  // [R][K] activations
+  const bool staged = (uint64_t)K * 4 * R <= (uint64_t)kGemvRed;
+  const uint32_t row0 = cb * 16 + wave * 4;
   // Fast form (uniform per task): contiguous int8 rows, 16-byte aligned
   // chunk starts, K a multiple of 16.  Every load is then issued
   // unconditionally from a clamped in-bounds address, so all sixteen chunks
@@ -899,95 +903,124 @@ DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off
   const bool fast = staged && Q.stride[1] == 1 && K % 16 == 0 && (Q.offset & 15) == 0 && (Q.stride[0] & 15) == 0 &&
                     aligned16(pq);
   constexpr int NC = 4;  // chunks per lane per pass (4096 columns)
-  float acc[4] = {0, 0, 0, 0};
+  float acc[4][R];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < R; ++r) acc[i][r] = 0.0f;
   for (uint32_t kpass = 0; kpass < K; kpass += 1024 * NC) {
     u32x4 qv[4][NC];
     float sv[4][NC];
-    uint32_t okm = 0;  // bit r * NC + j: chunk (r, j) exists
+    uint32_t okm = 0;  // bit i * NC + j: chunk (i, j) exists
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const uint32_t row = row0 + r;
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t row = row0 + i;
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         const uint32_t kc = kpass + 1024 * j + lane * 16;
-        okm |= (row < t.n && kc < K ? 1u : 0u) << (r * NC + j);
+        okm |= (row < t.n && kc < K ? 1u : 0u) << (i * NC + j);
       }
     }
     if (fast) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t row = row0 + r < t.n ? row0 + r : 0;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t row = row0 + i < t.n ? row0 + i : 0;
         const int64_t qrow = Q.offset + (int64_t)row * Q.stride[0];
         const int64_t srow = S.offset + (int64_t)row * S.stride[0];
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
           const uint32_t kc0 = kpass + 1024 * j + lane * 16;
           const uint32_t kc = kc0 < K ? kc0 : 0;
-          qv[r][j] = *(const GLOBAL u32x4*)(pq + qrow + kc);
+          qv[i][j] = *(const GLOBAL u32x4*)(pq + qrow + kc);
           // a 16-wide chunk starting at a multiple of 16 lies inside one 32-block
-          sv[r][j] = ps[srow + (int64_t)(kc / 32) * S.stride[1]];
+          sv[i][j] = ps[srow + (int64_t)(kc / 32) * S.stride[1]];
         }
       }
     } else {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const uint32_t row = row0 + r;
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t row = row0 + i;
         const int64_t qrow = Q.offset + (int64_t)row * Q.stride[0];
         const int64_t srow = S.offset + (int64_t)row * S.stride[0];
 #pragma unroll
         for (int j = 0; j < NC; ++j) {
           const uint32_t kc = kpass + 1024 * j + lane * 16;
-          const bool ok = (okm >> (r * NC + j)) & 1u;
+          const bool ok = (okm >> (i * NC + j)) & 1u;
           const int64_t qidx = qrow + (int64_t)kc * Q.stride[1];
           uint32_t w[4] = {0, 0, 0, 0};
           for (int e = 0; e < 16; ++e)
             if (ok && kc + e < K) w[e / 4] |= ((uint32_t)(uint8_t)pq[qidx + (int64_t)e * Q.stride[1]]) << (8 * (e % 4));
-          qv[r][j] = u32x4{w[0], w[1], w[2], w[3]};
-          sv[r][j] = ok ? ps[srow + (int64_t)(kc / 32) * S.stride[1]] : 0.0f;
+          qv[i][j] = u32x4{w[0], w[1], w[2], w[3]};
+          sv[i][j] = ok ? ps[srow + (int64_t)(kc / 32) * S.stride[1]] : 0.0f;
         }
       }
     }
     if (kpass == 0 && staged) {
-      for (uint32_t k = tid; k < K; k += kBlock)
-        xs[k] = load_elem(px, X.dtype, X.offset + (int64_t)k * X.stride[1]);
+      for (int r = 0; r < R; ++r)
+        for (uint32_t k = tid; k < K; k += kBlock)
+          xs[r * K + k] = load_elem(px, X.dtype, X.offset + (int64_t)(r0 + r) * X.stride[0] + (int64_t)k * X.stride[1]);
       __syncthreads();
     }
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       const uint32_t kc = kpass + 1024 * j + lane * 16;
       if (kc >= K) continue;
-      float xk[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e)
-        xk[e] = (kc + e < K) ? (staged ? xs[kc + e] : load_elem(px, X.dtype, X.offset + (int64_t)(kc + e) * X.stride[1]))
-                             : 0.0f;
       // q = b - 128 with b = q ^ 0x80 an unsigned byte (converted by the
-      // byte-select conversions), so the chunk's dot product is
+      // byte-select conversions), so a chunk's dot product is
       // sum(x b) - 128 sum(x), scaled once by the block scale
-      float xsum = 0.0f;
+      float xk[R][16], xoff[R];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) xsum = xsum + xk[e];
-      const float xoff = 128.0f * xsum;
+      for (int r = 0; r < R; ++r) {
+        float xsum = 0.0f;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float d = 0.0f;
+        for (int e = 0; e < 16; ++e) {
+          const int64_t xi = X.offset + (int64_t)(r0 + r) * X.stride[0] + (int64_t)(kc + e) * X.stride[1];
+          xk[r][e] = (kc + e < K) ? (staged ? xs[r * K + kc + e] : load_elem(px, X.dtype, xi)) : 0.0f;
+          xsum = xsum + xk[r][e];
+        }
+        xoff[r] = 128.0f * xsum;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        float wb[16];
 #pragma unroll
         for (int w4 = 0; w4 < 4; ++w4) {
-          const uint32_t u = qv[r][j][w4] ^ 0x80808080u;
+          const uint32_t u = qv[i][j][w4] ^ 0x80808080u;
 #pragma unroll
-          for (int by = 0; by < 4; ++by) d = __builtin_fmaf(xk[4 * w4 + by], (float)((u >> (8 * by)) & 0xffu), d);
+          for (int by = 0; by < 4; ++by) wb[4 * w4 + by] = (float)((u >> (8 * by)) & 0xffu);
         }
-        acc[r] = __builtin_fmaf(sv[r][j], d - xoff, acc[r]);
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float d = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) d = __builtin_fmaf(xk[r][e], wb[e], d);
+          acc[i][r] = __builtin_fmaf(sv[i][j], d - xoff[r], acc[i][r]);
+        }
       }
     }
   }
-  LDS float* red = (LDS float*)(g_smem + kGemvRed);
+  LDS float* red = (LDS float*)(g_smem + kGemvRed);  // [R][16]
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const float s = wave_sum(acc[r]);
-    if (lane == 0) red[wave * 4 + r] = s;
-  }
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const float s = wave_sum(acc[i][r]);
+      if (lane == 0) red[r * 16 + wave * 4 + i] = s;
+    }
   __syncthreads();
+}
+
+// Work item = slab * tiles_n + column block; a slab is kGemvRows activation
+// rows (the last may be shorter).
+DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
+  const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
+  const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
+  switch (rows) {
+    case 1: gemv_q8_rows<1>(tid, ka, t, views_off, cb, r0); break;
+    case 2: gemv_q8_rows<2>(tid, ka, t, views_off, cb, r0); break;
+    case 3: gemv_q8_rows<3>(tid, ka, t, views_off, cb, r0); break;
+    default: gemv_q8_rows<4>(tid, ka, t, views_off, cb, r0); break;
+  }
 }
 
 // Block-wide sum in a fixed order: wave butterflies, then waves 0..3 in order.
@@ -1119,20 +1152,24 @@ DEV bool fill(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, uin
       return true;
     }
     case T_GEMV_Q8: {
-      // epilogue over the 16 row sums: threads 0..1 take 8-wide chunks (or
-      // thread 0 sixteen singles)
+      // epilogue over the slab's [rows][16] sums: per activation row, two
+      // threads take 8-wide chunks (or one thread sixteen singles)
       if (bi > 0) return false;
       expr_batch(b, t, ins_off);
       task_space(b, t);
       const LDS float* red = (const LDS float*)(g_smem + kGemvRed);
-      const uint32_t rb = item * 16;
-      if (tid < (W == 8 ? 2u : 1u)) {
+      const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
+      const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
+      const uint32_t per = W == 8 ? 2u : 1u;  // threads per activation row
+      const uint32_t rb = cb * 16;
+      if (tid < per * rows) {
+        const uint32_t r = tid / per, half = tid % per;
         for (int q = 0; q < C; ++q) {
-          const uint32_t col = rb + (W == 8 ? tid * 8 : q);
+          const uint32_t col = rb + (W == 8 ? half * 8 : q);
           const bool ok = (W == 8 ? q == 0 : true) && col < t.n;
           live |= (ok ? 1u : 0u) << q;
-          xe(tid, q) = ok ? col : 0;
-          for (int j = 0; j < W; ++j) xv(tid, q * W + j) = red[W == 8 ? tid * 8 + j : q];
+          xe(tid, q) = ok ? (r0 + r) * t.n + col : 0;
+          for (int j = 0; j < W; ++j) xv(tid, q * W + j) = red[r * 16 + (W == 8 ? half * 8 + j : q)];
         }
       }
       return true;

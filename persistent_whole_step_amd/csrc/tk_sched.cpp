@@ -1330,9 +1330,9 @@ struct Builder {
     const int64_t m = A.shape[0], k = A.shape[1], n = mm.out.shape[1];
     GemmChoice g{};
     if (mm.cls == OC_MM_Q8) {
-      if (m != 1) raise(TK_E_UNSUPPORTED, "int8-weight products support one activation row");
+      // slabs of kGemvRows activation rows share each weight chunk they load
       g.kind = T_GEMV_Q8;
-      g.tm = 1;
+      g.tm = (uint32_t)((m + kGemvRows - 1) / kGemvRows);
       g.tn = (uint32_t)((n + 15) / 16);
       g.split = 1;
       return g;

@@ -343,19 +343,20 @@ def residual_step(width: int, layers: int, batch: int, dtype: str, lr: float,
     return p
 
 
-def gemv_q8_stack(k: int, n: int, layers: int, block: int = 32) -> Program:
-    """y_l = relu(addmm_q8(b_l, y_{l-1}, q_l, s_l)) in bf16, y_0 = x [1,k].
+def gemv_q8_stack(k: int, n: int, layers: int, block: int = 32, rows: int = 1) -> Program:
+    """y_l = relu(addmm_q8(b_l, y_{l-1}, q_l, s_l)) in bf16, y_0 = x [rows,k]
+    (rows > 1: several decode rows sharing each weight pass).
     q_l is int8 [n,k] (row n holds output n's weights, blocks of ``block``
     along k), s_l float32 [n, ceil(k/block)], b_l float32 [n]."""
     p = Program()
-    y = p.input("x", "bf16", (1, k))
+    y = p.input("x", "bf16", (rows, k))
     nb = (k + block - 1) // block
     params = []
     for i in range(layers):
         params.append((p.input(f"q{i + 1}", "i8", (n, k)), p.input(f"s{i + 1}", "f32", (n, nb)),
                        p.input(f"b{i + 1}", "f32", (n,))))
     for i, (q, s, b) in enumerate(params):
-        z = p.op("addmm_q8", [b, y, q, s], "bf16", (1, n), name=f"z{i + 1}")
+        z = p.op("addmm_q8", [b, y, q, s], "bf16", (rows, n), name=f"z{i + 1}")
         y = p.op("relu", [z], "bf16", name=f"y{i + 1}")
     p.output(y)
     return p
@@ -381,7 +382,7 @@ def build(cfg: dict, **variant) -> Program:
     if kind == "residual":
         return residual_step(cfg["width"], cfg["layers"], cfg["batch"], cfg["dtype"], cfg["lr"], **variant)
     if kind == "gemv":
-        return gemv_q8_stack(cfg["k"], cfg["n"], cfg["layers"])
+        return gemv_q8_stack(cfg["k"], cfg["n"], cfg["layers"], rows=cfg.get("rows", 1))
     raise ValueError(kind)
 
 
@@ -402,7 +403,7 @@ def inputs_for(cfg: dict, seed: int):
         return (base + synth.adamw_state(seed + 1, [a.shape for a in base[2:]])
                 + [np.array([c1], np.float32), np.array([c2], np.float32)])
     if kind == "gemv":
-        return synth.gemv_q8_inputs(seed, cfg["k"], cfg["n"], cfg["layers"])
+        return synth.gemv_q8_inputs(seed, cfg["k"], cfg["n"], cfg["layers"], rows=cfg.get("rows", 1))
     raise ValueError(kind)
 
 

@@ -73,12 +73,12 @@ def residual_inputs(seed: int, width: int, layers: int, batch: int, dtype: str):
     return out
 
 
-def gemv_q8_inputs(seed: int, k: int, n: int, layers: int, block: int = 32):
-    """x ~ N(0,1) bf16 [1,k]; per layer q ~ U{-127..127} int8 [n,k],
+def gemv_q8_inputs(seed: int, k: int, n: int, layers: int, block: int = 32, rows: int = 1):
+    """x ~ N(0,1) bf16 [rows,k]; per layer q ~ U{-127..127} int8 [n,k],
     s ~ U(0, 0.01] float32 [n, ceil(k/block)], b ~ N(0, 0.1) float32 [n].
     Layers chain, so n == k is required for more than one layer."""
     rng = np.random.Generator(np.random.PCG64(seed))
-    out = [normal(rng, (1, k), 1.0, "bf16")]
+    out = [normal(rng, (rows, k), 1.0, "bf16")]
     nb = (k + block - 1) // block
     for _ in range(layers):
         q = rng.integers(-127, 128, size=(n, k), dtype=np.int64).astype(np.int8)

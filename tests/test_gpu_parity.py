@@ -233,19 +233,22 @@ def test_mfma_split_k(oracle_mod, split):
     _mm_case(oracle_mod, 192, 1024, 320, "bf16", False, False, seed=split, gemm_split_k=split)
 
 
-@pytest.mark.parametrize("k,n", [(4096, 64), (96, 40), (1000, 24), (64, 7)])
-def test_gemv_q8(oracle_mod, k, n):
-    say("gemv q8", k, n)
-    rng = np.random.default_rng(k + n)
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 64), (1, 96, 40), (1, 1000, 24), (1, 64, 7),
+                                   # multi-row slabs (decode-shaped): full, ragged and several slabs
+                                   (2, 4096, 48), (3, 1000, 24), (4, 512, 40), (5, 96, 7), (8, 4096, 64),
+                                   (6, 2048, 37)])
+def test_gemv_q8(oracle_mod, m, k, n):
+    say("gemv q8", m, k, n)
+    rng = np.random.default_rng(k + n + m)
     nb = (k + 31) // 32
     p = Program()
-    x = p.input("x", "bf16", (1, k))
+    x = p.input("x", "bf16", (m, k))
     q = p.input("q", "i8", (n, k))
     s = p.input("s", "f32", (n, nb))
     b = p.input("b", "f32", (n,))
-    z = p.op("addmm_q8", [b, x, q, s], "bf16", (1, n))
+    z = p.op("addmm_q8", [b, x, q, s], "bf16", (m, n))
     p.output(p.op("relu", [z], "bf16"))
-    ins = [synth.random_tensor(rng, (1, k), "bf16"), synth.random_tensor(rng, (n, k), "i8"),
+    ins = [synth.random_tensor(rng, (m, k), "bf16"), synth.random_tensor(rng, (n, k), "i8"),
            (0.01 * (1 - rng.random((n, nb)))).astype(np.float32), synth.random_tensor(rng, (n,), "f32", 0.3)]
     got, _ = parity.gpu_run(p, ins)
     want = oracle_mod.run(p.text(), ins)
@@ -259,6 +262,7 @@ SMALL = {
     "c1": dict(programs.CONFIGS["c1"]),
     "c2s": dict(kind="mlp", dims=(192, 320, 256, 48), batch=96, dtype="bf16", lr=1e-3),
     "c3s": dict(kind="gemv", k=1024, n=1024, layers=3),
+    "c3r": dict(kind="gemv", k=1024, n=1024, layers=3, rows=6),  # decode rows in two slabs
     "c4s": dict(kind="mlp", dims=(256, 384, 256, 128), batch=160, dtype="bf16", lr=1e-4),
     "c5s": dict(kind="residual", width=256, layers=4, batch=96, dtype="f16", lr=1e-4),
     # AdamW in place of SGD: two float32 states per parameter, updated in place

@@ -273,20 +273,21 @@ def test_bf16_matmul_output_rounded(oracle_mod):
     assert int(y[0, 0]) == 0x3F80  # 1 + 2^-8 -> ties to even -> 1.0
 
 
-def test_q8_contraction_exact_with_power_of_two_scales(oracle_mod):
+@pytest.mark.parametrize("m", [1, 3])
+def test_q8_contraction_exact_with_power_of_two_scales(oracle_mod, m):
     rng = np.random.default_rng(5)
     k, n = 96, 7
     nb = (k + 31) // 32
     q = rng.integers(-127, 128, size=(n, k)).astype(np.int8)
     s = (2.0 ** rng.integers(-6, 1, size=(n, nb))).astype(np.float32)
-    x = rng.integers(-3, 4, size=(1, k)).astype(np.float32)
+    x = rng.integers(-3, 4, size=(m, k)).astype(np.float32)
     b = np.array(rng.integers(-5, 6, size=n), np.float32)
     p = Program()
-    xi = p.input("x", "f32", (1, k))
+    xi = p.input("x", "f32", (m, k))
     qi = p.input("q", "i8", (n, k))
     si = p.input("s", "f32", (n, nb))
     bi = p.input("b", "f32", (n,))
-    p.output(p.op("addmm_q8", [bi, xi, qi, si], "f32", (1, n)))
+    p.output(p.op("addmm_q8", [bi, xi, qi, si], "f32", (m, n)))
     (y,) = run1(oracle_mod, p, [x, q, s, b])
     W = q.astype(np.float64) * np.repeat(s.astype(np.float64), 32, axis=1)[:, :k]
     np.testing.assert_array_equal(y, (x.astype(np.float64) @ W.T + b).astype(np.float32))
