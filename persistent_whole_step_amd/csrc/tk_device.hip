@@ -411,6 +411,10 @@ DEV void vm_run(uint32_t tid, const Ctx& ka, const Batch& b, uint32_t views_off,
         continue;
       }
       load_chunks<W, C>(p, dt, vec, s, idx, x);
+      // Wait for the operand here, on the only path that loads one: the
+      // compiler would otherwise wait at its use on every path, and that wait
+      // would also cover stores of earlier instructions still in flight.
+      __builtin_amdgcn_s_waitcnt(0);
     } else if (src == SRC_SLOT) {
       const LDS float* sb = slot_base(arg);
 #pragma unroll
