@@ -884,11 +884,52 @@ DEV float wave_sum(float v) {
 
 constexpr uint32_t kGemvRed = kSmemBytes - 64 * kGemvRows;  // byte offset of the [rows][16] output sums
 
+// Cross-stage weight prefetch for the one-row GEMV (tasks marked F_QPREFETCH:
+// weight and scales are program inputs no stage writes).  While the grid
+// barrier before its stage completes, a workgroup copies the int8 weight
+// chunks of its first item into LDS [0, 64 KB) and the block scales into the
+// index-exchange region, so the weight stream overlaps the barrier.  Slot
+// qs = (wave * 4 + row) * 4 + chunk holds what lane l of `wave` needs for that
+// row and chunk; waves 1..3 issue the direct-to-LDS loads (wave 0 runs the
+// barrier's fences, which would otherwise wait for them).
+constexpr uint32_t kPrefQ = 0;        // 64 slots x 64 lanes x 16 B
+constexpr uint32_t kPrefS = kXeOff;   // 64 slots x 64 lanes x 4 B
+constexpr uint32_t kPrefX = kXvOff;   // the activation row, staged as floats (K <= 4096)
+
+DEV bool gemv_prefetchable(const Ctx& ka, const DTask& t, uint32_t views_off) {
+  if (t.kind != T_GEMV_Q8 || !(t.flags & F_QPREFETCH) || t.m != 1 || t.k > 4096 || t.k % 16 != 0) return false;
+  const VView Q = load_view(views_off + t.vb * sizeof(DView));
+  const GLOBAL int8_t* pq = (const GLOBAL int8_t*)base_ptr(ka, Q.base);
+  return Q.stride[1] == 1 && (Q.offset & 15) == 0 && (Q.stride[0] & 15) == 0 && aligned16(pq);
+}
+
+DEV void gemv_prefetch(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
+  const uint32_t wave = uniform(tid / 64), lane = tid % 64;
+  if (wave == 0) return;
+  const VView Q = load_view(views_off + t.vb * sizeof(DView)), S = load_view(views_off + t.vs * sizeof(DView));
+  const GLOBAL int8_t* pq = (const GLOBAL int8_t*)base_ptr(ka, Q.base);
+  const GLOBAL float* ps = (const GLOBAL float*)base_ptr(ka, S.base);
+  const uint32_t K = t.k;
+  const uint32_t lds = (uint32_t)(uintptr_t)(LDS uint8_t*)g_smem;
+  for (uint32_t qs = wave - 1; qs < 64; qs += 3) {
+    const uint32_t cw = qs / 16, i = (qs / 4) % 4, j = qs % 4;
+    const uint32_t row0 = item * 16 + cw * 4 + i;
+    const uint32_t row = row0 < t.n ? row0 : 0;
+    const uint32_t kc0 = 1024 * j + lane * 16;
+    const uint32_t kc = kc0 < K ? kc0 : 0;
+    const GLOBAL int8_t* gq = pq + Q.offset + (int64_t)row * Q.stride[0] + kc;
+    const GLOBAL float* gs = ps + S.offset + (int64_t)row * S.stride[0] + (int64_t)(kc / 32) * S.stride[1];
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gq), "s"(lds + kPrefQ + qs * 1024) : "m0");
+    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gs), "s"(lds + kPrefS + qs * 256) : "m0");
+  }
+}
+
 // Split-K GEMV slab: output columns cb*16 .. +16 (rows of the int8 weight q,
 // four per wave) for activation rows r0 .. r0+R-1.  Each lane takes 16-wide
 // K chunks; the weight chunks are loaded once and serve all R rows.
 template <int R>
-DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t cb, uint32_t r0) {
+DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t cb, uint32_t r0,
+                      bool pref) {
   const VView X = load_view(views_off + t.va * sizeof(DView)), Q = load_view(views_off + t.vb * sizeof(DView)),
               S = load_view(views_off + t.vs * sizeof(DView));
   const GLOBAL uint8_t* px = base_ptr(ka, X.base);
@@ -896,16 +937,23 @@ DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t view
   const GLOBAL float* ps = (const GLOBAL float*)base_ptr(ka, S.base);
   const int wave = tid / 64, lane = tid % 64;
   const uint32_t K = t.k;
-  LDS float* xs = (LDS float*)g_smem;  // [R][K] activations
-  const bool staged = (uint64_t)K * 4 * R <= (uint64_t)kGemvRed;
+  // [R][K] activations; with prefetched weights occupying [0, 64 KB) the one
+  // row goes to the value-exchange region
+  LDS float* xs = (LDS float*)(g_smem + (pref ? kPrefX : 0));
+  // A contiguous, 16-byte aligned bf16 row is read straight into registers
+  // (each lane needs only its own 64 values): no staging, and none of the
+  // bank conflicts of lane-strided LDS reads.
+  const GLOBAL uint16_t* xrow = (const GLOBAL uint16_t*)px + X.offset + (int64_t)r0 * X.stride[0];
+  const bool xreg = R == 1 && X.dtype == DT_BF16 && X.stride[1] == 1 && K % 16 == 0 && aligned16(xrow);
+  const bool staged = !xreg && (uint64_t)K * 4 * R <= (uint64_t)kGemvRed;
   const uint32_t row0 = cb * 16 + wave * 4;
   // Fast form (uniform per task): contiguous int8 rows, 16-byte aligned
   // chunk starts, K a multiple of 16.  Every load is then issued
   // unconditionally from a clamped in-bounds address, so all sixteen chunks
   // of a lane are in flight at once; lanes past the end mask the weights
   // when they use them.
-  const bool fast = staged && Q.stride[1] == 1 && K % 16 == 0 && (Q.offset & 15) == 0 && (Q.stride[0] & 15) == 0 &&
-                    aligned16(pq);
+  const bool fast = (staged || xreg) && Q.stride[1] == 1 && K % 16 == 0 && (Q.offset & 15) == 0 &&
+                    (Q.stride[0] & 15) == 0 && aligned16(pq);
   constexpr int NC = 4;  // chunks per lane per pass (4096 columns)
   float acc[4][R];
 #pragma unroll
@@ -925,7 +973,19 @@ DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t view
         okm |= (row < t.n && kc < K ? 1u : 0u) << (i * NC + j);
       }
     }
-    if (fast) {
+    if (pref) {
+      // every lane's prefetch has landed, and every wave sees every slot
+      wait_vmcnt<0>();
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < NC; ++j) {
+          const uint32_t qs = (wave * 4 + i) * 4 + j;
+          qv[i][j] = *(const LDS u32x4*)(g_smem + kPrefQ + qs * 1024 + lane * 16);
+          sv[i][j] = *(const LDS float*)(g_smem + kPrefS + qs * 256 + lane * 4);
+        }
+    } else if (fast) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t row = row0 + i < t.n ? row0 + i : 0;
@@ -959,10 +1019,51 @@ DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t view
         }
       }
     }
+    u32x4 xr[NC][2];  // xreg: this lane's 16 bf16 activations per chunk
+    if (xreg) {
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const uint32_t kc0 = kpass + 1024 * j + lane * 16;
+        const GLOBAL u32x4* xp = (const GLOBAL u32x4*)(xrow + (kc0 < K ? kc0 : 0));
+        xr[j][0] = xp[0];
+        xr[j][1] = xp[1];
+      }
+    }
     if (kpass == 0 && staged) {
+      // 16 elements per thread and row per round, every load issued before
+      // any is stored (one latency per round, not one per element)
       for (int r = 0; r < R; ++r)
-        for (uint32_t k = tid; k < K; k += kBlock)
-          xs[r * K + k] = load_elem(px, X.dtype, X.offset + (int64_t)(r0 + r) * X.stride[0] + (int64_t)k * X.stride[1]);
+        for (uint32_t k0 = 0; k0 < K; k0 += 16 * kBlock) {
+          const int64_t rb = X.offset + (int64_t)(r0 + r) * X.stride[0];
+          float v[16];
+          if (X.dtype == DT_F32) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              const uint32_t k = k0 + tid + kBlock * u;
+              v[u] = ((const GLOBAL float*)px)[rb + (int64_t)(k < K ? k : 0) * X.stride[1]];
+            }
+          } else if (X.dtype == DT_I8) {
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              const uint32_t k = k0 + tid + kBlock * u;
+              v[u] = (float)((const GLOBAL int8_t*)px)[rb + (int64_t)(k < K ? k : 0) * X.stride[1]];
+            }
+          } else {
+            uint32_t h[16];
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+              const uint32_t k = k0 + tid + kBlock * u;
+              h[u] = ((const GLOBAL uint16_t*)px)[rb + (int64_t)(k < K ? k : 0) * X.stride[1]];
+            }
+#pragma unroll
+            for (int u = 0; u < 16; ++u) v[u] = half_bits_to_f32(h[u], X.dtype == DT_BF16);
+          }
+#pragma unroll
+          for (int u = 0; u < 16; ++u) {
+            const uint32_t k = k0 + tid + kBlock * u;
+            if (k < K) xs[r * K + k] = v[u];
+          }
+        }
       __syncthreads();
     }
 #pragma unroll
@@ -979,7 +1080,12 @@ DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t view
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int64_t xi = X.offset + (int64_t)(r0 + r) * X.stride[0] + (int64_t)(kc + e) * X.stride[1];
-          xk[r][e] = (kc + e < K) ? (staged ? xs[r * K + kc + e] : load_elem(px, X.dtype, xi)) : 0.0f;
+          if (xreg) {
+            const uint32_t w = xr[j][e / 8][(e % 8) / 2];
+            xk[r][e] = __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16));
+          } else {
+            xk[r][e] = (kc + e < K) ? (staged ? xs[r * K + kc + e] : load_elem(px, X.dtype, xi)) : 0.0f;
+          }
           xsum = xsum + xk[r][e];
         }
         xoff[r] = 128.0f * xsum;
@@ -1016,14 +1122,14 @@ DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t view
 
 // Work item = slab * tiles_n + column block; a slab is kGemvRows activation
 // rows (the last may be shorter).
-DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
+DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, bool pref) {
   const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
   const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
   switch (rows) {
-    case 1: gemv_q8_rows<1>(tid, ka, t, views_off, cb, r0); break;
-    case 2: gemv_q8_rows<2>(tid, ka, t, views_off, cb, r0); break;
-    case 3: gemv_q8_rows<3>(tid, ka, t, views_off, cb, r0); break;
-    default: gemv_q8_rows<4>(tid, ka, t, views_off, cb, r0); break;
+    case 1: gemv_q8_rows<1>(tid, ka, t, views_off, cb, r0, pref); break;
+    case 2: gemv_q8_rows<2>(tid, ka, t, views_off, cb, r0, false); break;
+    case 3: gemv_q8_rows<3>(tid, ka, t, views_off, cb, r0, false); break;
+    default: gemv_q8_rows<4>(tid, ka, t, views_off, cb, r0, false); break;
   }
 }
 
@@ -1341,7 +1447,7 @@ DEV DStage load_stage(const GLOBAL uint8_t* stages, uint32_t s) {
 }
 
 // One work item: prologue, then batches through the machine.
-DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item) {
+DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item, bool pref) {
   // The thread index passes through an empty asm once per item, so values
   // derived from it (LDS addresses, tile offsets) are computed per item
   // instead of being hoisted out of the stage loop and held in registers
@@ -1377,7 +1483,7 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
       break;
     }
     case T_GEMV_Q8:
-      gemv_q8(tid, ka, t, sd.off_views, item);
+      gemv_q8(tid, ka, t, sd.off_views, item, pref);
       break;
     default:
       break;
@@ -1410,7 +1516,11 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
 // monotonically across launches on a workspace (the base is kept in the
 // header), so flags never need resetting.  Every spin is bounded by the
 // deadline; a timeout sets the abort word, which every spinner also watches.
-DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline) {
+// `pre` runs in every thread after this workgroup's release fence and before
+// its arrival: work that may stay in flight across the barrier (wave 0, which
+// runs the barrier's fences, issues no memory operation in it).
+template <class Pre>
+DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline, Pre pre) {
   __shared__ uint32_t s_ok;
   GLOBAL uint32_t* arrive = (GLOBAL uint32_t*)(ka.ws + kHdrArrive);
   GLOBAL uint32_t* release = (GLOBAL uint32_t*)(ka.ws + kHdrRelease);
@@ -1419,10 +1529,10 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
   const uint32_t G = gridDim.x, bid = blockIdx.x;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+  pre();
+  if (threadIdx.x == 0)
     __hip_atomic_store(arrive + bid * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
   if (bid == 0 && threadIdx.x < 64) {
     uint32_t ok = 1;
     const uint32_t lane = threadIdx.x;
@@ -1531,6 +1641,7 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
   if ((ka.flags & K_TIMESTAMPS) && blockIdx.x == 0 && threadIdx.x == 0)
     ((GLOBAL uint64_t*)(ka.ws + kHdrStamps))[0] = __builtin_amdgcn_s_memrealtime();
   trace_stamp(ka, 0xffffffffu);
+  bool pref = false;  // this stage's first item of the workgroup had its weights prefetched
   for (uint32_t s = 0; s < n_stages; ++s) {
     uint32_t ti = 0;
     for (uint32_t item = blockIdx.x; item < sd.n_items; item += gridDim.x) {
@@ -1541,9 +1652,10 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
         for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
       }
       trace_stamp(ka, 0x1000 + s);
-      run_item(ka, t, sd, item - t.item_begin);
+      run_item(ka, t, sd, item - t.item_begin, pref && item == blockIdx.x);
       trace_stamp(ka, 0x2000 + s);
     }
+    pref = false;
     if (s + 1 < n_stages) {
       const bool stamp = (ka.flags & K_TIMESTAMPS) && blockIdx.x == 0 && threadIdx.x == 0 && s < kMaxTimedStages;
       GLOBAL uint64_t* stamps = (GLOBAL uint64_t*)(ka.ws + kHdrStamps) + 4 * s;
@@ -1553,7 +1665,24 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
       sd = load_stage(stages, s + 1);
       stage_blob_to_lds(ka.plan, sd);
       if (stamp) stamps[2] = __builtin_amdgcn_s_memrealtime();
-      if (!grid_barrier(ka, epoch0 + s + 1, s, deadline)) return;
+      // the next stage's first item of this workgroup may prefetch its weights
+      // (decided inside the barrier, once the staged descriptors are visible
+      // to every thread)
+      bool will_pref = false;
+      auto pre = [&]() {
+        const uint32_t first = blockIdx.x;
+        if (first >= sd.n_items) return;
+        uint32_t nti = 0;
+        while (nti + 1 < sd.n_tasks && first >= task_item_begin(nti + 1)) ++nti;
+        const DTask nt = load_task(nti);
+        will_pref = gemv_prefetchable(ka, nt, sd.off_views);
+        if (will_pref) gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin);
+      };
+      if (!grid_barrier(ka, epoch0 + s + 1, s, deadline, pre)) {
+        wait_vmcnt<0>();  // no prefetch may still be writing LDS when the workgroup ends
+        return;
+      }
+      pref = will_pref;
       if (stamp) stamps[3] = __builtin_amdgcn_s_memrealtime();
       if (stamp && s + 1 < kMaxTimedStages) stamps[4] = stamps[3];
     }

@@ -1760,6 +1760,15 @@ struct Builder {
       ops.push_back(operand_view(A, 0, 1));       // x over (row, k)
       ops.push_back(operand_view(B, 0, 1));       // q over (n, k)
       ops.push_back(operand_view(mm.S(), 0, 1));  // s over (n, block)
+      // weight and scales that are inputs no in-place output overwrites may
+      // be fetched before the barrier that precedes this stage
+      bool stable = true;
+      for (const std::string& b : {B.buf, mm.S().buf}) {
+        if (!is_input(b)) stable = false;
+        for (auto& kv : P.inplace)
+          if (P.inputs[kv.second].buf == b) stable = false;
+      }
+      if (stable && m == 1 && k <= 4096) t.flags |= F_QPREFETCH;
     } else {
       ops.push_back(operand_view(A, 0, 1));  // A over (m, k)
       ops.push_back(operand_view(B, 0, 1));  // B over (k, n)
