@@ -1782,6 +1782,7 @@ struct Builder {
     uint32_t code_first = commit_code(code, vb);
     std::string desc = mm.name + " (" + mm.opcode + " " + std::to_string(m) + "x" + std::to_string(k) + "x" +
                        std::to_string(n) + ")";
+    if (t.flags & F_QPREFETCH) desc += " [weights fetched across the barrier]";
     if (!e.chain.empty()) {
       desc += e.update ? " +update" : " +epilogue";
       for (int c : e.chain) desc += " " + op(c).name;

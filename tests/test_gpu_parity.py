@@ -256,6 +256,22 @@ def test_gemv_q8(oracle_mod, m, k, n):
     parity.assert_contraction(got[0], want[0], np.maximum(exact, 0), mag, "bf16", "gemv q8")
 
 
+def test_gemv_prefetch_matches_plain_loads():
+    """A 3-layer int8 stack on a 24-workgroup grid: each workgroup's first item
+    of a layer has its weights fetched across the barrier, its later items
+    load them in place; the outputs equal those of the default grid (one item
+    per workgroup) bit for bit."""
+    say("gemv prefetch vs plain loads")
+    cfg = dict(kind="gemv", k=1024, n=1024, layers=3)
+    prog = programs.build(cfg)
+    ins = programs.inputs_for(cfg, 4)
+    a, pa = parity.gpu_run(prog, [x.copy() for x in ins])
+    b, pb = parity.gpu_run(prog, [x.copy() for x in ins], force_grid=24)
+    assert pb.query()["grid_size"] == 24 and "[weights fetched across the barrier]" in pb.dump()
+    for x, y, sp in zip(a, b, prog.outputs):
+        parity.assert_bitexact(y, x, sp.dtype, sp.buf)
+
+
 # ------------------------------------------------------------ whole steps --
 
 SMALL = {

@@ -83,6 +83,34 @@ def test_adamw_update_folds_like_sgd():
         assert q["materialized_ops"] == sgd["materialized_ops"]
 
 
+def _gemv_program(scale_kind: str):
+    p = Program()
+    x = p.input("x", "bf16", (1, 256))
+    q = p.input("q", "i8", (64, 256))
+    s = p.input("s", "f32", (64, 8))
+    b = p.input("b", "f32", (64,))
+    h = p.op("addmm_q8", [b, x, q, s], "bf16", (1, 64))
+    if scale_kind == "computed":
+        s2 = p.op("mul", [s, 2.0], "f32")
+        p.output(p.op("addmm_q8", [b, x, q, s2], "bf16", (1, 64)))
+    elif scale_kind == "updated":
+        p.output(p.op("addmm_q8", [b, x, q, s], "bf16", (1, 64)))
+        p.output(p.op("mul", [s, 0.5], "f32"), inplace_of=s)
+    p.output(h)
+    return p
+
+
+@pytest.mark.parametrize("kind,tagged", [("input", 2), ("computed", 1), ("updated", 0)])
+def test_gemv_weight_prefetch_only_for_stable_inputs(kind, tagged):
+    # weights and scales that are inputs nothing overwrites may be fetched
+    # before the barrier; a computed or in-place-updated scale may not
+    p = _gemv_program(kind)
+    if kind == "input":
+        p.output(p.op("addmm_q8", [p.inputs[3], p.inputs[0], p.inputs[1], p.inputs[2]], "bf16", (1, 64)))
+    d = tk.compile(p.text(), device=-1).dump()
+    assert d.count("[weights fetched across the barrier]") == tagged
+
+
 def _tile_update(later_read: bool):
     p = Program()
     a = p.input("a", "f32", (8, 8))
