@@ -729,10 +729,11 @@ DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
 }
 
 // MFMA fragment of `row0 + lane%32` (rows of an R-row operand), k = kk + 8*(lane/32) .. +7.
-template <int R>
-DEV u32x4 frag(uint32_t tid, const LDS uint16_t* s, bool kmajor, int row0, int kk) {
+// KM: the operand is staged k-major (else row-major, read transposed).
+template <int R, bool KM>
+DEV u32x4 frag(uint32_t tid, const LDS uint16_t* s, int row0, int kk) {
   const int lane = tid % 64;
-  if (kmajor) return *(const LDS u32x4*)(s + swz(row0 + lane % 32, kk / 8 + lane / 32));
+  if (KM) return *(const LDS u32x4*)(s + swz(row0 + lane % 32, kk / 8 + lane / 32));
   typedef short v4s __attribute__((ext_vector_type(4)));
   const int g = lane / 16, i = lane % 16;
   const int n = row0 + 16 * (g % 2) + 4 * (i % 4);
@@ -748,26 +749,64 @@ DEV u32x4 frag(uint32_t tid, const LDS uint16_t* s, bool kmajor, int row0, int k
   return v;
 }
 
-// One 64-deep K slice from LDS into the wave's accumulators.  a_km / b_km:
-// operand staged k-major (else row-major, read transposed).
-template <int BM, int BN, bool BF16>
-DEV void mfma_slice(uint32_t tid, const LDS uint16_t* sa, const LDS uint16_t* sb, bool a_km, bool b_km,
-                    f32x16 (&acc)[BM / 64][BN / 64]) {
-  constexpr int FM = BM / 64, FN = BN / 64;
+// One 64-deep K slice from LDS into the wave's accumulators.  AKM / BKM:
+// operand staged k-major (else row-major, read transposed).  The layouts are
+// template parameters so the slice is straight-line code: every fragment read
+// of the slice is issued before the first MFMA, and the reads of later k steps
+// overlap the MFMAs of earlier ones (with one wave per SIMD nothing else hides
+// the LDS latency).
+template <int BM, int BN, bool BF16, bool AKM, bool BKM>
+DEV void mfma_slice(uint32_t tid, const LDS uint16_t* sa, const LDS uint16_t* sb, f32x16 (&acc)[BM / 64][BN / 64]) {
+  constexpr int FM = BM / 64, FN = BN / 64, KS = kBK / 16;
   const int wave = tid / 64;
   const int wm = wave / 2, wn = wave % 2;
+  u32x4 af[KS][FM], bfr[KS][FN];
 #pragma unroll
-  for (int kk = 0; kk < kBK; kk += 16) {
-    u32x4 af[FM], bfr[FN];
+  for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-    for (int i = 0; i < FM; ++i) af[i] = frag<BM>(tid, sa, a_km, wm * (BM / 2) + i * 32, kk);
+    for (int i = 0; i < FM; ++i) af[ks][i] = frag<BM, AKM>(tid, sa, wm * (BM / 2) + i * 32, ks * 16);
 #pragma unroll
-    for (int j = 0; j < FN; ++j) bfr[j] = frag<BN>(tid, sb, b_km, wn * (BN / 2) + j * 32, kk);
+    for (int j = 0; j < FN; ++j) bfr[ks][j] = frag<BN, BKM>(tid, sb, wn * (BN / 2) + j * 32, ks * 16);
+  }
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<BF16>(af[i], bfr[j], acc[i][j]);
+      for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<BF16>(af[ks][i], bfr[ks][j], acc[i][j]);
+}
+
+// Fast-path main loop (see gemm_mfma): a ring of S stages, S - 1 slices in flight.
+template <int BM, int BN, bool BF16, bool AKM, bool BKM, int S>
+DEV void direct_loop(uint32_t tid, const DirectOp<BM>& da, const DirectOp<BN>& db, uint32_t nk,
+                     f32x16 (&acc)[BM / 64][BN / 64]) {
+  constexpr int SA = BM * kBK * 2, SB = BN * kBK * 2;
+  constexpr int LPS = BM / 32 + BN / 32;  // direct loads per wave per slice
+  const uint32_t last = nk - 1;
+  // slices 0 .. S-2 in flight (past the last slice, loads repeat it into a
+  // stage that is not read again)
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) {
+    const uint32_t sl = (uint32_t)s < last ? (uint32_t)s : last;
+    da.issue(sl, s * (SA + SB));
+    db.issue(sl, s * (SA + SB) + SA);
   }
+  for (uint32_t k = 0; k < nk; ++k) {
+    // this wave's loads of slice k have landed once at most the S-2 younger
+    // slices are in flight; the barrier then covers every wave's loads and
+    // every wave's last read of stage (k-1) % S, which the next issue refills
+    wait_vmcnt<(S - 2) * LPS>();
+    __syncthreads();
+    const uint32_t nx = k + S - 1 < last ? k + S - 1 : last;
+    const uint32_t ns = (k + S - 1) % S;
+    da.issue(nx, ns * (SA + SB));
+    db.issue(nx, ns * (SA + SB) + SA);
+    const uint32_t cs = (k % S) * (SA + SB);
+    mfma_slice<BM, BN, BF16, AKM, BKM>(tid, (const LDS uint16_t*)(g_smem + cs), (const LDS uint16_t*)(g_smem + cs + SA),
+                                       acc);
+  }
+  wait_vmcnt<0>();  // no load may still be writing the arena
+  __syncthreads();  // every wave is done with the ring (the C tile reuses it)
 }
 
 // BF16: operand dtype (bf16, else f16), a template parameter so the MFMA
@@ -777,7 +816,6 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
   constexpr int FM = BM / 64, FN = BN / 64;  // 32x32 blocks per wave along m / n
   constexpr int S = BM == 128 ? 3 : 4;       // ring stages (S * (BM + BN) * 128 bytes <= 96 KB)
   constexpr int SA = BM * kBK * 2, SB = BN * kBK * 2;
-  constexpr int LPS = BM / 32 + BN / 32;     // direct loads per wave per slice
   static_assert(S * (SA + SB) <= 98304, "operand ring exceeds the arena");
   const uint32_t tiles = t.tiles_m * t.tiles_n;
   const uint32_t split_index = item / tiles;
@@ -813,31 +851,17 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
     DirectOp<BN> db;
     da.init(tid, a_kc, pa, A.offset, A.stride[0], A.stride[1], m0, kbeg);
     db.init(tid, b_kc, pb, B.offset, B.stride[1], B.stride[0], n0, kbeg);
-    const uint32_t last = nk - 1;
-    // slices 0 .. S-2 in flight (past the last slice, loads repeat it into a
-    // stage that is not read again)
-#pragma unroll
-    for (int s = 0; s < S - 1; ++s) {
-      const uint32_t sl = (uint32_t)s < last ? (uint32_t)s : last;
-      da.issue(sl, s * (SA + SB));
-      db.issue(sl, s * (SA + SB) + SA);
+    if (a_kc) {
+      if (b_kc)
+        direct_loop<BM, BN, BF16, true, true, S>(tid, da, db, nk, acc);
+      else
+        direct_loop<BM, BN, BF16, true, false, S>(tid, da, db, nk, acc);
+    } else {
+      if (b_kc)
+        direct_loop<BM, BN, BF16, false, true, S>(tid, da, db, nk, acc);
+      else
+        direct_loop<BM, BN, BF16, false, false, S>(tid, da, db, nk, acc);
     }
-    for (uint32_t k = 0; k < nk; ++k) {
-      // this wave's loads of slice k have landed once at most the S-2 younger
-      // slices are in flight; the barrier then covers every wave's loads and
-      // every wave's last read of stage (k-1) % S, which the next issue refills
-      wait_vmcnt<(S - 2) * LPS>();
-      __syncthreads();
-      const uint32_t nx = k + S - 1 < last ? k + S - 1 : last;
-      const uint32_t ns = (k + S - 1) % S;
-      da.issue(nx, ns * (SA + SB));
-      db.issue(nx, ns * (SA + SB) + SA);
-      const uint32_t cs = (k % S) * (SA + SB);
-      mfma_slice<BM, BN, BF16>(tid, (const LDS uint16_t*)(g_smem + cs), (const LDS uint16_t*)(g_smem + cs + SA), a_kc,
-                               b_kc, acc);
-    }
-    wait_vmcnt<0>();  // no load may still be writing the arena
-    __syncthreads();  // every wave is done with the ring (the C tile reuses it)
   } else {
     LDS uint16_t* sa0 = (LDS uint16_t*)g_smem;
     LDS uint16_t* sb0 = (LDS uint16_t*)(g_smem + SA);
@@ -846,7 +870,7 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
       slow_stage<BM>(tid, pa, A.offset, A.stride[0], A.stride[1], m0, t.m, k0, kend, sa0);
       slow_stage<BN>(tid, pb, B.offset, B.stride[1], B.stride[0], n0, t.n, k0, kend, sb0);
       __syncthreads();
-      mfma_slice<BM, BN, BF16>(tid, sa0, sb0, true, true, acc);
+      mfma_slice<BM, BN, BF16, true, true>(tid, sa0, sb0, acc);
       __syncthreads();
     }
   }
