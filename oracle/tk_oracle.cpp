@@ -26,6 +26,7 @@
 // integer matmuls and Higham's bound, exact reductions, finite differences and
 // a hand-derived gradient of tiny MLPs, SGD closed forms, and invariants.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdint>
 #include <cstdio>
@@ -488,6 +489,32 @@ struct Interp {
 
   static T fma_(T a, T b, T c) { return std::fma(a, b, c); }
 
+  // Q8_0 quantisation of activation row r (blocks of 32 along k, the last one
+  // possibly shorter): d = amax / 127 in the working precision, each code the
+  // quotient x / d rounded to the nearest integer (ties to even) and held in
+  // [-127, 127]; an all-zero block has d = 0 and codes 0.  Finite inputs.
+  void quantise_row(const Value<T>& VA, const View& A, int64_t r, int64_t k, std::vector<int32_t>& code,
+                    std::vector<T>& scale) {
+    const int64_t nb = (k + 31) / 32;
+    code.assign(k, 0);
+    scale.assign(nb, 0);
+    for (int64_t b = 0; b < nb; ++b) {
+      const int64_t k0 = b * 32, k1 = std::min<int64_t>(k, k0 + 32);
+      T amax = 0;
+      for (int64_t kk = k0; kk < k1; ++kk) {
+        const T a = std::fabs(read2(VA, A, r, kk));
+        if (a > amax) amax = a;
+      }
+      const T d = amax / (T)127;
+      scale[b] = d;
+      if (d == (T)0) continue;
+      for (int64_t kk = k0; kk < k1; ++kk) {
+        const T q = std::nearbyint(read2(VA, A, r, kk) / d);
+        code[kk] = (int32_t)std::max((T)-127, std::min((T)127, q));
+      }
+    }
+  }
+
   void run_mm(const Op& op, Value<T>& out) {
     const bool add = op.opcode == "addmm" || op.opcode == "addmm_q8";
     const bool q8 = op.opcode == "mm_q8" || op.opcode == "addmm_q8";
@@ -518,6 +545,11 @@ struct Interp {
       fail("matrix output shape does not match its inputs");
     const T alpha = (T)(op.attrs.count("alpha") ? op.attrs.at("alpha") : 1.0f);
     const T beta = (T)(op.attrs.count("beta") ? op.attrs.at("beta") : 1.0f);
+    // xq: the activation rows are themselves quantised to Q8_0 before the
+    // product (the decode lane's activation quantisation step, `lk_quant`, in
+    // the emit.rs page's launch list).
+    const bool xq = q8 && op.attrs.count("xq") && op.attrs.at("xq") != 0.0f;
+    if (op.attrs.count("xq") && !q8) fail("xq applies to the q8 products only");
     const View* bias = add ? &op.args[0].view : nullptr;
     if (bias) check_broadcast(*bias, op.out.shape);
     out.data.assign(m * n, 0);
@@ -527,9 +559,23 @@ struct Interp {
 #pragma omp parallel for schedule(static)
     for (int64_t r = 0; r < m; ++r) {
       std::vector<int64_t> coord(2);
+      std::vector<int32_t> xcode;
+      std::vector<T> xscale;
+      if (xq) quantise_row(VA, A, r, k, xcode, xscale);
       for (int64_t c = 0; c < n; ++c) {
         T acc = 0;
-        for (int64_t kk = 0; kk < k; ++kk) {
+        if (xq) {
+          // Q8_0 x Q8_0: per 32-block an exact integer dot product of the
+          // codes, weighted by the product of the two block scales
+          for (int64_t b = 0; b * 32 < k; ++b) {
+            int64_t idot = 0;
+            for (int64_t kk = b * 32; kk < k && kk < b * 32 + 32; ++kk)
+              idot += (int64_t)xcode[kk] * (int64_t)read2(VB, B, c, kk);
+            const T w = xscale[b] * read2(*VS, *S, c, b);
+            acc = fma_(w, (T)idot, acc);
+          }
+        }
+        for (int64_t kk = 0; kk < (xq ? 0 : k); ++kk) {
           T a = read2(VA, A, r, kk);
           T b;
           if (q8) {

@@ -199,7 +199,8 @@ Program parse_program(const std::string& text) {
               if (!val.empty())
                 for (auto& d : split(val, ',')) op.dims.push_back(to_int(d));
             }
-          } else if (key == "alpha" || key == "beta" || key == "threshold" || key == "value" || key == "exponent") {
+          } else if (key == "alpha" || key == "beta" || key == "threshold" || key == "value" || key == "exponent" ||
+                     key == "xq") {
             op.attrs[key] = to_scalar(val);
           } else {
             raise(TK_E_PARSE, "unknown attribute '" + key + "'");
@@ -272,6 +273,7 @@ void validate_program(const Program& p) {
       if (!a.scalar) check_operand(a.spec, "operand");
     const std::string& c = op.opcode;
     const size_t n = op.args.size();
+    if (op.attrs.count("xq") && c != "mm_q8" && c != "addmm_q8") raise(TK_E_ARG, "xq applies to the q8 products only");
     if (pointwise.count(c)) {
       const_cast<Op&>(op).cls = OC_POINTWISE;
       for (auto& a : op.args)
@@ -303,6 +305,8 @@ void validate_program(const Program& p) {
         if (S.dtype != DT_F32 || S.shape.size() != 2 || S.shape[0] != nn || S.shape[1] != (k + 31) / 32)
           raise(TK_E_SHAPE, "q8 scales must be float32 [n, ceil(k/32)]");
         if (A.dtype == DT_I8) raise(TK_E_DTYPE, "activations must be float");
+        if (op.attrs.count("xq") && op.attrs.at("xq") != 0.0f && op.attrs.at("xq") != 1.0f)
+          raise(TK_E_ARG, "xq must be 0 or 1");
       } else {
         if (B.shape[0] != k) raise(TK_E_SHAPE, "mm requires compatible rank-two tensors");
         if (A.dtype == DT_I8 || B.dtype == DT_I8) raise(TK_E_DTYPE, "int8 operands need the q8 form");

@@ -343,11 +343,13 @@ def residual_step(width: int, layers: int, batch: int, dtype: str, lr: float,
     return p
 
 
-def gemv_q8_stack(k: int, n: int, layers: int, block: int = 32, rows: int = 1) -> Program:
+def gemv_q8_stack(k: int, n: int, layers: int, block: int = 32, rows: int = 1, xq: bool = False) -> Program:
     """y_l = relu(addmm_q8(b_l, y_{l-1}, q_l, s_l)) in bf16, y_0 = x [rows,k]
     (rows > 1: several decode rows sharing each weight pass).
     q_l is int8 [n,k] (row n holds output n's weights, blocks of ``block``
-    along k), s_l float32 [n, ceil(k/block)], b_l float32 [n]."""
+    along k), s_l float32 [n, ceil(k/block)], b_l float32 [n].
+    xq: each product first quantises its activation rows to Q8_0 (blocks of
+    32, one float32 scale each) and multiplies codes by codes."""
     p = Program()
     y = p.input("x", "bf16", (rows, k))
     nb = (k + block - 1) // block
@@ -356,7 +358,7 @@ def gemv_q8_stack(k: int, n: int, layers: int, block: int = 32, rows: int = 1) -
         params.append((p.input(f"q{i + 1}", "i8", (n, k)), p.input(f"s{i + 1}", "f32", (n, nb)),
                        p.input(f"b{i + 1}", "f32", (n,))))
     for i, (q, s, b) in enumerate(params):
-        z = p.op("addmm_q8", [b, y, q, s], "bf16", (rows, n), name=f"z{i + 1}")
+        z = p.op("addmm_q8", [b, y, q, s], "bf16", (rows, n), name=f"z{i + 1}", **({"xq": 1.0} if xq else {}))
         y = p.op("relu", [z], "bf16", name=f"y{i + 1}")
     p.output(y)
     return p
@@ -382,7 +384,7 @@ def build(cfg: dict, **variant) -> Program:
     if kind == "residual":
         return residual_step(cfg["width"], cfg["layers"], cfg["batch"], cfg["dtype"], cfg["lr"], **variant)
     if kind == "gemv":
-        return gemv_q8_stack(cfg["k"], cfg["n"], cfg["layers"], rows=cfg.get("rows", 1))
+        return gemv_q8_stack(cfg["k"], cfg["n"], cfg["layers"], rows=cfg.get("rows", 1), xq=cfg.get("xq", False))
     raise ValueError(kind)
 
 
