@@ -37,17 +37,22 @@ WORKLOAD_NAMES = {
     "c5": "resmlp16-fp16-b512-w2048",
     "c2a": "mlp3-bf16-b256-512-1024-1024-64-adamw",
     "c3r4": "gemv8-int8w-bf16x-4x4096x4096",
+    "c3q": "gemv8-int8w-q8x-4096x4096",
 }
 
 
 def config(name: str) -> dict:
     """The workload's configuration; c2a is C2 with AdamW (defaults 0.9,
-    0.999, 1e-8, weight decay 1e-2) in place of SGD, at step t = 10."""
+    0.999, 1e-8, weight decay 1e-2) in place of SGD, at step t = 10; c3r4 is
+    C3 with 4 decode rows; c3q is C3 with its activations quantised to Q8_0
+    inside each product."""
     from persistent_whole_step_amd import programs
     if name == "c2a":
         return dict(programs.CONFIGS["c2"], optimizer=programs.AdamW(), adam_t=10)
     if name == "c3r4":
         return dict(programs.CONFIGS["c3"], rows=4)
+    if name == "c3q":
+        return dict(programs.CONFIGS["c3"], xq=True)
     return programs.CONFIGS[name]
 
 
@@ -263,7 +268,7 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--others", default="c1,c2a,c3,c3r4,c4,c5", help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--others", default="c1,c2a,c3,c3r4,c3q,c4,c5", help="comma list of extra workloads ('' for none)")
     ap.add_argument("--other-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")

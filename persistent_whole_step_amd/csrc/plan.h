@@ -104,6 +104,8 @@ constexpr uint32_t kGemvRows = 4;      // int8-weight products: activation rows 
 constexpr uint32_t F_ROWWG = 4u;       // combine: one workgroup per output, parts summed across its threads
 constexpr uint32_t F_QPREFETCH = 16u;  // one-row int8 GEMV whose weight and scales no stage writes: their
                                        //   loads may start before the grid barrier that precedes the stage
+constexpr uint32_t F_XQ = 32u;         // int8 GEMV: quantise the activation rows to Q8_0 (blocks of 32,
+                                       //   d = amax/127, codes round(x/d)) and multiply codes by codes
 
 struct DTask {
   uint8_t kind;

@@ -1090,6 +1090,53 @@ DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t view
         }
       __syncthreads();
     }
+    if (t.flags & F_XQ) {
+      // Q8_0 activations: the two lanes of a 32-block exchange their
+      // absolute maxima, d = amax / 127, codes round(x / d) (ties to even;
+      // d = 0 gives codes 0), then per weight row an exact integer dot of
+      // the lane's 16 codes with its 16 weight bytes, weighted by d * s.
+      // The quotients are correctly rounded divisions, as on the CPU side.
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        const uint32_t kc = kpass + 1024 * j + lane * 16;
+#pragma unroll
+        for (int r = 0; r < R; ++r) {
+          float xk[16], amax = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const int64_t xi = X.offset + (int64_t)(r0 + r) * X.stride[0] + (int64_t)(kc + e) * X.stride[1];
+            if (xreg) {
+              const uint32_t w = xr[j][e / 8][(e % 8) / 2];
+              xk[e] = kc < K ? __uint_as_float((e & 1) ? (w & 0xffff0000u) : (w << 16)) : 0.0f;
+            } else {
+              xk[e] = (kc + e < K) ? (staged ? xs[r * K + kc + e] : load_elem(px, X.dtype, xi)) : 0.0f;
+            }
+            amax = fmaxf(amax, fabsf(xk[e]));
+          }
+          amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
+          const float d = amax / 127.0f;
+          int32_t cw[4] = {0, 0, 0, 0};
+          if (d != 0.0f) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const float c = fminf(127.0f, fmaxf(-127.0f, __builtin_rintf(xk[e] / d)));
+              cw[e / 4] |= ((int32_t)c & 0xff) << (8 * (e % 4));
+            }
+          }
+          if (kc < K) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              int32_t idot = 0;
+#pragma unroll
+              for (int w4 = 0; w4 < 4; ++w4) idot = __builtin_amdgcn_sdot4((int32_t)qv[i][j][w4], cw[w4], idot, false);
+              const float wsc = d * sv[i][j];
+              acc[i][r] = __builtin_fmaf(wsc, (float)idot, acc[i][r]);
+            }
+          }
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int j = 0; j < NC; ++j) {
       const uint32_t kc = kpass + 1024 * j + lane * 16;

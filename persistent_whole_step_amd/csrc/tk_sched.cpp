@@ -1769,6 +1769,7 @@ struct Builder {
           if (P.inputs[kv.second].buf == b) stable = false;
       }
       if (stable && m == 1 && k <= 4096) t.flags |= F_QPREFETCH;
+      if (mm.attrs.count("xq") && mm.attrs.at("xq") != 0.0f) t.flags |= F_XQ;
     } else {
       ops.push_back(operand_view(A, 0, 1));  // A over (m, k)
       ops.push_back(operand_view(B, 0, 1));  // B over (k, n)
@@ -1783,6 +1784,7 @@ struct Builder {
     std::string desc = mm.name + " (" + mm.opcode + " " + std::to_string(m) + "x" + std::to_string(k) + "x" +
                        std::to_string(n) + ")";
     if (t.flags & F_QPREFETCH) desc += " [weights fetched across the barrier]";
+    if (t.flags & F_XQ) desc += " [activations quantised to Q8_0]";
     if (!e.chain.empty()) {
       desc += e.update ? " +update" : " +epilogue";
       for (int c : e.chain) desc += " " + op(c).name;

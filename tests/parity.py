@@ -146,10 +146,14 @@ def contraction_reference(op, vals: dict, value_specs: dict):
         q = _view_read(vals[Q.buf], Q).astype(np.float64)
         s = _view_read(vals[S.buf], S).astype(np.float64)
         k = a.shape[1]
-        w = (q * np.repeat(s, 32, axis=1)[:, :k]).astype(np.float32).astype(np.float64)  # fl(q*s)
-        b = w.T
-    exact = a @ b
-    mag = np.abs(a) @ np.abs(b)
+        if op.attrs.get("xq"):
+            exact, mag = _xq_reference(a, q, s)
+        else:
+            w = (q * np.repeat(s, 32, axis=1)[:, :k]).astype(np.float32).astype(np.float64)  # fl(q*s)
+            b = w.T
+    if op.opcode in ("mm", "addmm") or not op.attrs.get("xq"):
+        exact = a @ b
+        mag = np.abs(a) @ np.abs(b)
     if op.opcode in ("addmm", "addmm_q8"):
         alpha = op.attrs.get("alpha", 1.0)
         beta = op.attrs.get("beta", 1.0)
@@ -158,6 +162,45 @@ def contraction_reference(op, vals: dict, value_specs: dict):
         bv = np.broadcast_to(bv, exact.shape)
         exact = alpha * exact + (beta * bv if beta != 0 else 0.0)
         mag = abs(alpha) * mag + (abs(beta) * np.abs(bv) if beta != 0 else 0.0)
+    return exact, mag
+
+
+def xq_codes(a: np.ndarray):
+    """Q8_0 codes and block scales of activation rows a [m, k] (float32
+    arithmetic: d = amax / 127, codes round-half-even(x / d) in [-127, 127])."""
+    a32 = a.astype(np.float32)
+    m, k = a32.shape
+    nb = (k + 31) // 32
+    codes = np.zeros((m, k), np.int64)
+    d = np.zeros((m, nb), np.float32)
+    for b in range(nb):
+        blk = a32[:, 32 * b:32 * b + 32]
+        amax = np.abs(blk).max(axis=1)
+        db = amax / np.float32(127)
+        d[:, b] = db
+        nz = db != 0
+        with np.errstate(divide="ignore", invalid="ignore"):
+            c = np.rint(blk / db[:, None])
+        codes[nz, 32 * b:32 * b + blk.shape[1]] = np.clip(c[nz], -127, 127).astype(np.int64)
+    return codes, d
+
+
+def _xq_reference(a, q, s):
+    """float64 value of the quantised-activation product and its magnitude
+    sum_b |d_b s_b| sum_k |code q| (codes from xq_codes)."""
+    codes, d = xq_codes(a)
+    m, k = a.shape
+    n = q.shape[0]
+    exact = np.zeros((m, n))
+    mag = np.zeros((m, n))
+    qi = q.astype(np.int64)
+    for b in range(d.shape[1]):
+        sl = slice(32 * b, min(k, 32 * b + 32))
+        idot = codes[:, sl] @ qi[:, sl].T
+        amag = np.abs(codes[:, sl]) @ np.abs(qi[:, sl]).T
+        w = (d[:, b][:, None] * s[:, b].astype(np.float32)[None, :]).astype(np.float64)  # fl(d * s)
+        exact += w * idot
+        mag += np.abs(w) * amag
     return exact, mag
 
 

@@ -256,6 +256,49 @@ def test_gemv_q8(oracle_mod, m, k, n):
     parity.assert_contraction(got[0], want[0], np.maximum(exact, 0), mag, "bf16", "gemv q8")
 
 
+@pytest.mark.parametrize("m,k,xdt", [(1, 4096, "bf16"), (1, 96, "bf16"), (1, 1000, "bf16"), (1, 200, "f32"),
+                                     (3, 1000, "bf16"), (5, 256, "f16"), (4, 4096, "bf16")])
+def test_gemv_xq_codes_bitexact(oracle_mod, m, k, xdt):
+    """One-hot weights (n = k, scales 1) return fl(d * code) per activation
+    element: the quantised codes and block scales equal the oracle's bit for
+    bit (ragged K, the register and LDS activation paths, several slabs)."""
+    say("gemv xq codes", m, k, xdt)
+    rng = np.random.default_rng(k + m)
+    nb = (k + 31) // 32
+    p = Program()
+    x = p.input("x", xdt, (m, k))
+    q = p.input("q", "i8", (k, k))
+    s = p.input("s", "f32", (k, nb))
+    p.output(p.op("mm_q8", [x, q, s], "f32", (m, k), xq=1.0))
+    xv = synth.random_tensor(rng, (m, k), xdt, 2.0)
+    if k >= 64:
+        xv.reshape(-1)[:32] = 0  # an all-zero block (d = 0) in row 0
+    ins = [xv, np.eye(k, dtype=np.int8), np.ones((k, nb), np.float32)]
+    got, _ = parity.gpu_run(p, ins)
+    (want,) = oracle_mod.run(p.text(), ins)
+    parity.assert_bitexact(got[0], want, "f32", "xq codes")
+
+
+@pytest.mark.parametrize("m,k,n", [(1, 4096, 64), (1, 1000, 24), (2, 4096, 48), (6, 2048, 37), (4, 96, 7)])
+def test_gemv_xq(oracle_mod, m, k, n):
+    say("gemv xq", m, k, n)
+    rng = np.random.default_rng(k + n + m + 1)
+    nb = (k + 31) // 32
+    p = Program()
+    x = p.input("x", "bf16", (m, k))
+    q = p.input("q", "i8", (n, k))
+    s = p.input("s", "f32", (n, nb))
+    b = p.input("b", "f32", (n,))
+    z = p.op("addmm_q8", [b, x, q, s], "bf16", (m, n), xq=1.0)
+    p.output(p.op("relu", [z], "bf16"))
+    ins = [synth.random_tensor(rng, (m, k), "bf16"), synth.random_tensor(rng, (n, k), "i8"),
+           (0.01 * (1 - rng.random((n, nb)))).astype(np.float32), synth.random_tensor(rng, (n,), "f32", 0.3)]
+    got, _ = parity.gpu_run(p, ins)
+    want = oracle_mod.run(p.text(), ins)
+    exact, mag = parity.contraction_reference(p.ops[0], dict(zip(["x", "q", "s", "b"], ins)), None)
+    parity.assert_contraction(got[0], want[0], np.maximum(exact, 0), mag, "bf16", "gemv xq")
+
+
 def test_gemv_prefetch_matches_plain_loads():
     """A 3-layer int8 stack on a 24-workgroup grid: each workgroup's first item
     of a layer has its weights fetched across the barrier, its later items
@@ -279,6 +322,9 @@ SMALL = {
     "c2s": dict(kind="mlp", dims=(192, 320, 256, 48), batch=96, dtype="bf16", lr=1e-3),
     "c3s": dict(kind="gemv", k=1024, n=1024, layers=3),
     "c3r": dict(kind="gemv", k=1024, n=1024, layers=3, rows=6),  # decode rows in two slabs
+    # activations quantised to Q8_0 inside each product
+    "c3q": dict(kind="gemv", k=1024, n=1024, layers=3, xq=True),
+    "c3qr": dict(kind="gemv", k=1024, n=1024, layers=3, rows=6, xq=True),
     "c4s": dict(kind="mlp", dims=(256, 384, 256, 128), batch=160, dtype="bf16", lr=1e-4),
     "c5s": dict(kind="residual", width=256, layers=4, batch=96, dtype="f16", lr=1e-4),
     # AdamW in place of SGD: two float32 states per parameter, updated in place

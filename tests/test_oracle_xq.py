@@ -156,3 +156,18 @@ def test_xq_rejected_outside_q8(oracle_mod):
     p.output(p.op("mm", [a, b], "f32", (2, 4), xq=1.0))
     with pytest.raises(Exception):
         oracle_mod.run(p.text(), [np.ones((2, 3), np.float32), np.ones((3, 4), np.float32)])
+
+
+def test_parity_harness_codes_match_oracle(oracle_mod):
+    """The parity harness's own float32 quantiser (used for the tolerance
+    reference of GPU results) gives the oracle's codes and scales."""
+    from tests import parity
+    k = 1000
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((3, k)) * 3).astype(np.float32)
+    x[1, :32] = 0
+    q, s = _one_hot(k)
+    (y,) = oracle_mod.run(_prog(3, k, k).text(), [x, q, s])
+    codes, d = parity.xq_codes(x)
+    want = (np.repeat(d, 32, axis=1)[:, :k] * codes.astype(np.float32)).astype(np.float32)
+    np.testing.assert_array_equal(y, want)

@@ -111,6 +111,28 @@ def test_gemv_weight_prefetch_only_for_stable_inputs(kind, tagged):
     assert d.count("[weights fetched across the barrier]") == tagged
 
 
+def test_activation_quantisation_flag():
+    # xq on a q8 product reaches its GEMV task; it is refused elsewhere and
+    # for values other than 0 and 1
+    d = tk.compile(programs.gemv_q8_stack(256, 256, 2, xq=True).text(), device=-1).dump()
+    assert d.count("[activations quantised to Q8_0]") == 2
+    d = tk.compile(programs.gemv_q8_stack(256, 256, 2).text(), device=-1).dump()
+    assert "quantised" not in d
+    p = Program()
+    a = p.input("a", "f32", (2, 3))
+    b = p.input("b", "f32", (3, 4))
+    p.output(p.op("mm", [a, b], "f32", (2, 4), xq=1.0))
+    with pytest.raises(tk.TkError, match="xq"):
+        tk.compile(p.text(), device=-1)
+    p = Program()
+    x = p.input("x", "bf16", (1, 64))
+    q = p.input("q", "i8", (8, 64))
+    s = p.input("s", "f32", (8, 2))
+    p.output(p.op("mm_q8", [x, q, s], "f32", (1, 8), xq=2.0))
+    with pytest.raises(tk.TkError, match="xq"):
+        tk.compile(p.text(), device=-1)
+
+
 def _tile_update(later_read: bool):
     p = Program()
     a = p.input("a", "f32", (8, 8))
