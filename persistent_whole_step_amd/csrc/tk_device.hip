@@ -1254,6 +1254,84 @@ DEV void fin_batch(Batch& b, const DTask& t, uint32_t ins_off, uint32_t width) {
   set_1d(b, t.m);
 }
 
+// Epilogue of an int8-weight GEMV item: its 16 x rows outputs, one per thread
+// of wave 0, evaluated from the row sums in registers.  The same programs
+// and arithmetic as the expression machine (vm_run), element by element, but
+// without a batch: a slab has too few outputs for the exchange and the
+// per-chunk machinery to pay.
+DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
+                       uint32_t item) {
+  if (tid >= 64) return;
+  const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
+  const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
+  const uint32_t r = tid / 16, col = cb * 16 + tid % 16;
+  const bool ok = r < rows && col < t.n;
+  const LDS float* red = (const LDS float*)(g_smem + kGemvRed);
+  float y = ok ? red[r * 16 + tid % 16] : 0.0f;
+  Batch b;
+  expr_batch(b, t, ins_off);
+  task_space(b, t);
+  uint32_t c[kMaxDims];
+  unravel(ok ? (r0 + r) * t.n + col : 0u, b, c);  // other threads address element 0
+  for (uint32_t pc = 0; pc < b.n; ++pc) {
+    const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + b.ins + pc * sizeof(DIns));
+    const uint32_t w0 = uniform(iw[0]), w1 = uniform(iw[1]);
+    const float a = __uint_as_float(uniform(iw[2])), sv = __uint_as_float(uniform(iw[3]));
+    const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff, rnd = (w0 >> 16) & 0xff, rev = w0 >> 24;
+    const uint32_t arg = w1 & 0xffff;
+    float o = 0.0f;
+    if (src == SRC_VIEW || op == VM_STORE) {
+      const VView v = load_view(views_off + arg * sizeof(DView));
+      GLOBAL uint8_t* p = base_ptr(ka, v.base);
+      const int32_t idx = view_index(v, c);
+      if (op == VM_STORE) {
+        if (ok) {
+          if (v.dtype == DT_F32)
+            ((GLOBAL float*)p)[idx] = y;
+          else if (v.dtype != DT_I8)
+            ((GLOBAL uint16_t*)p)[idx] = (uint16_t)f32_to_half_bits(y, v.dtype == DT_BF16);
+        }
+        continue;
+      }
+      o = load_elem(p, v.dtype, idx);
+    } else if (src == SRC_SLOT) {
+      o = slot_base(arg)[tid];
+    } else if (src == SRC_SCALAR) {
+      o = sv;
+    }
+    switch (op) {
+      case VM_LOAD: y = o; break;
+      case VM_ADD:
+        if (rev) { const float u = a * y; y = o + u; }
+        else { const float u = a * o; y = y + u; }
+        break;
+      case VM_SUB:
+        if (rev) { const float u = a * y; y = o - u; }
+        else { const float u = a * o; y = y - u; }
+        break;
+      case VM_MUL: y = y * o; break;
+      case VM_DIV: y = rev ? o / y : y / o; break;
+      case VM_NEG: y = -y; break;
+      case VM_RELU: y = y < 0.0f ? 0.0f : y; break;
+      case VM_SQUARE: y = y * y; break;
+      case VM_POW: y = powf(y, a); break;
+      case VM_TB:
+        if (rev) y = y <= a ? 0.0f : o;
+        else y = o <= a ? 0.0f : y;
+        break;
+      case VM_SAVE: slot_base(arg)[tid] = y; break;
+      case VM_SCALE: y = a * y; break;
+      case VM_ZERO: y = 0.0f; break;
+      case VM_SQRT: y = sqrtf(y); break;
+      default: break;
+    }
+    if (rnd == DT_BF16)
+      y = bf16_bits_to_f32(f32_to_bf16_bits(y));
+    else if (rnd == DT_F16)
+      y = f16_bits_to_f32(f32_to_f16_bits(y));
+  }
+}
+
 // Fill batch `bi` of a work item: set up the program and the exchange, and
 // set this thread's live-chunk mask.  Returns false when the item has no
 // batch `bi` (uniform across the workgroup).
@@ -1328,29 +1406,6 @@ DEV bool fill(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, uin
           float a = ok ? P[e + j] : 0.0f;
           for (uint32_t s = 1; s < t.split; ++s) a = a + (ok ? P[s * total + e + j] : 0.0f);
           xv(tid, q * W + j) = a;
-        }
-      }
-      return true;
-    }
-    case T_GEMV_Q8: {
-      // epilogue over the slab's [rows][16] sums: per activation row, two
-      // threads take 8-wide chunks (or one thread sixteen singles)
-      if (bi > 0) return false;
-      expr_batch(b, t, ins_off);
-      task_space(b, t);
-      const LDS float* red = (const LDS float*)(g_smem + kGemvRed);
-      const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
-      const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
-      const uint32_t per = W == 8 ? 2u : 1u;  // threads per activation row
-      const uint32_t rb = cb * 16;
-      if (tid < per * rows) {
-        const uint32_t r = tid / per, half = tid % per;
-        for (int q = 0; q < C; ++q) {
-          const uint32_t col = rb + (W == 8 ? half * 8 : q);
-          const bool ok = (W == 8 ? q == 0 : true) && col < t.n;
-          live |= (ok ? 1u : 0u) << q;
-          xe(tid, q) = ok ? (r0 + r) * t.n + col : 0;
-          for (int j = 0; j < W; ++j) xv(tid, q * W + j) = red[r * 16 + (W == 8 ? half * 8 + j : q)];
         }
       }
       return true;
@@ -1555,7 +1610,9 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
     }
     case T_GEMV_Q8:
       gemv_q8(tid, ka, t, sd.off_views, item, pref);
-      break;
+      gemv_epilogue(tid, ka, t, sd.off_views, sd.off_ins, item);
+      __syncthreads();  // the next item may overwrite the row sums and the slots
+      return;
     default:
       break;
   }

@@ -299,6 +299,62 @@ def test_gemv_xq(oracle_mod, m, k, n):
     parity.assert_contraction(got[0], want[0], np.maximum(exact, 0), mag, "bf16", "gemv xq")
 
 
+def _gemv_chain(m, k, n, xq, slots):
+    """An int8 GEMV whose whole pointwise chain fuses into its epilogue:
+    broadcast and full-shape view operands, scalars, alpha forms, rev
+    division, square, sqrt, neg, relu, mixed dtypes, and (slots=True) a value
+    saved and reused by threshold_backward."""
+    nb = (k + 31) // 32
+    p = Program()
+    x = p.input("x", "bf16", (m, k))
+    q = p.input("q", "i8", (n, k))
+    s = p.input("s", "f32", (n, nb))
+    b = p.input("b", "f32", (n,))
+    c = p.input("c", "bf16", (n,))
+    T = p.input("T", "f32", (m, n))
+    b2 = p.input("b2", "f16", (n,))
+    z = p.op("addmm_q8", [b, x, q, s], "bf16", (m, n), **({"xq": 1.0} if xq else {}))
+    u = p.op("sub", [z, c], "bf16", alpha=0.75)
+    v = p.op("mul", [u, 1.5], "f32")
+    if slots:
+        w = p.op("div", [T, v], "f32")
+        y = p.op("threshold_backward", [w, u], "bf16", threshold=0.125)
+    else:
+        w = p.op("div", [v, T], "f32")
+        w2 = p.op("pow", [w], "f16", exponent=2.0)
+        w3 = p.op("sqrt", [w2], "f32")
+        w4 = p.op("neg", [w3], "bf16")
+        w5 = p.op("add", [w4, b2], "f32", alpha=2.0)
+        y = p.op("relu", [w5], "f16")
+    p.output(y)
+    rng = np.random.default_rng(m * 7 + k + n)
+    ins = [synth.random_tensor(rng, (m, k), "bf16"), synth.random_tensor(rng, (n, k), "i8"),
+           (0.01 * (1 - rng.random((n, nb)))).astype(np.float32), synth.random_tensor(rng, (n,), "f32", 0.3),
+           synth.random_tensor(rng, (n,), "bf16", 0.5), synth.random_tensor(rng, (m, n), "f32", 2.0),
+           synth.random_tensor(rng, (n,), "f16", 0.5)]
+    return p, ins
+
+
+@pytest.mark.parametrize("m,k,n,xq,slots", [(1, 1024, 40, False, False), (3, 256, 40, False, True),
+                                           (6, 512, 37, True, False), (1, 4096, 64, True, True)])
+def test_gemv_epilogue_chain(oracle_mod, m, k, n, xq, slots):
+    """The GEMV epilogue evaluates a fused chain element by element; with
+    epilogue fusion off the chain runs as elementwise tasks through the
+    expression machine.  Both agree bit for bit, and every node of the probe
+    (which fuses the chain too, storing each value) matches the oracle."""
+    say("gemv epilogue chain", m, k, n, xq, slots)
+    base, ins = _gemv_chain(m, k, n, xq, slots)
+    o1, p1 = parity.gpu_run(base, [a.copy() for a in ins])
+    assert "+side" in p1.dump() and p1.query()["n_stages"] == 1
+    o2, p2 = parity.gpu_run(base, [a.copy() for a in ins], fuse_epilogues=0)
+    assert p2.query()["n_stages"] > 1
+    parity.assert_bitexact(o1[0], o2[0], base.outputs[0].dtype, "chain output")
+    probe = base.probe()
+    o3, _ = parity.gpu_run(probe, [a.copy() for a in ins])
+    vals = parity.probe_values(base, probe, o3)
+    assert parity.check_per_node(oracle_mod, base, ins, vals) == len(base.ops)
+
+
 def test_gemv_prefetch_matches_plain_loads():
     """A 3-layer int8 stack on a 24-workgroup grid: each workgroup's first item
     of a layer has its weights fetched across the barrier, its later items
