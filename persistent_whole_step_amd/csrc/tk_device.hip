@@ -1332,6 +1332,62 @@ DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t vie
   }
 }
 
+// A contraction tile's batch (chunks q0 + q * kBlock + tid of the [bm][bn]
+// tile, W elements each) into the exchange, or its split-K partial into the
+// workspace.  All tile reads are issued before the exchange writes.  Returns
+// the live-chunk mask.
+template <int W>
+DEV uint32_t fill_tile(uint32_t tid, const Ctx& ka, const DTask& t, const ItemState& st, int q0) {
+  constexpr int C = kVmElems / W;
+  const int pitch = st.bn + 4;
+  const int lcpr = __builtin_ctz((uint32_t)(st.bn / W));  // log2 chunks per row
+  const int nchunks = st.bm << lcpr;
+  const LDS float* ctile = (const LDS float*)g_smem;
+  float v[C][W];
+  uint32_t e[C];
+  bool ok[C], in[C];
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    const int qq = q0 + q * kBlock + (int)tid;
+    in[q] = qq < nchunks;
+    const int r = in[q] ? qq >> lcpr : 0, cc = in[q] ? (qq & ((1 << lcpr) - 1)) * W : 0;
+    const uint32_t row = st.m0 + r, col = st.n0 + cc;
+    ok[q] = in[q] && row < t.m && col < t.n;
+    e[q] = ok[q] ? row * t.n + col : 0;
+    const LDS float* src = ctile + r * pitch + cc;
+    if constexpr (W == 8) {
+      // rows are 16-byte aligned (pitch a multiple of 4) and chunks start at
+      // multiples of 8 columns
+      const u32x4 a = *(const LDS u32x4*)src, c = *(const LDS u32x4*)(src + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        v[q][j] = __uint_as_float(a[j]);
+        v[q][4 + j] = __uint_as_float(c[j]);
+      }
+    } else {
+      v[q][0] = *src;
+    }
+  }
+  if (t.flags & F_PARTIAL) {
+    GLOBAL float* P = ws_f32(ka, t.scratch) + (uint64_t)st.split_index * t.m * t.n;
+#pragma unroll
+    for (int q = 0; q < C; ++q)
+      if (ok[q])
+#pragma unroll
+        for (int j = 0; j < W; ++j) P[e[q] + j] = v[q][j];
+    return 0u;
+  }
+  uint32_t live = 0;
+#pragma unroll
+  for (int q = 0; q < C; ++q) {
+    live |= (ok[q] ? 1u : 0u) << q;
+    xe(tid, q) = e[q];
+#pragma unroll
+    for (int j = 0; j < W; ++j) xv(tid, q * W + j) = in[q] ? v[q][j] : 0.0f;
+  }
+  return live;
+}
+
 // Fill batch `bi` of a work item: set up the program and the exchange, and
 // set this thread's live-chunk mask.  Returns false when the item has no
 // batch `bi` (uniform across the workgroup).
@@ -1363,31 +1419,15 @@ DEV bool fill(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, uin
     case T_GEMM_SIMT: {
       // epilogue over the fp32 tile in LDS ([bm][bn + 4]), 16 elements per
       // thread per batch; split-K partial tiles are written out instead
-      const int pitch = st.bn + 4;
-      const int cpr = st.bn / W;  // chunks per row
-      const int nchunks = st.bm * cpr;
+      const int cpr = st.bn / W;  // chunks per row (a power of two)
       const int q0 = (int)bi * kBlock * C;
-      if (q0 >= nchunks) return false;
+      if (q0 >= st.bm * cpr) return false;
       expr_batch(b, t, ins_off);
       task_space(b, t);
-      const LDS float* ctile = (const LDS float*)g_smem;
-      const bool partial = (t.flags & F_PARTIAL) != 0;
-      GLOBAL float* P = ws_f32(ka, t.scratch) + (uint64_t)st.split_index * t.m * t.n;
-      for (int q = 0; q < C; ++q) {
-        const int qq = q0 + q * kBlock + (int)tid;
-        const int r = qq / cpr, cc = (qq % cpr) * W;
-        const uint32_t row = st.m0 + r, col = st.n0 + cc;
-        const bool ok = qq < nchunks && row < t.m && col < t.n;
-        const uint32_t e = ok ? row * t.n + col : 0;
-        if (partial) {
-          if (ok)
-            for (int j = 0; j < W; ++j) P[e + j] = ctile[r * pitch + cc + j];
-          continue;
-        }
-        live |= (ok ? 1u : 0u) << q;
-        xe(tid, q) = e;
-        for (int j = 0; j < W; ++j) xv(tid, q * W + j) = qq < nchunks ? ctile[r * pitch + cc + j] : 0.0f;
-      }
+      if (W == 8)
+        live = fill_tile<8>(tid, ka, t, st, q0);
+      else
+        live = fill_tile<1>(tid, ka, t, st, q0);
       return true;
     }
     case T_GEMM_REDUCE: {
