@@ -106,6 +106,12 @@ constexpr uint32_t F_QPREFETCH = 16u;  // one-row int8 GEMV whose weight and sca
                                        //   loads may start before the grid barrier that precedes the stage
 constexpr uint32_t F_XQ = 32u;         // int8 GEMV: quantise the activation rows to Q8_0 (blocks of 32,
                                        //   d = amax/127, codes round(x/d)) and multiply codes by codes
+constexpr uint32_t F_FASTEPI = 64u;    // contraction tile: the epilogue runs as a register program (at most
+                                       //   kFastIns instructions, no slots, 2-D views with column stride 1
+                                       //   or 0 and 8-element chunk alignment, at most kFastLoads loaded
+                                       //   views, no load after a store that may overlap it)
+constexpr int kFastIns = 8;
+constexpr int kFastLoads = 3;
 
 struct DTask {
   uint8_t kind;

@@ -216,6 +216,7 @@ tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int3
     so.gemm_split_k = o.gemm_split_k;
     so.launch_mode = o.launch_mode;
     so.gemm_tile = o.gemm_tile;
+    so.fast_epilogue = o.batch_epilogues == 0;
     so.num_cus = o.num_cus > 0 ? o.num_cus : 256;
     int occupancy = 0;
     hipFuncAttributes attr{};

@@ -1600,6 +1600,301 @@ DEV void consume(uint32_t tid, const DTask& t, const Batch& b, uint32_t live, It
   }
 }
 
+// ------------------------------------------------------ register epilogue --
+// A contraction tile whose epilogue the scheduler marked F_FASTEPI runs it
+// here instead of through machine batches.  The program (at most kFastIns
+// instructions; loads and stores of 2-D views over (row, col) with column
+// stride 1, or 0 for loads, and 8-element chunk alignment) is decoded once per
+// item.  Each thread takes G 8-wide column chunks of the LDS tile at a time
+// (consecutive threads, consecutive chunks), issues the loads of every loaded
+// view for them before the first instruction runs (the scheduler proved that
+// no load reads bytes an earlier store of the program writes), and carries
+// the values in registers through to the stores.  The arithmetic, its order
+// and every rounding are vm_run's, so results are identical bit for bit.
+
+struct FastProg {
+  uint32_t n;                      // instructions
+  uint32_t w0[kFastIns];           // op | src << 8 | rnd << 16 | rev << 24
+  float a[kFastIns], s[kFastIns];  // alpha / threshold, scalar operand
+  uint32_t slot[kFastIns];         // loaded-view slot of a view operand
+  GLOBAL uint8_t* sp[kFastIns];    // store views: base, offset, row stride, dtype
+  int32_t soff[kFastIns], ss0[kFastIns];
+  uint32_t sdt[kFastIns];
+  uint32_t nl;                     // loaded views, in program order
+  const GLOBAL uint8_t* lp[kFastLoads];
+  int32_t loff[kFastLoads], ls0[kFastLoads];
+  uint32_t ldt[kFastLoads], ls1[kFastLoads];
+};
+
+// Decode the program; false (uniform) when a unit-stride view's base is not
+// 16-byte aligned, in which case the batches take over.
+DEV bool fast_decode(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off, FastProg& fp) {
+  fp.n = t.expr_len;
+  fp.nl = 0;
+  bool ok = true;
+#pragma unroll
+  for (int l = 0; l < kFastLoads; ++l) {
+    fp.lp[l] = base_ptr(ka, 0);
+    fp.loff[l] = fp.ls0[l] = 0;
+    fp.ldt[l] = DT_F32;
+    fp.ls1[l] = 0;
+  }
+#pragma unroll
+  for (int pc = 0; pc < kFastIns; ++pc) {
+    fp.w0[pc] = 0;
+    fp.a[pc] = fp.s[pc] = 0.0f;
+    fp.slot[pc] = 0;
+    fp.sp[pc] = base_ptr(ka, 0);
+    fp.soff[pc] = fp.ss0[pc] = 0;
+    fp.sdt[pc] = DT_F32;
+    if ((uint32_t)pc >= fp.n) continue;
+    const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + ins_off + (t.expr_first + pc) * sizeof(DIns));
+    const uint32_t w0 = uniform(iw[0]), w1 = uniform(iw[1]);
+    fp.w0[pc] = w0;
+    fp.a[pc] = __uint_as_float(uniform(iw[2]));
+    fp.s[pc] = __uint_as_float(uniform(iw[3]));
+    const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff;
+    if (op != VM_STORE && src != SRC_VIEW) continue;
+    const VView v = load_view(views_off + (w1 & 0xffff) * sizeof(DView));
+    GLOBAL uint8_t* p = base_ptr(ka, v.base);
+    if (v.stride[1] == 1 && ((uintptr_t)p & 15) != 0) ok = false;
+    if (op == VM_STORE) {
+      fp.sp[pc] = p;
+      fp.soff[pc] = v.offset;
+      fp.ss0[pc] = v.stride[0];
+      fp.sdt[pc] = v.dtype;
+      continue;
+    }
+    const uint32_t l = fp.nl;  // < kFastLoads (scheduler)
+    fp.slot[pc] = l;
+#pragma unroll
+    for (int j = 0; j < kFastLoads; ++j)
+      if ((uint32_t)j == l) {
+        fp.lp[j] = p;
+        fp.loff[j] = v.offset;
+        fp.ls0[j] = v.stride[0];
+        fp.ldt[j] = v.dtype;
+        fp.ls1[j] = (uint32_t)v.stride[1];
+      }
+    fp.nl = l + 1;
+  }
+  return ok;
+}
+
+// One 8-wide chunk per index of a view with column stride s1 (1: 16-byte
+// vector loads; 0: one element broadcast), as load_chunks.
+template <int G>
+DEV void fast_load(const GLOBAL uint8_t* p, uint32_t dt, uint32_t s1, const int32_t (&idx)[G], float (&x)[G][8]) {
+  if (dt == DT_F32) {
+    const GLOBAL float* q = (const GLOBAL float*)p;
+    if (s1) {
+      u32x4 r[G][2];
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        r[g][0] = *(const GLOBAL u32x4*)(q + idx[g]);
+        r[g][1] = *(const GLOBAL u32x4*)(q + idx[g] + 4);
+      }
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[g][j] = __uint_as_float(r[g][j / 4][j % 4]);
+    } else {
+      float r[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) r[g] = q[idx[g]];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[g][j] = r[g];
+    }
+  } else {
+    const GLOBAL uint16_t* q = (const GLOBAL uint16_t*)p;
+    const bool bf = dt == DT_BF16;
+    if (s1) {
+      u32x4 r[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) r[g] = *(const GLOBAL u32x4*)(q + idx[g]);
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          x[g][j] = half_bits_to_f32((j & 1) ? r[g][j / 2] >> 16 : r[g][j / 2] & 0xffffu, bf);
+    } else {
+      uint32_t r[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g) r[g] = q[idx[g]];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[g][j] = half_bits_to_f32(r[g], bf);
+    }
+  }
+}
+
+// Stores of the chunks in bounds, converted to the view's dtype (RNE), as
+// store_chunks.
+template <int G>
+DEV void fast_store(GLOBAL uint8_t* p, uint32_t dt, const int32_t (&idx)[G], const bool (&ok)[G],
+                    const float (&y)[G][8]) {
+  if (dt == DT_F32) {
+    GLOBAL float* q = (GLOBAL float*)p;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (!ok[g]) continue;
+      u32x4 r0, r1;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        r0[j] = __float_as_uint(y[g][j]);
+        r1[j] = __float_as_uint(y[g][4 + j]);
+      }
+      *(GLOBAL u32x4*)(q + idx[g]) = r0;
+      *(GLOBAL u32x4*)(q + idx[g] + 4) = r1;
+    }
+  } else {
+    GLOBAL uint16_t* q = (GLOBAL uint16_t*)p;
+    const bool bf = dt == DT_BF16;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (!ok[g]) continue;
+      u32x4 r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        r[j] = f32_to_half_bits(y[g][2 * j], bf) | (f32_to_half_bits(y[g][2 * j + 1], bf) << 16);
+      *(GLOBAL u32x4*)(q + idx[g]) = r;
+    }
+  }
+}
+
+template <int G>
+DEV void fast_run(uint32_t tid, const DTask& t, const ItemState& st, const FastProg& fp) {
+  const int pitch = st.bn + 4;
+  const int lcpr = __builtin_ctz((uint32_t)(st.bn / 8));  // log2 chunks per row
+  const int nchunks = st.bm << lcpr;
+  const LDS float* ctile = (const LDS float*)g_smem;
+  for (int q0 = 0; q0 < nchunks; q0 += G * kBlock) {
+    float y[G][8];
+    int32_t row[G], col[G];
+    bool ok[G];
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int qq = q0 + g * kBlock + (int)tid;
+      const bool in = qq < nchunks;
+      const int r = in ? qq >> lcpr : 0, cc = in ? (qq & ((1 << lcpr) - 1)) * 8 : 0;
+      row[g] = (int32_t)st.m0 + r;
+      col[g] = (int32_t)st.n0 + cc;
+      ok[g] = in && (uint32_t)row[g] < t.m && (uint32_t)col[g] < t.n;
+      // rows are 16-byte aligned (pitch a multiple of 4), chunks start at multiples of 8
+      const LDS float* src = ctile + r * pitch + cc;
+      const u32x4 lo = *(const LDS u32x4*)src, hi = *(const LDS u32x4*)(src + 4);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        y[g][j] = __uint_as_float(lo[j]);
+        y[g][4 + j] = __uint_as_float(hi[j]);
+      }
+    }
+    // every loaded view's chunks in flight together
+    float lv[kFastLoads][G][8];
+#pragma unroll
+    for (int l = 0; l < kFastLoads; ++l) {
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) lv[l][g][j] = 0.0f;
+      if ((uint32_t)l >= fp.nl) continue;
+      int32_t idx[G];
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+        idx[g] = ok[g] ? fp.loff[l] + row[g] * fp.ls0[l] + col[g] * (int32_t)fp.ls1[l] : fp.loff[l];
+      fast_load<G>(fp.lp[l], fp.ldt[l], fp.ls1[l], idx, lv[l]);
+    }
+#pragma unroll
+    for (int pc = 0; pc < kFastIns; ++pc) {
+      if ((uint32_t)pc >= fp.n) break;
+      const uint32_t w = fp.w0[pc];
+      const uint32_t op = w & 0xff, src = (w >> 8) & 0xff, rnd = (w >> 16) & 0xff, rev = w >> 24;
+      const float a = fp.a[pc];
+      if (op == VM_STORE) {
+        int32_t idx[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) idx[g] = ok[g] ? fp.soff[pc] + row[g] * fp.ss0[pc] + col[g] : fp.soff[pc];
+        fast_store<G>(fp.sp[pc], fp.sdt[pc], idx, ok, y);
+        continue;
+      }
+      float x[G][8];
+      if (src == SRC_VIEW) {
+        const uint32_t l = fp.slot[pc];
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[g][j] = l == 0 ? lv[0][g][j] : l == 1 ? lv[1][g][j] : lv[2][g][j];
+      } else {
+        const float k = src == SRC_SCALAR ? fp.s[pc] : 0.0f;
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[g][j] = k;
+      }
+#define TK_EACH_R(expr)                          \
+  _Pragma("unroll") for (int g = 0; g < G; ++g)  \
+  _Pragma("unroll") for (int j = 0; j < 8; ++j) { \
+    float& v = y[g][j];                          \
+    const float o = x[g][j];                     \
+    (void)o;                                     \
+    expr;                                        \
+  }
+      switch (op) {
+        case VM_LOAD: TK_EACH_R(v = o) break;
+        case VM_ADD:
+          if (rev) { TK_EACH_R(float u = a * v; v = o + u) }
+          else { TK_EACH_R(float u = a * o; v = v + u) }
+          break;
+        case VM_SUB:
+          if (rev) { TK_EACH_R(float u = a * v; v = o - u) }
+          else { TK_EACH_R(float u = a * o; v = v - u) }
+          break;
+        case VM_MUL: TK_EACH_R(v = v * o) break;
+        case VM_DIV:
+          if (rev) { TK_EACH_R(v = o / v) }
+          else { TK_EACH_R(v = v / o) }
+          break;
+        case VM_NEG: TK_EACH_R(v = -v) break;
+        case VM_RELU: TK_EACH_R(v = v < 0.0f ? 0.0f : v) break;
+        case VM_SQUARE: TK_EACH_R(v = v * v) break;
+        case VM_TB:
+          if (rev) { TK_EACH_R(v = v <= a ? 0.0f : o) }
+          else { TK_EACH_R(v = o <= a ? 0.0f : v) }
+          break;
+        case VM_SCALE: TK_EACH_R(v = a * v) break;
+        case VM_ZERO: TK_EACH_R(v = 0.0f) break;
+        default: break;
+      }
+#undef TK_EACH_R
+      if (rnd == DT_BF16) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y[g][j] = bf16_bits_to_f32(f32_to_bf16_bits(y[g][j]));
+      } else if (rnd == DT_F16) {
+#pragma unroll
+        for (int g = 0; g < G; ++g)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) y[g][j] = f16_bits_to_f32(f32_to_f16_bits(y[g][j]));
+      }
+    }
+  }
+}
+
+// The register epilogue of a contraction item whose fp32 tile is in LDS;
+// false when the item's epilogue must run through batches.
+DEV bool fast_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, const ItemState& st) {
+  if (!(t.flags & F_FASTEPI)) return false;
+  FastProg fp;
+  if (!fast_decode(ka, t, sd.off_views, sd.off_ins, fp)) return false;
+  fast_run<2>(tid, t, st, fp);
+  __syncthreads();  // the next item may overwrite the LDS tile
+  return true;
+}
+
 // A stage record from the plan (wave-uniform).
 DEV DStage load_stage(const GLOBAL uint8_t* stages, uint32_t s) {
   constexpr int N = sizeof(DStage) / 4;
@@ -1630,6 +1925,7 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
     case T_GEMM_SIMT:
       gemm_simt(tid, ka, t, sd.off_views, item, st);
       __syncthreads();
+      if (fast_epilogue(tid, ka, t, sd, st)) return;
       break;
     case T_GEMM_MFMA: {
       // the operand dtype is the A view's (both operands share it)
@@ -1646,6 +1942,7 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
           gemm_mfma<64, 64, false>(tid, ka, t, sd.off_views, item, st);
       }
       __syncthreads();
+      if (fast_epilogue(tid, ka, t, sd, st)) return;
       break;
     }
     case T_GEMV_Q8:

@@ -1312,6 +1312,59 @@ struct Builder {
     }
   }
 
+  // Whether a contraction tile's epilogue `code` (peepholed, view indices into
+  // `vt`) over an m x n output can run as the kernel's register program: a
+  // short straight-line program over 8-wide column chunks, every view loaded
+  // once per chunk before the first instruction runs.  Loads are hoisted, so
+  // a load may not follow a store whose bytes it may read.
+  static bool fast_epilogue_ok(const std::vector<DIns>& code, const std::vector<DView>& vt, int64_t m, int64_t n) {
+    if (n % 8 != 0 || m <= 0 || code.empty() || code.size() > (size_t)kFastIns) return false;
+    int loads = 0;
+    auto range = [&](const DView& v, int64_t& lo, int64_t& hi) {
+      const int64_t es = dtype_size(v.dtype);
+      int64_t a = v.offset, b = v.offset;
+      const int64_t ext[2] = {m - 1, n - 1};
+      for (int d = 0; d < 2; ++d) {
+        const int64_t step = v.stride[d] * ext[d];
+        if (step < 0) a += step; else b += step;
+      }
+      lo = a * es;
+      hi = (b + 1) * es;
+    };
+    for (size_t i = 0; i < code.size(); ++i) {
+      const DIns& d = code[i];
+      switch (d.op) {
+        case VM_LOAD: case VM_ADD: case VM_SUB: case VM_MUL: case VM_DIV: case VM_NEG: case VM_RELU:
+        case VM_SQUARE: case VM_TB: case VM_STORE: case VM_SCALE: case VM_ZERO: break;
+        default: return false;
+      }
+      if (d.src == SRC_SLOT) return false;
+      const bool is_store = d.op == VM_STORE;
+      if (d.src != SRC_VIEW && !is_store) continue;
+      if (d.arg >= vt.size()) return false;
+      const DView& v = vt[d.arg];
+      if (v.dtype == DT_I8) return false;
+      for (int k = 2; k < kMaxDims; ++k)
+        if (v.stride[k] != 0) return false;
+      const int64_t s1 = v.stride[1], epc = v.dtype == DT_F32 ? 4 : 8;
+      if (is_store ? s1 != 1 : (s1 != 1 && s1 != 0)) return false;
+      if (s1 == 1 && (v.offset % epc != 0 || v.stride[0] % epc != 0)) return false;
+      if (is_store) continue;
+      if (++loads > kFastLoads) return false;
+      int64_t lo, hi;
+      range(v, lo, hi);
+      for (size_t j = 0; j < i; ++j) {
+        if (code[j].op != VM_STORE) continue;
+        const DView& w = vt[code[j].arg];
+        if (w.base != v.base) continue;
+        int64_t wlo, whi;
+        range(w, wlo, whi);
+        if (lo < whi && wlo < hi) return false;
+      }
+    }
+    return true;
+  }
+
   uint32_t commit_code(std::vector<DIns>& code, uint32_t view_base) {
     peephole(code);
     uint32_t first = (uint32_t)ins.size();
@@ -1781,8 +1834,12 @@ struct Builder {
     t.vs = (uint16_t)(vbase + (ops.size() > 2 ? 2 : 1));
     uint32_t vb = commit_views(cx);
     uint32_t code_first = commit_code(code, vb);
+    if ((g.kind == T_GEMM_MFMA || g.kind == T_GEMM_SIMT) && g.split <= 1 && O.fast_epilogue &&
+        fast_epilogue_ok(code, cx.vtab, m, n))
+      t.flags |= F_FASTEPI;
     std::string desc = mm.name + " (" + mm.opcode + " " + std::to_string(m) + "x" + std::to_string(k) + "x" +
                        std::to_string(n) + ")";
+    if (t.flags & F_FASTEPI) desc += " [register epilogue]";
     if (t.flags & F_QPREFETCH) desc += " [weights fetched across the barrier]";
     if (t.flags & F_XQ) desc += " [activations quantised to Q8_0]";
     if (!e.chain.empty()) {

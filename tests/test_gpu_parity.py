@@ -421,6 +421,22 @@ def test_fused_equals_unfused(name):
         parity.assert_bitexact(a, b, s.dtype, s.buf)
 
 
+@pytest.mark.parametrize("name", ["c1", "c2s", "c4s", "c5s", "c2sa"])
+def test_register_epilogue_matches_batches(name):
+    """Contraction epilogues run from registers (the default where the
+    scheduler marks them) give the same bits as the expression machine's
+    batches (batch_epilogues=1) on every output."""
+    cfg = SMALL[name]
+    say("register epilogue == batches", name)
+    base = programs.build(cfg)
+    ins = programs.inputs_for(cfg, 3)
+    o1, p1 = parity.gpu_run(base, [a.copy() for a in ins])
+    o2, _ = parity.gpu_run(base, [a.copy() for a in ins], batch_epilogues=1)
+    assert "[register epilogue]" in p1.dump()
+    for a, b, s in zip(o1, o2, base.outputs):
+        parity.assert_bitexact(a, b, s.dtype, s.buf)
+
+
 @pytest.mark.parametrize("name", ["c2s", "c5s"])
 def test_ordinary_launch_matches_cooperative(name):
     """launch_mode=1 (ordinary launch of the co-resident grid) runs the same

@@ -373,3 +373,17 @@ def test_run_refused_for_plan_only_program():
     arr_out = tk._array(outs)
     st = tk.lib().tk_run_into(prog._h, arr_in, 2, arr_out, 2, ctypes.byref(ws), None)
     assert tk.STATUS[st] == "TK_E_DEVICE"
+
+
+@pytest.mark.parametrize("name,marked,gemms", [("c1", 3, 5), ("c2", 7, 8), ("c5", 46, 47)])
+def test_register_epilogue_marking(name, marked, gemms):
+    """Contraction tiles whose epilogue is short and simple (no slots, 2-D
+    chunk-aligned views, at most three loaded views) are marked to run it
+    from registers; C1's 10-wide outputs and the loss-head programs that save
+    slots keep the batches.  batch_epilogues=1 turns the register path off."""
+    text = programs.build(programs.CONFIGS[name]).text()
+    d = tk.compile(text, device=-1).dump()
+    assert d.count("gemm_") == gemms
+    assert d.count("[register epilogue]") == marked
+    d1 = tk.compile(text, device=-1, batch_epilogues=1).dump()
+    assert d1.count("[register epilogue]") == 0
