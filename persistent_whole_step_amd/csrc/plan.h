@@ -110,6 +110,8 @@ constexpr uint32_t F_FASTEPI = 64u;    // contraction tile: the epilogue runs as
                                        //   kFastIns instructions, no slots, 2-D views with column stride 1
                                        //   or 0 and 8-element chunk alignment, at most kFastLoads loaded
                                        //   views, no load after a store that may overlap it)
+constexpr uint32_t F_COLDIRECT = 128u;  // column reduction whose source program is one load of a 2-D view with
+                                       //   column stride 1: rows are summed straight from memory, not in batches
 constexpr int kFastIns = 8;
 constexpr int kFastLoads = 3;
 

@@ -1497,7 +1497,8 @@ DEV bool fill(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, uin
       const uint32_t rb = part * t.kchunk;
       const uint32_t re = (rb + t.kchunk < R) ? rb + t.kchunk : R;
       const uint32_t per = 8 * C;
-      const uint32_t nb = re > rb ? (re - rb + per - 1) / per : 0;
+      // F_COLDIRECT: the rows were summed before the first batch (red_cols_direct)
+      const uint32_t nb = (t.flags & F_COLDIRECT) ? 0u : re > rb ? (re - rb + per - 1) / per : 0u;
       if (bi < nb) {
         expr_batch(b, t, ins_off);
         task_space(b, t);
@@ -1895,6 +1896,83 @@ DEV bool fast_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, const DStage
   return true;
 }
 
+// A column reduction whose source program is one load of a 2-D view with
+// column stride 1 (F_COLDIRECT): thread (row lane rl = tid / 32, chunk
+// cc = tid % 32) sums rows rb + rl, rb + rl + 8, ... of its 8 columns straight
+// from memory, 16 rows in flight at a time, into its running sums.  The rows
+// and the additions come in the order the batches would take them, so the
+// sums are bit-identical; the combine across row lanes and the finishing
+// program then run as for the batches.
+DEV void red_cols_direct(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item,
+                         ItemState& st) {
+  const uint32_t cb = item / t.split, part = item % t.split;
+  const uint32_t cols = t.m, R = t.k;
+  const uint32_t cc = tid % 32, rl = tid / 32;
+  const uint32_t col = cb * 256 + cc * 8;
+  const uint32_t rb = part * t.kchunk;
+  const uint32_t re = (rb + t.kchunk < R) ? rb + t.kchunk : R;
+  const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + sd.off_ins + t.expr_first * sizeof(DIns));
+  const VView v = load_view(sd.off_views + (uniform(iw[1]) & 0xffff) * sizeof(DView));
+  const GLOBAL uint8_t* p = base_ptr(ka, v.base);
+  const uint32_t dt = v.dtype;
+  const int32_t epc = dt == DT_F32 ? 4 : 8;
+  const bool vec = aligned16(p) && v.offset % epc == 0 && v.stride[0] % epc == 0;
+  if (col >= cols || rb >= re) return;
+  constexpr int U = 16;
+  for (uint32_t r0 = rb + rl; r0 < re; r0 += 8 * U) {
+    float x[U][8];
+    int32_t idx[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint32_t r = r0 + 8 * u;
+      idx[u] = v.offset + (int32_t)(r < re ? r : rb) * v.stride[0] + (int32_t)col;
+    }
+    if (dt == DT_F32) {
+      const GLOBAL float* q = (const GLOBAL float*)p;
+      if (vec) {
+        u32x4 a[U][2];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          a[u][0] = *(const GLOBAL u32x4*)(q + idx[u]);
+          a[u][1] = *(const GLOBAL u32x4*)(q + idx[u] + 4);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[u][j] = __uint_as_float(a[u][j / 4][j % 4]);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[u][j] = q[idx[u] + j];
+      }
+    } else {
+      const GLOBAL uint16_t* q = (const GLOBAL uint16_t*)p;
+      const bool bf = dt == DT_BF16;
+      if (vec) {
+        u32x4 a[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) a[u] = *(const GLOBAL u32x4*)(q + idx[u]);
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            x[u][j] = half_bits_to_f32((j & 1) ? a[u][j / 2] >> 16 : a[u][j / 2] & 0xffffu, bf);
+      } else {
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int j = 0; j < 8; ++j) x[u][j] = half_bits_to_f32(q[idx[u] + j], bf);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (r0 + 8 * u < re)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) st.acc8[j] = st.acc8[j] + x[u][j];
+  }
+}
+
 // A stage record from the plan (wave-uniform).
 DEV DStage load_stage(const GLOBAL uint8_t* stages, uint32_t s) {
   constexpr int N = sizeof(DStage) / 4;
@@ -1950,6 +2028,9 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
       gemv_epilogue(tid, ka, t, sd.off_views, sd.off_ins, item);
       __syncthreads();  // the next item may overwrite the row sums and the slots
       return;
+    case T_RED_COLS:
+      if (t.flags & F_COLDIRECT) red_cols_direct(tid, ka, t, sd, item, st);
+      break;
     default:
       break;
   }

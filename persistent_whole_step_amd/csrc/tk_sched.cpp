@@ -1470,8 +1470,14 @@ struct Builder {
       // 32 rows per part: a work item is at most two machine batches (8 row
       // lanes x 2 rows per batch for 8-wide chunks), so parts run in parallel
       // across workgroups instead of in sequence within one
-      // (up to 64 rows stay one part: a combine stage would cost more)
-      int64_t parts = rr <= 64 ? 1 : std::min<int64_t>(64, (rr + 31) / 32);
+      // (up to 64 rows stay one part: a combine stage would cost more).  A
+      // source read straight from memory (an input or a materialised value,
+      // summed without batches) stays one part up to 256 rows: 32 loads per
+      // thread cost less than the combine stage and its barrier.
+      const Arg& src = r.args[0];
+      const int sp = src.scalar ? -2 : prod(src.spec.buf);
+      const bool direct = !src.scalar && src.spec.dtype != DT_I8 && (sp == -1 || (sp >= 0 && !inlined.count(sp)));
+      int64_t parts = (rr <= 64 || (direct && rr <= 256)) ? 1 : std::min<int64_t>(64, (rr + 31) / 32);
       int64_t kc = (rr + parts - 1) / parts;
       parts = (rr + kc - 1) / std::max<int64_t>(1, kc);
       c.parts = (uint32_t)std::max<int64_t>(1, parts);
@@ -2007,9 +2013,15 @@ struct Builder {
     }
     if (rc.kind == T_RED_COLS) {
       t.width = (rc.rows % 8 == 0) ? 8 : 1;
+      if (t.width == 8 && dims.size() == 2 && code.size() == 1 && code[0].op == VM_LOAD &&
+          code[0].src == SRC_VIEW && code[0].rnd == RND_NONE && code[0].arg < cx.vtab.size()) {
+        const DView& v = cx.vtab[code[0].arg];
+        if (v.dtype != DT_I8 && v.stride[1] == 1) t.flags |= F_COLDIRECT;
+      }
       const uint32_t cols_per_item = 32u * t.width;
       t.tiles_n = (uint32_t)((rc.rows + cols_per_item - 1) / cols_per_item);
       t.n_items = rc.rows == 0 ? 0 : t.tiles_n * rc.parts;
+      if (t.flags & F_COLDIRECT) desc += " [rows summed directly]";
     } else {
       t.width = (dims.back() % 8 == 0 && rc.R % 8 == 0) ? 8 : 1;
       t.n_items = (uint32_t)(rc.rows * rc.parts);

@@ -387,3 +387,16 @@ def test_register_epilogue_marking(name, marked, gemms):
     assert d.count("[register epilogue]") == marked
     d1 = tk.compile(text, device=-1, batch_epilogues=1).dump()
     assert d1.count("[register epilogue]") == 0
+
+
+def test_column_sums_read_directly():
+    """Bias-gradient sums over at most 256 rows of a materialised gradient are
+    one part each (no combine stage) and are summed straight from memory;
+    the 3-layer bf16 MLP step then needs 6 stages."""
+    d = tk.compile(programs.build(programs.CONFIGS["c2"]).text(), device=-1)
+    text = d.dump()
+    assert text.count("[rows summed directly]") == 3
+    assert d.query()["n_stages"] == 6
+    # over 256 rows the sums keep their partials (combine stage) and still read directly
+    d5 = tk.compile(programs.build(programs.CONFIGS["c5"]).text(), device=-1).dump()
+    assert "reduce_final" in d5 and "[rows summed directly]" in d5
