@@ -88,8 +88,10 @@ typedef struct {
                                   (tk_workspace_status), never a hang. */
   int32_t gemm_tile;           /* 0: automatic; 1: force 128x128 MFMA tiles; 2: force 64x64 */
   int32_t batch_epilogues;     /* 0 (default): a contraction tile whose epilogue program is short
-                                  and simple runs it from registers; 1: every epilogue runs on the
-                                  expression machine's batches (same results, bit for bit) */
+                                  and simple runs it from registers, and a column sum whose source
+                                  is one load reads its rows straight into registers; 1: every
+                                  epilogue and reduction source runs on the expression machine's
+                                  batches (same partitions, same results, bit for bit) */
   int32_t reserved[1];
 } tk_options;
 

@@ -85,7 +85,7 @@ struct Options {
   int gemm_split_k = 0;
   int launch_mode = 0;  // 0 cooperative, 1 ordinary launch of a co-resident grid
   int gemm_tile = 0;    // 0 automatic, 1 force 128x128, 2 force 64x64
-  bool fast_epilogue = true;  // contraction epilogues may run as register programs
+  bool fast_epilogue = true;  // contraction epilogues may run as register programs, column sums read directly
 };
 
 // Compiled plan: device bytes plus host-side description for queries/dumps.

@@ -2013,7 +2013,7 @@ struct Builder {
     }
     if (rc.kind == T_RED_COLS) {
       t.width = (rc.rows % 8 == 0) ? 8 : 1;
-      if (t.width == 8 && dims.size() == 2 && code.size() == 1 && code[0].op == VM_LOAD &&
+      if (O.fast_epilogue && t.width == 8 && dims.size() == 2 && code.size() == 1 && code[0].op == VM_LOAD &&
           code[0].src == SRC_VIEW && code[0].rnd == RND_NONE && code[0].arg < cx.vtab.size()) {
         const DView& v = cx.vtab[code[0].arg];
         if (v.dtype != DT_I8 && v.stride[1] == 1) t.flags |= F_COLDIRECT;

@@ -423,9 +423,10 @@ def test_fused_equals_unfused(name):
 
 @pytest.mark.parametrize("name", ["c1", "c2s", "c4s", "c5s", "c2sa"])
 def test_register_epilogue_matches_batches(name):
-    """Contraction epilogues run from registers (the default where the
-    scheduler marks them) give the same bits as the expression machine's
-    batches (batch_epilogues=1) on every output."""
+    """Contraction epilogues run from registers and column sums read straight
+    from memory (the defaults where the scheduler marks them) give the same
+    bits as the expression machine's batches (batch_epilogues=1) on every
+    output."""
     cfg = SMALL[name]
     say("register epilogue == batches", name)
     base = programs.build(cfg)
@@ -433,6 +434,7 @@ def test_register_epilogue_matches_batches(name):
     o1, p1 = parity.gpu_run(base, [a.copy() for a in ins])
     o2, _ = parity.gpu_run(base, [a.copy() for a in ins], batch_epilogues=1)
     assert "[register epilogue]" in p1.dump()
+    assert "[rows summed directly]" in p1.dump()
     for a, b, s in zip(o1, o2, base.outputs):
         parity.assert_bitexact(a, b, s.dtype, s.buf)
 

@@ -386,7 +386,7 @@ def test_register_epilogue_marking(name, marked, gemms):
     assert d.count("gemm_") == gemms
     assert d.count("[register epilogue]") == marked
     d1 = tk.compile(text, device=-1, batch_epilogues=1).dump()
-    assert d1.count("[register epilogue]") == 0
+    assert d1.count("[register epilogue]") == 0 and d1.count("[rows summed directly]") == 0
 
 
 def test_column_sums_read_directly():
