@@ -257,3 +257,117 @@ def probe_values(prog: Program, probe: Program, outs):
     for spec, v in zip(probe.outputs, outs):
         vals[spec.buf] = v
     return vals
+
+
+# ------------------------------------------- full sizes: sampled contractions --
+
+def _gather(buf: np.ndarray, spec: Spec, idx) -> np.ndarray:
+    """Elements of view `spec` at index arrays idx[d] (one per view dim), from
+    the flat buffer `buf` (indexing only)."""
+    flat = buf.reshape(-1)
+    pos = np.full(np.broadcast(*idx).shape if idx else (), spec.offset, dtype=np.int64)
+    for d, c in enumerate(idx):
+        pos = pos + np.asarray(c, dtype=np.int64) * spec.strides[d]
+    return flat[pos]
+
+
+def _bias_at(buf: np.ndarray, spec: Spec, rows, cols) -> np.ndarray:
+    """A bias view broadcast over an [m, n] output, read at (rows[i], cols[i])."""
+    r = len(spec.shape)
+    full = (rows, cols)
+    idx = []
+    for d in range(r):
+        c = full[2 - r + d]
+        idx.append(np.zeros_like(c) if spec.shape[d] == 1 else c)
+    return _gather(buf, spec, idx)
+
+
+def sampled_contraction_program(op, vals: dict, rows, cols):
+    """A small program whose output diagonal (i, i) is op's output at
+    (rows[i], cols[i]): the sampled rows of the activation operand and the
+    sampled columns (output features) of the weight operand, and a diagonal
+    bias holding the bias at each sampled output.  Each output of a
+    contraction depends on its own row and column only, so the oracle's value
+    there is the value it computes for the full op."""
+    s = len(rows)
+    p = Program()
+    arrays = []
+    bias_first = op.opcode in ("addmm", "addmm_q8")
+    ops_in = op.operands[1:] if bias_first else op.operands
+    if op.opcode in ("mm", "addmm"):
+        A, B = ops_in
+        k = A.shape[1]
+        kk = np.arange(k)
+        a = _gather(vals[A.buf], A, (np.asarray(rows)[:, None], kk[None, :]))
+        b = _gather(vals[B.buf], B, (kk[:, None], np.asarray(cols)[None, :]))
+        sa = p.input("A", A.dtype, (s, k))
+        sb = p.input("B", B.dtype, (k, s))
+        operands = [sa, sb]
+        arrays += [np.ascontiguousarray(a), np.ascontiguousarray(b)]
+    else:
+        X, Q, S = ops_in
+        k = X.shape[1]
+        kk = np.arange(k)
+        nb = S.shape[1]
+        x = _gather(vals[X.buf], X, (np.asarray(rows)[:, None], kk[None, :]))
+        q = _gather(vals[Q.buf], Q, (np.asarray(cols)[:, None], kk[None, :]))
+        sc = _gather(vals[S.buf], S, (np.asarray(cols)[:, None], np.arange(nb)[None, :]))
+        sx = p.input("x", X.dtype, (s, k))
+        sq = p.input("q", Q.dtype, (s, k))
+        ss = p.input("s", S.dtype, (s, nb))
+        operands = [sx, sq, ss]
+        arrays += [np.ascontiguousarray(x), np.ascontiguousarray(q), np.ascontiguousarray(sc)]
+    if bias_first:
+        Bi = op.operands[0]
+        diag = _bias_at(vals[Bi.buf], Bi, np.asarray(rows), np.asarray(cols))
+        full = np.zeros((s, s), dtype=diag.dtype)
+        full[np.arange(s), np.arange(s)] = diag
+        sbias = p.input("bias", Bi.dtype, (s, s))
+        operands = [sbias] + operands
+        arrays = arrays + [full]  # in the order of the program's inputs
+    out = p.op(op.opcode, operands, op.out.dtype, (s, s), name="y", **op.attrs)
+    p.output(out)
+    return p, arrays
+
+
+def check_per_node_sampled(oracle_mod, prog: Program, inputs, gpu_vals: dict, samples: int = 48, seed: int = 0,
+                           rel=1e-4):
+    """Teacher-forced per-op parity at full size: pointwise ops and reductions
+    are re-evaluated whole by the oracle (bit-exact / contraction tolerance);
+    each contraction is checked at `samples` outputs (the four corners and
+    random ones), each computed by the oracle from the GPU's own operand
+    values, against its exact float64 value."""
+    rng = np.random.default_rng(seed)
+    value_specs = {s.buf: s for s in prog.inputs}
+    for op in prog.ops:
+        value_specs[op.out.buf] = op.out
+    vals = {s.buf: a for s, a in zip(prog.inputs, inputs)}
+    vals.update(gpu_vals)
+    checked = 0
+    for j, op in enumerate(prog.ops):
+        if op.out.buf not in gpu_vals:
+            continue
+        got = gpu_vals[op.out.buf]
+        if op.opcode in programs.CONTRACTIONS:
+            m, n = op.out.shape
+            rows = np.concatenate([[0, m - 1, 0, m - 1], rng.integers(0, m, samples - 4)])
+            cols = np.concatenate([[0, n - 1, n - 1, 0], rng.integers(0, n, samples - 4)])
+            sp, arrays = sampled_contraction_program(op, vals, rows, cols)
+            (want,) = oracle_mod.run(sp.text(), arrays)
+            svals = {s.buf: a for s, a in zip(sp.inputs, arrays)}
+            exact, mag = contraction_reference(sp.ops[0], svals, None)
+            d = np.arange(len(rows))
+            g = got.reshape(m, n)[rows, cols]
+            assert_contraction(g, want.reshape(len(rows), len(rows))[d, d], exact[d, d], mag[d, d], op.out.dtype,
+                               f"{op.name} ({op.opcode}, {len(rows)} sampled outputs)", rel)
+        else:
+            sp, names = single_op_program(prog, j, value_specs)
+            (want,) = oracle_mod.run(sp.text(), [np.ascontiguousarray(vals[nm]) for nm in names])
+            if op.opcode in programs.POINTWISE:
+                assert_bitexact(got, want, op.out.dtype, f"{op.name} ({op.opcode})")
+            else:
+                exact, mag = reduction_reference(op, vals)
+                assert_contraction(got.reshape(op.out.shape), want.reshape(op.out.shape), exact, mag, op.out.dtype,
+                                   f"{op.name} ({op.opcode})", rel)
+        checked += 1
+    return checked

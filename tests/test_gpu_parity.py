@@ -506,3 +506,38 @@ def test_c1_end_to_end_close_to_oracle(oracle_mod):
     want = oracle_mod.run(base.text(), [a.copy() for a in ins])
     for g, w, s in zip(got, want, base.outputs):
         np.testing.assert_allclose(parity.f32_of(g, s.dtype), parity.f32_of(w, s.dtype), rtol=1e-5, atol=1e-6)
+
+
+# ------------------------------------------------------------- full sizes --
+
+FULL = {
+    "c2": dict(programs.CONFIGS["c2"]),
+    "c2a": dict(programs.CONFIGS["c2"], optimizer=programs.AdamW(), adam_t=10),
+    "c3": dict(programs.CONFIGS["c3"]),
+    "c3q": dict(programs.CONFIGS["c3"], xq=True),
+    "c3r4": dict(programs.CONFIGS["c3"], rows=4),
+    "c4": dict(programs.CONFIGS["c4"]),
+    "c5": dict(programs.CONFIGS["c5"]),
+}
+
+
+@pytest.mark.parametrize("name", list(FULL))
+def test_full_size_sampled_per_node(oracle_mod, name):
+    """The workloads at their full sizes, in the launch configuration the
+    bench times (ordinary launch of the co-resident grid): every op checked
+    per node with teacher forcing (pointwise ops and reductions whole,
+    contractions at 48 sampled outputs each computed by the oracle), then the
+    bench's fused schedule equal to the probe schedule bit for bit on the
+    step's outputs."""
+    cfg = FULL[name]
+    say("full size, sampled per node", name)
+    base = programs.build(cfg)
+    probe = base.probe()
+    ins = programs.inputs_for(cfg, 0)
+    outs, _ = parity.gpu_run(probe, [a.copy() for a in ins], launch_mode=1)
+    vals = parity.probe_values(base, probe, outs)
+    n = parity.check_per_node_sampled(oracle_mod, base, ins, vals, samples=48, seed=len(name))
+    assert n == len(base.ops)
+    fused, _ = parity.gpu_run(base, [a.copy() for a in ins], launch_mode=1)
+    for a, b, s in zip(fused, outs, base.outputs):
+        parity.assert_bitexact(a, b, s.dtype, s.buf)
