@@ -541,3 +541,65 @@ def test_full_size_sampled_per_node(oracle_mod, name):
     fused, _ = parity.gpu_run(base, [a.copy() for a in ins], launch_mode=1)
     for a, b, s in zip(fused, outs, base.outputs):
         parity.assert_bitexact(a, b, s.dtype, s.buf)
+
+
+# ------------------------------------------------- fast paths' fallbacks --
+
+def _misaligned_copy(t):
+    """A copy of `t` whose data pointer lies 2 bytes past a 16-byte boundary
+    (a view one element into a larger buffer), with `t`'s shape and strides."""
+    import torch
+    big = torch.zeros(t.numel() + 16, dtype=t.dtype, device=t.device)
+    v = big[1:1 + t.numel()].view(t.shape)
+    v.copy_(t)
+    assert v.data_ptr() % 16 != 0 and v.is_contiguous()
+    return v
+
+
+def test_register_epilogue_misaligned_bias_uses_batches(oracle_mod):
+    """A marked tile whose bias base is not 16-byte aligned at run time runs
+    its epilogue through the batches: same bits as with an aligned bias, and
+    within tolerance of the oracle."""
+    from persistent_whole_step_amd import tk
+    say("register epilogue, misaligned bias")
+    m, k, n = 192, 160, 256
+    rng = np.random.default_rng(11)
+    p = Program()
+    A = p.input("A", "bf16", (m, k))
+    B = p.input("B", "bf16", (k, n))
+    bi = p.input("bias", "bf16", (n,))
+    y = p.op("addmm", [bi, A, B], "bf16", (m, n), alpha=1.0, beta=1.0)
+    p.output(p.op("relu", [y], "bf16"))
+    ins = [synth.random_tensor(rng, (m, k), "bf16"), synth.random_tensor(rng, (k, n), "bf16"),
+           synth.random_tensor(rng, (n,), "bf16")]
+    prog = tk.compile(p.text(), device=0)
+    assert "[register epilogue]" in prog.dump()
+    tA, tB, tb = (parity.to_torch(a, s.dtype) for a, s in zip(ins, p.inputs))
+    aligned = parity.to_numpy(prog(tA, tB, tb)[0], "bf16")
+    shifted = parity.to_numpy(prog(tA, tB, _misaligned_copy(tb))[0], "bf16")
+    parity.assert_bitexact(shifted, aligned, "bf16", "misaligned bias")
+    want = oracle_mod.run(p.text(), ins)[0]
+    exact, mag = parity.contraction_reference(p.ops[0], {"A": ins[0], "B": ins[1], "bias": ins[2]}, None)
+    parity.assert_contraction(aligned, want, np.maximum(exact, 0), mag, "bf16", "addmm + relu")
+
+
+def test_direct_column_sum_misaligned_source(oracle_mod):
+    """A column sum read straight from a misaligned input takes element loads:
+    same bits as from an aligned input, within tolerance of the oracle."""
+    from persistent_whole_step_amd import tk
+    say("direct column sum, misaligned source")
+    rows, cols = 200, 512
+    rng = np.random.default_rng(12)
+    p = Program()
+    g = p.input("g", "bf16", (rows, cols))
+    p.output(p.op("sum", [g], "f32", (cols,), dims=(0,)))
+    ins = [synth.random_tensor(rng, (rows, cols), "bf16")]
+    prog = tk.compile(p.text(), device=0)
+    assert "[rows summed directly]" in prog.dump()
+    tg = parity.to_torch(ins[0], "bf16")
+    aligned = parity.to_numpy(prog(tg)[0], "f32")
+    shifted = parity.to_numpy(prog(_misaligned_copy(tg))[0], "f32")
+    parity.assert_bitexact(shifted, aligned, "f32", "misaligned column sum")
+    want = oracle_mod.run(p.text(), ins)[0]
+    exact, mag = parity.reduction_reference(p.ops[0], {"g": ins[0]})
+    parity.assert_contraction(aligned, want, exact, mag, "f32", "column sum")
