@@ -8,7 +8,8 @@ benchmark set: the default workload is the 3-layer bf16 MLP (batch 256,
 already resident in HBM; parameters are updated in place every step (state
 feedback) and the (x, target) batch rotates over 4 resident batches.  The
 other workloads (2-layer fp32 MLP, the default MLP with AdamW in place of
-SGD, int8-weight GEMV stack rotating 3 weight sets, 4096-wide bf16 MLP,
+SGD, the default MLP's step written with torch.func and captured by the
+front end, int8-weight GEMV stack rotating 3 weight sets, 4096-wide bf16 MLP,
 16-layer fp16 residual MLP) are timed briefly and reported under "others".
 
 Prints one JSON line on stdout.  --gpus N with N > 1 is refused: this
@@ -38,6 +39,7 @@ WORKLOAD_NAMES = {
     "c2a": "mlp3-bf16-b256-512-1024-1024-64-adamw",
     "c3r4": "gemv8-int8w-bf16x-4x4096x4096",
     "c3q": "gemv8-int8w-q8x-4096x4096",
+    "c2cap": "mlp3-bf16-b256-512-1024-1024-64-captured",
 }
 
 
@@ -53,7 +55,38 @@ def config(name: str) -> dict:
         return dict(programs.CONFIGS["c3"], rows=4)
     if name == "c3q":
         return dict(programs.CONFIGS["c3"], xq=True)
+    if name == "c2cap":
+        return dict(programs.CONFIGS["c2"], captured=True)
     return programs.CONFIGS[name]
+
+
+def captured_mlp(cfg):
+    """C2's step written as a torch.func training step and captured by the
+    front end (state first, so the updated parameters commit in place).
+    Returns the program and the permutation from the workload's input order
+    (x, t, W1, b1, ...) to the captured order (W1, b1, ..., x, t)."""
+    import torch
+    from persistent_whole_step_amd import frontend
+    dims, B, lr = cfg["dims"], cfg["batch"], cfg["lr"]
+    L = len(dims) - 1
+
+    def step(params, x, target):
+        def loss(p):
+            h = x
+            for i in range(L):
+                h = torch.addmm(p[2 * i + 1], h, p[2 * i])
+                if i + 1 < L:
+                    h = torch.relu(h)
+            return ((h - target) ** 2).mean()
+        g, v = torch.func.grad_and_value(loss)(params)
+        return v, tuple(w - lr * gw for w, gw in zip(params, g))
+
+    bf = torch.bfloat16
+    params = tuple(t for i in range(L) for t in (torch.zeros(dims[i], dims[i + 1], dtype=bf),
+                                                 torch.zeros(dims[i + 1], dtype=bf)))
+    c = frontend._capture(step, (params, torch.zeros(B, dims[0], dtype=bf), torch.zeros(B, dims[-1], dtype=bf)))
+    c.program.inplace = frontend._update_mapping(c)
+    return c.program, list(range(2, 2 + 2 * L)) + [0, 1]
 
 
 def log(*a):
@@ -84,7 +117,12 @@ class Runner:
         to_torch = tk.tensor_from_storage
         self.name = name
         self.cfg = config(name)
-        self.prog = programs.build(self.cfg)
+        order = None
+        if self.cfg.get("captured"):
+            self.prog, order = captured_mlp(self.cfg)
+        else:
+            self.prog = programs.build(self.cfg)
+        reorder = (lambda ins: [ins[i] for i in order]) if order else (lambda ins: ins)
         self.p = tk.compile(self.prog.text(), device=0, **opts)
         self.stats = self.p.query()
         cfg = self.cfg
@@ -92,12 +130,12 @@ class Runner:
             sets = [programs.inputs_for(cfg, seed0 + j) for j in range(3)]
             self.inputs = [[to_torch(a, s.dtype) for a, s in zip(ins, self.prog.inputs)] for ins in sets]
         else:
-            base = [to_torch(a, s.dtype) for a, s in zip(programs.inputs_for(cfg, seed0), self.prog.inputs)]
-            self.inputs = [base]
+            wl = [to_torch(a, s.dtype) for a, s in zip(programs.inputs_for(cfg, seed0), programs.build(cfg).inputs)]
+            self.inputs = [reorder(wl)]
             for j in range(1, 4):
                 ins = programs.inputs_for(cfg, seed0 + 100 + j)
-                self.inputs.append([to_torch(ins[0], self.prog.inputs[0].dtype),
-                                    to_torch(ins[1], self.prog.inputs[1].dtype)] + base[2:])
+                dt = cfg.get("dtype", "bf16")
+                self.inputs.append(reorder([to_torch(ins[0], dt), to_torch(ins[1], dt)] + wl[2:]))
         self.buffers = self.p.allocate(*self.inputs[0])
         self.variants = []
         for ins in self.inputs:
@@ -268,7 +306,8 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=50)
     ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--others", default="c1,c2a,c3,c3r4,c3q,c4,c5", help="comma list of extra workloads ('' for none)")
+    ap.add_argument("--others", default="c1,c2a,c2cap,c3,c3r4,c3q,c4,c5",
+                    help="comma list of extra workloads ('' for none)")
     ap.add_argument("--other-steps", type=int, default=100)
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu", action="store_true")

@@ -603,3 +603,42 @@ def test_direct_column_sum_misaligned_source(oracle_mod):
     want = oracle_mod.run(p.text(), ins)[0]
     exact, mag = parity.reduction_reference(p.ops[0], {"g": ins[0]})
     parity.assert_contraction(aligned, want, exact, mag, "f32", "column sum")
+
+
+# ------------------------------------------------------- capture front end --
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_compile_training_step(oracle_mod, dtype):
+    """A torch.func training step captured and compiled: its program checked
+    per node against the oracle on the GPU, then the compiled step run on GPU
+    tensors gives the same bits as the program, with the updated state
+    written into the state tensors passed in."""
+    import torch
+    from persistent_whole_step_amd import frontend, tk
+    from .test_frontend import mlp_step
+    say("capture front end", dtype)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    gen = torch.Generator().manual_seed(5)
+    shapes = {"W1": (96, 160), "b1": (160,), "W2": (160, 48), "b2": (48,)}
+    params = {k: (torch.randn(*s, generator=gen) / 6).to(tdt) for k, s in shapes.items()}
+    x = torch.randn(40, 96, generator=gen).to(tdt)
+    t = torch.randn(40, 48, generator=gen).to(tdt)
+    step = frontend.compile_training(mlp_step, (params, x, t))
+    prog = step.program
+    assert sorted(prog.inplace.values()) == [0, 1, 2, 3]
+    from torch.utils import _pytree as pytree
+    leaves, _ = pytree.tree_flatten((params, x, t))
+    ins = [tk.storage_from_tensor(v, s.dtype) for v, s in zip(leaves, prog.inputs)]
+    probe = prog.probe()
+    outs, _ = parity.gpu_run(probe, [a.copy() for a in ins])
+    vals = parity.probe_values(prog, probe, outs)
+    assert parity.check_per_node(oracle_mod, prog, ins, vals) == len(prog.ops)
+    ref, _ = parity.gpu_run(prog, [a.copy() for a in ins])
+    pg = {k: v.cuda() for k, v in params.items()}
+    loss, new = step(pg, x.cuda(), t.cuda())
+    torch.cuda.synchronize()
+    for k in pg:
+        assert new[k].data_ptr() == pg[k].data_ptr()
+    got, _ = pytree.tree_flatten((loss, new))  # the program's outputs, in the same order
+    for g, r, s in zip(got, ref, prog.outputs):
+        parity.assert_bitexact(tk.storage_from_tensor(g, s.dtype), r, s.dtype, s.buf)
