@@ -914,8 +914,10 @@ constexpr uint32_t kGemvRed = kSmemBytes - 64 * kGemvRows;  // byte offset of th
 // chunks of its first item into LDS [0, 64 KB) and the block scales into the
 // index-exchange region, so the weight stream overlaps the barrier.  Slot
 // qs = (wave * 4 + row) * 4 + chunk holds what lane l of `wave` needs for that
-// row and chunk; waves 1..3 issue the direct-to-LDS loads (wave 0 runs the
-// barrier's fences, which would otherwise wait for them).
+// row and chunk.  Waves 1..3 issue their direct-to-LDS loads before the
+// workgroup arrives (wave 0 runs the barrier's fences, which would otherwise
+// wait for them); wave 0 adds its share after the arrival, except in the
+// workgroup that gathers the arrivals.
 constexpr uint32_t kPrefQ = 0;        // 64 slots x 64 lanes x 16 B
 constexpr uint32_t kPrefS = kXeOff;   // 64 slots x 64 lanes x 4 B
 constexpr uint32_t kPrefX = kXvOff;   // the activation row, staged as floats (K <= 4096)
@@ -927,15 +929,16 @@ DEV bool gemv_prefetchable(const Ctx& ka, const DTask& t, uint32_t views_off) {
   return Q.stride[1] == 1 && (Q.offset & 15) == 0 && (Q.stride[0] & 15) == 0 && aligned16(pq);
 }
 
-DEV void gemv_prefetch(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
-  const uint32_t wave = uniform(tid / 64), lane = tid % 64;
-  if (wave == 0) return;
+// The calling wave issues slots q0, q0 + qstep, ... (wave-uniform).
+DEV void gemv_prefetch(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, uint32_t q0,
+                       uint32_t qstep) {
+  const uint32_t lane = tid % 64;
   const VView Q = load_view(views_off + t.vb * sizeof(DView)), S = load_view(views_off + t.vs * sizeof(DView));
   const GLOBAL int8_t* pq = (const GLOBAL int8_t*)base_ptr(ka, Q.base);
   const GLOBAL float* ps = (const GLOBAL float*)base_ptr(ka, S.base);
   const uint32_t K = t.k;
   const uint32_t lds = (uint32_t)(uintptr_t)(LDS uint8_t*)g_smem;
-  for (uint32_t qs = wave - 1; qs < 64; qs += 3) {
+  for (uint32_t qs = q0; qs < 64; qs += qstep) {
     const uint32_t cw = qs / 16, i = (qs / 4) % 4, j = qs % 4;
     const uint32_t row0 = item * 16 + cw * 4 + i;
     const uint32_t row = row0 < t.n ? row0 : 0;
@@ -2065,8 +2068,12 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
 // `pre` runs in every thread after this workgroup's release fence and before
 // its arrival: work that may stay in flight across the barrier (wave 0, which
 // runs the barrier's fences, issues no memory operation in it).
-template <class Pre>
-DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline, Pre pre) {
+// `post` runs in every thread right after this workgroup's arrival: work that
+// may stay in flight while the barrier completes and that must not delay the
+// arrival (wave 0's share of a weight prefetch, outside the gathering
+// workgroup).
+template <class Pre, class Post>
+DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline, Pre pre, Post post) {
   __shared__ uint32_t s_ok;
   GLOBAL uint32_t* arrive = (GLOBAL uint32_t*)(ka.ws + kHdrArrive);
   GLOBAL uint32_t* release = (GLOBAL uint32_t*)(ka.ws + kHdrRelease);
@@ -2079,6 +2086,7 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
   pre();
   if (threadIdx.x == 0)
     __hip_atomic_store(arrive + bid * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  post();
   if (bid == 0 && threadIdx.x < 64) {
     uint32_t ok = 1;
     const uint32_t lane = threadIdx.x;
@@ -2222,9 +2230,26 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
         while (nti + 1 < sd.n_tasks && first >= task_item_begin(nti + 1)) ++nti;
         const DTask nt = load_task(nti);
         will_pref = gemv_prefetchable(ka, nt, sd.off_views);
-        if (will_pref) gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin);
+        // Waves 1..3 issue their slots before the arrival.  Outside the
+        // gathering workgroup 0, wave 0 takes every fourth slot after its
+        // arrival (post); in workgroup 0 it gathers, and waves 1..3 take all.
+        const uint32_t wave = uniform(threadIdx.x / 64);
+        if (will_pref && wave != 0) {
+          if (blockIdx.x == 0)
+            gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin, wave - 1, 3);
+          else
+            gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin, wave, 4);
+        }
       };
-      if (!grid_barrier(ka, epoch0 + s + 1, s, deadline, pre)) {
+      auto post = [&]() {
+        if (!will_pref || blockIdx.x == 0 || threadIdx.x >= 64) return;
+        const uint32_t first = blockIdx.x;
+        uint32_t nti = 0;
+        while (nti + 1 < sd.n_tasks && first >= task_item_begin(nti + 1)) ++nti;
+        const DTask nt = load_task(nti);
+        gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin, 0, 4);
+      };
+      if (!grid_barrier(ka, epoch0 + s + 1, s, deadline, pre, post)) {
         wait_vmcnt<0>();  // no prefetch may still be writing LDS when the workgroup ends
         return;
       }
