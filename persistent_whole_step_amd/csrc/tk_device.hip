@@ -528,19 +528,53 @@ DEV void tile_coords(const DTask& t, uint32_t tile, uint32_t& tm, uint32_t& tn) 
 // slice is consumed.  Each output accumulates acc = fma(a_k, b_k, acc) for
 // k = 0, 1, ... in order.
 
-DEV void simt_load(uint32_t tid, const GLOBAL uint8_t* p, const VView& v, bool mn_contig, bool is_a, uint32_t r0, uint32_t rmax,
-                   uint32_t k0, uint32_t kmax, float (&reg)[8]) {
+// The 8 elements of one thread, all loads issued before any is used: the
+// operand dtype is a template parameter, so no branch separates the loads.
+template <uint32_t DT>
+DEV void simt_load_t(uint32_t tid, const GLOBAL uint8_t* p, const VView& v, bool mn_contig, bool is_a, uint32_t r0,
+                     uint32_t rmax, uint32_t k0, uint32_t kmax, float (&reg)[8]) {
   const int64_t s_r = is_a ? v.stride[0] : v.stride[1], s_k = is_a ? v.stride[1] : v.stride[0];
-  const uint32_t dt = v.dtype;
+  int64_t idx[8];
+  bool ok[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     const int q = tid + i * kBlock;  // 0 .. 2047 over a 64 x 32 slice
     const int r = mn_contig ? q % 64 : q / 32, kk = mn_contig ? q / 64 : q % 32;
     const uint32_t gr = r0 + r, gk = k0 + kk;
-    const bool ok = gr < rmax && gk < kmax;
-    const int64_t idx = v.offset + (int64_t)(ok ? gr : 0) * s_r + (int64_t)(ok ? gk : 0) * s_k;
-    const float val = load_elem(p, dt, idx);
-    reg[i] = ok ? val : 0.0f;
+    ok[i] = gr < rmax && gk < kmax;
+    idx[i] = v.offset + (int64_t)(ok[i] ? gr : 0) * s_r + (int64_t)(ok[i] ? gk : 0) * s_k;
+  }
+  float x[8];
+  if constexpr (DT == DT_F32) {
+    float w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = ((const GLOBAL float*)p)[idx[i]];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = w[i];
+  } else if constexpr (DT == DT_I8) {
+    int32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = ((const GLOBAL int8_t*)p)[idx[i]];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = (float)w[i];
+  } else {
+    uint32_t w[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = ((const GLOBAL uint16_t*)p)[idx[i]];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) x[i] = half_bits_to_f32(w[i], DT == DT_BF16);
+  }
+#pragma unroll
+  for (int i = 0; i < 8; ++i) reg[i] = ok[i] ? x[i] : 0.0f;
+}
+
+DEV void simt_load(uint32_t tid, const GLOBAL uint8_t* p, const VView& v, bool mn_contig, bool is_a, uint32_t r0,
+                   uint32_t rmax, uint32_t k0, uint32_t kmax, float (&reg)[8]) {
+  switch (v.dtype) {
+    case DT_F32: simt_load_t<DT_F32>(tid, p, v, mn_contig, is_a, r0, rmax, k0, kmax, reg); break;
+    case DT_BF16: simt_load_t<DT_BF16>(tid, p, v, mn_contig, is_a, r0, rmax, k0, kmax, reg); break;
+    case DT_F16: simt_load_t<DT_F16>(tid, p, v, mn_contig, is_a, r0, rmax, k0, kmax, reg); break;
+    default: simt_load_t<DT_I8>(tid, p, v, mn_contig, is_a, r0, rmax, k0, kmax, reg); break;
   }
 }
 
