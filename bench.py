@@ -317,7 +317,7 @@ def main():
                     help="0: cooperative launch; 1: ordinary launch of the co-resident grid (default)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py: this build runs on one GPU; the multi-GPU path is design only (see DESIGN.md)",
+        print("bench.py: runs on one GPU only; sharding across GPUs is a design, not an implementation",
               file=sys.stderr)
         sys.exit(2)
     import torch
