@@ -12,8 +12,8 @@ SGD, the default MLP's step written with torch.func and captured by the
 front end, int8-weight GEMV stack rotating 3 weight sets, 4096-wide bf16 MLP,
 16-layer fp16 residual MLP) are timed briefly and reported under "others".
 
-Prints one JSON line on stdout.  --gpus N with N > 1 is refused: this
-build runs on one GPU.
+Prints one JSON line on stdout.  --gpus N with N > 1 is refused: the
+kernel runs on one GPU.
 """
 from __future__ import annotations
 
