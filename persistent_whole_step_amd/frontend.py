@@ -78,6 +78,16 @@ class _Lowering:
             if not _is_contiguous(x):
                 raise NotImplementedError(f"capture: {t} of a non-contiguous view")
             return x.view(shape, contiguous_strides(shape), x.offset)
+        if t in (aten.unsqueeze.default, aten.squeeze.dim):
+            x = self.val(a[0])
+            r = len(x.shape)
+            if t == aten.unsqueeze.default:
+                d = int(a[1]) % (r + 1)
+                return x.view(x.shape[:d] + (1,) + x.shape[d:], x.strides[:d] + (0,) + x.strides[d:], x.offset)
+            d = int(a[1]) % max(r, 1)
+            if r == 0 or x.shape[d] != 1:
+                return x
+            return x.view(x.shape[:d] + x.shape[d + 1:], x.strides[:d] + x.strides[d + 1:], x.offset)
         if t == aten.expand.default:
             x = self.val(a[0])
             r = len(shape) - len(x.shape)

@@ -40,17 +40,30 @@ def residual_step(params, x, target):
     return v, tuple((W - 1e-2 * gW, b - 1e-2 * gb) for (W, b), (gW, gb) in zip(params, g))
 
 
+def misc_step(w, x, target):
+    """A step whose gradient needs div, neg, keepdim and dim-wise sums and
+    means, unsqueeze and broadcast expansions."""
+    def loss(v):
+        h = torch.relu(x @ v)
+        h = h / (h.sum(dim=1, keepdim=True) * 0.01 + 1.0)
+        return ((-h + target) ** 2).mean(dim=0).sum()
+    g, val = torch.func.grad_and_value(loss)(w)
+    return val, w - 0.1 * g
+
+
 def _examples(name, seed=0):
     gen = torch.Generator().manual_seed(seed)
     r = lambda *s: torch.randn(*s, generator=gen)
     if name == "readme":
+        return (r(24, 16) / 5, r(8, 24), r(8, 16))
+    if name == "misc":
         return (r(24, 16) / 5, r(8, 24), r(8, 16))
     if name == "mlp":
         return ({"W1": r(24, 40) / 5, "b1": r(40) / 5, "W2": r(40, 16) / 6, "b2": r(16) / 6}, r(12, 24), r(12, 16))
     return (tuple((r(32, 32) / 8, r(32) / 8) for _ in range(3)), r(10, 32), r(10, 32))
 
 
-STEPS = {"readme": readme_step, "mlp": mlp_step, "residual": residual_step}
+STEPS = {"readme": readme_step, "mlp": mlp_step, "residual": residual_step, "misc": misc_step}
 
 
 def _storage(t):

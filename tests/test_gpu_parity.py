@@ -642,3 +642,35 @@ def test_compile_training_step(oracle_mod, dtype):
     got, _ = pytree.tree_flatten((loss, new))  # the program's outputs, in the same order
     for g, r, s in zip(got, ref, prog.outputs):
         parity.assert_bitexact(tk.storage_from_tensor(g, s.dtype), r, s.dtype, s.buf)
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_compile_training_broadcast_step(oracle_mod, dtype):
+    """A captured step whose gradient uses division, negation, keepdim and
+    dim-wise reductions, unsqueeze and stride-0 broadcast views: per node
+    against the oracle on the GPU, and the compiled step equal to the
+    program run bit for bit."""
+    import torch
+    from persistent_whole_step_amd import frontend, tk
+    from .test_frontend import misc_step
+    say("capture front end, broadcast step", dtype)
+    tdt = {"bf16": torch.bfloat16, "f32": torch.float32}[dtype]
+    gen = torch.Generator().manual_seed(7)
+    w = (torch.randn(64, 48, generator=gen) / 8).to(tdt)
+    x = torch.randn(24, 64, generator=gen).to(tdt)
+    t = torch.randn(24, 48, generator=gen).to(tdt)
+    step = frontend.compile_training(misc_step, (w, x, t))
+    prog = step.program
+    assert prog.inplace == {1: 0}
+    ins = [tk.storage_from_tensor(v, s.dtype) for v, s in zip((w, x, t), prog.inputs)]
+    probe = prog.probe()
+    outs, _ = parity.gpu_run(probe, [a.copy() for a in ins])
+    vals = parity.probe_values(prog, probe, outs)
+    assert parity.check_per_node(oracle_mod, prog, ins, vals) == len(prog.ops)
+    ref, _ = parity.gpu_run(prog, [a.copy() for a in ins])
+    wg = w.cuda()
+    loss, w_new = step(wg, x.cuda(), t.cuda())
+    torch.cuda.synchronize()
+    assert w_new.data_ptr() == wg.data_ptr()
+    for g, r, s in zip((loss, w_new), ref, prog.outputs):
+        parity.assert_bitexact(tk.storage_from_tensor(g, s.dtype), r, s.dtype, s.buf)
