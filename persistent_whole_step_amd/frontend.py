@@ -19,6 +19,7 @@ from __future__ import annotations
 
 from dataclasses import dataclass
 
+from . import programs
 from .programs import Program, Spec, contiguous_strides
 
 
@@ -232,19 +233,37 @@ def _capture(fn, examples) -> Captured:
 
 
 def _update_mapping(c: Captured):
-    """In-place pairs {output slot: input index} for the updated state: the
+    """In-place pairs {output slot: input index} for the updated state.  The
     state is the first argument's tree; the updated state is the last output
-    subtree with the same structure whose every leaf is produced by an add or
-    sub that reads the matching state leaf first (w - lr * g).  The gradients
-    (the same structure, produced otherwise) stay ordinary outputs."""
+    subtree with the same structure whose every leaf is an update of the
+    matching state leaf: an add or sub (w - lr * g, or an optimizer state's
+    beta * m + (1 - beta) * g) whose chain of first operands, through
+    pointwise ops, leads back to that leaf, with its shape and dtype.  The
+    gradients (the same structure, produced otherwise) stay ordinary
+    outputs."""
     from torch.utils import _pytree as pytree
     p = c.program
-    # leaves of the first argument: the first `n_state` program inputs
     first = pytree.tree_unflatten(list(range(len(p.inputs))), c.in_spec)[0]
     state_leaves, state_spec = pytree.tree_flatten(first)
-    n_state = len(state_leaves)
     out_idx = pytree.tree_unflatten(list(range(len(p.outputs))), c.out_spec)
     producers = {op.out.buf: op for op in p.ops}
+
+    def updates(buf: str, src: str) -> bool:
+        op = producers.get(buf)
+        if op is None or op.opcode not in ("add", "sub"):
+            return False
+        seen = 0
+        while op is not None and seen < 64:
+            head = op.operands[0] if op.operands else None
+            if not isinstance(head, Spec):
+                return False
+            if head.buf == src:
+                return True
+            op = producers.get(head.buf)
+            if op is not None and op.opcode not in programs.POINTWISE:
+                return False
+            seen += 1
+        return False
 
     def candidates(tree):
         leaves, spec = pytree.tree_flatten(tree)
@@ -261,18 +280,13 @@ def _update_mapping(c: Captured):
     for leaves in candidates(out_idx):
         ok = True
         for slot, si in zip(leaves, state_leaves):
-            o = p.outputs[slot]
-            op = producers.get(o.buf)
-            src = p.inputs[si]
-            if (op is None or op.opcode not in ("add", "sub") or not isinstance(op.operands[0], Spec)
-                    or op.operands[0].buf != src.buf or o.shape != src.shape or o.dtype != src.dtype):
+            o, src = p.outputs[slot], p.inputs[si]
+            if o.shape != src.shape or o.dtype != src.dtype or not updates(o.buf, src.buf):
                 ok = False
                 break
         if ok:
             best = leaves
-    if best is None:
-        return {}
-    if len(set(best)) != len(best) or n_state != len(best):
+    if best is None or len(set(best)) != len(best) or len(best) != len(state_leaves):
         return {}
     return {slot: si for slot, si in zip(best, state_leaves)}
 

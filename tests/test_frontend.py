@@ -51,11 +51,25 @@ def misc_step(w, x, target):
     return val, w - 0.1 * g
 
 
+def adamw_step(state, x, target):
+    """AdamW on a one-layer model, written in torch: the state is
+    (weights, m, v) and every leaf is updated."""
+    w, m, v = state
+    lr, b1, b2, eps, wd, c1, c2 = 1e-2, 0.9, 0.999, 1e-8, 1e-2, 1.0 / (1 - 0.9 ** 3), 1.0 / (1 - 0.999 ** 3)
+    g, val = torch.func.grad_and_value(lambda u: ((torch.relu(x @ u) - target) ** 2).mean())(w)
+    m2 = m * b1 + g * (1 - b1)
+    v2 = v * b2 + (g * g) * (1 - b2)
+    w2 = w * (1 - lr * wd) - lr * (m2 * c1) / (torch.sqrt(v2 * c2) + eps)
+    return val, (w2, m2, v2)
+
+
 def _examples(name, seed=0):
     gen = torch.Generator().manual_seed(seed)
     r = lambda *s: torch.randn(*s, generator=gen)
     if name == "readme":
         return (r(24, 16) / 5, r(8, 24), r(8, 16))
+    if name == "adamw":
+        return ((r(24, 16) / 5, r(24, 16) / 100, r(24, 16).abs() / 100), r(8, 24), r(8, 16))
     if name == "misc":
         return (r(24, 16) / 5, r(8, 24), r(8, 16))
     if name == "mlp":
@@ -63,7 +77,8 @@ def _examples(name, seed=0):
     return (tuple((r(32, 32) / 8, r(32) / 8) for _ in range(3)), r(10, 32), r(10, 32))
 
 
-STEPS = {"readme": readme_step, "mlp": mlp_step, "residual": residual_step, "misc": misc_step}
+STEPS = {"readme": readme_step, "mlp": mlp_step, "residual": residual_step, "misc": misc_step,
+         "adamw": adamw_step}
 
 
 def _storage(t):
@@ -94,6 +109,13 @@ def test_update_mapping_marks_the_updated_state_only():
     assert sorted(m.values()) == [0, 1, 2, 3] and 0 not in m
     c = frontend._capture(residual_step, _examples("residual"))
     assert sorted(frontend._update_mapping(c).values()) == list(range(6))
+
+
+def test_update_mapping_covers_optimizer_states():
+    """An AdamW step written in torch commits the weights and both moment
+    states in place."""
+    c = frontend._capture(adamw_step, _examples("adamw"))
+    assert frontend._update_mapping(c) == {1: 0, 2: 1, 3: 2}
 
 
 def test_no_update_mapping_without_an_update():

@@ -674,3 +674,32 @@ def test_compile_training_broadcast_step(oracle_mod, dtype):
     assert w_new.data_ptr() == wg.data_ptr()
     for g, r, s in zip((loss, w_new), ref, prog.outputs):
         parity.assert_bitexact(tk.storage_from_tensor(g, s.dtype), r, s.dtype, s.buf)
+
+
+def test_compile_training_adamw_step(oracle_mod):
+    """AdamW written in torch and compiled: weights and both moment states
+    committed in place, per node against the oracle, and equal to the
+    program run bit for bit."""
+    import torch
+    from persistent_whole_step_amd import frontend, tk
+    from .test_frontend import adamw_step, _examples
+    from torch.utils import _pytree as pytree
+    say("capture front end, AdamW step")
+    ex = _examples("adamw", seed=3)
+    step = frontend.compile_training(adamw_step, ex)
+    prog = step.program
+    assert prog.inplace == {1: 0, 2: 1, 3: 2}
+    leaves, _ = pytree.tree_flatten(ex)
+    ins = [tk.storage_from_tensor(v, s.dtype) for v, s in zip(leaves, prog.inputs)]
+    probe = prog.probe()
+    outs, _ = parity.gpu_run(probe, [a.copy() for a in ins])
+    vals = parity.probe_values(prog, probe, outs)
+    assert parity.check_per_node(oracle_mod, prog, ins, vals) == len(prog.ops)
+    ref, _ = parity.gpu_run(prog, [a.copy() for a in ins])
+    state = tuple(v.cuda() for v in ex[0])
+    loss, new = step(state, ex[1].cuda(), ex[2].cuda())
+    torch.cuda.synchronize()
+    assert all(a.data_ptr() == b.data_ptr() for a, b in zip(new, state))
+    got, _ = pytree.tree_flatten((loss, new))
+    for g, r, s in zip(got, ref, prog.outputs):
+        parity.assert_bitexact(tk.storage_from_tensor(g, s.dtype), r, s.dtype, s.buf)
