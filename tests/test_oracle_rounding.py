@@ -136,3 +136,70 @@ def test_nan_stays_nan(oracle_mod):
         h = int(oracle_mod.round_f16(_f32(bits))[0])
         assert (b & 0x7F80) == 0x7F80 and (b & 0x7F)
         assert (h & 0x7C00) == 0x7C00 and (h & 0x3FF)
+
+
+# ------------------------------------------------------------ widening --
+# Every bf16 / f16 value the oracle reads (a program input, or an op's result
+# held at its dtype's precision) is widened to float32.  These pins compare the
+# oracle's widening of all 65,536 bit patterns of each format with conversions
+# that do not share its code: numpy's float16 -> float32 cast, and for bf16 the
+# format's definition (its bits are the top half of a float32).
+
+def _same_bits_or_both_nan(got: np.ndarray, want: np.ndarray) -> np.ndarray:
+    g, w = got.view(np.uint32), want.view(np.uint32)
+    return (g == w) | (np.isnan(got) & np.isnan(want))
+
+
+def _widen_program(dt):
+    from persistent_whole_step_amd.programs import Program
+    p = Program()
+    x = p.input("x", dt, (1 << 16,))
+    p.output(p.op("cast", [x], "f32"))
+    return p
+
+
+def test_widen_f16_all_patterns(oracle_mod):
+    h = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16).view(np.float16)
+    (got,) = oracle_mod.run(_widen_program("f16").text(), [h])
+    want = h.astype(np.float32)
+    ok = _same_bits_or_both_nan(got, want)
+    bad = np.flatnonzero(~ok)
+    assert bad.size == 0, [(hex(int(h.view(np.uint16)[i])), got[i], want[i]) for i in bad[:5]]
+    # the subnormal range is covered: 1023 positive and 1023 negative patterns
+    sub = (h.view(np.uint16) & 0x7C00) == 0
+    assert int((sub & (h.view(np.uint16) & 0x3FF != 0)).sum()) == 2046
+
+
+def test_widen_bf16_all_patterns(oracle_mod):
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    (got,) = oracle_mod.run(_widen_program("bf16").text(), [bits])
+    want = (bits.astype(np.uint32) << 16).view(np.float32)
+    bad = np.flatnonzero(~_same_bits_or_both_nan(got, want))
+    assert bad.size == 0, [(hex(int(bits[i])), got[i], want[i]) for i in bad[:5]]
+    # torch's bfloat16 -> float32 conversion agrees on every non-NaN pattern
+    tw = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float32).numpy()
+    assert _same_bits_or_both_nan(got, tw).all()
+
+
+@pytest.mark.parametrize("dt", ["f16", "bf16"])
+def test_op_results_held_at_dtype_precision(oracle_mod, dt):
+    """An op whose result dtype is f16/bf16 holds the rounded value widened
+    back to float32 (the value model): multiplying every finite value of the
+    format by 1 and reading the result as float32 gives the value itself,
+    subnormals included, and the stored result has the input's bits."""
+    from persistent_whole_step_amd.programs import Program
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    if dt == "f16":
+        x32 = bits.view(np.float16).astype(np.float32)
+    else:
+        x32 = (bits.astype(np.uint32) << 16).view(np.float32)
+    keep = np.isfinite(x32)
+    x32, bits = x32[keep], bits[keep]
+    p = Program()
+    x = p.input("x", "f32", x32.shape)
+    y = p.op("mul", [x, 1.0], dt)
+    p.output(y)
+    p.output(p.op("cast", [y], "f32"))
+    stored, wide = oracle_mod.run(p.text(), [x32])
+    assert (stored.view(np.uint16) == bits).all()
+    assert (wide.view(np.uint32) == x32.view(np.uint32)).all()
