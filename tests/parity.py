@@ -271,25 +271,43 @@ def _gather(buf: np.ndarray, spec: Spec, idx) -> np.ndarray:
     return flat[pos]
 
 
-def _bias_at(buf: np.ndarray, spec: Spec, rows, cols) -> np.ndarray:
-    """A bias view broadcast over an [m, n] output, read at (rows[i], cols[i])."""
+def tile_cover(n: int, rng, block: int = 64) -> np.ndarray:
+    """Sorted, unique indices into a dimension of size n: one random index
+    inside every block of `block` consecutive indices (the last block may be
+    short), plus the first and the last index.  Sampling rows and columns this
+    way puts at least one sampled output in every output tile of any tiling
+    whose tile edges are multiples of `block` (64x64 and 128x128 tiles)."""
+    if n <= 0:
+        return np.zeros(0, np.int64)
+    starts = np.arange(0, n, block)
+    ends = np.minimum(starts + block, n)
+    picks = starts + (rng.random(len(starts)) * (ends - starts)).astype(np.int64)
+    return np.unique(np.concatenate([[0, n - 1], picks]).astype(np.int64))
+
+
+def _bias_block(buf: np.ndarray, spec: Spec, rows, cols) -> np.ndarray:
+    """A bias view broadcast over an [m, n] output, read at every (rows[i],
+    cols[j]) (indexing only): an array [len(rows), len(cols)]."""
     r = len(spec.shape)
-    full = (rows, cols)
+    full = (np.asarray(rows)[:, None], np.asarray(cols)[None, :])
     idx = []
     for d in range(r):
         c = full[2 - r + d]
         idx.append(np.zeros_like(c) if spec.shape[d] == 1 else c)
-    return _gather(buf, spec, idx)
+    shape = (len(rows), len(cols))
+    return np.broadcast_to(_gather(buf, spec, idx), shape).copy()
 
 
 def sampled_contraction_program(op, vals: dict, rows, cols):
-    """A small program whose output diagonal (i, i) is op's output at
-    (rows[i], cols[i]): the sampled rows of the activation operand and the
-    sampled columns (output features) of the weight operand, and a diagonal
-    bias holding the bias at each sampled output.  Each output of a
-    contraction depends on its own row and column only, so the oracle's value
-    there is the value it computes for the full op."""
-    s = len(rows)
+    """A small program whose output (i, j) is op's output at (rows[i],
+    cols[j]): the sampled rows of the activation operand, the sampled columns
+    (output features) of the weight operand, and the bias read at every
+    sampled output.  Each output of a contraction depends on its own row and
+    column only, so the oracle's value there is the value it computes for the
+    full op."""
+    rows = np.asarray(rows, dtype=np.int64)
+    cols = np.asarray(cols, dtype=np.int64)
+    sr, sc = len(rows), len(cols)
     p = Program()
     arrays = []
     bias_first = op.opcode in ("addmm", "addmm_q8")
@@ -298,10 +316,10 @@ def sampled_contraction_program(op, vals: dict, rows, cols):
         A, B = ops_in
         k = A.shape[1]
         kk = np.arange(k)
-        a = _gather(vals[A.buf], A, (np.asarray(rows)[:, None], kk[None, :]))
-        b = _gather(vals[B.buf], B, (kk[:, None], np.asarray(cols)[None, :]))
-        sa = p.input("A", A.dtype, (s, k))
-        sb = p.input("B", B.dtype, (k, s))
+        a = _gather(vals[A.buf], A, (rows[:, None], kk[None, :]))
+        b = _gather(vals[B.buf], B, (kk[:, None], cols[None, :]))
+        sa = p.input("A", A.dtype, (sr, k))
+        sb = p.input("B", B.dtype, (k, sc))
         operands = [sa, sb]
         arrays += [np.ascontiguousarray(a), np.ascontiguousarray(b)]
     else:
@@ -309,34 +327,33 @@ def sampled_contraction_program(op, vals: dict, rows, cols):
         k = X.shape[1]
         kk = np.arange(k)
         nb = S.shape[1]
-        x = _gather(vals[X.buf], X, (np.asarray(rows)[:, None], kk[None, :]))
-        q = _gather(vals[Q.buf], Q, (np.asarray(cols)[:, None], kk[None, :]))
-        sc = _gather(vals[S.buf], S, (np.asarray(cols)[:, None], np.arange(nb)[None, :]))
-        sx = p.input("x", X.dtype, (s, k))
-        sq = p.input("q", Q.dtype, (s, k))
-        ss = p.input("s", S.dtype, (s, nb))
+        x = _gather(vals[X.buf], X, (rows[:, None], kk[None, :]))
+        q = _gather(vals[Q.buf], Q, (cols[:, None], kk[None, :]))
+        sc_ = _gather(vals[S.buf], S, (cols[:, None], np.arange(nb)[None, :]))
+        sx = p.input("x", X.dtype, (sr, k))
+        sq = p.input("q", Q.dtype, (sc, k))
+        ss = p.input("s", S.dtype, (sc, nb))
         operands = [sx, sq, ss]
-        arrays += [np.ascontiguousarray(x), np.ascontiguousarray(q), np.ascontiguousarray(sc)]
+        arrays += [np.ascontiguousarray(x), np.ascontiguousarray(q), np.ascontiguousarray(sc_)]
     if bias_first:
         Bi = op.operands[0]
-        diag = _bias_at(vals[Bi.buf], Bi, np.asarray(rows), np.asarray(cols))
-        full = np.zeros((s, s), dtype=diag.dtype)
-        full[np.arange(s), np.arange(s)] = diag
-        sbias = p.input("bias", Bi.dtype, (s, s))
+        sbias = p.input("bias", Bi.dtype, (sr, sc))
         operands = [sbias] + operands
-        arrays = arrays + [full]  # in the order of the program's inputs
-    out = p.op(op.opcode, operands, op.out.dtype, (s, s), name="y", **op.attrs)
+        arrays = arrays + [np.ascontiguousarray(_bias_block(vals[Bi.buf], Bi, rows, cols))]
+    out = p.op(op.opcode, operands, op.out.dtype, (sr, sc), name="y", **op.attrs)
     p.output(out)
     return p, arrays
 
 
-def check_per_node_sampled(oracle_mod, prog: Program, inputs, gpu_vals: dict, samples: int = 48, seed: int = 0,
-                           rel=1e-4):
+def check_per_node_sampled(oracle_mod, prog: Program, inputs, gpu_vals: dict, seed: int = 0, rel=1e-4,
+                           block: int = 64):
     """Teacher-forced per-op parity at full size: pointwise ops and reductions
     are re-evaluated whole by the oracle (bit-exact / contraction tolerance);
-    each contraction is checked at `samples` outputs (the four corners and
-    random ones), each computed by the oracle from the GPU's own operand
-    values, against its exact float64 value."""
+    each contraction is checked on the block of outputs at the rows and
+    columns `tile_cover` picks (one in every 64 along each dimension, and the
+    edges), so every output tile holds checked outputs.  Each checked output
+    is computed by the oracle from the GPU's own operand values and compared
+    with its exact float64 value."""
     rng = np.random.default_rng(seed)
     value_specs = {s.buf: s for s in prog.inputs}
     for op in prog.ops:
@@ -350,16 +367,14 @@ def check_per_node_sampled(oracle_mod, prog: Program, inputs, gpu_vals: dict, sa
         got = gpu_vals[op.out.buf]
         if op.opcode in programs.CONTRACTIONS:
             m, n = op.out.shape
-            rows = np.concatenate([[0, m - 1, 0, m - 1], rng.integers(0, m, samples - 4)])
-            cols = np.concatenate([[0, n - 1, n - 1, 0], rng.integers(0, n, samples - 4)])
+            rows, cols = tile_cover(m, rng, block), tile_cover(n, rng, block)
             sp, arrays = sampled_contraction_program(op, vals, rows, cols)
             (want,) = oracle_mod.run(sp.text(), arrays)
             svals = {s.buf: a for s, a in zip(sp.inputs, arrays)}
             exact, mag = contraction_reference(sp.ops[0], svals, None)
-            d = np.arange(len(rows))
-            g = got.reshape(m, n)[rows, cols]
-            assert_contraction(g, want.reshape(len(rows), len(rows))[d, d], exact[d, d], mag[d, d], op.out.dtype,
-                               f"{op.name} ({op.opcode}, {len(rows)} sampled outputs)", rel)
+            g = got.reshape(m, n)[rows[:, None], cols[None, :]]
+            assert_contraction(g, want.reshape(len(rows), len(cols)), exact, mag, op.out.dtype,
+                               f"{op.name} ({op.opcode}, {len(rows)}x{len(cols)} sampled outputs)", rel)
         else:
             sp, names = single_op_program(prog, j, value_specs)
             (want,) = oracle_mod.run(sp.text(), [np.ascontiguousarray(vals[nm]) for nm in names])
