@@ -69,11 +69,24 @@ class _Lowering:
         # views: no op, a new view of the same buffer
         if t in (aten.t.default, aten.transpose.int, aten.permute.default):
             x = self.val(a[0])
-            if len(x.shape) != 2:
-                raise NotImplementedError(f"capture: {t} of a rank-{len(x.shape)} tensor")
-            if t == aten.permute.default and list(a[1]) != [1, 0]:
+            r = len(x.shape)
+            if t == aten.permute.default:
+                perm = [int(d) % max(r, 1) for d in a[1]]
+                if sorted(perm) != list(range(r)):
+                    raise NotImplementedError(f"capture: permute dims {list(a[1])} of a rank-{r} tensor")
+            else:
+                if t == aten.t.default:
+                    if r > 2:
+                        raise NotImplementedError(f"capture: t() of a rank-{r} tensor")
+                    d0, d1 = (0, 1) if r == 2 else (0, 0)
+                else:
+                    d0, d1 = int(a[1]) % max(r, 1), int(a[2]) % max(r, 1)
+                perm = list(range(r))
+                if r:
+                    perm[d0], perm[d1] = perm[d1], perm[d0]
+            if perm == list(range(r)):  # the identity permutation: the same view
                 return x
-            return x.T
+            return x.view(tuple(x.shape[d] for d in perm), tuple(x.strides[d] for d in perm), x.offset)
         if t in (aten.view.default, aten._unsafe_view.default, aten.reshape.default):
             x = self.val(a[0])
             if not _is_contiguous(x):
@@ -314,6 +327,52 @@ class CompiledTrainingStep:
 
     def query(self) -> dict:
         return self.compiled.query()
+
+    def capture(self, *args, warmup: int = 2) -> "CapturedProgram":
+        """A reusable graph of one step on these arguments (the runtime page
+        README's ``compiled.capture``): ``warmup`` eager steps, then one
+        launch captured into a HIP graph; the state tensors are restored to
+        the values they held on entry after warmup and capture.  Replays run
+        the step on the same tensors: the state advances in place, and other
+        outputs live in buffers allocated here (fixed shapes and addresses,
+        overwritten by every replay)."""
+        import torch
+        from torch.utils import _pytree as pytree
+        from . import tk
+        leaves, spec = pytree.tree_flatten(tuple(args))
+        if spec != self.captured.in_spec:
+            raise TypeError("compiled step: arguments do not match the captured tree")
+        prog = self.compiled
+        if getattr(prog, "launch_mode", 0) != 1:
+            # graph capture records ordinary launches only
+            prog = tk.compile(self.program.text(), device=self.compiled.device, launch_mode=1)
+        targets = sorted(set(self.program.inplace.values()))
+        saved = {i: leaves[i].detach().clone() for i in targets}
+        bufs = prog.allocate(*leaves)
+        for _ in range(max(0, int(warmup))):
+            prog.run_into(*leaves, buffers=bufs)
+        torch.cuda.synchronize()
+        graph = tk.StepGraph(prog, [(leaves, bufs)])
+        for i, v in saved.items():
+            leaves[i].copy_(v)
+        torch.cuda.synchronize()
+        return CapturedProgram(graph, bufs, self.captured.out_spec)
+
+
+class CapturedProgram:
+    """A captured step (see ``CompiledTrainingStep.capture``).  ``replay()``
+    enqueues one step on the current stream and returns the output tree,
+    whose tensors are the captured buffers and state tensors."""
+
+    def __init__(self, graph, buffers, out_spec):
+        self.graph = graph
+        self.buffers = buffers
+        self.out_spec = out_spec
+
+    def replay(self):
+        from torch.utils import _pytree as pytree
+        self.graph.replay()
+        return pytree.tree_unflatten(list(self.buffers.outputs), self.out_spec)
 
 
 def compile_training(fn, examples, device: int = 0, inplace: bool = True, **opts) -> CompiledTrainingStep:

@@ -136,3 +136,31 @@ def test_plan_only_compile_of_a_captured_step():
     c.program.inplace = frontend._update_mapping(c)
     q = tk.compile(c.program.text(), device=-1).query()
     assert q["n_stages"] >= 3 and q["direct_state_commits"] + q["staged_commits"] == 4
+
+
+@pytest.mark.parametrize("view", ["permute(-1,-2)", "permute(0,1)", "permute(1,0)", "transpose(1,1)",
+                                  "transpose(0,1)", "transpose(-1,-2)", "t()"])
+def test_view_permutations_match_eager(oracle_mod, view):
+    """Square weights make a missed or spurious transpose shape-correct, so
+    each view form is compared with eager torch through the oracle: the
+    identity forms (permute(0,1), transpose(1,1)) leave the operand as it
+    is, the swaps transpose it."""
+    def step(w, x):
+        v = eval(f"w.{view}")
+        return x @ v + v.sum(dim=0)
+
+    gen = torch.Generator().manual_seed(4)
+    w, x = torch.randn(16, 16, generator=gen), torch.randn(5, 16, generator=gen)
+    prog, _ = frontend.capture(step, (w, x))
+    (got,) = oracle_mod.run(prog.text(), [_storage(w), _storage(x)])
+    np.testing.assert_allclose(got, step(w, x).numpy(), rtol=2e-5, atol=2e-5)
+
+
+def test_rank3_permute_is_lowered_as_a_view(oracle_mod):
+    def step(a):
+        return a.permute(2, 0, 1) * 2.0
+
+    a = torch.randn(2, 3, 4, generator=torch.Generator().manual_seed(6))
+    prog, _ = frontend.capture(step, (a,))
+    (got,) = oracle_mod.run(prog.text(), [_storage(a)])
+    np.testing.assert_array_equal(got, step(a).numpy())
