@@ -148,6 +148,13 @@ class Runner:
         self.stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
         self.tk = tk
 
+    def close(self):
+        """Free the compiled program and drop the resident tensors."""
+        self.p.close()
+        self.variants = []
+        self.inputs = []
+        self.buffers = None
+
     def step(self, i: int):
         ci, ni, co, no, cw = self.variants[i % len(self.variants)]
         rc = self.run_c(self.p._h, ci, ni, co, no, ctypes.byref(cw), self.stream)

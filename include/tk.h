@@ -15,8 +15,8 @@
  *     the program's device.
  *   - Programs are immutable after tk_compile and may be used from several
  *     threads and streams at once given distinct output and workspace
- *     buffers (the pages: "Calls allocate independent buffers for stream
- *     safety").
+ *     buffers (trainkernel runtime.py, class `CompiledProgram`: each call
+ *     gets buffers of its own, which is what makes concurrent streams safe).
  */
 #ifndef TK_H
 #define TK_H
@@ -43,7 +43,8 @@ typedef enum {
   TK_E_WORKSPACE = 9,    /* workspace too small, misaligned, or on the wrong device */
   TK_E_COUNT = 10,       /* wrong number of inputs / outputs */
   TK_E_HIP = 11,         /* a HIP runtime call failed (message has the HIP error) */
-  TK_E_ABORTED = 12      /* a launch stopped at a timed-out grid barrier */
+  TK_E_ABORTED = 12      /* an earlier launch of this program stopped at a grid barrier
+                            that timed out (see tk_run_into) */
 } tk_status;
 
 /* A caller-owned tensor view.  `storage_base`/`storage_bytes` give the whole
@@ -142,6 +143,12 @@ tk_status tk_query(const tk_program* prog, tk_stats* out);
  * NUL-terminated when len > 0).  *needed receives the full length + 1. */
 tk_status tk_dump_plan(const tk_program* prog, char* buf, size_t len, size_t* needed);
 
+/* Copy the device plan (the bytes tk_compile uploads: a DHeader, the DStage
+ * table and one descriptor blob per stage, laid out as in csrc/plan.h) into
+ * buf, at most len bytes.  *needed receives the plan's size.  For tools that
+ * check a schedule on the host (the schedule race checker). */
+tk_status tk_plan_bytes(const tk_program* prog, void* buf, size_t len, size_t* needed);
+
 /* Fill `outputs` (n_out descriptors) and `workspace` for a run on `inputs`
  * (pages: `allocate`).  In-place output slots receive their input's own
  * descriptor; other outputs and the workspace come from `alloc` (contiguous,
@@ -166,12 +173,21 @@ tk_status tk_validate_into(const tk_program* prog, const tk_tensor* inputs, size
  * launch; every stage ends in a global-memory grid barrier.  The workspace
  * header must have been initialised once (tk_allocate or tk_workspace_init);
  * it stays valid across launches.  Reuse of outputs/workspace must be ordered
- * by the caller; calls overlapping on one workspace race. */
+ * by the caller; calls overlapping on one workspace race.
+ * Every wait at a grid barrier is bounded.  A launch whose barrier times out
+ * stops (its outputs and in-place targets are then partly written), marks its
+ * workspace aborted and records that in host memory the program owns; from
+ * then on tk_run_into returns TK_E_ABORTED before any check or launch, and a
+ * launch on the aborted workspace runs nothing, until tk_workspace_init
+ * re-initialises the workspace.  The launch that timed out itself returned
+ * TK_OK (the error is detected asynchronously): tk_workspace_status reports
+ * it after synchronising the stream. */
 tk_status tk_run_into(const tk_program* prog, const tk_tensor* inputs, size_t n_in, const tk_tensor* outputs,
                       size_t n_out, const tk_tensor* workspace, void* stream);
 
 /* Zero the workspace header (barrier state, abort flag) on `stream` with a
- * small kernel (safe under graph capture). */
+ * small kernel (safe under graph capture), and clear the program's record of
+ * an aborted launch (TK_E_ABORTED). */
 tk_status tk_workspace_init(const tk_program* prog, const tk_tensor* workspace, void* stream);
 
 /* Synchronise `stream` and read the workspace header: *aborted = 1 when a
@@ -191,9 +207,16 @@ tk_status tk_set_debug(tk_program* prog, int32_t timestamps, uint32_t stagger_se
 tk_status tk_read_timestamps(const tk_program* prog, const tk_tensor* workspace, void* stream, uint64_t* out,
                              size_t n);
 
+/* Free the program's device plan and host memory (the counterpart of
+ * tk_compile; trainkernel runtime.py holds a compiled program as an object
+ * that owns its loaded kernel).  NULL is ignored.  No launch of the program
+ * may still be running; caller tensors are never touched. */
 void tk_destroy(tk_program* prog);
 
-/* Thread-local message of the last failed call on this thread. */
+/* Thread-local message ("tk: ...") of the last failed call on this thread.
+ * The messages name the failed check the way trainkernel runtime.py's
+ * `run_into` and `_validate_inputs` do (e.g. "incorrect output buffer
+ * count", "inplace target must not alias another input"). */
 const char* tk_last_error(void);
 
 #ifdef __cplusplus

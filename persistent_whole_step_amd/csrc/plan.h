@@ -174,6 +174,7 @@ struct KArgs {
   uint32_t stagger_seed;
   uint32_t n_bases;
   uint32_t pad;
+  uint32_t* host_abort;        // pinned host words [aborted, stage] of the program, or null
   void* bases[kMaxBases];
 };
 constexpr uint32_t K_TIMESTAMPS = 1u;

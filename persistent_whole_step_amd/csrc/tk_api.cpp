@@ -29,6 +29,12 @@ struct tk_program {
   uint32_t dbg_flags = 0;
   uint32_t stagger = 0;
   uint64_t deadline = 0;
+  // Pinned, device-visible host words [aborted, stage]: a launch that stops at
+  // a timed-out grid barrier (or finds its workspace already aborted) sets
+  // them, so later tk_run_into calls report TK_E_ABORTED without waiting on
+  // the device.  tk_workspace_init clears them.
+  volatile uint32_t* h_abort = nullptr;
+  uint32_t* d_abort = nullptr;
 };
 
 namespace {
@@ -256,9 +262,19 @@ tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int3
       }
       if (e == hipSuccess) e = hipMalloc(&p->d_plan, p->plan.bytes.size());
       if (e == hipSuccess) e = hipMemcpy(p->d_plan, p->plan.bytes.data(), p->plan.bytes.size(), hipMemcpyHostToDevice);
+      void* hflag = nullptr;
+      if (e == hipSuccess) e = hipHostMalloc(&hflag, 64, hipHostMallocMapped | hipHostMallocCoherent);
+      if (e == hipSuccess) {
+        p->h_abort = (volatile uint32_t*)hflag;
+        p->h_abort[0] = p->h_abort[1] = 0u;
+        void* dflag = nullptr;
+        e = hipHostGetDevicePointer(&dflag, hflag, 0);
+        p->d_abort = (uint32_t*)dflag;
+      }
       hipSetDevice(cur);
       if (e != hipSuccess) {
         if (p->d_plan) hipFree(p->d_plan);
+        if (p->h_abort) hipHostFree((void*)p->h_abort);
         delete p;
         return hip_fail(e, "plan upload");
       }
@@ -304,6 +320,14 @@ tk_status tk_dump_plan(const tk_program* p, char* buf, size_t len, size_t* neede
   return TK_OK;
 }
 
+tk_status tk_plan_bytes(const tk_program* p, void* buf, size_t len, size_t* needed) {
+  if (!p) return fail(TK_E_ARG, "program is NULL");
+  const auto& b = p->plan.bytes;
+  if (needed) *needed = b.size();
+  if (buf && len) std::memcpy(buf, b.data(), std::min(len, b.size()));
+  return TK_OK;
+}
+
 tk_status tk_validate_into(const tk_program* p, const tk_tensor* inputs, size_t n_in, const tk_tensor* outputs,
                            size_t n_out, const tk_tensor* workspace) {
   if (!p) return fail(TK_E_ARG, "program is NULL");
@@ -325,6 +349,7 @@ tk_status tk_workspace_init(const tk_program* p, const tk_tensor* ws, void* stre
   hipError_t e = tk_device_zero_header((uint8_t*)ws->data, (hipStream_t)stream);
   hipSetDevice(cur);
   if (e != hipSuccess) return hip_fail(e, "workspace header init");
+  if (p->h_abort) p->h_abort[0] = p->h_abort[1] = 0u;
   return TK_OK;
 }
 
@@ -382,6 +407,11 @@ tk_status tk_run_into(const tk_program* p, const tk_tensor* inputs, size_t n_in,
                       size_t n_out, const tk_tensor* workspace, void* stream) {
   if (!p) return fail(TK_E_ARG, "program is NULL");
   if (p->device < 0) return fail(TK_E_DEVICE, "plan-only program: compile for a device to run");
+  if (p->h_abort && p->h_abort[0] != 0u)
+    return fail(TK_E_ABORTED, "a launch of this program stopped at a grid barrier that timed out (stage " +
+                                  std::to_string(p->h_abort[1]) +
+                                  "); its outputs are incomplete; re-initialise the workspace (tk_workspace_init) "
+                                  "before running again");
   TK_TRY({
     check_buffers(p, inputs, n_in, outputs, n_out, workspace, p->device);
     KArgs ka;
@@ -391,6 +421,7 @@ tk_status tk_run_into(const tk_program* p, const tk_tensor* inputs, size_t n_in,
     ka.deadline_ticks = p->deadline;
     ka.flags = p->dbg_flags;
     ka.stagger_seed = p->stagger;
+    ka.host_abort = p->d_abort;
     const auto& pl = p->plan;
     ka.n_bases = (uint32_t)(pl.ws_base + 1);
     for (size_t i = 0; i < n_in; ++i) ka.bases[i] = inputs[i].data;
@@ -446,6 +477,7 @@ void tk_destroy(tk_program* p) {
     hipFree(p->d_plan);
     hipSetDevice(cur);
   }
+  if (p->h_abort) hipHostFree((void*)p->h_abort);
   delete p;
 }
 

@@ -119,7 +119,21 @@ struct Ctx {
   const GLOBAL uint8_t* plan;  // device-resident plan
   uint32_t flags;              // K_* debug switches
   uint32_t stagger_seed;
+  uint32_t* host_abort;        // pinned host words [aborted, stage], or null
 };
+
+// Record a stopped launch: the workspace's abort word and stage, and the
+// program's pinned host words that tk_run_into reads before the next launch.
+DEV void set_abort(const Ctx& ka, uint32_t stage) {
+  GLOBAL uint32_t* abort = (GLOBAL uint32_t*)(ka.ws + kHdrAbort);
+  GLOBAL uint32_t* abort_stage = (GLOBAL uint32_t*)(ka.ws + kHdrAbortStage);
+  __hip_atomic_store(abort_stage, stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (ka.host_abort) {
+    __hip_atomic_store(ka.host_abort + 1, stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+    __hip_atomic_store(ka.host_abort, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+  }
+}
 
 DEV GLOBAL uint8_t* base_ptr(const Ctx&, uint32_t base) {
   return (GLOBAL uint8_t*)uniform64((int64_t)((const LDS uint64_t*)g_bases)[base]);
@@ -2112,7 +2126,6 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
   GLOBAL uint32_t* arrive = (GLOBAL uint32_t*)(ka.ws + kHdrArrive);
   GLOBAL uint32_t* release = (GLOBAL uint32_t*)(ka.ws + kHdrRelease);
   GLOBAL uint32_t* abort = (GLOBAL uint32_t*)(ka.ws + kHdrAbort);
-  GLOBAL uint32_t* abort_stage = (GLOBAL uint32_t*)(ka.ws + kHdrAbortStage);
   const uint32_t G = gridDim.x, bid = blockIdx.x;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -2148,8 +2161,7 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
           break;
         }
         if (__builtin_amdgcn_s_memrealtime() - t0 > deadline) {
-          __hip_atomic_store(abort_stage, stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          __hip_atomic_store(abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          set_abort(ka, stage);
           ok = 0;
           break;
         }
@@ -2172,8 +2184,7 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
         break;
       }
       if (__builtin_amdgcn_s_memrealtime() - t0 > deadline) {
-        __hip_atomic_store(abort_stage, stage, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        set_abort(ka, stage);
         ok = 0;
         break;
       }
@@ -2214,13 +2225,23 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
   ka.plan = (const GLOBAL uint8_t*)uniform64((int64_t)kargs.plan);
   ka.flags = uniform(kargs.flags);
   ka.stagger_seed = uniform(kargs.stagger_seed);
+  ka.host_abort = (uint32_t*)uniform64((int64_t)kargs.host_abort);
   const uint32_t n_bases = kargs.n_bases < (uint32_t)kMaxBases ? kargs.n_bases : (uint32_t)kMaxBases;
   for (uint32_t i = threadIdx.x; i < n_bases; i += kBlock) ((LDS uint64_t*)g_bases)[i] = (uint64_t)kargs.bases[i];
   const uint64_t deadline = kargs.deadline_ticks ? kargs.deadline_ticks : 400000000ull;  // 4 s at 100 MHz
   const GLOBAL DHeader* h = (const GLOBAL DHeader*)ka.plan;
   const GLOBAL uint8_t* stages = ka.plan + h->off_stages;
   const uint32_t n_stages = h->n_stages;
-  if (*(volatile GLOBAL uint32_t*)(ka.ws + kHdrAbort) != 0u) return;  // a previous launch on this workspace aborted
+  if (*(volatile GLOBAL uint32_t*)(ka.ws + kHdrAbort) != 0u) {
+    // a previous launch on this workspace stopped: run nothing, and say so
+    // to the host again (its words may have been cleared for another workspace)
+    if (blockIdx.x == 0 && threadIdx.x == 0 && ka.host_abort) {
+      __hip_atomic_store(ka.host_abort + 1, *(volatile GLOBAL uint32_t*)(ka.ws + kHdrAbortStage), __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_SYSTEM);
+      __hip_atomic_store(ka.host_abort, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_SYSTEM);
+    }
+    return;
+  }
   const uint32_t epoch0 = *(volatile GLOBAL uint32_t*)(ka.ws + kHdrEpoch);
   if (n_stages == 0) return;
   DStage sd = load_stage(stages, 0);

@@ -53,6 +53,13 @@ def cmd_run(args):
     torch.cuda.synchronize()
     dst.copy_(src)
     torch.cuda.synchronize()
+    # Release every device resource here, while the runtime is whole: a
+    # device call made from a finaliser after the profiler's tool has shut
+    # down at exit crashes the process.
+    r.close()
+    del src, dst, r
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     print(f"[profiling] {args.workload}: {args.launches} launches, copy of {COPY_BYTES} bytes", flush=True)
 
 

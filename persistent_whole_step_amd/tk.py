@@ -11,12 +11,14 @@ from __future__ import annotations
 
 import ctypes
 import os
+import sys
 from dataclasses import dataclass
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libtk.so")
 
 TK_F32, TK_F16, TK_BF16, TK_I8 = 0, 1, 2, 3
+TK_E_ABORTED = 12
 DTYPE_CODES = {"f32": TK_F32, "f16": TK_F16, "bf16": TK_BF16, "i8": TK_I8}
 STATUS = {0: "TK_OK", 1: "TK_E_ARG", 2: "TK_E_PARSE", 3: "TK_E_UNSUPPORTED", 4: "TK_E_SHAPE", 5: "TK_E_STRIDE",
           6: "TK_E_DTYPE", 7: "TK_E_DEVICE", 8: "TK_E_ALIAS", 9: "TK_E_WORKSPACE", 10: "TK_E_COUNT",
@@ -73,6 +75,7 @@ def lib():
         l.tk_compile.argtypes = [ctypes.c_char_p, ctypes.c_size_t, P(TkOptions), ctypes.c_int32, P(ctypes.c_void_p)]
         l.tk_query.argtypes = [ctypes.c_void_p, P(TkStats)]
         l.tk_dump_plan.argtypes = [ctypes.c_void_p, ctypes.c_char_p, ctypes.c_size_t, P(ctypes.c_size_t)]
+        l.tk_plan_bytes.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, P(ctypes.c_size_t)]
         l.tk_allocate.argtypes = [ctypes.c_void_p, P(TkTensor), ctypes.c_size_t, ALLOC_FN, ctypes.c_void_p,
                                   P(TkTensor), ctypes.c_size_t, P(TkTensor), ctypes.c_void_p]
         l.tk_validate_into.argtypes = [ctypes.c_void_p, P(TkTensor), ctypes.c_size_t, P(TkTensor), ctypes.c_size_t,
@@ -87,7 +90,7 @@ def lib():
         l.tk_destroy.argtypes = [ctypes.c_void_p]
         l.tk_destroy.restype = None
         l.tk_last_error.restype = ctypes.c_char_p
-        for f in ("tk_compile", "tk_query", "tk_dump_plan", "tk_allocate", "tk_validate_into", "tk_run_into",
+        for f in ("tk_compile", "tk_query", "tk_dump_plan", "tk_plan_bytes", "tk_allocate", "tk_validate_into", "tk_run_into",
                   "tk_workspace_init", "tk_workspace_status", "tk_set_debug", "tk_read_timestamps"):
             getattr(l, f).restype = ctypes.c_int
         _lib = l
@@ -111,8 +114,7 @@ def options(**kw) -> TkOptions:
 
 def _torch_dtype_code(t) -> int:
     import torch
-    m = {torch.float32: TK_F32, torch.float16: TK_F16, torch.bfloat16: TK_BF16, torch.int8: TK_I8,
-         torch.uint8: TK_I8}
+    m = {torch.float32: TK_F32, torch.float16: TK_F16, torch.bfloat16: TK_BF16, torch.int8: TK_I8}
     if t.dtype not in m:
         raise TypeError(f"unsupported tensor dtype {t.dtype}")
     return m[t.dtype]
@@ -140,11 +142,19 @@ def storage_from_tensor(t, dt: str):
     return t.numpy().copy()
 
 
-def describe(t) -> TkTensor:
-    """A tk_tensor for a torch tensor (storage extent used for aliasing)."""
+def describe(t, raw_bytes: bool = False) -> TkTensor:
+    """A tk_tensor for a torch tensor (storage extent used for aliasing).
+    raw_bytes: a uint8 workspace, described as bytes (TK_I8); otherwise uint8
+    is rejected, since no program value is unsigned."""
+    import torch
     d = TkTensor()
     d.data = t.data_ptr() if t.numel() else 0
-    d.dtype = _torch_dtype_code(t)
+    if raw_bytes:
+        if t.dtype != torch.uint8:
+            raise TypeError(f"workspace must be a uint8 byte tensor, got {t.dtype}")
+        d.dtype = TK_I8
+    else:
+        d.dtype = _torch_dtype_code(t)
     d.ndim = t.dim()
     for i, (s, st) in enumerate(zip(t.shape, t.stride())):
         d.shape[i] = s
@@ -209,11 +219,21 @@ class Program:
         self.device = device
         self._outputs = None
 
-    def __del__(self):
+    def __del__(self, _finalizing=sys.is_finalizing):
+        # At interpreter shutdown the HIP runtime (and a profiler's tool
+        # library) may already be torn down: device calls from a finaliser
+        # then crash the process.  Programs still alive then are left to the
+        # process exit; close() releases one deterministically.
+        if _finalizing():
+            return
+        self.close()
+
+    def close(self):
+        """tk_destroy: free the program's plan (no launch may be running)."""
         h = getattr(self, "_h", None)
         if h and _lib is not None:
             _lib.tk_destroy(h)
-            self._h = None
+        self._h = None
 
     # ---------------------------------------------------------- queries --
     def query(self) -> dict:
@@ -230,6 +250,14 @@ class Program:
         buf = ctypes.create_string_buffer(need.value)
         _check(lib().tk_dump_plan(self._h, buf, need.value, None))
         return buf.value.decode()
+
+    def plan_bytes(self) -> bytes:
+        """tk_plan_bytes: the device plan as uploaded (csrc/plan.h layout)."""
+        need = ctypes.c_size_t(0)
+        _check(lib().tk_plan_bytes(self._h, None, 0, ctypes.byref(need)))
+        buf = ctypes.create_string_buffer(max(1, need.value))
+        _check(lib().tk_plan_bytes(self._h, buf, need.value, None))
+        return buf.raw[:need.value]
 
     def resource_usage(self) -> dict:
         q = self.query()
@@ -299,8 +327,7 @@ class Program:
     def _descs(self, inputs, buffers):
         ins = _array([describe(t) for t in inputs])
         outs = _array([describe(t) for t in buffers.outputs])
-        ws = describe(buffers.workspace)
-        ws.dtype = TK_I8
+        ws = describe(buffers.workspace, raw_bytes=True)
         return ins, outs, ws
 
     def validate_into(self, *inputs, buffers: ExecutionBuffers):
@@ -308,8 +335,7 @@ class Program:
         _check(lib().tk_validate_into(self._h, ins, len(inputs), outs, len(buffers.outputs), ctypes.byref(ws)))
 
     def init_workspace(self, workspace, stream=None):
-        ws = describe(workspace)
-        ws.dtype = TK_I8
+        ws = describe(workspace, raw_bytes=True)
         _check(lib().tk_workspace_init(self._h, ctypes.byref(ws), _stream_handle(stream)))
 
     def run_into(self, *inputs, buffers: ExecutionBuffers, stream=None):
@@ -326,19 +352,31 @@ class Program:
         return buffers.outputs
 
     def __call__(self, *inputs):
-        return self.run_into(*inputs, buffers=self.allocate(*inputs))
+        """Allocate fresh buffers, run, wait for the step and check that it
+        completed: a launch that stopped at a timed-out grid barrier raises
+        TkError (TK_E_ABORTED) instead of returning partial outputs."""
+        bufs = self.allocate(*inputs)
+        outs = self.run_into(*inputs, buffers=bufs)
+        self.check_workspace(bufs.workspace)
+        return outs
+
+    def check_workspace(self, workspace, stream=None):
+        """Synchronise `stream` and raise TkError (TK_E_ABORTED) when a launch
+        on `workspace` stopped at a timed-out grid barrier."""
+        aborted, stage = self.workspace_status(workspace, stream)
+        if aborted:
+            raise TkError(TK_E_ABORTED, f"tk: a launch stopped at a grid barrier that timed out (stage {stage}); "
+                                        "its outputs are incomplete")
 
     def workspace_status(self, workspace, stream=None):
-        ws = describe(workspace)
-        ws.dtype = TK_I8
+        ws = describe(workspace, raw_bytes=True)
         a, s = ctypes.c_int32(0), ctypes.c_int32(0)
         _check(lib().tk_workspace_status(ctypes.byref(ws), _stream_handle(stream), ctypes.byref(a), ctypes.byref(s)))
         return bool(a.value), s.value
 
     def read_timestamps(self, workspace, stream=None):
         n = 4 * self.query()["n_stages"]
-        ws = describe(workspace)
-        ws.dtype = TK_I8
+        ws = describe(workspace, raw_bytes=True)
         arr = (ctypes.c_uint64 * max(1, n))()
         _check(lib().tk_read_timestamps(self._h, ctypes.byref(ws), _stream_handle(stream), arr, n))
         return list(arr)[:n]
