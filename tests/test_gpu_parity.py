@@ -497,6 +497,193 @@ def test_graph_replay_matches_eager_steps():
     assert not aborted
 
 
+def _staged_program(kind: str, dt: str, n: int) -> Program:
+    """Programs whose in-place update cannot be written where it is computed,
+    so the scheduler stages it and commits it after the last read of the
+    target (the codegen page's final commit stage):
+      tile_reads: the update's gradient tile reads the target itself;
+      after_store: an op of the same tile reads the target after the update;
+      pointwise: a later pointwise op reads the target."""
+    p = Program()
+    a = p.input("a", dt, (n, n))
+    W = p.input("W", dt, (n, n))
+    if kind == "tile_reads":
+        g = p.op("mm", [a, W], dt, (n, n))
+        p.output(p.op("sub", [W, g], dt, alpha=0.5), inplace_of=W)
+        p.output(g)
+    elif kind == "after_store":
+        b = p.input("b", dt, (n, n))
+        g = p.op("mm", [a, b], dt, (n, n))
+        wn = p.op("sub", [W, g], dt, alpha=0.5)
+        p.output(p.op("mul", [W, g], dt))
+        p.output(wn, inplace_of=W)
+    else:
+        wn = p.op("sub", [W, a], dt, alpha=0.5)
+        p.output(wn, inplace_of=W)
+        p.output(p.op("mul", [W, 2.0], dt))
+    return p
+
+
+@pytest.mark.parametrize("kind", ["tile_reads", "after_store", "pointwise"])
+@pytest.mark.parametrize("dt,n", [("bf16", 192), ("bf16", 520), ("f32", 130)])
+def test_staged_commit(oracle_mod, kind, dt, n):
+    """Staged (transactional) in-place commits on the GPU: the plan stages the
+    update; every op, checked per node against the oracle from the original
+    inputs, saw the target's old value; the fused run leaves the same bits in
+    the caller's target tensor as the probe run."""
+    say("staged commit", kind, dt, n)
+    from persistent_whole_step_amd import tk
+    base = _staged_program(kind, dt, n)
+    probe = base.probe()
+    for prog in (base, probe):
+        assert tk.compile(prog.text(), device=-1).query()["staged_commits"] >= 1
+    rng = np.random.default_rng(n)
+    ins = [synth.random_tensor(rng, s.shape, s.dtype, 0.25) for s in base.inputs]
+    outs, _ = parity.gpu_run(probe, [a.copy() for a in ins])
+    vals = parity.probe_values(base, probe, outs)
+    assert parity.check_per_node(oracle_mod, base, ins, vals) == len(base.ops)
+    fused, p = parity.gpu_run(base, [a.copy() for a in ins])
+    assert p.query()["staged_commits"] >= 1
+    for a, b, s in zip(fused, outs, base.outputs):
+        parity.assert_bitexact(a, b, s.dtype, s.buf)
+
+
+def test_graph_replayed_probe_steps_per_node(oracle_mod):
+    """A captured 20-step replay checked against the oracle: the probe program
+    (every op's value returned) of the c2s step is captured once per resident
+    batch (4 graphs, state fed back through the in-place updates) and the
+    graphs are replayed in rotation for 20 steps; after each step every op is
+    checked per node against the oracle on that step's batch and on the
+    parameters the previous replay left."""
+    import torch
+    from persistent_whole_step_amd import tk
+    cfg = SMALL["c2s"]
+    say("graph-replayed probe, 20 steps, c2s")
+    base = programs.build(cfg)
+    probe = base.probe()
+    p = tk.compile(probe.text(), device=0, launch_mode=1)
+    start = programs.inputs_for(cfg, 4)
+    batches = [programs.inputs_for(cfg, 20 + j)[:2] for j in range(4)]
+    params = [parity.to_torch(a, s.dtype) for a, s in zip(start[2:], probe.inputs[2:])]
+    xs = [[parity.to_torch(b[0], probe.inputs[0].dtype), parity.to_torch(b[1], probe.inputs[1].dtype)]
+          for b in batches]
+    bufs = p.allocate(*(xs[0] + params))
+    graphs = [tk.StepGraph(p, [(x + params, bufs)]) for x in xs]
+    state = [a.copy() for a in start[2:]]
+    for step in range(20):
+        j = step % 4
+        graphs[j].replay()
+        torch.cuda.synchronize()
+        outs = [parity.to_numpy(o, sp.dtype) for o, sp in zip(bufs.outputs, probe.outputs)]
+        vals = parity.probe_values(base, probe, outs)
+        ins = [batches[j][0], batches[j][1]] + state
+        assert parity.check_per_node(oracle_mod, base, ins, vals) == len(base.ops), step
+        state = [parity.to_numpy(t, sp.dtype) for t, sp in zip(params, probe.inputs[2:])]
+    p.check_workspace(bufs.workspace)
+
+
+def test_compiled_step_capture_restores_state_and_replays():
+    """CompiledTrainingStep.capture: warmup and capture leave the supplied
+    state as it was; each replay advances it exactly as the eager compiled
+    step does from the same state, for 20 steps (the eager step's program is
+    checked per node against the oracle in test_compile_training_step)."""
+    import torch
+    from persistent_whole_step_amd import frontend
+    from .test_frontend import mlp_step
+    say("capture API, 20 replays")
+    gen = torch.Generator().manual_seed(9)
+    shapes = {"W1": (96, 160), "b1": (160,), "W2": (160, 48), "b2": (48,)}
+    params = {k: (torch.randn(*s, generator=gen) / 6).to(torch.bfloat16) for k, s in shapes.items()}
+    x = torch.randn(40, 96, generator=gen).to(torch.bfloat16).cuda()
+    t = torch.randn(40, 48, generator=gen).to(torch.bfloat16).cuda()
+    step = frontend.compile_training(mlp_step, (params, x.cpu(), t.cpu()))
+    pg = {k: v.cuda() for k, v in params.items()}
+    pe = {k: v.cuda() for k, v in params.items()}
+    cap = step.capture(pg, x, t, warmup=3)
+    for k in pg:
+        assert torch.equal(pg[k].view(torch.int16), pe[k].view(torch.int16)), k
+    for i in range(20):
+        loss_g, new_g = cap.replay()
+        loss_e, new_e = step(pe, x, t)
+        torch.cuda.synchronize()
+        assert torch.equal(loss_g.view(torch.int16), loss_e.view(torch.int16)), i
+        for k in pg:
+            assert new_g[k].data_ptr() == pg[k].data_ptr()
+            assert torch.equal(pg[k].view(torch.int16), pe[k].view(torch.int16)), (i, k)
+
+
+@pytest.mark.parametrize("name", ["c2s", "c5s", "c2sa", "c3s"])
+def test_race_modes_bit_identical(name):
+    """The schedule's race-exposing run modes give the default run's bits:
+    every workgroup sleeping a seeded pseudo-random time before each work
+    item (stagger), the workspace filled with a NaN byte pattern before the
+    launch (poison: no value is read before it is written), and one op per
+    stage (barrier_every_op)."""
+    import torch
+    from persistent_whole_step_amd import tk
+    cfg = SMALL[name]
+    say("race modes", name)
+    base = programs.build(cfg)
+    ins = programs.inputs_for(cfg, 5)
+    ref, _ = parity.gpu_run(base, [a.copy() for a in ins], launch_mode=1)
+
+    def run(poison=False, stagger=0, **opts):
+        p = tk.compile(base.text(), device=0, launch_mode=1, **opts)
+        tins = [parity.to_torch(a.copy(), sp.dtype) for a, sp in zip(ins, base.inputs)]
+        bufs = p.allocate(*tins)
+        if poison:
+            hdr = 147456  # the header keeps its barrier state; the arena gets NaN bytes
+            bufs.workspace[hdr:].fill_(0xFF)
+            for o, sp in zip(bufs.outputs, base.outputs):
+                if not any(o.data_ptr() == t.data_ptr() for t in tins):
+                    o.view(torch.uint8).fill_(0xFF)
+        p.set_debug(stagger_seed=stagger)
+        p.run_into(*tins, buffers=bufs)
+        p.check_workspace(bufs.workspace)
+        return [parity.to_numpy(o, sp.dtype) for o, sp in zip(bufs.outputs, base.outputs)]
+
+    for mode in (dict(stagger=0x5eed), dict(stagger=77), dict(poison=True), dict(barrier_every_op=1),
+                 dict(poison=True, stagger=3, barrier_every_op=1)):
+        got = run(**mode)
+        for g, r, sp in zip(got, ref, base.outputs):
+            parity.assert_bitexact(g, r, sp.dtype, f"{sp.buf} under {mode}")
+
+
+def test_barrier_timeout_reports_aborted():
+    """A grid barrier that times out (forced from the host with a one-tick
+    wait limit; every workgroup still leaves the kernel) marks the workspace
+    aborted: the status reads it back, the next run_into fails with
+    TK_E_ABORTED before launching, and after tk_workspace_init the program
+    runs again and gives a clean run's bits."""
+    from persistent_whole_step_amd import tk
+    cfg = SMALL["c2s"]
+    say("barrier timeout -> TK_E_ABORTED")
+    base = programs.build(cfg)
+    ins = programs.inputs_for(cfg, 6)
+    ref, _ = parity.gpu_run(base, [a.copy() for a in ins], launch_mode=1)
+    p = tk.compile(base.text(), device=0, launch_mode=1)
+    tins = [parity.to_torch(a.copy(), sp.dtype) for a, sp in zip(ins, base.inputs)]
+    bufs = p.allocate(*tins)
+    p.set_debug(deadline_ticks=1)
+    p.run_into(*tins, buffers=bufs)
+    aborted, stage = p.workspace_status(bufs.workspace)
+    assert aborted and 0 <= stage < p.query()["n_stages"]
+    with pytest.raises(tk.TkError) as e:
+        p.run_into(*tins, buffers=bufs)
+    assert e.value.status_name == "TK_E_ABORTED"
+    with pytest.raises(tk.TkError):
+        p.check_workspace(bufs.workspace)
+    p.set_debug(deadline_ticks=0)
+    p.init_workspace(bufs.workspace)
+    tins = [parity.to_torch(a.copy(), sp.dtype) for a, sp in zip(ins, base.inputs)]
+    bufs = tk.ExecutionBuffers(tuple(tins[p._inplace_map()[s]] if s in p._inplace_map() else o
+                                     for s, o in enumerate(bufs.outputs)), bufs.workspace)
+    p.run_into(*tins, buffers=bufs)
+    p.check_workspace(bufs.workspace)
+    for g, r, sp in zip(bufs.outputs, ref, base.outputs):
+        parity.assert_bitexact(parity.to_numpy(g, sp.dtype), r, sp.dtype, sp.buf)
+
+
 def test_c1_end_to_end_close_to_oracle(oracle_mod):
     cfg = SMALL["c1"]
     say("c1 end to end")
@@ -521,22 +708,24 @@ FULL = {
 }
 
 
+@pytest.mark.parametrize("seed", [0, 1, 2])
 @pytest.mark.parametrize("name", list(FULL))
-def test_full_size_sampled_per_node(oracle_mod, name):
+def test_full_size_sampled_per_node(oracle_mod, name, seed):
     """The workloads at their full sizes, in the launch configuration the
-    bench times (ordinary launch of the co-resident grid): every op checked
-    per node with teacher forcing (pointwise ops and reductions whole,
-    contractions at 48 sampled outputs each computed by the oracle), then the
-    bench's fused schedule equal to the probe schedule bit for bit on the
-    step's outputs."""
+    bench times (ordinary launch of the co-resident grid), on three input
+    seeds: every op checked per node with teacher forcing (pointwise ops and
+    reductions whole, each contraction on a block of outputs with at least
+    one in every 64x64 output tile, plus the edges, each computed by the
+    oracle), then the bench's fused schedule equal to the probe schedule bit
+    for bit on the step's outputs."""
     cfg = FULL[name]
-    say("full size, sampled per node", name)
+    say("full size, sampled per node", name, "seed", seed)
     base = programs.build(cfg)
     probe = base.probe()
-    ins = programs.inputs_for(cfg, 0)
+    ins = programs.inputs_for(cfg, seed)
     outs, _ = parity.gpu_run(probe, [a.copy() for a in ins], launch_mode=1)
     vals = parity.probe_values(base, probe, outs)
-    n = parity.check_per_node_sampled(oracle_mod, base, ins, vals, samples=48, seed=len(name))
+    n = parity.check_per_node_sampled(oracle_mod, base, ins, vals, seed=len(name) + 10 * seed)
     assert n == len(base.ops)
     fused, _ = parity.gpu_run(base, [a.copy() for a in ins], launch_mode=1)
     for a, b, s in zip(fused, outs, base.outputs):
@@ -634,6 +823,9 @@ def test_compile_training_step(oracle_mod, dtype):
     vals = parity.probe_values(prog, probe, outs)
     assert parity.check_per_node(oracle_mod, prog, ins, vals) == len(prog.ops)
     ref, _ = parity.gpu_run(prog, [a.copy() for a in ins])
+    # the fused, in-place schedule equals the oracle-checked probe run bit for bit
+    for i, sp in enumerate(prog.outputs):
+        parity.assert_bitexact(ref[i], outs[i], sp.dtype, f"fused vs probe {sp.buf}")
     pg = {k: v.cuda() for k, v in params.items()}
     loss, new = step(pg, x.cuda(), t.cuda())
     torch.cuda.synchronize()
@@ -668,6 +860,9 @@ def test_compile_training_broadcast_step(oracle_mod, dtype):
     vals = parity.probe_values(prog, probe, outs)
     assert parity.check_per_node(oracle_mod, prog, ins, vals) == len(prog.ops)
     ref, _ = parity.gpu_run(prog, [a.copy() for a in ins])
+    # the fused, in-place schedule equals the oracle-checked probe run bit for bit
+    for i, sp in enumerate(prog.outputs):
+        parity.assert_bitexact(ref[i], outs[i], sp.dtype, f"fused vs probe {sp.buf}")
     wg = w.cuda()
     loss, w_new = step(wg, x.cuda(), t.cuda())
     torch.cuda.synchronize()
@@ -696,6 +891,9 @@ def test_compile_training_adamw_step(oracle_mod):
     vals = parity.probe_values(prog, probe, outs)
     assert parity.check_per_node(oracle_mod, prog, ins, vals) == len(prog.ops)
     ref, _ = parity.gpu_run(prog, [a.copy() for a in ins])
+    # the fused, in-place schedule equals the oracle-checked probe run bit for bit
+    for i, sp in enumerate(prog.outputs):
+        parity.assert_bitexact(ref[i], outs[i], sp.dtype, f"fused vs probe {sp.buf}")
     state = tuple(v.cuda() for v in ex[0])
     loss, new = step(state, ex[1].cuda(), ex[2].cuda())
     torch.cuda.synchronize()
