@@ -27,6 +27,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "plan.h"
 
 using namespace tkplan;
@@ -37,14 +39,16 @@ using namespace tkplan;
 
 namespace {
 
-// Workgroup LDS arena (104 KB).  A contraction's operand ring uses up to
-// 96 KB during its main loop; afterwards the fp32 C tile (at most 128 x 132
-// floats) takes the bottom and the machine exchange the top 32 KB.  Every
-// other task uses the bottom 72 KB for staging or scratch.
-constexpr int kArenaBytes = 106496;
-constexpr int kSmemBytes = 73728;        // staging / scratch region below the exchange
-constexpr int kXvOff = kSmemBytes;       // machine exchange: values
-constexpr int kXeOff = kSmemBytes + 16384;
+// Workgroup LDS arena (128 KB).  A contraction's operand ring uses all of it
+// during its main loop; afterwards the fp32 C tile (at most 128 x 132 floats)
+// takes the bottom, and the expression machine's third slot and its exchange
+// the top 48 KB.  Every other task uses the bottom 80 KB for staging or
+// scratch.
+constexpr int kArenaBytes = 131072;
+constexpr int kSmemBytes = 81920;        // staging / scratch region below the slots
+constexpr int kSlot2Off = kSmemBytes;    // machine slot 2
+constexpr int kXvOff = kSmemBytes + 16384;  // machine exchange: values (slot 0)
+constexpr int kXeOff = kSmemBytes + 32768;  // machine exchange: chunk starts (slot 1)
 constexpr int kVmElems = 16;                       // elements per thread per machine batch
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -64,14 +68,15 @@ DEV LDS uint32_t& xe(uint32_t tid, int q) { return ((LDS uint32_t*)(g_smem + kXe
 // (element j of thread t at j * kBlock + t, so each thread touches only its
 // own words): slot 0 reuses the value exchange and slot 1 the index exchange
 // (both are read at the start of a batch and rewritten only at its end),
-// slot 2 has a region of its own.  Holding them in registers made every join
-// of the interpreter loop copy them.
-__shared__ __attribute__((aligned(16))) float g_slot2[kVmElems * kBlock];
+// slot 2 has a region of its own below them.  Holding them in registers made
+// every join of the interpreter loop copy them.
 static_assert(kMaxSlots == 3, "three LDS slots");
 DEV LDS float* slot_base(uint32_t k) {
-  return k == 0 ? (LDS float*)(g_smem + kXvOff) : k == 1 ? (LDS float*)(g_smem + kXeOff) : (LDS float*)g_slot2;
+  return (LDS float*)(g_smem + (k == 0 ? kXvOff : k == 1 ? kXeOff : kSlot2Off));
 }
+static_assert(kSlot2Off + kVmElems * kBlock * 4 == kXvOff, "arena layout");
 static_assert(kXeOff + kVmElems * kBlock * 4 == kArenaBytes, "arena layout");
+static_assert(128 * 132 * 4 <= kSmemBytes, "the largest C tile fits below the slots");
 
 // ------------------------------------------------------------ conversions --
 
@@ -349,8 +354,17 @@ DEV int32_t view_index(const VView& v, const uint32_t (&c)[kMaxDims]) {
   return idx;
 }
 
+// The stride of the innermost iteration dim.  Written as a chain of
+// selects on scalars: the compiler must not turn it into an indexed load from
+// a stack copy of the strides (private memory).
 DEV int32_t inner_stride(const VView& v, uint32_t nd) {
-  return nd <= 1 ? v.stride[0] : nd == 2 ? v.stride[1] : nd == 3 ? v.stride[2] : v.stride[3];
+  int32_t s = v.stride[0];
+  s = nd >= 2 ? v.stride[1] : s;
+  asm volatile("" : "+s"(s));
+  s = nd >= 3 ? v.stride[2] : s;
+  asm volatile("" : "+s"(s));
+  s = nd >= 4 ? v.stride[3] : s;
+  return s;
 }
 
 // ------------------------------------------------------ expression machine --
@@ -824,12 +838,37 @@ DEV void mfma_slice(uint32_t tid, const LDS uint16_t* sa, const LDS uint16_t* sb
       for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<BF16>(af[ks][i], bfr[ks][j], acc[i][j]);
 }
 
-// Fast-path main loop (see gemm_mfma): a ring of S stages, S - 1 slices in flight.
+// The fragments of k step `ks` (16 deep) of a staged slice, for this wave's
+// (BM/2) x (BN/2) block.
+template <int BM, int BN, bool AKM, bool BKM>
+DEV void read_frags(uint32_t tid, const LDS uint16_t* sa, const LDS uint16_t* sb, int ks, u32x4 (&fa)[BM / 64],
+                    u32x4 (&fb)[BN / 64]) {
+  const int wave = tid / 64;
+  const int wm = wave / 2, wn = wave % 2;
+#pragma unroll
+  for (int i = 0; i < BM / 64; ++i) fa[i] = frag<BM, AKM>(tid, sa, wm * (BM / 2) + i * 32, ks * 16);
+#pragma unroll
+  for (int j = 0; j < BN / 64; ++j) fb[j] = frag<BN, BKM>(tid, sb, wn * (BN / 2) + j * 32, ks * 16);
+}
+
+// Fast-path main loop (see gemm_mfma): a ring of S stages, S - 1 slices in
+// flight, software-pipelined by 16-deep k steps: the fragments of step s + 1
+// are read from LDS while the MFMAs of step s run (the two are interleaved
+// in the instruction stream, so the LDS reads hide behind the matrix cores
+// instead of preceding them).  At the last step of slice k the wave waits
+// for slice k + 1, the workgroup meets (every wave has its fragments of slice
+// k in registers and every wave's copy of slice k + 1 has landed), slice
+// k + S is issued into slice k's stage, and the first fragments of slice
+// k + 1 are read under the last MFMAs of slice k.
 template <int BM, int BN, bool BF16, bool AKM, bool BKM, int S>
 DEV void direct_loop(uint32_t tid, const DirectOp<BM>& da, const DirectOp<BN>& db, uint32_t nk,
                      f32x16 (&acc)[BM / 64][BN / 64]) {
+  constexpr int FM = BM / 64, FN = BN / 64, KS = kBK / 16;
   constexpr int SA = BM * kBK * 2, SB = BN * kBK * 2;
   constexpr int LPS = BM / 32 + BN / 32;  // direct loads per wave per slice
+  constexpr int NMF = FM * FN;            // MFMAs per k step
+  constexpr int NDS = FM * (AKM ? 1 : 2) + FN * (BKM ? 1 : 2);  // LDS reads per k step
+  constexpr int DPM = (NDS + NMF - 1) / NMF;                    // LDS reads between two MFMAs
   const uint32_t last = nk - 1;
   // slices 0 .. S-2 in flight (past the last slice, loads repeat it into a
   // stage that is not read again)
@@ -839,38 +878,162 @@ DEV void direct_loop(uint32_t tid, const DirectOp<BM>& da, const DirectOp<BN>& d
     da.issue(sl, s * (SA + SB));
     db.issue(sl, s * (SA + SB) + SA);
   }
+  wait_vmcnt<(S - 2) * LPS>();  // this wave's copy of slice 0 has landed
+  __syncthreads();              // ... and every wave's
+  {
+    const uint32_t sl = (uint32_t)(S - 1) < last ? (uint32_t)(S - 1) : last;
+    da.issue(sl, (S - 1) * (SA + SB));
+    db.issue(sl, (S - 1) * (SA + SB) + SA);
+  }
+  u32x4 fa[2][FM], fb[2][FN];
+  read_frags<BM, BN, AKM, BKM>(tid, (const LDS uint16_t*)g_smem, (const LDS uint16_t*)(g_smem + SA), 0, fa[0], fb[0]);
   for (uint32_t k = 0; k < nk; ++k) {
-    // this wave's loads of slice k have landed once at most the S-2 younger
-    // slices are in flight; the barrier then covers every wave's loads and
-    // every wave's last read of stage (k-1) % S, which the next issue refills
-    wait_vmcnt<(S - 2) * LPS>();
-    __syncthreads();
-    const uint32_t nx = k + S - 1 < last ? k + S - 1 : last;
-    const uint32_t ns = (k + S - 1) % S;
-    da.issue(nx, ns * (SA + SB));
-    db.issue(nx, ns * (SA + SB) + SA);
     const uint32_t cs = (k % S) * (SA + SB);
-    mfma_slice<BM, BN, BF16, AKM, BKM>(tid, (const LDS uint16_t*)(g_smem + cs), (const LDS uint16_t*)(g_smem + cs + SA),
-                                       acc);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      const int cur = ks & 1;
+      if (ks + 1 < KS) {
+        read_frags<BM, BN, AKM, BKM>(tid, (const LDS uint16_t*)(g_smem + cs), (const LDS uint16_t*)(g_smem + cs + SA),
+                                     ks + 1, fa[cur ^ 1], fb[cur ^ 1]);
+      } else {
+        // slice k + 1: this wave's copy has landed once at most the S-2
+        // younger slices are in flight; the barrier (which first waits for
+        // this wave's fragment reads) covers every wave's copy and every
+        // wave's last read of slice k, whose stage the next issue refills.
+        // After the last slice this runs too, without branching (the loads
+        // repeat the last slice into a stage that is not read again, and the
+        // fragments read are not used), so the step stays one basic block in
+        // which the reads interleave with the MFMAs.
+        wait_vmcnt<(S - 2) * LPS>();
+        __syncthreads();
+        const uint32_t nx = k + S < last ? k + S : last;
+        da.issue(nx, cs);
+        db.issue(nx, cs + SA);
+        const uint32_t ns = ((k + 1) % S) * (SA + SB);
+        read_frags<BM, BN, AKM, BKM>(tid, (const LDS uint16_t*)(g_smem + ns), (const LDS uint16_t*)(g_smem + ns + SA),
+                                     0, fa[cur ^ 1], fb[cur ^ 1]);
+      }
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<BF16>(fa[cur][i], fb[cur][j], acc[i][j]);
+      // interleave: MFMA, DPM fragment reads, MFMA, ...
+#pragma unroll
+      for (int m = 0; m < NMF; ++m) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, DPM, 0);
+      }
+    }
   }
   wait_vmcnt<0>();  // no load may still be writing the arena
   __syncthreads();  // every wave is done with the ring (the C tile reuses it)
 }
 
+// Fast-path main loop of a 64x64 tile.  Each wave owns a 32x32 block, one
+// MFMA per 16-deep k step, so a single accumulator would chain every MFMA
+// on the previous one's result; instead k step s of every slice accumulates
+// into partial sum s % 4 (four independent chains), and the partials are
+// added in a fixed order at the end.  The fragments are double-buffered by
+// slice: all of slice k + 1's fragments are read from LDS while slice k's
+// four MFMAs run.
+template <bool BF16, bool AKM, bool BKM, int S>
+DEV void direct_loop64(uint32_t tid, const DirectOp<64>& da, const DirectOp<64>& db, uint32_t nk,
+                       f32x16 (&acc)[1][1]) {
+  constexpr int KS = kBK / 16;
+  constexpr int SA = 64 * kBK * 2, SB = 64 * kBK * 2;
+  constexpr int LPS = 4;                                  // direct loads per wave per slice
+  constexpr int NDS = KS * ((AKM ? 1 : 2) + (BKM ? 1 : 2));  // LDS reads per slice
+  constexpr int DPM = NDS / KS;                            // LDS reads between two MFMAs
+  const int wave = tid / 64;
+  const int wm = wave / 2, wn = wave % 2;
+  const uint32_t last = nk - 1;
+  f32x16 part[KS];
+#pragma unroll
+  for (int q = 0; q < KS; ++q)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) part[q][r] = 0.0f;
+#pragma unroll
+  for (int s = 0; s < S - 1; ++s) {
+    const uint32_t sl = (uint32_t)s < last ? (uint32_t)s : last;
+    da.issue(sl, s * (SA + SB));
+    db.issue(sl, s * (SA + SB) + SA);
+  }
+  wait_vmcnt<(S - 2) * LPS>();
+  __syncthreads();
+  {
+    const uint32_t sl = (uint32_t)(S - 1) < last ? (uint32_t)(S - 1) : last;
+    da.issue(sl, (S - 1) * (SA + SB));
+    db.issue(sl, (S - 1) * (SA + SB) + SA);
+  }
+  u32x4 fa[2][KS], fb[2][KS];
+  auto read_slice = [&](uint32_t stage, u32x4 (&a)[KS], u32x4 (&b)[KS]) {
+    const LDS uint16_t* sa = (const LDS uint16_t*)(g_smem + stage * (SA + SB));
+    const LDS uint16_t* sb = (const LDS uint16_t*)(g_smem + stage * (SA + SB) + SA);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      a[ks] = frag<64, AKM>(tid, sa, wm * 32, ks * 16);
+      b[ks] = frag<64, BKM>(tid, sb, wn * 32, ks * 16);
+    }
+  };
+  read_slice(0, fa[0], fb[0]);
+  // slice k: with slice k + 1 landed and every wave's fragments of slice k in
+  // registers, refill slice k's stage with slice k + S, read slice k + 1's
+  // fragments, and run slice k's MFMAs under those reads
+  // (after the last slice this runs too, without branching: the loads repeat
+  // the last slice into a stage that is not read again and the fragments
+  // read are not used, so the body stays one basic block in which the reads
+  // interleave with the MFMAs)
+  auto body = [&](uint32_t k, auto cur) {
+    constexpr int C = decltype(cur)::value;
+    {
+      wait_vmcnt<(S - 2) * LPS>();
+      __syncthreads();
+      const uint32_t nx = k + S < last ? k + S : last;
+      const uint32_t cs = (k % S) * (SA + SB);
+      da.issue(nx, cs);
+      db.issue(nx, cs + SA);
+      read_slice((k + 1) % S, fa[C ^ 1], fb[C ^ 1]);
+    }
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) part[ks] = mfma32<BF16>(fa[C][ks], fb[C][ks], part[ks]);
+#pragma unroll
+    for (int m = 0; m < KS; ++m) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, DPM, 0);
+    }
+  };
+  uint32_t k = 0;
+  for (; k + 1 < nk; k += 2) {
+    body(k, std::integral_constant<int, 0>());
+    body(k + 1, std::integral_constant<int, 1>());
+  }
+  if (k < nk) body(k, std::integral_constant<int, 0>());
+  wait_vmcnt<0>();  // no load may still be writing the arena
+  __syncthreads();  // every wave is done with the ring (the C tile reuses it)
+#pragma unroll
+  for (int r = 0; r < 16; ++r) acc[0][0][r] = ((part[0][r] + part[1][r]) + part[2][r]) + part[3][r];
+}
+
 // BF16: operand dtype (bf16, else f16), a template parameter so the MFMA
 // accumulators never change registers between the two instruction forms.
-template <int BM, int BN, bool BF16>
-DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st) {
+template <int BM, int BN, bool BF16, class AfterLoop>
+DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st,
+                   AfterLoop after_loop) {
   constexpr int FM = BM / 64, FN = BN / 64;  // 32x32 blocks per wave along m / n
-  constexpr int S = BM == 128 ? 3 : 4;       // ring stages (S * (BM + BN) * 128 bytes <= 96 KB)
+  constexpr int S = BM == 128 ? 3 : 4;       // ring stages (S * (BM + BN) * 128 bytes <= the arena)
   constexpr int SA = BM * kBK * 2, SB = BN * kBK * 2;
-  static_assert(S * (SA + SB) <= 98304, "operand ring exceeds the arena");
+  static_assert(S * (SA + SB) <= kArenaBytes, "operand ring exceeds the arena");
   const uint32_t tiles = t.tiles_m * t.tiles_n;
   const uint32_t split_index = item / tiles;
   const uint32_t tile = xcd_tile(item % tiles, tiles);
   uint32_t tm, tn;
   tile_coords(t, tile, tm, tn);
   const uint32_t m0 = tm * BM, n0 = tn * BN;
+  st.m0 = m0;
+  st.n0 = n0;
+  st.bm = BM;
+  st.bn = BN;
+  st.split_index = split_index;
   const uint32_t kbeg = split_index * t.kchunk;
   const uint32_t kend = (kbeg + t.kchunk < t.k) ? kbeg + t.kchunk : t.k;
   const VView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
@@ -899,7 +1062,19 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
     DirectOp<BN> db;
     da.init(tid, a_kc, pa, A.offset, A.stride[0], A.stride[1], m0, kbeg);
     db.init(tid, b_kc, pb, B.offset, B.stride[1], B.stride[0], n0, kbeg);
-    if (a_kc) {
+    if constexpr (BM == 64 && BN == 64) {
+      if (a_kc) {
+        if (b_kc)
+          direct_loop64<BF16, true, true, S>(tid, da, db, nk, acc);
+        else
+          direct_loop64<BF16, true, false, S>(tid, da, db, nk, acc);
+      } else {
+        if (b_kc)
+          direct_loop64<BF16, false, true, S>(tid, da, db, nk, acc);
+        else
+          direct_loop64<BF16, false, false, S>(tid, da, db, nk, acc);
+      }
+    } else if (a_kc) {
       if (b_kc)
         direct_loop<BM, BN, BF16, true, true, S>(tid, da, db, nk, acc);
       else
@@ -922,6 +1097,8 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
       __syncthreads();
     }
   }
+  // the operand ring is drained: the arena above the C tile is free
+  after_loop();
   // accumulators -> LDS tile [BM][BN + 4]
   LDS float* C = (LDS float*)g_smem;
   const int pitch = BN + 4;
@@ -935,11 +1112,6 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
         const int col = wn * (BN / 2) + j * 32 + (lane % 32);
         C[row * pitch + col] = acc[i][j][r];
       }
-  st.m0 = m0;
-  st.n0 = n0;
-  st.bm = BM;
-  st.bn = BN;
-  st.split_index = split_index;
 }
 
 // ------------------------------------------------------ int8-weight GEMV --
@@ -1654,83 +1826,109 @@ DEV void consume(uint32_t tid, const DTask& t, const Batch& b, uint32_t live, It
 
 // ------------------------------------------------------ register epilogue --
 // A contraction tile whose epilogue the scheduler marked F_FASTEPI runs it
-// here instead of through machine batches.  The program (at most kFastIns
-// instructions; loads and stores of 2-D views over (row, col) with column
-// stride 1, or 0 for loads, and 8-element chunk alignment) is decoded once per
-// item.  Each thread takes G 8-wide column chunks of the LDS tile at a time
-// (consecutive threads, consecutive chunks), issues the loads of every loaded
-// view for them before the first instruction runs (the scheduler proved that
-// no load reads bytes an earlier store of the program writes), and carries
-// the values in registers through to the stores.  The arithmetic, its order
-// and every rounding are vm_run's, so results are identical bit for bit.
+// here instead of through machine batches: a straight-line program of at most
+// kFastIns instructions over 8-wide column chunks of the fp32 tile in LDS
+// (loads and stores of 2-D views over (row, col) with column stride 1, or 0
+// for loads).  Every thread owns G chunks (chunk g * kBlock + tid of the
+// tile: the whole tile in one pass) and carries their values in registers
+// through the program to the stores.
+//   * As soon as the main loop has drained its operand ring, every loaded
+//     view with column stride 1 is copied global -> LDS, each lane its own
+//     chunks, into the arena above the C tile (fast_prefetch): the loads are
+//     in flight while the accumulators are written out, and the program
+//     reads its operands from LDS.
+//   * The program is interpreted one instruction at a time from the LDS
+//     plan, so only the current instruction's fields occupy scalar registers
+//     (a decoded copy of the whole program does not fit them and spills).
+// The arithmetic, its order and every rounding are vm_run's, so results are
+// identical bit for bit.  Hoisting every load before the first store is
+// safe for the programs the scheduler marks: no load reads bytes an earlier
+// store of the program may write.
 
-struct FastProg {
-  uint32_t n;                      // instructions
-  uint32_t w0[kFastIns];           // op | src << 8 | rnd << 16 | rev << 24
-  float a[kFastIns], s[kFastIns];  // alpha / threshold, scalar operand
-  uint32_t slot[kFastIns];         // loaded-view slot of a view operand
-  GLOBAL uint8_t* sp[kFastIns];    // store views: base, offset, row stride, dtype
-  int32_t soff[kFastIns], ss0[kFastIns];
-  uint32_t sdt[kFastIns];
-  uint32_t nl;                     // loaded views, in program order
-  const GLOBAL uint8_t* lp[kFastLoads];
-  int32_t loff[kFastLoads], ls0[kFastLoads];
-  uint32_t ldt[kFastLoads], ls1[kFastLoads];
+// A view operand of the epilogue, read from the LDS plan (wave-uniform).
+struct FView {
+  GLOBAL uint8_t* p;
+  int32_t off, s0, s1;
+  uint32_t dt;
 };
 
-// Decode the program; false (uniform) when a unit-stride view's base is not
-// 16-byte aligned, in which case the batches take over.
-DEV bool fast_decode(const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off, FastProg& fp) {
-  fp.n = t.expr_len;
-  fp.nl = 0;
-  bool ok = true;
+DEV FView fast_view(const Ctx& ka, uint32_t views_off, uint32_t vi) {
+  const LDS uint8_t* v = (const LDS uint8_t*)g_plan + views_off + vi * sizeof(DView);
+  const u32x4 lo = *(const LDS u32x4*)v;               // offset, stride[0] (low words)
+  const uint32_t s1 = *(const LDS uint32_t*)(v + 16);  // stride[1] (low word)
+  const uint32_t bd = *(const LDS uint32_t*)(v + 40);  // base | dtype << 16
+  FView f;
+  f.off = (int32_t)uniform(lo[0]);
+  f.s0 = (int32_t)uniform(lo[2]);
+  f.s1 = (int32_t)uniform(s1);
+  const uint32_t w = uniform(bd);
+  f.p = base_ptr(ka, (w & 0xffff) < (uint32_t)kMaxBases ? (w & 0xffff) : 0u);
+  f.dt = (w >> 16) & 0xff;
+  return f;
+}
+
+// Output coordinates of this thread's G chunks.
+template <int G>
+struct FastChunks {
+  int32_t row[G], col[G];  // output coordinates
+  int r[G], cc[G];         // tile-local row and first column
+  bool ok[G];              // inside the output
+};
+
+template <int G>
+DEV void fast_chunks(uint32_t tid, const DTask& t, const ItemState& st, FastChunks<G>& c) {
+  const int lcpr = __builtin_ctz((uint32_t)(st.bn / 8));  // log2 chunks per row
 #pragma unroll
-  for (int l = 0; l < kFastLoads; ++l) {
-    fp.lp[l] = base_ptr(ka, 0);
-    fp.loff[l] = fp.ls0[l] = 0;
-    fp.ldt[l] = DT_F32;
-    fp.ls1[l] = 0;
+  for (int g = 0; g < G; ++g) {
+    const int qq = g * kBlock + (int)tid;  // < bm * bn / 8 == G * kBlock
+    c.r[g] = qq >> lcpr;
+    c.cc[g] = (qq & ((1 << lcpr) - 1)) * 8;
+    c.row[g] = (int32_t)st.m0 + c.r[g];
+    c.col[g] = (int32_t)st.n0 + c.cc[g];
+    c.ok[g] = (uint32_t)c.row[g] < t.m && (uint32_t)c.col[g] < t.n;
   }
-#pragma unroll
-  for (int pc = 0; pc < kFastIns; ++pc) {
-    fp.w0[pc] = 0;
-    fp.a[pc] = fp.s[pc] = 0.0f;
-    fp.slot[pc] = 0;
-    fp.sp[pc] = base_ptr(ka, 0);
-    fp.soff[pc] = fp.ss0[pc] = 0;
-    fp.sdt[pc] = DT_F32;
-    if ((uint32_t)pc >= fp.n) continue;
-    const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + ins_off + (t.expr_first + pc) * sizeof(DIns));
-    const uint32_t w0 = uniform(iw[0]), w1 = uniform(iw[1]);
-    fp.w0[pc] = w0;
-    fp.a[pc] = __uint_as_float(uniform(iw[2]));
-    fp.s[pc] = __uint_as_float(uniform(iw[3]));
+}
+
+// Copy every unit-stride loaded view's chunks into LDS above the C tile, in
+// program order: a 16-bit view takes 16 bytes per chunk (chunk q at
+// off + 16 q), an fp32 view two such planes (elements 0-3, then 4-7).  Each
+// lane copies exactly the chunks its own thread reads later.  Returns false
+// (uniform) when a unit-stride view's base is not 16-byte aligned or the
+// views do not fit; the batches then run the epilogue.
+template <int G>
+DEV bool fast_prefetch(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
+                       const ItemState& st) {
+  FastChunks<G> c;
+  fast_chunks<G>(tid, t, st, c);
+  const uint32_t wave = uniform(tid / 64);
+  const uint32_t lds = (uint32_t)(uintptr_t)(LDS uint8_t*)g_smem;
+  constexpr uint32_t kPlane = 16u * G * kBlock;  // bytes of one 16-byte-per-chunk plane
+  uint32_t off = kSmemBytes;
+  for (uint32_t pc = 0; pc < t.expr_len; ++pc) {
+    const u32x4 w = *(const LDS u32x4*)(g_plan + ins_off + (t.expr_first + pc) * sizeof(DIns));
+    const uint32_t w0 = uniform(w[0]), w1 = uniform(w[1]);
     const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff;
     if (op != VM_STORE && src != SRC_VIEW) continue;
-    const VView v = load_view(views_off + (w1 & 0xffff) * sizeof(DView));
-    GLOBAL uint8_t* p = base_ptr(ka, v.base);
-    if (v.stride[1] == 1 && ((uintptr_t)p & 15) != 0) ok = false;
-    if (op == VM_STORE) {
-      fp.sp[pc] = p;
-      fp.soff[pc] = v.offset;
-      fp.ss0[pc] = v.stride[0];
-      fp.sdt[pc] = v.dtype;
-      continue;
-    }
-    const uint32_t l = fp.nl;  // < kFastLoads (scheduler)
-    fp.slot[pc] = l;
+    const FView v = fast_view(ka, views_off, w1 & 0xffff);
+    if (v.s1 == 1 && ((uintptr_t)v.p & 15) != 0) return false;
+    if (op == VM_STORE || v.s1 != 1) continue;
+    const uint32_t planes = v.dt == DT_F32 ? 2u : 1u;
+    if (off + planes * kPlane > (uint32_t)kArenaBytes) return false;
+    const uint32_t es = v.dt == DT_F32 ? 4u : 2u;
 #pragma unroll
-    for (int j = 0; j < kFastLoads; ++j)
-      if ((uint32_t)j == l) {
-        fp.lp[j] = p;
-        fp.loff[j] = v.offset;
-        fp.ls0[j] = v.stride[0];
-        fp.ldt[j] = v.dtype;
-        fp.ls1[j] = (uint32_t)v.stride[1];
+    for (int g = 0; g < G; ++g) {
+      const int32_t idx = c.ok[g] ? v.off + c.row[g] * v.s0 + c.col[g] : v.off;
+      const GLOBAL uint8_t* gp = v.p + (int64_t)idx * es;
+      const uint32_t m0 = lds + off + 16u * (uint32_t)(g * kBlock) + 1024u * wave;
+      asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(m0) : "m0");
+      if (planes == 2) {
+        const GLOBAL uint8_t* gp2 = gp + 16;
+        asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp2), "s"(m0 + kPlane) : "m0");
       }
-    fp.nl = l + 1;
+    }
+    off += planes * kPlane;
   }
-  return ok;
+  return true;
 }
 
 // One 8-wide chunk per index of a view with column stride s1 (1: 16-byte
@@ -1817,75 +2015,80 @@ DEV void fast_store(GLOBAL uint8_t* p, uint32_t dt, const int32_t (&idx)[G], con
   }
 }
 
+// Run the program over this thread's G chunks (fast_prefetch issued the
+// loads of its unit-stride views).
 template <int G>
-DEV void fast_run(uint32_t tid, const DTask& t, const ItemState& st, const FastProg& fp) {
+DEV void fast_run(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
+                  const ItemState& st) {
+  wait_vmcnt<0>();  // this lane's prefetched chunks have landed in LDS
+  asm volatile("" ::: "memory");
+  constexpr uint32_t kPlane = 16u * G * kBlock;
+  FastChunks<G> c;
+  fast_chunks<G>(tid, t, st, c);
   const int pitch = st.bn + 4;
-  const int lcpr = __builtin_ctz((uint32_t)(st.bn / 8));  // log2 chunks per row
-  const int nchunks = st.bm << lcpr;
   const LDS float* ctile = (const LDS float*)g_smem;
-  for (int q0 = 0; q0 < nchunks; q0 += G * kBlock) {
-    float y[G][8];
-    int32_t row[G], col[G];
-    bool ok[G];
+  float y[G][8];
 #pragma unroll
-    for (int g = 0; g < G; ++g) {
-      const int qq = q0 + g * kBlock + (int)tid;
-      const bool in = qq < nchunks;
-      const int r = in ? qq >> lcpr : 0, cc = in ? (qq & ((1 << lcpr) - 1)) * 8 : 0;
-      row[g] = (int32_t)st.m0 + r;
-      col[g] = (int32_t)st.n0 + cc;
-      ok[g] = in && (uint32_t)row[g] < t.m && (uint32_t)col[g] < t.n;
-      // rows are 16-byte aligned (pitch a multiple of 4), chunks start at multiples of 8
-      const LDS float* src = ctile + r * pitch + cc;
-      const u32x4 lo = *(const LDS u32x4*)src, hi = *(const LDS u32x4*)(src + 4);
+  for (int g = 0; g < G; ++g) {
+    // rows are 16-byte aligned (pitch a multiple of 4), chunks start at multiples of 8
+    const LDS float* src = ctile + c.r[g] * pitch + c.cc[g];
+    const u32x4 lo = *(const LDS u32x4*)src, hi = *(const LDS u32x4*)(src + 4);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        y[g][j] = __uint_as_float(lo[j]);
-        y[g][4 + j] = __uint_as_float(hi[j]);
-      }
+    for (int j = 0; j < 4; ++j) {
+      y[g][j] = __uint_as_float(lo[j]);
+      y[g][4 + j] = __uint_as_float(hi[j]);
     }
-    // every loaded view's chunks in flight together
-    float lv[kFastLoads][G][8];
-#pragma unroll
-    for (int l = 0; l < kFastLoads; ++l) {
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) lv[l][g][j] = 0.0f;
-      if ((uint32_t)l >= fp.nl) continue;
-      int32_t idx[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-        idx[g] = ok[g] ? fp.loff[l] + row[g] * fp.ls0[l] + col[g] * (int32_t)fp.ls1[l] : fp.loff[l];
-      fast_load<G>(fp.lp[l], fp.ldt[l], fp.ls1[l], idx, lv[l]);
-    }
-#pragma unroll
-    for (int pc = 0; pc < kFastIns; ++pc) {
-      if ((uint32_t)pc >= fp.n) break;
-      const uint32_t w = fp.w0[pc];
-      const uint32_t op = w & 0xff, src = (w >> 8) & 0xff, rnd = (w >> 16) & 0xff, rev = w >> 24;
-      const float a = fp.a[pc];
+  }
+  uint32_t off = kSmemBytes;  // next prefetched view (program order, as fast_prefetch)
+#pragma nounroll
+  for (uint32_t pc = 0; pc < t.expr_len; ++pc) {
+    const u32x4 w = *(const LDS u32x4*)(g_plan + ins_off + (t.expr_first + pc) * sizeof(DIns));
+    const uint32_t w0 = uniform(w[0]), w1 = uniform(w[1]);
+    const float a = __uint_as_float(uniform(w[2])), sv = __uint_as_float(uniform(w[3]));
+    const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff, rnd = (w0 >> 16) & 0xff, rev = w0 >> 24;
+    float x[G][8];
+    if (op == VM_STORE || src == SRC_VIEW) {
+      const FView v = fast_view(ka, views_off, w1 & 0xffff);
       if (op == VM_STORE) {
         int32_t idx[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) idx[g] = ok[g] ? fp.soff[pc] + row[g] * fp.ss0[pc] + col[g] : fp.soff[pc];
-        fast_store<G>(fp.sp[pc], fp.sdt[pc], idx, ok, y);
+        for (int g = 0; g < G; ++g) idx[g] = c.ok[g] ? v.off + c.row[g] * v.s0 + c.col[g] : v.off;
+        fast_store<G>(v.p, v.dt, idx, c.ok, y);
         continue;
       }
-      float x[G][8];
-      if (src == SRC_VIEW) {
-        const uint32_t l = fp.slot[pc];
+      if (v.s1 == 1) {
+        const bool f32 = v.dt == DT_F32, bf = v.dt == DT_BF16;
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+        for (int g = 0; g < G; ++g) {
+          const uint32_t q = (uint32_t)(g * kBlock) + tid;
+          const u32x4 r = *(const LDS u32x4*)(g_smem + off + 16u * q);
+          if (f32) {
+            const u32x4 r2 = *(const LDS u32x4*)(g_smem + off + kPlane + 16u * q);
 #pragma unroll
-          for (int j = 0; j < 8; ++j) x[g][j] = l == 0 ? lv[0][g][j] : l == 1 ? lv[1][g][j] : lv[2][g][j];
+            for (int j = 0; j < 4; ++j) {
+              x[g][j] = __uint_as_float(r[j]);
+              x[g][4 + j] = __uint_as_float(r2[j]);
+            }
+          } else {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) x[g][j] = half_bits_to_f32((j & 1) ? r[j / 2] >> 16 : r[j / 2] & 0xffffu, bf);
+          }
+        }
+        off += (f32 ? 2u : 1u) * kPlane;
       } else {
-        const float k = src == SRC_SCALAR ? fp.s[pc] : 0.0f;
+        // column stride 0: one element per chunk, broadcast along the chunk
+        int32_t idx[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g)
-#pragma unroll
-          for (int j = 0; j < 8; ++j) x[g][j] = k;
+        for (int g = 0; g < G; ++g) idx[g] = c.ok[g] ? v.off + c.row[g] * v.s0 : v.off;
+        fast_load<G>(v.p, v.dt, 0u, idx, x);
       }
+    } else {
+      const float k = src == SRC_SCALAR ? sv : 0.0f;
+#pragma unroll
+      for (int g = 0; g < G; ++g)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) x[g][j] = k;
+    }
 #define TK_EACH_R(expr)                          \
   _Pragma("unroll") for (int g = 0; g < G; ++g)  \
   _Pragma("unroll") for (int j = 0; j < 8; ++j) { \
@@ -1894,57 +2097,45 @@ DEV void fast_run(uint32_t tid, const DTask& t, const ItemState& st, const FastP
     (void)o;                                     \
     expr;                                        \
   }
-      switch (op) {
-        case VM_LOAD: TK_EACH_R(v = o) break;
-        case VM_ADD:
-          if (rev) { TK_EACH_R(float u = a * v; v = o + u) }
-          else { TK_EACH_R(float u = a * o; v = v + u) }
-          break;
-        case VM_SUB:
-          if (rev) { TK_EACH_R(float u = a * v; v = o - u) }
-          else { TK_EACH_R(float u = a * o; v = v - u) }
-          break;
-        case VM_MUL: TK_EACH_R(v = v * o) break;
-        case VM_DIV:
-          if (rev) { TK_EACH_R(v = o / v) }
-          else { TK_EACH_R(v = v / o) }
-          break;
-        case VM_NEG: TK_EACH_R(v = -v) break;
-        case VM_RELU: TK_EACH_R(v = v < 0.0f ? 0.0f : v) break;
-        case VM_SQUARE: TK_EACH_R(v = v * v) break;
-        case VM_TB:
-          if (rev) { TK_EACH_R(v = v <= a ? 0.0f : o) }
-          else { TK_EACH_R(v = o <= a ? 0.0f : v) }
-          break;
-        case VM_SCALE: TK_EACH_R(v = a * v) break;
-        case VM_ZERO: TK_EACH_R(v = 0.0f) break;
-        default: break;
-      }
+    switch (op) {
+      case VM_LOAD: TK_EACH_R(v = o) break;
+      case VM_ADD:
+        if (rev) { TK_EACH_R(float u = a * v; v = o + u) }
+        else { TK_EACH_R(float u = a * o; v = v + u) }
+        break;
+      case VM_SUB:
+        if (rev) { TK_EACH_R(float u = a * v; v = o - u) }
+        else { TK_EACH_R(float u = a * o; v = v - u) }
+        break;
+      case VM_MUL: TK_EACH_R(v = v * o) break;
+      case VM_DIV:
+        if (rev) { TK_EACH_R(v = o / v) }
+        else { TK_EACH_R(v = v / o) }
+        break;
+      case VM_NEG: TK_EACH_R(v = -v) break;
+      case VM_RELU: TK_EACH_R(v = v < 0.0f ? 0.0f : v) break;
+      case VM_SQUARE: TK_EACH_R(v = v * v) break;
+      case VM_TB:
+        if (rev) { TK_EACH_R(v = v <= a ? 0.0f : o) }
+        else { TK_EACH_R(v = o <= a ? 0.0f : v) }
+        break;
+      case VM_SCALE: TK_EACH_R(v = a * v) break;
+      case VM_ZERO: TK_EACH_R(v = 0.0f) break;
+      default: break;
+    }
 #undef TK_EACH_R
-      if (rnd == DT_BF16) {
+    if (rnd == DT_BF16) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) y[g][j] = bf16_bits_to_f32(f32_to_bf16_bits(y[g][j]));
-      } else if (rnd == DT_F16) {
+        for (int j = 0; j < 8; ++j) y[g][j] = bf16_bits_to_f32(f32_to_bf16_bits(y[g][j]));
+    } else if (rnd == DT_F16) {
 #pragma unroll
-        for (int g = 0; g < G; ++g)
+      for (int g = 0; g < G; ++g)
 #pragma unroll
-          for (int j = 0; j < 8; ++j) y[g][j] = f16_bits_to_f32(f32_to_f16_bits(y[g][j]));
-      }
+        for (int j = 0; j < 8; ++j) y[g][j] = f16_bits_to_f32(f32_to_f16_bits(y[g][j]));
     }
   }
-}
-
-// The register epilogue of a contraction item whose fp32 tile is in LDS;
-// false when the item's epilogue must run through batches.
-DEV bool fast_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, const ItemState& st) {
-  if (!(t.flags & F_FASTEPI)) return false;
-  FastProg fp;
-  if (!fast_decode(ka, t, sd.off_views, sd.off_ins, fp)) return false;
-  fast_run<2>(tid, t, st, fp);
-  __syncthreads();  // the next item may overwrite the LDS tile
-  return true;
 }
 
 // A column reduction whose source program is one load of a 2-D view with
@@ -2054,24 +2245,42 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
     case T_GEMM_SIMT:
       gemm_simt(tid, ka, t, sd.off_views, item, st);
       __syncthreads();
-      if (fast_epilogue(tid, ka, t, sd, st)) return;
+      if ((t.flags & F_FASTEPI) && fast_prefetch<2>(tid, ka, t, sd.off_views, sd.off_ins, st)) {
+        fast_run<2>(tid, ka, t, sd.off_views, sd.off_ins, st);
+        __syncthreads();  // the next item may overwrite the LDS tile and the prefetched operands
+        return;
+      }
       break;
     case T_GEMM_MFMA: {
       // the operand dtype is the A view's (both operands share it)
       const bool bf16 = uniform(((const LDS DView*)(g_plan + sd.off_views + t.va * sizeof(DView)))->dtype) == DT_BF16;
+      // a register epilogue's operands are prefetched as soon as the main loop ends
+      bool fast = false;
+      auto after_loop = [&]() {
+        if (!(t.flags & F_FASTEPI)) return;
+        fast = t.tile == 0 ? fast_prefetch<8>(tid, ka, t, sd.off_views, sd.off_ins, st)
+                           : fast_prefetch<2>(tid, ka, t, sd.off_views, sd.off_ins, st);
+      };
       if (t.tile == 0) {
         if (bf16)
-          gemm_mfma<128, 128, true>(tid, ka, t, sd.off_views, item, st);
+          gemm_mfma<128, 128, true>(tid, ka, t, sd.off_views, item, st, after_loop);
         else
-          gemm_mfma<128, 128, false>(tid, ka, t, sd.off_views, item, st);
+          gemm_mfma<128, 128, false>(tid, ka, t, sd.off_views, item, st, after_loop);
       } else {
         if (bf16)
-          gemm_mfma<64, 64, true>(tid, ka, t, sd.off_views, item, st);
+          gemm_mfma<64, 64, true>(tid, ka, t, sd.off_views, item, st, after_loop);
         else
-          gemm_mfma<64, 64, false>(tid, ka, t, sd.off_views, item, st);
+          gemm_mfma<64, 64, false>(tid, ka, t, sd.off_views, item, st, after_loop);
       }
       __syncthreads();
-      if (fast_epilogue(tid, ka, t, sd, st)) return;
+      if (fast) {
+        if (t.tile == 0)
+          fast_run<8>(tid, ka, t, sd.off_views, sd.off_ins, st);
+        else
+          fast_run<2>(tid, ka, t, sd.off_views, sd.off_ins, st);
+        __syncthreads();  // the next item may overwrite the LDS tile and the prefetched operands
+        return;
+      }
       break;
     }
     case T_GEMV_Q8:

@@ -1313,13 +1313,19 @@ struct Builder {
   }
 
   // Whether a contraction tile's epilogue `code` (peepholed, view indices into
-  // `vt`) over an m x n output can run as the kernel's register program: a
-  // short straight-line program over 8-wide column chunks, every view loaded
-  // once per chunk before the first instruction runs.  Loads are hoisted, so
-  // a load may not follow a store whose bytes it may read.
-  static bool fast_epilogue_ok(const std::vector<DIns>& code, const std::vector<DView>& vt, int64_t m, int64_t n) {
+  // `vt`) over an m x n output, on tiles of `tile` x `tile`, can run as the
+  // kernel's register program: a short straight-line program over 8-wide
+  // column chunks, every view loaded once per chunk before the first
+  // instruction runs.  Loads are hoisted, so a load may not follow a store
+  // whose bytes it may read.  The unit-stride loaded views of a tile are
+  // staged in the 48 KB of LDS above the fp32 tile: 16 bytes per 8-element
+  // chunk and plane, two planes for fp32.
+  static bool fast_epilogue_ok(const std::vector<DIns>& code, const std::vector<DView>& vt, int64_t m, int64_t n,
+                               int tile) {
     if (n % 8 != 0 || m <= 0 || code.empty() || code.size() > (size_t)kFastIns) return false;
     int loads = 0;
+    const int64_t plane = 16 * (int64_t)tile * tile / 8, budget = 49152;
+    int64_t staged = 0;
     auto range = [&](const DView& v, int64_t& lo, int64_t& hi) {
       const int64_t es = dtype_size(v.dtype);
       int64_t a = v.offset, b = v.offset;
@@ -1351,6 +1357,7 @@ struct Builder {
       if (s1 == 1 && (v.offset % epc != 0 || v.stride[0] % epc != 0)) return false;
       if (is_store) continue;
       if (++loads > kFastLoads) return false;
+      if (s1 == 1 && (staged += (v.dtype == DT_F32 ? 2 : 1) * plane) > budget) return false;
       int64_t lo, hi;
       range(v, lo, hi);
       for (size_t j = 0; j < i; ++j) {
@@ -1841,7 +1848,7 @@ struct Builder {
     uint32_t vb = commit_views(cx);
     uint32_t code_first = commit_code(code, vb);
     if ((g.kind == T_GEMM_MFMA || g.kind == T_GEMM_SIMT) && g.split <= 1 && O.fast_epilogue &&
-        fast_epilogue_ok(code, cx.vtab, m, n))
+        fast_epilogue_ok(code, cx.vtab, m, n, g.kind == T_GEMM_MFMA && g.tile == 0 ? 128 : 64))
       t.flags |= F_FASTEPI;
     std::string desc = mm.name + " (" + mm.opcode + " " + std::to_string(m) + "x" + std::to_string(k) + "x" +
                        std::to_string(n) + ")";

@@ -43,7 +43,9 @@ def _bench():
 def cmd_run(args):
     import torch
     bench = _bench()
-    r = bench.Runner(args.workload)
+    # the bench's launch configuration: an ordinary launch of the co-resident
+    # grid (cooperative launches make the profiler crash in its exit handlers)
+    r = bench.Runner(args.workload, launch_mode=1)
     for i in range(args.launches):
         r.step(i)
     torch.cuda.synchronize()
