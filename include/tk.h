@@ -185,6 +185,25 @@ tk_status tk_validate_into(const tk_program* prog, const tk_tensor* inputs, size
 tk_status tk_run_into(const tk_program* prog, const tk_tensor* inputs, size_t n_in, const tk_tensor* outputs,
                       size_t n_out, const tk_tensor* workspace, void* stream);
 
+/* tk_run_into without a workspace argument and without allocating anything:
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation).  The
+ * step runs in the library's own workspace, a static device array of
+ * TK_STATIC_WORKSPACE_BYTES (128 MiB) per device, held from the first call
+ * on a device until the process ends; programs whose workspace_bytes
+ * exceed it are rejected with TK_E_WORKSPACE before anything else is
+ * checked (use tk_run_into).  Every call first clears the workspace header
+ * (barrier flags, epochs, abort word) with a small fill kernel on `stream`,
+ * then launches; the arena keeps whatever the last call left.  All calls on
+ * one device share that one workspace: calls that overlap on a device (on
+ * different streams, or from different threads without ordering) race.
+ * Inputs and outputs are checked as in tk_run_into.  When an earlier launch
+ * of the program stopped at a timed-out barrier, the call returns
+ * TK_E_ABORTED once (nothing launched) and clears that record. */
+#define TK_STATIC_WORKSPACE_BYTES (128ull << 20)
+tk_status tk_run_into_noalloc(const tk_program* prog, const tk_tensor* inputs, size_t n_in, const tk_tensor* outputs,
+                              size_t n_out, void* stream);
+
 /* Zero the workspace header (barrier state, abort flag) on `stream` with a
  * small kernel (safe under graph capture), and clear the program's record of
  * an aborted launch (TK_E_ABORTED). */

@@ -28,6 +28,9 @@ constexpr uint32_t kHdrArrive = 16384;     // u32 [kMaxGrid * kFlagStride] arriv
 constexpr uint32_t kHdrRelease = kHdrArrive + kMaxGrid * kFlagStride * 4;  // u32 release epochs
 constexpr uint32_t kHeaderBytes = kHdrRelease + kMaxGrid * kFlagStride * 4;  // 147456: header size
 constexpr uint32_t kMaxTimedStages = 400;
+// The library's own per-device workspace for callers that cannot allocate
+// (tk_run_into_noalloc): header plus arena of at most this many bytes.
+constexpr uint64_t kStaticWorkspaceBytes = 128ull << 20;
 
 // Workspace header layout (bytes).  Each word sits on its own 64-byte line.
 constexpr uint32_t kHdrEpoch = 0;      // last barrier epoch of the previous launch on this workspace

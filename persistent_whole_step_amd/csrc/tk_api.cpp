@@ -19,6 +19,7 @@ hipError_t tk_device_launch_resident(const KArgs& ka, int grid, hipStream_t stre
 hipError_t tk_device_occupancy(int* blocks_per_cu);
 hipError_t tk_device_attributes(hipFuncAttributes* attr);
 hipError_t tk_device_zero_header(uint8_t* ws, hipStream_t stream);
+hipError_t tk_device_static_workspace(int device, void** out);
 
 struct tk_program {
   tk::Plan plan;
@@ -403,38 +404,87 @@ tk_status tk_allocate(const tk_program* p, const tk_tensor* inputs, size_t n_in,
   })
 }
 
+namespace {
+
+// Launch the step on checked buffers (tk_run_into, tk_run_into_noalloc).
+tk_status launch_step(const tk_program* p, const tk_tensor* inputs, size_t n_in, const tk_tensor* outputs,
+                      size_t n_out, void* ws, void* stream, bool reset_header) {
+  KArgs ka;
+  std::memset(&ka, 0, sizeof(ka));
+  ka.plan = (const uint8_t*)p->d_plan;
+  ka.ws = (uint8_t*)ws;
+  ka.deadline_ticks = p->deadline;
+  ka.flags = p->dbg_flags;
+  ka.stagger_seed = p->stagger;
+  ka.host_abort = p->d_abort;
+  const auto& pl = p->plan;
+  ka.n_bases = (uint32_t)(pl.ws_base + 1);
+  for (size_t i = 0; i < n_in; ++i) ka.bases[i] = inputs[i].data;
+  for (size_t s = 0; s < n_out; ++s) ka.bases[pl.n_in + s] = outputs[s].data;
+  ka.bases[pl.ws_base] = ws;
+  int cur = 0;
+  hipGetDevice(&cur);
+  if (cur != p->device) hipSetDevice(p->device);
+  hipError_t e = hipSuccess;
+  if (reset_header) e = tk_device_zero_header((uint8_t*)ws, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = p->opts.launch_mode == 1 ? tk_device_launch_resident(ka, p->grid, (hipStream_t)stream)
+                                 : tk_device_launch(ka, p->grid, (hipStream_t)stream);
+  if (cur != p->device) hipSetDevice(cur);
+  if (e != hipSuccess) return hip_fail(e, p->opts.launch_mode == 1 ? "launch" : "cooperative launch");
+  return TK_OK;
+}
+
+tk_status aborted_status(const tk_program* p) {
+  return fail(TK_E_ABORTED, "a launch of this program stopped at a grid barrier that timed out (stage " +
+                                std::to_string(p->h_abort[1]) +
+                                "); its outputs are incomplete; re-initialise the workspace (tk_workspace_init) "
+                                "before running again");
+}
+
+}  // namespace
+
 tk_status tk_run_into(const tk_program* p, const tk_tensor* inputs, size_t n_in, const tk_tensor* outputs,
                       size_t n_out, const tk_tensor* workspace, void* stream) {
   if (!p) return fail(TK_E_ARG, "program is NULL");
   if (p->device < 0) return fail(TK_E_DEVICE, "plan-only program: compile for a device to run");
-  if (p->h_abort && p->h_abort[0] != 0u)
-    return fail(TK_E_ABORTED, "a launch of this program stopped at a grid barrier that timed out (stage " +
-                                  std::to_string(p->h_abort[1]) +
-                                  "); its outputs are incomplete; re-initialise the workspace (tk_workspace_init) "
-                                  "before running again");
+  if (p->h_abort && p->h_abort[0] != 0u) return aborted_status(p);
   TK_TRY({
     check_buffers(p, inputs, n_in, outputs, n_out, workspace, p->device);
-    KArgs ka;
-    std::memset(&ka, 0, sizeof(ka));
-    ka.plan = (const uint8_t*)p->d_plan;
-    ka.ws = (uint8_t*)workspace->data;
-    ka.deadline_ticks = p->deadline;
-    ka.flags = p->dbg_flags;
-    ka.stagger_seed = p->stagger;
-    ka.host_abort = p->d_abort;
-    const auto& pl = p->plan;
-    ka.n_bases = (uint32_t)(pl.ws_base + 1);
-    for (size_t i = 0; i < n_in; ++i) ka.bases[i] = inputs[i].data;
-    for (size_t s = 0; s < n_out; ++s) ka.bases[pl.n_in + s] = outputs[s].data;
-    ka.bases[pl.ws_base] = workspace->data;
-    int cur = 0;
-    hipGetDevice(&cur);
-    if (cur != p->device) hipSetDevice(p->device);
-    hipError_t e = p->opts.launch_mode == 1 ? tk_device_launch_resident(ka, p->grid, (hipStream_t)stream)
-                                             : tk_device_launch(ka, p->grid, (hipStream_t)stream);
-    if (cur != p->device) hipSetDevice(cur);
-    if (e != hipSuccess) return hip_fail(e, p->opts.launch_mode == 1 ? "launch" : "cooperative launch");
-    return TK_OK;
+    return launch_step(p, inputs, n_in, outputs, n_out, workspace->data, stream, false);
+  })
+}
+
+tk_status tk_run_into_noalloc(const tk_program* p, const tk_tensor* inputs, size_t n_in, const tk_tensor* outputs,
+                              size_t n_out, void* stream) {
+  if (!p) return fail(TK_E_ARG, "program is NULL");
+  if (p->plan.workspace_bytes > kStaticWorkspaceBytes)
+    return fail(TK_E_WORKSPACE, "the program needs a workspace of " + std::to_string(p->plan.workspace_bytes) +
+                                    " bytes; the library's static workspace holds " +
+                                    std::to_string(kStaticWorkspaceBytes) + " (use tk_run_into)");
+  if (p->device < 0) return fail(TK_E_DEVICE, "plan-only program: compile for a device to run");
+  if (p->h_abort && p->h_abort[0] != 0u) {
+    // reported once: every call re-initialises the static workspace's header
+    const tk_status st = aborted_status(p);
+    p->h_abort[0] = p->h_abort[1] = 0u;
+    return st;
+  }
+  TK_TRY({
+    void* ws = nullptr;
+    hipError_t e = tk_device_static_workspace(p->device, &ws);
+    if (e != hipSuccess) return hip_fail(e, "static workspace lookup");
+    tk_tensor w;
+    std::memset(&w, 0, sizeof(w));
+    w.data = ws;
+    w.dtype = TK_I8;
+    w.ndim = 1;
+    w.shape[0] = (int64_t)kStaticWorkspaceBytes;
+    w.strides[0] = 1;
+    w.storage_base = ws;
+    w.storage_bytes = kStaticWorkspaceBytes;
+    w.device = p->device;
+    check_buffers(p, inputs, n_in, outputs, n_out, &w, p->device);
+    return launch_step(p, inputs, n_in, outputs, n_out, ws, stream, true);
   })
 }
 

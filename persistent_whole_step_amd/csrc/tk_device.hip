@@ -27,6 +27,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <mutex>
 #include <type_traits>
 
 #include "plan.h"
@@ -2531,6 +2532,35 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
 
 __global__ void tk_zero_header(uint8_t* ws, uint32_t bytes) {
   for (uint32_t i = threadIdx.x * 4; i < bytes; i += blockDim.x * 4) *(uint32_t*)(ws + i) = 0u;
+}
+
+// The workspace of tk_run_into_noalloc, for callers that cannot allocate:
+// one copy per device, in the code object's own memory, held until the
+// process ends.  Host code never uses this name as an address (on the host
+// it is a stand-in, not device memory): tk_device_static_workspace looks up
+// each device's copy once, with that device current, and every launch and
+// fill takes that pointer.
+static __device__ __align__(256) uint8_t scratch[kStaticWorkspaceBytes];
+
+hipError_t tk_device_static_workspace(int device, void** out) {
+  constexpr int kDevices = 64;
+  static std::mutex mu;
+  static void* ptrs[kDevices] = {};
+  if (device < 0 || device >= kDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (!ptrs[device]) {
+    int cur = 0;
+    hipError_t e = hipGetDevice(&cur);
+    if (e == hipSuccess) e = hipSetDevice(device);
+    void* p = nullptr;
+    if (e == hipSuccess) e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    hipSetDevice(cur);
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    ptrs[device] = p;
+  }
+  *out = ptrs[device];
+  return hipSuccess;
 }
 
 // Host-side launch helpers used by the C ABI.

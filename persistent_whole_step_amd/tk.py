@@ -69,6 +69,10 @@ def lib():
     if _lib is None:
         if not os.path.exists(LIB_PATH):
             raise RuntimeError(f"libtk.so is not built ({LIB_PATH}); run persistent_whole_step_amd.build")
+        # PyTorch ships its own HIP runtime library.  Import it first, so that
+        # libtk binds to that same runtime: loading libtk first would bring in
+        # a second copy of the runtime, which then finds no device.
+        import torch  # noqa: F401
         l = ctypes.CDLL(LIB_PATH)
         P = ctypes.POINTER
         l.tk_default_options.argtypes = [P(TkOptions)]
@@ -82,6 +86,8 @@ def lib():
                                        P(TkTensor)]
         l.tk_run_into.argtypes = [ctypes.c_void_p, P(TkTensor), ctypes.c_size_t, P(TkTensor), ctypes.c_size_t,
                                   P(TkTensor), ctypes.c_void_p]
+        l.tk_run_into_noalloc.argtypes = [ctypes.c_void_p, P(TkTensor), ctypes.c_size_t, P(TkTensor),
+                                          ctypes.c_size_t, ctypes.c_void_p]
         l.tk_workspace_init.argtypes = [ctypes.c_void_p, P(TkTensor), ctypes.c_void_p]
         l.tk_workspace_status.argtypes = [P(TkTensor), ctypes.c_void_p, P(ctypes.c_int32), P(ctypes.c_int32)]
         l.tk_set_debug.argtypes = [ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.c_uint64]
@@ -90,7 +96,8 @@ def lib():
         l.tk_destroy.argtypes = [ctypes.c_void_p]
         l.tk_destroy.restype = None
         l.tk_last_error.restype = ctypes.c_char_p
-        for f in ("tk_compile", "tk_query", "tk_dump_plan", "tk_plan_bytes", "tk_allocate", "tk_validate_into", "tk_run_into",
+        for f in ("tk_compile", "tk_query", "tk_dump_plan", "tk_plan_bytes", "tk_allocate", "tk_validate_into",
+                  "tk_run_into", "tk_run_into_noalloc",
                   "tk_workspace_init", "tk_workspace_status", "tk_set_debug", "tk_read_timestamps"):
             getattr(l, f).restype = ctypes.c_int
         _lib = l
@@ -350,6 +357,22 @@ class Program:
             import torch
             torch.autograd.graph.increment_version([inputs[i] for i in inplace.values()])
         return buffers.outputs
+
+    def run_into_noalloc(self, *inputs, outputs, stream=None):
+        """tk_run_into_noalloc: run in the library's static per-device
+        workspace; `outputs` are caller tensors as for run_into (in-place
+        slots are their input tensors).  Nothing is allocated."""
+        for t in inputs:
+            if t.is_neg() or t.is_conj():
+                raise ValueError("tk: resolve lazy negative or conjugate input views before execution")
+        ins = _array([describe(t) for t in inputs])
+        outs = _array([describe(t) for t in outputs])
+        _check(lib().tk_run_into_noalloc(self._h, ins, len(inputs), outs, len(outputs), _stream_handle(stream)))
+        inplace = self._inplace_map()
+        if inplace:
+            import torch
+            torch.autograd.graph.increment_version([inputs[i] for i in inplace.values()])
+        return tuple(outputs)
 
     def __call__(self, *inputs):
         """Allocate fresh buffers, run, wait for the step and check that it
