@@ -30,6 +30,8 @@ def lib():
                                  ctypes.POINTER(ctypes.c_void_p), ctypes.c_int, ctypes.c_int]
         l.oracle_error.restype = ctypes.c_char_p
         l.oracle_threads.restype = ctypes.c_int
+        l.oracle_set_threads.restype = None
+        l.oracle_set_threads.argtypes = [ctypes.c_int]
         for name in ("oracle_round_bf16", "oracle_round_f16"):
             f = getattr(l, name)
             f.restype = None
@@ -89,6 +91,11 @@ def run64(text: str, inputs):
 
 def threads() -> int:
     return int(lib().oracle_threads())
+
+
+def set_threads(n: int) -> None:
+    """Thread count of the oracle's parallel loops (results do not depend on it)."""
+    lib().oracle_set_threads(int(n))
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:

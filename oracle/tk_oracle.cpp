@@ -768,6 +768,16 @@ int oracle_threads(void) {
 #endif
 }
 
+// Set the thread count of later parallel loops (n >= 1).  Results do not
+// depend on it: every output is computed by one thread in a fixed order.
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  if (n >= 1) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}
+
 void oracle_round_bf16(const float* x, uint16_t* out, int64_t n) {
 #pragma omp parallel for schedule(static)
   for (int64_t i = 0; i < n; ++i) out[i] = to_bf16(x[i]);
