@@ -2,15 +2,19 @@
 """Throughput of whole training steps run as one persistent kernel each, on one MI355X.
 
 A step is one launch of the persistent kernel over the whole compiled program
-(forward, MSE loss, explicit backward, in-place SGD), as in the whole-step
-benchmark set: the default workload is the 3-layer bf16 MLP (batch 256,
-512 -> 1024 -> 1024 -> 64, lr 1e-3).  Inputs are seeded synthetic tensors
-already resident in HBM; parameters are updated in place every step (state
-feedback) and the (x, target) batch rotates over 4 resident batches.  The
-other workloads (2-layer fp32 MLP, the default MLP with AdamW in place of
-SGD, the default MLP's step written with torch.func and captured by the
-front end, int8-weight GEMV stack rotating 3 weight sets, 4096-wide bf16 MLP,
-16-layer fp16 residual MLP) are timed briefly and reported under "others".
+(forward, MSE loss, explicit backward, in-place SGD).  The default workload is
+the largest single-GPU configuration: the 16-layer fp16 residual MLP (batch
+512, width 2048, h = h + relu(addmm(h, W_i, b_i)), MSE head to 2048 targets,
+full backward, lr 1e-4; 47 contractions, 201.9 GFLOP per step).  Inputs are
+seeded synthetic tensors already resident in HBM; parameters are updated in
+place every step (state feedback) and the (x, target) batch rotates over 4
+resident batches.  The timed region is 5 batches of back-to-back launches,
+each bracketed by HIP events on the launch stream; the value is the median
+batch's rate, and the raw batch times are kept.  The 4096-wide bf16 MLP gets
+its own roofline block; the other workloads (2-layer fp32 MLP, 3-layer bf16
+MLP with SGD, with AdamW and captured from torch.func, int8-weight GEMV stack
+rotating 3 weight sets, with 4 decode rows and with Q8_0 activations) are
+timed briefly under "others".
 
 Prints one JSON line on stdout.  --gpus N with N > 1 is refused: the
 kernel runs on one GPU.
@@ -191,22 +195,56 @@ class Runner:
         if aborted:
             raise RuntimeError(f"{self.name}: a grid barrier timed out in stage {stage}")
 
-    def time_steps(self, steps: int, warmup: int):
+    def time_batches(self, steps: int, warmup: int, batches: int = 5):
+        """`steps` launches in `batches` equal batches of back-to-back launches,
+        each bracketed by HIP events on the launch stream, after `warmup`
+        untimed launches; the whole timed region is bracketed by device
+        synchronisation.  Returns (wall seconds, [batch ms], steps per batch)."""
         import torch
+        per = max(1, steps // batches)
         for i in range(warmup):
             self.step(i)
         torch.cuda.synchronize()
-        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(batches)]
         t0 = time.perf_counter()
-        start.record()
-        for i in range(steps):
-            self.step(i)
-        end.record()
+        i = 0
+        for a, b in evs:
+            a.record()
+            for _ in range(per):
+                self.step(i)
+                i += 1
+            b.record()
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
-        ev_ms = start.elapsed_time(end)
         self.check_not_aborted()
-        return wall, ev_ms
+        return wall, [a.elapsed_time(b) for a, b in evs], per
+
+    def stage_stamps(self):
+        """In-situ stage timing of one launch (workgroup 0's stamps: items
+        done, descriptors staged, barrier passed), in microseconds."""
+        import torch
+        self.p.set_debug(timestamps=True)
+        for i in range(3):
+            self.step(i)
+        torch.cuda.synchronize()
+        ts = self.p.read_timestamps(self.buffers.workspace)
+        self.p.set_debug(timestamps=False)
+        self.check_not_aborted()
+        n = self.stats["n_stages"]
+        items, staging, barrier = [], [], []
+        for st in range(n):
+            start, done, blob, bar = ts[4 * st:4 * st + 4]
+            if done >= start:
+                items.append((done - start) / 100.0)
+            if st + 1 < n:
+                staging.append((blob - done) / 100.0)
+                barrier.append((bar - blob) / 100.0)
+        med = lambda v: round(sorted(v)[len(v) // 2], 3) if v else None
+        return {"stages": n, "sum_items_us": round(sum(items), 2), "sum_staging_us": round(sum(staging), 2),
+                "sum_barrier_us": round(sum(barrier), 2), "median_barrier_us": med(barrier),
+                "median_items_us": med(items),
+                "note": "workgroup 0: barrier = waiting at the grid barrier after its own items, which includes "
+                        "the slowest workgroup's lag"}
 
     def kernel_ms(self, n: int = 50) -> float:
         """Average duration of one launch, HIP events on the launch stream."""
@@ -287,36 +325,102 @@ def barrier_latency(n_small: int = 8, n_large: int = 264):
             "launch_ms_%d_stages" % n_large: round(res[n_large], 4)}
 
 
-def cpu_baseline(name: str, seconds: float):
-    """The oracle, as it stands, on the same workload: whole steps until `seconds` pass."""
+def cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _oracle_time(text, ins, runs: int):
+    from oracle import oracle
+    ts = []
+    for _ in range(runs):
+        t0 = time.perf_counter()
+        oracle.run(text, [a.copy() for a in ins])
+        ts.append(time.perf_counter() - t0)
+    return sorted(ts)[len(ts) // 2]
+
+
+def cpu_baseline(name: str):
+    """The oracle, as it stands, timed on this host's cores.  The headline
+    workload is timed on a bounded sample: the same step with 2 of its 16
+    residual layers (same batch and width), whose time is scaled to the whole
+    step by the contraction FLOPs (the step's cost is in its contractions).
+    C1-C3 (the oracle finishes them in seconds) are timed whole: all threads,
+    median of 3, and one thread (median of 3; one run for C2)."""
     from oracle import oracle
     from persistent_whole_step_amd import programs
+    threads = oracle.threads()
     cfg = config(name)
-    prog = programs.build(cfg)
-    text = prog.text()
-    ins = programs.inputs_for(cfg, 0)
-    n = 0
-    t0 = time.perf_counter()
-    while True:
-        oracle.run(text, [a.copy() for a in ins])
-        n += 1
-        el = time.perf_counter() - t0
-        if el >= seconds or (n >= 1 and el * (n + 1) / n > 3 * seconds):
-            break
-    return {"value": round(n / el, 4), "unit": "steps/s", "cores": oracle.threads(), "kind": "oracle",
-            "sample": f"{n} full {WORKLOAD_NAMES[name]} steps (fp32 CPU oracle) in {el:.1f} s"}
+    res = {"unit": "steps/s", "kind": "oracle", "cpu": cpu_model(), "cores": threads}
+    if cfg["kind"] == "residual" and cfg["layers"] > 2:
+        small = dict(cfg, layers=2)
+        prog, full = programs.build(small), programs.build(cfg)
+        scale = programs.contraction_flops(full) / programs.contraction_flops(prog)
+        t = _oracle_time(prog.text(), programs.inputs_for(small, 0), 1)
+        res.update(value=round(1.0 / (t * scale), 6),
+                   sample=f"one step of the same residual MLP with 2 of its {cfg['layers']} layers "
+                          f"(batch {cfg['batch']}, width {cfg['width']}) in {t:.2f} s, scaled by the contraction "
+                          f"FLOPs ({scale:.2f}x) to the whole step")
+    else:
+        prog = programs.build(cfg)
+        t = _oracle_time(prog.text(), programs.inputs_for(cfg, 0), 3)
+        res.update(value=round(1.0 / t, 4), sample=f"whole {WORKLOAD_NAMES[name]} steps, median of 3")
+    per_config = {}
+    for c in ("c1", "c2", "c3"):
+        cc = config(c)
+        prog = programs.build(cc)
+        ins = programs.inputs_for(cc, 0)
+        oracle.set_threads(threads)
+        t_all = _oracle_time(prog.text(), ins, 3)
+        oracle.set_threads(1)
+        t_one = _oracle_time(prog.text(), ins, 1 if c == "c2" else 3)
+        oracle.set_threads(threads)
+        per_config[WORKLOAD_NAMES[c]] = {"steps_per_s_all_threads": round(1.0 / t_all, 3),
+                                         "steps_per_s_one_thread": round(1.0 / t_one, 3)}
+        log(f"[bench] oracle {c}: {per_config[WORKLOAD_NAMES[c]]}")
+    res["whole_steps"] = per_config
+    return res
+
+
+def measure(name: str, steps: int, warmup: int, launch_mode: int, stamps: bool = False):
+    """Time one workload: batched events, launch duration, roofline."""
+    r = Runner(name, launch_mode=launch_mode)
+    log(f"[bench] {name}: stages={r.stats['n_stages']} grid={r.stats['grid_size']}; timing {steps} steps")
+    wall, batch_ms, per = r.time_batches(steps, warmup)
+    med = sorted(batch_ms)[len(batch_ms) // 2]
+    kms = r.kernel_ms()
+    out = {
+        "value": per / (med * 1e-3),
+        "ms_per_step": med / per,
+        "steps": per * len(batch_ms),
+        "wall_steps_per_s": per * len(batch_ms) / wall,
+        "batch_ms": [round(x, 4) for x in batch_ms],
+        "steps_per_batch": per,
+        "kernel_ms": kms,
+        "roofline": roofline(name, r.cfg, r.prog, kms, traffic_for(name)),
+        "stats": r.stats,
+    }
+    if stamps:
+        out["stage_stamps"] = r.stage_stamps()
+    return r, out
 
 
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=1000)
-    ap.add_argument("--warmup", type=int, default=50)
-    ap.add_argument("--config", default="c2", choices=sorted(WORKLOAD_NAMES))
-    ap.add_argument("--others", default="c1,c2a,c2cap,c3,c3r4,c3q,c4,c5",
+    ap.add_argument("--steps", type=int, default=500)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--config", default="c5", choices=sorted(WORKLOAD_NAMES))
+    ap.add_argument("--others", default="c1,c2,c2a,c2cap,c3,c3r4,c3q",
                     help="comma list of extra workloads ('' for none)")
     ap.add_argument("--other-steps", type=int, default=100)
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-c4", action="store_true", help="skip the 4096-wide MLP's roofline block")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-barrier", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="report the eager launch loop only")
@@ -335,70 +439,77 @@ def main():
     tk.lib()
 
     log(f"[bench] workload {args.config}: compiling")
-    r = Runner(args.config, launch_mode=args.launch_mode)
-    log(f"[bench] {args.config}: stages={r.stats['n_stages']} grid={r.stats['grid_size']}; timing {args.steps} steps")
-    wall, ev_ms = r.time_steps(args.steps, args.warmup)
-    kms = r.kernel_ms()
-    eager_value = args.steps / wall
-    timing = "eager launch loop"
-    steps, value, ms_per_step = args.steps, eager_value, wall / args.steps * 1e3
+    r, m = measure(args.config, args.steps, args.warmup, args.launch_mode, stamps=True)
     graph = None
     if args.launch_mode == 1 and not args.no_graph:
         # the steady-state loop replayed from a captured graph, state fed back
         # through the in-place updates
-        n_rep = max(1, args.steps // len(r.inputs))
+        n_rep = max(1, min(args.steps, 200) // len(r.inputs))
         gsteps, gwall, gev = r.graph_time(n_rep)
         graph = {"steps_per_s": round(gsteps / gwall, 2), "ms_per_step": round(gwall / gsteps * 1e3, 5),
                  "steps": gsteps, "event_ms_per_step": round(gev / gsteps, 5)}
-        # reported beside the eager loop; the headline stays the eager loop
+    st = m["stats"]
     line = {
         "metric": "training steps/sec per program",
-        "value": round(value, 2),
+        "value": round(m["value"], 2),
         "unit": "steps/s",
         "n_gpus": 1,
-        "steps": steps,
+        "steps": m["steps"],
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 5),
+        "ms_per_step": round(m["ms_per_step"], 5),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": r.cfg.get("dtype", "bf16"),
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.config], "batch": r.cfg.get("batch"), "dims": r.cfg.get("dims"),
+        "config": {"workload": WORKLOAD_NAMES[args.config], "batch": r.cfg.get("batch"),
+                   "dims": r.cfg.get("dims"), "width": r.cfg.get("width"), "layers": r.cfg.get("layers"),
                    "lr": r.cfg.get("lr"), "parallelism": "single-gpu", "resident_batches": 4,
-                   "stages": r.stats["n_stages"], "grid_barriers": r.stats["grid_barriers"],
-                   "grid": r.stats["grid_size"],
+                   "stages": st["n_stages"], "grid_barriers": st["grid_barriers"], "grid": st["grid_size"],
                    "launch": "ordinary, co-resident grid" if args.launch_mode == 1 else "cooperative"},
-        "timing": timing,
-        "eager": {"steps_per_s": round(eager_value, 2), "ms_per_step": round(wall / args.steps * 1e3, 5),
-                  "event_ms_per_step": round(ev_ms / args.steps, 5)},
+        "timing": f"median of {len(m['batch_ms'])} event-timed batches of {m['steps_per_batch']} launches",
+        "batch_ms": m["batch_ms"],
+        "wall_steps_per_s": round(m["wall_steps_per_s"], 2),
         "graph_replay": graph,
-        "kernel_ms": round(kms, 5),
-        "roofline": roofline(args.config, r.cfg, r.prog, kms, traffic_for(args.config)),
+        "kernel_ms": round(m["kernel_ms"], 5),
+        "roofline": m["roofline"],
+        "stage_stamps": m["stage_stamps"],
     }
-    log(f"[bench] {args.config}: {value:.1f} steps/s, kernel {kms * 1e3:.1f} us")
+    log(f"[bench] {args.config}: {m['value']:.1f} steps/s, kernel {m['kernel_ms'] * 1e3:.1f} us")
+    r.close()
+    del r
+    torch.cuda.empty_cache()
     if not args.no_barrier:
         log("[bench] barrier microbenchmark")
         line["barrier"] = barrier_latency()
+    if not args.no_c4 and args.config != "c4":
+        log("[bench] 4096-wide MLP")
+        r4, m4 = measure("c4", args.other_steps, 10, args.launch_mode, stamps=True)
+        line["c4"] = {"workload": WORKLOAD_NAMES["c4"], "steps_per_s": round(m4["value"], 2),
+                      "ms_per_step": round(m4["ms_per_step"], 5), "batch_ms": m4["batch_ms"],
+                      "kernel_ms": round(m4["kernel_ms"], 5), "roofline": m4["roofline"],
+                      "stage_stamps": m4["stage_stamps"]}
+        r4.close()
+        del r4
+        torch.cuda.empty_cache()
     others = {}
     for name in [x for x in args.others.split(",") if x and x != args.config]:
         log(f"[bench] other workload {name}")
-        o = Runner(name, launch_mode=args.launch_mode)
-        w, _ = o.time_steps(args.other_steps, 10)
-        k = o.kernel_ms(20)
-        rf = roofline(name, o.cfg, o.prog, k, traffic_for(name))
-        others[WORKLOAD_NAMES[name]] = {"steps_per_s": round(args.other_steps / w, 2),
-                                       "ms_per_step": round(w / args.other_steps * 1e3, 4),
-                                       "kernel_ms": round(k, 4), "stages": o.stats["n_stages"],
+        o, mo = measure(name, args.other_steps, 10, args.launch_mode)
+        rf = mo["roofline"]
+        others[WORKLOAD_NAMES[name]] = {"steps_per_s": round(mo["value"], 2),
+                                       "ms_per_step": round(mo["ms_per_step"], 4),
+                                       "kernel_ms": round(mo["kernel_ms"], 4), "stages": mo["stats"]["n_stages"],
                                        "achieved": rf["achieved"], "unit": rf["unit"], "frac": rf["frac"]}
         log(f"[bench] {name}: {others[WORKLOAD_NAMES[name]]}")
+        o.close()
         del o
         torch.cuda.empty_cache()
     if others:
         line["others"] = others
     if not args.no_cpu:
         log("[bench] CPU oracle baseline")
-        line["cpu_baseline"] = cpu_baseline(args.config, args.cpu_seconds)
+        line["cpu_baseline"] = cpu_baseline(args.config)
     print(json.dumps(line), flush=True)
 
 
