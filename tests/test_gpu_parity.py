@@ -636,7 +636,7 @@ def test_race_modes_bit_identical(name):
             bufs.workspace[hdr:].fill_(0xFF)
             for o, sp in zip(bufs.outputs, base.outputs):
                 if not any(o.data_ptr() == t.data_ptr() for t in tins):
-                    o.view(torch.uint8).fill_(0xFF)
+                    o.reshape(-1).view(torch.uint8).fill_(0xFF)
         p.set_debug(stagger_seed=stagger)
         p.run_into(*tins, buffers=bufs)
         p.check_workspace(bufs.workspace)
