@@ -23,10 +23,8 @@ constexpr int kMaxDims = 4;         // iteration dims after collapsing
 constexpr int kMaxSlots = 3;        // saved values in the expression machine (LDS-resident)
 constexpr uint32_t kPlanLds = 16384;       // LDS bytes for the current stage's descriptors (every stage blob fits)
 constexpr uint32_t kMaxGrid = 1024;        // workgroups per launch (barrier flag slots)
-constexpr uint32_t kFlagStride = 16;       // u32 words between two workgroups' flags (64 B)
-constexpr uint32_t kHdrArrive = 16384;     // u32 [kMaxGrid * kFlagStride] arrival epochs
-constexpr uint32_t kHdrRelease = kHdrArrive + kMaxGrid * kFlagStride * 4;  // u32 release epochs
-constexpr uint32_t kHeaderBytes = kHdrRelease + kMaxGrid * kFlagStride * 4;  // 147456: header size
+constexpr uint32_t kHdrArrive = 16384;     // u32 [kMaxGrid] arrival epochs, one per workgroup
+constexpr uint32_t kHeaderBytes = kHdrArrive + kMaxGrid * 4;  // 20480: header size
 constexpr uint32_t kMaxTimedStages = 400;
 // The library's own per-device workspace for callers that cannot allocate
 // (tk_run_into_noalloc): header plus arena of at most this many bytes.
@@ -117,6 +115,21 @@ constexpr uint32_t F_COLDIRECT = 128u;  // column reduction whose source program
                                        //   column stride 1: rows are summed straight from memory, not in batches
 constexpr int kFastIns = 8;
 constexpr int kFastLoads = 3;
+// Register epilogues: the unit-stride loaded views of a tile are copied into
+// the top of the workgroup's LDS arena before the main loop starts, above the
+// operand ring (16 bytes per 8-element chunk and plane; an fp32 view takes
+// two planes).  Byte offsets within the arena:
+constexpr uint32_t kArenaBytes = 131072;     // the workgroup's LDS arena
+constexpr uint32_t kFastStage64 = 81920;     // 64x64 tiles (their operand ring ends at 64 KB)
+constexpr uint32_t kFastStage128 = 98304;    // 128x128 tiles (their operand ring ends at 96 KB)
+// A register epilogue's program is also encoded as one record per
+// instruction, two DIns slots each, at fin_first (fin_len = 2 * instructions):
+//   slot 0: the instruction itself; its pad field holds the byte offset / 16
+//           of the view's staged chunks in the arena (0xffff: not staged);
+//   slot 1: the instruction's view, resolved: op = src = 0, rnd = dtype,
+//           rev = column stride (0 or 1), arg = base slot, a = offset bits,
+//           s = row stride bits (32-bit element indices).
+constexpr uint16_t kFastNotStaged = 0xffff;
 
 struct DTask {
   uint8_t kind;

@@ -45,7 +45,6 @@ namespace {
 // takes the bottom, and the expression machine's third slot and its exchange
 // the top 48 KB.  Every other task uses the bottom 80 KB for staging or
 // scratch.
-constexpr int kArenaBytes = 131072;
 constexpr int kSmemBytes = 81920;        // staging / scratch region below the slots
 constexpr int kSlot2Off = kSmemBytes;    // machine slot 2
 constexpr int kXvOff = kSmemBytes + 16384;  // machine exchange: values (slot 0)
@@ -76,7 +75,7 @@ DEV LDS float* slot_base(uint32_t k) {
   return (LDS float*)(g_smem + (k == 0 ? kXvOff : k == 1 ? kXeOff : kSlot2Off));
 }
 static_assert(kSlot2Off + kVmElems * kBlock * 4 == kXvOff, "arena layout");
-static_assert(kXeOff + kVmElems * kBlock * 4 == kArenaBytes, "arena layout");
+static_assert(kXeOff + kVmElems * kBlock * 4 == (int)kArenaBytes, "arena layout");
 static_assert(128 * 132 * 4 <= kSmemBytes, "the largest C tile fits below the slots");
 
 // ------------------------------------------------------------ conversions --
@@ -1017,13 +1016,18 @@ DEV void direct_loop64(uint32_t tid, const DirectOp<64>& da, const DirectOp<64>&
 
 // BF16: operand dtype (bf16, else f16), a template parameter so the MFMA
 // accumulators never change registers between the two instruction forms.
-template <int BM, int BN, bool BF16, class AfterLoop>
+// before_loop() runs once the tile's coordinates are in `st`, before the
+// first operand load: its loads complete ahead of the ring's (loads retire in
+// issue order) and land in the arena above the ring.
+template <int BM, int BN, bool BF16, class BeforeLoop>
 DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st,
-                   AfterLoop after_loop) {
+                   BeforeLoop before_loop) {
   constexpr int FM = BM / 64, FN = BN / 64;  // 32x32 blocks per wave along m / n
   constexpr int S = BM == 128 ? 3 : 4;       // ring stages (S * (BM + BN) * 128 bytes <= the arena)
   constexpr int SA = BM * kBK * 2, SB = BN * kBK * 2;
-  static_assert(S * (SA + SB) <= kArenaBytes, "operand ring exceeds the arena");
+  static_assert(S * (SA + SB) <= (int)(BM == 128 ? kFastStage128 : kFastStage64),
+                "the operand ring overlaps the register epilogue's staged operands");
+  static_assert(BM * (BN + 4) * 4 <= S * (SA + SB), "the C tile exceeds the operand ring");
   const uint32_t tiles = t.tiles_m * t.tiles_n;
   const uint32_t split_index = item / tiles;
   const uint32_t tile = xcd_tile(item % tiles, tiles);
@@ -1035,6 +1039,7 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
   st.bm = BM;
   st.bn = BN;
   st.split_index = split_index;
+  before_loop();
   const uint32_t kbeg = split_index * t.kchunk;
   const uint32_t kend = (kbeg + t.kchunk < t.k) ? kbeg + t.kchunk : t.k;
   const VView A = load_view(views_off + t.va * sizeof(DView)), B = load_view(views_off + t.vb * sizeof(DView));
@@ -1098,8 +1103,6 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
       __syncthreads();
     }
   }
-  // the operand ring is drained: the arena above the C tile is free
-  after_loop();
   // accumulators -> LDS tile [BM][BN + 4]
   LDS float* C = (LDS float*)g_smem;
   const int pitch = BN + 4;
@@ -1833,40 +1836,19 @@ DEV void consume(uint32_t tid, const DTask& t, const Batch& b, uint32_t live, It
 // for loads).  Every thread owns G chunks (chunk g * kBlock + tid of the
 // tile: the whole tile in one pass) and carries their values in registers
 // through the program to the stores.
-//   * As soon as the main loop has drained its operand ring, every loaded
-//     view with column stride 1 is copied global -> LDS, each lane its own
-//     chunks, into the arena above the C tile (fast_prefetch): the loads are
-//     in flight while the accumulators are written out, and the program
-//     reads its operands from LDS.
-//   * The program is interpreted one instruction at a time from the LDS
-//     plan, so only the current instruction's fields occupy scalar registers
-//     (a decoded copy of the whole program does not fit them and spills).
+//   * Before the main loop's first operand load, every loaded view with
+//     column stride 1 is copied global -> LDS, each lane its own chunks, into
+//     the arena above the operand ring (fast_prefetch): the copies are in
+//     flight under the main loop, and the program reads its operands from LDS.
+//   * The program runs from host-encoded records, two 16-byte words per
+//     instruction (the instruction with its staged offset, and its view
+//     resolved to base, dtype, offset and strides), one instruction at a
+//     time: only the current record occupies scalar registers (a decoded copy
+//     of the whole program does not fit them and spills).
 // The arithmetic, its order and every rounding are vm_run's, so results are
 // identical bit for bit.  Hoisting every load before the first store is
 // safe for the programs the scheduler marks: no load reads bytes an earlier
 // store of the program may write.
-
-// A view operand of the epilogue, read from the LDS plan (wave-uniform).
-struct FView {
-  GLOBAL uint8_t* p;
-  int32_t off, s0, s1;
-  uint32_t dt;
-};
-
-DEV FView fast_view(const Ctx& ka, uint32_t views_off, uint32_t vi) {
-  const LDS uint8_t* v = (const LDS uint8_t*)g_plan + views_off + vi * sizeof(DView);
-  const u32x4 lo = *(const LDS u32x4*)v;               // offset, stride[0] (low words)
-  const uint32_t s1 = *(const LDS uint32_t*)(v + 16);  // stride[1] (low word)
-  const uint32_t bd = *(const LDS uint32_t*)(v + 40);  // base | dtype << 16
-  FView f;
-  f.off = (int32_t)uniform(lo[0]);
-  f.s0 = (int32_t)uniform(lo[2]);
-  f.s1 = (int32_t)uniform(s1);
-  const uint32_t w = uniform(bd);
-  f.p = base_ptr(ka, (w & 0xffff) < (uint32_t)kMaxBases ? (w & 0xffff) : 0u);
-  f.dt = (w >> 16) & 0xff;
-  return f;
-}
 
 // Output coordinates of this thread's G chunks.
 template <int G>
@@ -1890,46 +1872,70 @@ DEV void fast_chunks(uint32_t tid, const DTask& t, const ItemState& st, FastChun
   }
 }
 
-// Copy every unit-stride loaded view's chunks into LDS above the C tile, in
-// program order: a 16-bit view takes 16 bytes per chunk (chunk q at
-// off + 16 q), an fp32 view two such planes (elements 0-3, then 4-7).  Each
-// lane copies exactly the chunks its own thread reads later.  Returns false
-// (uniform) when a unit-stride view's base is not 16-byte aligned or the
-// views do not fit; the batches then run the epilogue.
+// One instruction of a register epilogue, from its record (plan.h): the
+// instruction and its view resolved (wave-uniform).
+struct FRec {
+  uint32_t w0;       // op | src << 8 | rnd << 16 | rev << 24
+  float a, s;
+  uint32_t staged;   // byte offset of the view's staged chunks in the arena, or 0
+  uint32_t base, dt, s1;
+  int32_t off, s0;
+};
+
+DEV u32x4 frec_word(uint32_t ins_off, uint32_t slot) {
+  return *(const LDS u32x4*)(g_plan + ins_off + slot * sizeof(DIns));
+}
+
+DEV FRec frec_decode(const u32x4& A, const u32x4& B) {
+  FRec r;
+  r.w0 = uniform(A[0]);
+  const uint32_t pad = uniform(A[1]) >> 16;
+  r.staged = pad == kFastNotStaged ? 0u : pad * 16u;
+  r.a = __uint_as_float(uniform(A[2]));
+  r.s = __uint_as_float(uniform(A[3]));
+  const uint32_t b0 = uniform(B[0]);
+  r.dt = (b0 >> 16) & 0xff;
+  r.s1 = b0 >> 24;
+  r.base = uniform(B[1]) & 0xffff;
+  r.off = (int32_t)uniform(B[2]);
+  r.s0 = (int32_t)uniform(B[3]);
+  return r;
+}
+
+// Copy the staged views' chunks (every loaded view with column stride 1)
+// into the arena, each lane its own chunks (chunk q at staged + 16 q; an fp32
+// view's second plane follows at + 16 * G * kBlock).  Issued before the main
+// loop, so the loads are in flight under it.  Returns false (uniform) when a
+// view's base is not 16-byte aligned: the batches then run the epilogue.
 template <int G>
-DEV bool fast_prefetch(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
-                       const ItemState& st) {
+DEV bool fast_prefetch(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, const ItemState& st) {
   FastChunks<G> c;
   fast_chunks<G>(tid, t, st, c);
   const uint32_t wave = uniform(tid / 64);
   const uint32_t lds = (uint32_t)(uintptr_t)(LDS uint8_t*)g_smem;
-  constexpr uint32_t kPlane = 16u * G * kBlock;  // bytes of one 16-byte-per-chunk plane
-  uint32_t off = kSmemBytes;
+  constexpr uint32_t kPlane = 16u * G * kBlock;
+  bool ok = true;
   for (uint32_t pc = 0; pc < t.expr_len; ++pc) {
-    const u32x4 w = *(const LDS u32x4*)(g_plan + ins_off + (t.expr_first + pc) * sizeof(DIns));
-    const uint32_t w0 = uniform(w[0]), w1 = uniform(w[1]);
-    const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff;
+    const FRec r = frec_decode(frec_word(ins_off, t.fin_first + 2 * pc), frec_word(ins_off, t.fin_first + 2 * pc + 1));
+    const uint32_t op = r.w0 & 0xff, src = (r.w0 >> 8) & 0xff;
     if (op != VM_STORE && src != SRC_VIEW) continue;
-    const FView v = fast_view(ka, views_off, w1 & 0xffff);
-    if (v.s1 == 1 && ((uintptr_t)v.p & 15) != 0) return false;
-    if (op == VM_STORE || v.s1 != 1) continue;
-    const uint32_t planes = v.dt == DT_F32 ? 2u : 1u;
-    if (off + planes * kPlane > (uint32_t)kArenaBytes) return false;
-    const uint32_t es = v.dt == DT_F32 ? 4u : 2u;
+    const GLOBAL uint8_t* p = base_ptr(ka, r.base < (uint32_t)kMaxBases ? r.base : 0u);
+    if (r.s1 == 1 && ((uintptr_t)p & 15) != 0) ok = false;
+    if (!r.staged || !ok) continue;
+    const uint32_t es = r.dt == DT_F32 ? 4u : 2u;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
-      const int32_t idx = c.ok[g] ? v.off + c.row[g] * v.s0 + c.col[g] : v.off;
-      const GLOBAL uint8_t* gp = v.p + (int64_t)idx * es;
-      const uint32_t m0 = lds + off + 16u * (uint32_t)(g * kBlock) + 1024u * wave;
+      const int32_t idx = c.ok[g] ? r.off + c.row[g] * r.s0 + c.col[g] : r.off;
+      const GLOBAL uint8_t* gp = p + (int64_t)idx * es;
+      const uint32_t m0 = lds + r.staged + 16u * (uint32_t)(g * kBlock) + 1024u * wave;
       asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp), "s"(m0) : "m0");
-      if (planes == 2) {
+      if (r.dt == DT_F32) {
         const GLOBAL uint8_t* gp2 = gp + 16;
         asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gp2), "s"(m0 + kPlane) : "m0");
       }
     }
-    off += planes * kPlane;
   }
-  return true;
+  return ok;
 }
 
 // One 8-wide chunk per index of a view with column stride s1 (1: 16-byte
@@ -2016,12 +2022,12 @@ DEV void fast_store(GLOBAL uint8_t* p, uint32_t dt, const int32_t (&idx)[G], con
   }
 }
 
-// Run the program over this thread's G chunks (fast_prefetch issued the
-// loads of its unit-stride views).
+// Run the program over this thread's G chunks (fast_prefetch staged the
+// loads of its unit-stride views).  The record of instruction pc + 1 is read
+// while instruction pc runs.
 template <int G>
-DEV void fast_run(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
-                  const ItemState& st) {
-  wait_vmcnt<0>();  // this lane's prefetched chunks have landed in LDS
+DEV void fast_run(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, const ItemState& st) {
+  wait_vmcnt<0>();  // this lane's staged chunks have landed in LDS
   asm volatile("" ::: "memory");
   constexpr uint32_t kPlane = 16u * G * kBlock;
   FastChunks<G> c;
@@ -2040,51 +2046,54 @@ DEV void fast_run(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_of
       y[g][4 + j] = __uint_as_float(hi[j]);
     }
   }
-  uint32_t off = kSmemBytes;  // next prefetched view (program order, as fast_prefetch)
+  const uint32_t n = t.expr_len;
+  FRec r = frec_decode(frec_word(ins_off, t.fin_first), frec_word(ins_off, t.fin_first + 1));
 #pragma nounroll
-  for (uint32_t pc = 0; pc < t.expr_len; ++pc) {
-    const u32x4 w = *(const LDS u32x4*)(g_plan + ins_off + (t.expr_first + pc) * sizeof(DIns));
-    const uint32_t w0 = uniform(w[0]), w1 = uniform(w[1]);
-    const float a = __uint_as_float(uniform(w[2])), sv = __uint_as_float(uniform(w[3]));
-    const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff, rnd = (w0 >> 16) & 0xff, rev = w0 >> 24;
+  for (uint32_t pc = 0; pc < n; ++pc) {
+    // the next record's words (clamped to the program), in flight while this one runs
+    const uint32_t nx = t.fin_first + 2 * (pc + 1 < n ? pc + 1 : pc);
+    const u32x4 nA = frec_word(ins_off, nx), nB = frec_word(ins_off, nx + 1);
+    const uint32_t op = r.w0 & 0xff, src = (r.w0 >> 8) & 0xff, rnd = (r.w0 >> 16) & 0xff, rev = r.w0 >> 24;
+    const float a = r.a;
     float x[G][8];
-    if (op == VM_STORE || src == SRC_VIEW) {
-      const FView v = fast_view(ka, views_off, w1 & 0xffff);
-      if (op == VM_STORE) {
-        int32_t idx[G];
+    if (op == VM_STORE) {
+      GLOBAL uint8_t* p = base_ptr(ka, r.base < (uint32_t)kMaxBases ? r.base : 0u);
+      int32_t idx[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) idx[g] = c.ok[g] ? v.off + c.row[g] * v.s0 + c.col[g] : v.off;
-        fast_store<G>(v.p, v.dt, idx, c.ok, y);
-        continue;
-      }
-      if (v.s1 == 1) {
-        const bool f32 = v.dt == DT_F32, bf = v.dt == DT_BF16;
+      for (int g = 0; g < G; ++g) idx[g] = c.ok[g] ? r.off + c.row[g] * r.s0 + c.col[g] : r.off;
+      fast_store<G>(p, r.dt, idx, c.ok, y);
+      r = frec_decode(nA, nB);
+      continue;
+    }
+    if (src == SRC_VIEW) {
+      if (r.staged) {
+        const bool f32 = r.dt == DT_F32, bf = r.dt == DT_BF16;
 #pragma unroll
         for (int g = 0; g < G; ++g) {
           const uint32_t q = (uint32_t)(g * kBlock) + tid;
-          const u32x4 r = *(const LDS u32x4*)(g_smem + off + 16u * q);
+          const u32x4 v = *(const LDS u32x4*)(g_smem + r.staged + 16u * q);
           if (f32) {
-            const u32x4 r2 = *(const LDS u32x4*)(g_smem + off + kPlane + 16u * q);
+            const u32x4 v2 = *(const LDS u32x4*)(g_smem + r.staged + kPlane + 16u * q);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              x[g][j] = __uint_as_float(r[j]);
-              x[g][4 + j] = __uint_as_float(r2[j]);
+              x[g][j] = __uint_as_float(v[j]);
+              x[g][4 + j] = __uint_as_float(v2[j]);
             }
           } else {
 #pragma unroll
-            for (int j = 0; j < 8; ++j) x[g][j] = half_bits_to_f32((j & 1) ? r[j / 2] >> 16 : r[j / 2] & 0xffffu, bf);
+            for (int j = 0; j < 8; ++j) x[g][j] = half_bits_to_f32((j & 1) ? v[j / 2] >> 16 : v[j / 2] & 0xffffu, bf);
           }
         }
-        off += (f32 ? 2u : 1u) * kPlane;
       } else {
         // column stride 0: one element per chunk, broadcast along the chunk
+        const GLOBAL uint8_t* p = base_ptr(ka, r.base < (uint32_t)kMaxBases ? r.base : 0u);
         int32_t idx[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) idx[g] = c.ok[g] ? v.off + c.row[g] * v.s0 : v.off;
-        fast_load<G>(v.p, v.dt, 0u, idx, x);
+        for (int g = 0; g < G; ++g) idx[g] = c.ok[g] ? r.off + c.row[g] * r.s0 : r.off;
+        fast_load<G>(p, r.dt, 0u, idx, x);
       }
     } else {
-      const float k = src == SRC_SCALAR ? sv : 0.0f;
+      const float k = src == SRC_SCALAR ? r.s : 0.0f;
 #pragma unroll
       for (int g = 0; g < G; ++g)
 #pragma unroll
@@ -2136,6 +2145,7 @@ DEV void fast_run(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_of
 #pragma unroll
         for (int j = 0; j < 8; ++j) y[g][j] = f16_bits_to_f32(f32_to_f16_bits(y[g][j]));
     }
+    r = frec_decode(nA, nB);
   }
 }
 
@@ -2246,42 +2256,47 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
     case T_GEMM_SIMT:
       gemm_simt(tid, ka, t, sd.off_views, item, st);
       __syncthreads();
-      if ((t.flags & F_FASTEPI) && fast_prefetch<2>(tid, ka, t, sd.off_views, sd.off_ins, st)) {
-        fast_run<2>(tid, ka, t, sd.off_views, sd.off_ins, st);
-        __syncthreads();  // the next item may overwrite the LDS tile and the prefetched operands
-        return;
+      if (t.flags & F_FASTEPI) {
+        if (fast_prefetch<2>(tid, ka, t, sd.off_ins, st)) {
+          fast_run<2>(tid, ka, t, sd.off_ins, st);
+          __syncthreads();  // the next item may overwrite the LDS tile and the prefetched operands
+          return;
+        }
+        wait_vmcnt<0>();  // staged loads may still be writing the slots the batches use
       }
       break;
     case T_GEMM_MFMA: {
       // the operand dtype is the A view's (both operands share it)
       const bool bf16 = uniform(((const LDS DView*)(g_plan + sd.off_views + t.va * sizeof(DView)))->dtype) == DT_BF16;
-      // a register epilogue's operands are prefetched as soon as the main loop ends
+      // a register epilogue's operands are fetched into LDS under the main loop
       bool fast = false;
-      auto after_loop = [&]() {
+      auto before_loop = [&]() {
         if (!(t.flags & F_FASTEPI)) return;
-        fast = t.tile == 0 ? fast_prefetch<8>(tid, ka, t, sd.off_views, sd.off_ins, st)
-                           : fast_prefetch<2>(tid, ka, t, sd.off_views, sd.off_ins, st);
+        fast = t.tile == 0 ? fast_prefetch<8>(tid, ka, t, sd.off_ins, st) : fast_prefetch<2>(tid, ka, t, sd.off_ins, st);
       };
       if (t.tile == 0) {
         if (bf16)
-          gemm_mfma<128, 128, true>(tid, ka, t, sd.off_views, item, st, after_loop);
+          gemm_mfma<128, 128, true>(tid, ka, t, sd.off_views, item, st, before_loop);
         else
-          gemm_mfma<128, 128, false>(tid, ka, t, sd.off_views, item, st, after_loop);
+          gemm_mfma<128, 128, false>(tid, ka, t, sd.off_views, item, st, before_loop);
       } else {
         if (bf16)
-          gemm_mfma<64, 64, true>(tid, ka, t, sd.off_views, item, st, after_loop);
+          gemm_mfma<64, 64, true>(tid, ka, t, sd.off_views, item, st, before_loop);
         else
-          gemm_mfma<64, 64, false>(tid, ka, t, sd.off_views, item, st, after_loop);
+          gemm_mfma<64, 64, false>(tid, ka, t, sd.off_views, item, st, before_loop);
       }
       __syncthreads();
       if (fast) {
         if (t.tile == 0)
-          fast_run<8>(tid, ka, t, sd.off_views, sd.off_ins, st);
+          fast_run<8>(tid, ka, t, sd.off_ins, st);
         else
-          fast_run<2>(tid, ka, t, sd.off_views, sd.off_ins, st);
+          fast_run<2>(tid, ka, t, sd.off_ins, st);
         __syncthreads();  // the next item may overwrite the LDS tile and the prefetched operands
         return;
       }
+      // a misaligned operand: the batches run the epilogue, over slots the
+      // staged loads may still be writing
+      if (t.flags & F_FASTEPI) wait_vmcnt<0>();
       break;
     }
     case T_GEMV_Q8:
@@ -2313,38 +2328,37 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
   __syncthreads();
 }
 
-// Grid barrier with per-workgroup flags.
+// Grid barrier: every workgroup gathers every arrival itself.
 //
 // Arrival: thread 0 of each workgroup releases its writes (agent-scope fence)
-// and stores the epoch into its own arrival flag (64-byte line).  Workgroup 0's
-// first wave polls all arrival flags (4 per lane, in flight together), then
-// writes every release flag.  Other workgroups poll only their own release
-// flag, so no line is contended by more than two agents.  Epochs grow
+// and stores the epoch into its own arrival flag (one u32 per workgroup, the
+// flags packed 16 to a 64-byte line).  Then the first wave of every workgroup
+// polls all arrival flags (4 per lane, in flight together) until each holds
+// at least the epoch, and acquires (agent-scope fence).  With no release flag
+// written by a gathering workgroup, the last arrival reaches every workgroup
+// after one store and one poll instead of two of each.  Epochs grow
 // monotonically across launches on a workspace (the base is kept in the
 // header), so flags never need resetting.  Every spin is bounded by the
 // deadline; a timeout sets the abort word, which every spinner also watches.
 // `pre` runs in every thread after this workgroup's release fence and before
-// its arrival: work that may stay in flight across the barrier (wave 0, which
-// runs the barrier's fences, issues no memory operation in it).
-// `post` runs in every thread right after this workgroup's arrival: work that
-// may stay in flight while the barrier completes and that must not delay the
-// arrival (wave 0's share of a weight prefetch, outside the gathering
-// workgroup).
+// its arrival: work that may stay in flight across the barrier (the first
+// wave, which runs the barrier's fences, issues no memory operation in it).
+// `post` runs in every thread right after the arrival: work that may stay in
+// flight while the barrier completes and must not delay the arrival (the
+// first wave's share of a weight prefetch, issued before it polls).
 template <class Pre, class Post>
 DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline, Pre pre, Post post) {
   __shared__ uint32_t s_ok;
   GLOBAL uint32_t* arrive = (GLOBAL uint32_t*)(ka.ws + kHdrArrive);
-  GLOBAL uint32_t* release = (GLOBAL uint32_t*)(ka.ws + kHdrRelease);
   GLOBAL uint32_t* abort = (GLOBAL uint32_t*)(ka.ws + kHdrAbort);
   const uint32_t G = gridDim.x, bid = blockIdx.x;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
   pre();
-  if (threadIdx.x == 0)
-    __hip_atomic_store(arrive + bid * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (threadIdx.x == 0) __hip_atomic_store(arrive + bid, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   post();
-  if (bid == 0 && threadIdx.x < 64) {
+  if (threadIdx.x < 64) {
     uint32_t ok = 1;
     const uint32_t lane = threadIdx.x;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -2355,7 +2369,7 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
       for (int i = 0; i < 4; ++i) {
         const uint32_t w = base + lane + 64 * i;
         live[i] = w < G;
-        f[i] = arrive + (live[i] ? w : 0) * kFlagStride;
+        f[i] = arrive + (live[i] ? w : 0);
       }
       for (;;) {
         bool done = true;
@@ -2365,7 +2379,7 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
             const uint32_t v = __hip_atomic_load(f[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             if ((int32_t)(v - epoch) < 0) done = false;
           }
-        if (done) break;
+        if (__all(done)) break;
         if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
           ok = 0;
           break;
@@ -2378,29 +2392,9 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
       }
       if (!ok) break;
     }
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "agent");
-    // release everyone (a timed-out master still releases: the abort word stops them)
-    for (uint32_t w = lane; w < G; w += 64)
-      __hip_atomic_store(release + w * kFlagStride, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const uint32_t all_ok = __builtin_amdgcn_readfirstlane(ok) & (uint32_t)__all(ok);
     if (lane == 0) s_ok = all_ok;
-  } else if (bid != 0 && threadIdx.x == 0) {
-    uint32_t ok = 1;
-    GLOBAL uint32_t* f = release + bid * kFlagStride;
-    const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
-    while ((int32_t)(__hip_atomic_load(f, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) - epoch) < 0) {
-      if (__hip_atomic_load(abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0u) {
-        ok = 0;
-        break;
-      }
-      if (__builtin_amdgcn_s_memrealtime() - t0 > deadline) {
-        set_abort(ka, stage);
-        ok = 0;
-        break;
-      }
-    }
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    s_ok = ok;
   }
   __syncthreads();
   return s_ok != 0;
@@ -2495,19 +2489,13 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
         while (nti + 1 < sd.n_tasks && first >= task_item_begin(nti + 1)) ++nti;
         const DTask nt = load_task(nti);
         will_pref = gemv_prefetchable(ka, nt, sd.off_views);
-        // Waves 1..3 issue their slots before the arrival.  Outside the
-        // gathering workgroup 0, wave 0 takes every fourth slot after its
-        // arrival (post); in workgroup 0 it gathers, and waves 1..3 take all.
+        // waves 1..3 issue their slots (every fourth) before the arrival,
+        // wave 0 its own after the arrival (post)
         const uint32_t wave = uniform(threadIdx.x / 64);
-        if (will_pref && wave != 0) {
-          if (blockIdx.x == 0)
-            gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin, wave - 1, 3);
-          else
-            gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin, wave, 4);
-        }
+        if (will_pref && wave != 0) gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin, wave, 4);
       };
       auto post = [&]() {
-        if (!will_pref || blockIdx.x == 0 || threadIdx.x >= 64) return;
+        if (!will_pref || threadIdx.x >= 64) return;
         const uint32_t first = blockIdx.x;
         uint32_t nti = 0;
         while (nti + 1 < sd.n_tasks && first >= task_item_begin(nti + 1)) ++nti;

@@ -1324,7 +1324,8 @@ struct Builder {
                                int tile) {
     if (n % 8 != 0 || m <= 0 || code.empty() || code.size() > (size_t)kFastIns) return false;
     int loads = 0;
-    const int64_t plane = 16 * (int64_t)tile * tile / 8, budget = 49152;
+    const int64_t plane = 16 * (int64_t)tile * tile / 8;
+    const int64_t budget = (int64_t)kArenaBytes - (tile == 128 ? kFastStage128 : kFastStage64);
     int64_t staged = 0;
     auto range = [&](const DView& v, int64_t& lo, int64_t& hi) {
       const int64_t es = dtype_size(v.dtype);
@@ -1370,6 +1371,37 @@ struct Builder {
       }
     }
     return true;
+  }
+
+  // The register epilogue's records (plan.h): for each committed
+  // instruction, the instruction (with its staged chunks' arena offset) and
+  // its view resolved to base, dtype, offset and strides.  Staged offsets are
+  // assigned in program order, as the kernel copies the views.
+  uint32_t fast_records(uint32_t code_first, uint32_t len, int tile) {
+    const uint32_t first = (uint32_t)ins.size();
+    const uint32_t plane = 16u * (uint32_t)tile * (uint32_t)tile / 8u;
+    uint32_t staged = tile == 128 ? kFastStage128 : kFastStage64;
+    for (uint32_t i = 0; i < len; ++i) {
+      DIns a = ins.at(code_first + i), b{};
+      a.pad = kFastNotStaged;
+      if (a.src == SRC_VIEW || a.op == VM_STORE) {
+        const DView& v = views.at(a.arg);
+        b.rnd = v.dtype;
+        b.rev = v.stride[1] == 1 ? 1 : 0;
+        b.arg = v.base;
+        const int32_t off = (int32_t)v.offset, s0 = (int32_t)v.stride[0];
+        std::memcpy(&b.a, &off, 4);
+        std::memcpy(&b.s, &s0, 4);
+        if (a.op != VM_STORE && v.stride[1] == 1) {
+          a.pad = (uint16_t)(staged / 16);
+          staged += (v.dtype == DT_F32 ? 2u : 1u) * plane;
+          if (staged > kArenaBytes) raise(TK_E_ARG, "internal: register epilogue operands exceed the arena");
+        }
+      }
+      ins.push_back(a);
+      ins.push_back(b);
+    }
+    return first;
   }
 
   uint32_t commit_code(std::vector<DIns>& code, uint32_t view_base) {
@@ -1847,9 +1879,13 @@ struct Builder {
     t.vs = (uint16_t)(vbase + (ops.size() > 2 ? 2 : 1));
     uint32_t vb = commit_views(cx);
     uint32_t code_first = commit_code(code, vb);
+    const int fast_tile = g.kind == T_GEMM_MFMA && g.tile == 0 ? 128 : 64;
     if ((g.kind == T_GEMM_MFMA || g.kind == T_GEMM_SIMT) && g.split <= 1 && O.fast_epilogue &&
-        fast_epilogue_ok(code, cx.vtab, m, n, g.kind == T_GEMM_MFMA && g.tile == 0 ? 128 : 64))
+        fast_epilogue_ok(code, cx.vtab, m, n, fast_tile)) {
       t.flags |= F_FASTEPI;
+      t.fin_first = fast_records(code_first, (uint32_t)code.size(), fast_tile);
+      t.fin_len = 2 * (uint32_t)code.size();
+    }
     std::string desc = mm.name + " (" + mm.opcode + " " + std::to_string(m) + "x" + std::to_string(k) + "x" +
                        std::to_string(n) + ")";
     if (t.flags & F_FASTEPI) desc += " [register epilogue]";
@@ -2254,7 +2290,7 @@ struct Builder {
           gd << "\n";
         };
         prog("code", task.expr_first, task.expr_len);
-        prog("finish", task.fin_first, task.fin_len);
+        if (!(task.flags & F_FASTEPI)) prog("finish", task.fin_first, task.fin_len);
       }
       DStage& d = e.d;
       d = DStage{};

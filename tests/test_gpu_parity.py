@@ -5,6 +5,7 @@ and ragged tails; pointwise-only work is compared bit for bit, contractions
 and reductions under the tolerance classes of tests/parity.py, whole steps
 per node with teacher forcing, and fused vs unfused schedules bitwise.
 """
+import re
 import sys
 
 import numpy as np
@@ -632,7 +633,8 @@ def test_race_modes_bit_identical(name):
         tins = [parity.to_torch(a.copy(), sp.dtype) for a, sp in zip(ins, base.inputs)]
         bufs = p.allocate(*tins)
         if poison:
-            hdr = 147456  # the header keeps its barrier state; the arena gets NaN bytes
+            # the header keeps its barrier state; the arena gets NaN bytes
+            hdr = int(re.search(r"workspace: (\d+) header", p.dump()).group(1))
             bufs.workspace[hdr:].fill_(0xFF)
             for o, sp in zip(bufs.outputs, base.outputs):
                 if not any(o.data_ptr() == t.data_ptr() for t in tins):
