@@ -497,19 +497,56 @@ struct Builder {
     }
   }
 
-  // Input buffers reachable from a view through inlined producers.
-  std::set<std::string> raw_inputs(const Spec& s) const {
-    if (is_input(s.buf)) return {s.buf};
-    if (inlined_bufs.count(s.buf)) {
-      std::set<std::string> r;
-      for (auto& a : op(prod(s.buf)).args)
-        if (!a.scalar) {
-          auto q = raw_inputs(a.spec);
-          r.insert(q.begin(), q.end());
+  // Which caller inputs a value's elements are computed from, through the
+  // producers inlined into its readers, and whether element i of the value
+  // depends on each such input only through its element i.  Filled once the
+  // inlining is fixed (producers precede their users in program order).
+  struct InputUse {
+    std::map<std::string, bool> aligned;  // input -> read element for element on every path
+  };
+  std::map<std::string, InputUse> input_use;
+
+  void build_input_use() {
+    input_use.clear();
+    for (auto& in : P.inputs) input_use[in.buf].aligned[in.buf] = true;
+    for (int j = 0; j < (int)P.ops.size(); ++j) {
+      const Op& o2 = op(j);
+      if (!inlined_bufs.count(o2.out.buf)) continue;
+      InputUse u;
+      for (auto& a : o2.args) {
+        if (a.scalar) continue;
+        auto it = input_use.find(a.spec.buf);
+        if (it == input_use.end()) continue;  // a materialised value: no input behind it
+        const bool hop = identity_view(a.spec, o2.out.shape);
+        for (auto& kv : it->second.aligned) {
+          auto ins = u.aligned.emplace(kv.first, true).first;
+          ins->second = ins->second && hop && kv.second;
         }
-      return r;
+      }
+      input_use[o2.out.buf] = u;
     }
-    return {};
+  }
+  // Whether reading view s reads any element of input buffer target.
+  bool reads_input(const Spec& s, const std::string& target) const {
+    auto it = input_use.find(s.buf);
+    return it != input_use.end() && it->second.aligned.count(target) != 0;
+  }
+  // Caller inputs read through view s.
+  std::set<std::string> inputs_read(const Spec& s) const {
+    std::set<std::string> r;
+    auto it = input_use.find(s.buf);
+    if (it != input_use.end())
+      for (auto& kv : it->second.aligned) r.insert(kv.first);
+    return r;
+  }
+  // Whether every read of target through view s, evaluated at element i of an
+  // iteration space of the given shape, reads the target's element i: the view
+  // and every inlined step below it are whole, contiguous and of that shape.
+  bool reads_aligned(const Spec& s, const std::string& target, const std::vector<int64_t>& shape) const {
+    if (!reads_input(s, target)) return true;
+    if (!identity_view(s, shape)) return false;
+    if (s.buf == target) return true;
+    return op(prod(s.buf)).out.shape == shape && input_use.at(s.buf).aligned.at(target);
   }
   // Materialized values reachable from a view through inlined producers.
   void root_values(const Spec& s, std::vector<std::string>& out) const {
@@ -521,15 +558,6 @@ struct Builder {
     }
     out.push_back(s.buf);
   }
-  bool identity_access(const Spec& s, const std::string& target, const std::vector<int64_t>& shape) const {
-    if (!raw_inputs(s).count(target)) return true;
-    if (s.shape != shape || s.offset != 0 || !s.contiguous()) return false;
-    if (s.buf == target) return true;
-    for (auto& a : op(prod(s.buf)).args)
-      if (!a.scalar && !identity_access(a.spec, target, shape)) return false;
-    return true;
-  }
-
   // Ops (by program index) and their operands as read by an entry.
   std::vector<const Arg*> entry_args(const Entry& e) const {
     std::vector<const Arg*> r;
@@ -640,60 +668,85 @@ struct Builder {
   }
 
   // ----------------------------------------------- direct in-place proof --
+  // An in-place output may be written straight into its target input T when
+  // no read of T's old contents can observe the new ones.  The reads of T that
+  // the write cannot disturb are
+  //   (1) reads by entries that finish before the writing entry starts (the
+  //       leveling puts every such reader at an earlier stage), and
+  //   (2) reads inside the writing entry of element i, made by the thread that
+  //       computes element i, before it stores element i.
+  // The checks below establish exactly that and nothing stronger.
+
+  // Index of the entry that stores value v, or -1.
+  int entry_writing(const std::string& v) const {
+    int who = -1;
+    for (size_t i = 0; i < sched.size(); ++i)
+      for (auto& w : written(sched[i]))
+        if (w == v) who = (int)i;
+    return who;
+  }
+  // Whether entry i reads any element of input T (through its operands).
+  bool entry_reads_input(int i, const std::string& T) const {
+    for (auto* a : entry_args(sched[i]))
+      if (!a->scalar && reads_input(a->spec, T)) return true;
+    return false;
+  }
+
+  // (2) for a plain pointwise entry: every operand reads T element for
+  // element over the output's shape.
+  bool plain_reads_in_step(const Entry& e, const std::string& T, const std::vector<int64_t>& shape) const {
+    for (auto& a : op(e.op).args)
+      if (!a.scalar && !reads_aligned(a.spec, T, shape)) return false;
+    return true;
+  }
+  // (2) for a contraction tile whose side op `wop` stores the new T: the
+  // contraction's operands (read across rows and columns) never touch T, and
+  // every side op reading T reads it element for element and runs no later
+  // than `wop` in the tile's per-element program.
+  bool tile_reads_in_step(const Entry& e, int wop, const std::string& T, const std::vector<int64_t>& shape) const {
+    for (auto& a : op(e.op).args)
+      if (!a.scalar && reads_input(a.spec, T)) return false;
+    const SidePlan sp = plan_side(e, inlined_bufs);
+    for (int c : e.side)
+      for (auto& a : op(c).args) {
+        if (a.scalar || !reads_input(a.spec, T)) continue;
+        if (!reads_aligned(a.spec, T, shape) || sp.pos.at(c) > sp.pos.at(wop)) return false;
+      }
+    return true;
+  }
+  // (1): no entry after the writer reads T, and no entry before it that
+  // reads T needs the writer's values (it could not then run first).
+  bool other_reads_precede(int owner, const std::string& T, bool check_deps) const {
+    for (size_t i = 0; i < sched.size(); ++i) {
+      if ((int)i == owner || !entry_reads_input((int)i, T)) continue;
+      if ((int)i > owner) return false;
+      if (check_deps && depends_on((int)i, owner)) return false;
+    }
+    return true;
+  }
+
   void prove_direct() {
     for (auto& kv : P.inplace) {
-      int slot = kv.first, tidx = kv.second;
+      const int slot = kv.first, tidx = kv.second;
       const Spec& out = P.outputs[slot];
-      const std::string& target = P.inputs[tidx].buf;
-      int owner = -1;
-      for (size_t i = 0; i < sched.size(); ++i)
-        for (auto& w : written(sched[i]))
-          if (w == out.buf) owner = (int)i;
-      if (owner < 0) continue;
+      const std::string& T = P.inputs[tidx].buf;
+      // the new value is returned once, through a whole contiguous view, and
+      // the old one is not returned at all
+      if (output_count[out.buf] != 1 || out.offset != 0 || !out.contiguous()) continue;
+      if (output_bufs.count(T)) continue;
+      const int owner = entry_writing(out.buf);
+      if (owner < 0 || sched[owner].kind != 0) continue;
       const Entry& e = sched[owner];
-      if (e.kind != 0) continue;
-      const bool plain = op(e.op).cls == OC_POINTWISE && e.chain.empty() && e.side.empty();
-      int writer_op = -1;
-      for (int c : e.side)
-        if (op(c).out.buf == out.buf) writer_op = c;
-      if (!plain && writer_op < 0) continue;
-      if (output_count[out.buf] != 1) continue;
-      if (out.offset != 0 || !out.contiguous()) continue;
-      bool named = false;
-      for (auto& o2 : P.outputs)
-        if (o2.buf == target) named = true;
-      if (named) continue;
-      bool later = false;
-      for (size_t i = owner + 1; i < sched.size(); ++i)
-        for (auto* a : entry_args(sched[i]))
-          if (!a->scalar && raw_inputs(a->spec).count(target)) later = true;
-      if (later) continue;
-      bool ident = true;
-      if (plain) {
-        for (auto& a : op(e.op).args)
-          if (!a.scalar && !identity_access(a.spec, target, out.shape)) ident = false;
+      bool ok;
+      if (op(e.op).cls == OC_POINTWISE && e.chain.empty() && e.side.empty()) {
+        ok = plain_reads_in_step(e, T, out.shape) && other_reads_precede(owner, T, false);
       } else {
-        // The root's own operands never see the target; side ops read it
-        // element for element, and none after the one that overwrites it.
-        for (auto& a : op(e.op).args)
-          if (!a.scalar && raw_inputs(a.spec).count(target)) ident = false;
-        const SidePlan sp = plan_side(e, inlined_bufs);
+        int wop = -1;
         for (int c : e.side)
-          for (auto& a : op(c).args) {
-            if (a.scalar || !raw_inputs(a.spec).count(target)) continue;
-            if (!identity_access(a.spec, target, out.shape) || sp.pos.at(c) > sp.pos.at(writer_op)) ident = false;
-          }
-        // and no earlier reader of the target waits for this entry's values
-        for (size_t i = 0; ident && i < sched.size(); ++i) {
-          if ((int)i == owner) continue;
-          bool reads = false;
-          for (auto* a : entry_args(sched[i]))
-            if (!a->scalar && raw_inputs(a->spec).count(target)) reads = true;
-          if (reads && depends_on((int)i, owner)) ident = false;
-        }
+          if (op(c).out.buf == out.buf) wop = c;
+        ok = wop >= 0 && tile_reads_in_step(e, wop, T, out.shape) && other_reads_precede(owner, T, true);
       }
-      if (!ident) continue;
-      direct[slot] = tidx;
+      if (ok) direct[slot] = tidx;
     }
   }
 
@@ -739,7 +792,7 @@ struct Builder {
       }
       // the tile must read nothing of the target
       for (auto& a : op(mj).args)
-        if (!a.scalar && raw_inputs(a.spec).count(target)) ok = false;
+        if (!a.scalar && reads_input(a.spec, target)) ok = false;
       if (!ok) continue;
       // The fused tile takes the update's place in program order (after every
       // reader of the target), so ordering constraints stay acyclic.
@@ -754,25 +807,36 @@ struct Builder {
   }
 
   // ---------------------------------------------------------- bindings --
+  // A stored value can be written straight into a caller's output buffer
+  // when that output is exactly the value's own layout (same dtype and
+  // element count, offset 0, contiguous): the value then needs no arena space
+  // and no copy task.  Each value takes the first such output slot; every
+  // other output of it gets a copy (add_copies_and_commits).  An in-place
+  // output not proven direct never binds: its value goes to the arena and a
+  // staged commit copies it into the target.
+  static bool same_layout(const Spec& out, const Spec& value) {
+    return out.dtype == value.dtype && out.offset == 0 && out.numel() == value.numel() && out.contiguous();
+  }
+
   void bind_outputs() {
-    std::map<std::string, const Entry*> writer;
+    std::set<std::string> stored;
     for (auto& e : sched)
-      for (auto& w : written(e)) writer[w] = &e;
+      for (auto& w : written(e)) stored.insert(w);
     for (int s = 0; s < n_out; ++s) {
-      if (P.inplace.count(s) && !direct.count(s)) continue;
       const Spec& o2 = P.outputs[s];
-      auto it = writer.find(o2.buf);
-      if (it == writer.end()) continue;
-      const Spec& pv = op(prod(o2.buf)).out;
-      if (pv.dtype == o2.dtype && o2.offset == 0 && o2.numel() == pv.numel() && o2.contiguous() &&
-          !bound.count(o2.buf))
-        bound[o2.buf] = s;
+      const bool staged = P.inplace.count(s) && !direct.count(s);
+      if (staged || !stored.count(o2.buf) || bound.count(o2.buf)) continue;
+      if (same_layout(o2, op(prod(o2.buf)).out)) bound[o2.buf] = s;
     }
-    // every returned side-epilogue value must be bound (pass 2 checked bindability)
+    // Side-epilogue values are computed inside a contraction tile and have no
+    // arena slot of their own; pass 2 only fuses a returned one when it can be
+    // bound, so an unbound one here is a scheduler bug.
     for (auto& e : sched)
-      for (int c : e.side)
-        if (output_bufs.count(op(c).out.buf) && !aliased.count(op(c).out.buf) && !bound.count(op(c).out.buf))
+      for (int c : e.side) {
+        const std::string& v = op(c).out.buf;
+        if (output_bufs.count(v) && !aliased.count(v) && !bound.count(v))
           raise(TK_E_UNSUPPORTED, "internal: side epilogue without a direct output binding");
+      }
   }
 
   // ---------------------------------------------------------- leveling --
@@ -806,7 +870,7 @@ struct Builder {
         for (auto* a : entry_args(e)) {
           if (a->scalar || internal.count(a->spec.buf)) continue;
           root_values(a->spec, e.reads_vals);
-          auto r = raw_inputs(a->spec);
+          auto r = inputs_read(a->spec);
           e.reads_inputs.insert(r.begin(), r.end());
         }
         for (auto& w : written(e)) e.writes_vals.insert(w);
@@ -2169,6 +2233,7 @@ struct Builder {
       pass2();
     }
     choose_inline();
+    build_input_use();
     build_schedule();
     prove_direct();
     pass3();
