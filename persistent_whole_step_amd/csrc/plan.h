@@ -103,8 +103,6 @@ constexpr uint32_t F_MEAN = 1u;        // divide the sum by `count`
 constexpr uint32_t F_PARTIAL = 2u;     // write fp32 partials to scratch instead of finishing
 constexpr uint32_t kGemvRows = 4;      // int8-weight products: activation rows per work item (a slab)
 constexpr uint32_t F_ROWWG = 4u;       // combine: one workgroup per output, parts summed across its threads
-constexpr uint32_t F_QPREFETCH = 16u;  // one-row int8 GEMV whose weight and scales no stage writes: their
-                                       //   loads may start before the grid barrier that precedes the stage
 constexpr uint32_t F_XQ = 32u;         // int8 GEMV: quantise the activation rows to Q8_0 (blocks of 32,
                                        //   d = amax/127, codes round(x/d)) and multiply codes by codes
 constexpr uint32_t F_FASTEPI = 64u;    // contraction tile: the epilogue runs as a register program (at most

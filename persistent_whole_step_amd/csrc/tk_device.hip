@@ -1132,55 +1132,11 @@ DEV float wave_sum(float v) {
 
 constexpr uint32_t kGemvRed = kSmemBytes - 64 * kGemvRows;  // byte offset of the [rows][16] output sums
 
-// Cross-stage weight prefetch for the one-row GEMV (tasks marked F_QPREFETCH:
-// weight and scales are program inputs no stage writes).  While the grid
-// barrier before its stage completes, a workgroup copies the int8 weight
-// chunks of its first item into LDS [0, 64 KB) and the block scales into the
-// index-exchange region, so the weight stream overlaps the barrier.  Slot
-// qs = (wave * 4 + row) * 4 + chunk holds what lane l of `wave` needs for that
-// row and chunk.  Waves 1..3 issue their direct-to-LDS loads before the
-// workgroup arrives (wave 0 runs the barrier's fences, which would otherwise
-// wait for them); wave 0 adds its share after the arrival, except in the
-// workgroup that gathers the arrivals.
-constexpr uint32_t kPrefQ = 0;        // 64 slots x 64 lanes x 16 B
-constexpr uint32_t kPrefS = kXeOff;   // 64 slots x 64 lanes x 4 B
-constexpr uint32_t kPrefX = kXvOff;   // the activation row, staged as floats (K <= 4096)
-
-DEV bool gemv_prefetchable(const Ctx& ka, const DTask& t, uint32_t views_off) {
-  if (t.kind != T_GEMV_Q8 || !(t.flags & F_QPREFETCH) || t.m != 1 || t.k > 4096 || t.k % 16 != 0) return false;
-  const VView Q = load_view(views_off + t.vb * sizeof(DView));
-  const GLOBAL int8_t* pq = (const GLOBAL int8_t*)base_ptr(ka, Q.base);
-  return Q.stride[1] == 1 && (Q.offset & 15) == 0 && (Q.stride[0] & 15) == 0 && aligned16(pq);
-}
-
-// The calling wave issues slots q0, q0 + qstep, ... (wave-uniform).
-DEV void gemv_prefetch(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, uint32_t q0,
-                       uint32_t qstep) {
-  const uint32_t lane = tid % 64;
-  const VView Q = load_view(views_off + t.vb * sizeof(DView)), S = load_view(views_off + t.vs * sizeof(DView));
-  const GLOBAL int8_t* pq = (const GLOBAL int8_t*)base_ptr(ka, Q.base);
-  const GLOBAL float* ps = (const GLOBAL float*)base_ptr(ka, S.base);
-  const uint32_t K = t.k;
-  const uint32_t lds = (uint32_t)(uintptr_t)(LDS uint8_t*)g_smem;
-  for (uint32_t qs = q0; qs < 64; qs += qstep) {
-    const uint32_t cw = qs / 16, i = (qs / 4) % 4, j = qs % 4;
-    const uint32_t row0 = item * 16 + cw * 4 + i;
-    const uint32_t row = row0 < t.n ? row0 : 0;
-    const uint32_t kc0 = 1024 * j + lane * 16;
-    const uint32_t kc = kc0 < K ? kc0 : 0;
-    const GLOBAL int8_t* gq = pq + Q.offset + (int64_t)row * Q.stride[0] + kc;
-    const GLOBAL float* gs = ps + S.offset + (int64_t)row * S.stride[0] + (int64_t)(kc / 32) * S.stride[1];
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(gq), "s"(lds + kPrefQ + qs * 1024) : "m0");
-    asm volatile("s_mov_b32 m0, %1\n\tglobal_load_lds_dword %0, off" ::"v"(gs), "s"(lds + kPrefS + qs * 256) : "m0");
-  }
-}
-
 // Split-K GEMV slab: output columns cb*16 .. +16 (rows of the int8 weight q,
 // four per wave) for activation rows r0 .. r0+R-1.  Each lane takes 16-wide
 // K chunks; the weight chunks are loaded once and serve all R rows.
 template <int R>
-DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t cb, uint32_t r0,
-                      bool pref) {
+DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t cb, uint32_t r0) {
   const VView X = load_view(views_off + t.va * sizeof(DView)), Q = load_view(views_off + t.vb * sizeof(DView)),
               S = load_view(views_off + t.vs * sizeof(DView));
   const GLOBAL uint8_t* px = base_ptr(ka, X.base);
@@ -1188,9 +1144,7 @@ DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t view
   const GLOBAL float* ps = (const GLOBAL float*)base_ptr(ka, S.base);
   const int wave = tid / 64, lane = tid % 64;
   const uint32_t K = t.k;
-  // [R][K] activations; with prefetched weights occupying [0, 64 KB) the one
-  // row goes to the value-exchange region
-  LDS float* xs = (LDS float*)(g_smem + (pref ? kPrefX : 0));
+  LDS float* xs = (LDS float*)g_smem;  // [R][K] activations, when staged
   // A contiguous, 16-byte aligned bf16 row is read straight into registers
   // (each lane needs only its own 64 values): no staging, and none of the
   // bank conflicts of lane-strided LDS reads.
@@ -1224,19 +1178,7 @@ DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t view
         okm |= (row < t.n && kc < K ? 1u : 0u) << (i * NC + j);
       }
     }
-    if (pref) {
-      // every lane's prefetch has landed, and every wave sees every slot
-      wait_vmcnt<0>();
-      __syncthreads();
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < NC; ++j) {
-          const uint32_t qs = (wave * 4 + i) * 4 + j;
-          qv[i][j] = *(const LDS u32x4*)(g_smem + kPrefQ + qs * 1024 + lane * 16);
-          sv[i][j] = *(const LDS float*)(g_smem + kPrefS + qs * 256 + lane * 4);
-        }
-    } else if (fast) {
+    if (fast) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const uint32_t row = row0 + i < t.n ? row0 + i : 0;
@@ -1420,14 +1362,14 @@ DEV void gemv_q8_rows(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t view
 
 // Work item = slab * tiles_n + column block; a slab is kGemvRows activation
 // rows (the last may be shorter).
-DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, bool pref) {
+DEV void gemv_q8(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item) {
   const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
   const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
   switch (rows) {
-    case 1: gemv_q8_rows<1>(tid, ka, t, views_off, cb, r0, pref); break;
-    case 2: gemv_q8_rows<2>(tid, ka, t, views_off, cb, r0, false); break;
-    case 3: gemv_q8_rows<3>(tid, ka, t, views_off, cb, r0, false); break;
-    default: gemv_q8_rows<4>(tid, ka, t, views_off, cb, r0, false); break;
+    case 1: gemv_q8_rows<1>(tid, ka, t, views_off, cb, r0); break;
+    case 2: gemv_q8_rows<2>(tid, ka, t, views_off, cb, r0); break;
+    case 3: gemv_q8_rows<3>(tid, ka, t, views_off, cb, r0); break;
+    default: gemv_q8_rows<4>(tid, ka, t, views_off, cb, r0); break;
   }
 }
 
@@ -2239,7 +2181,7 @@ DEV DStage load_stage(const GLOBAL uint8_t* stages, uint32_t s) {
 }
 
 // One work item: prologue, then batches through the machine.
-DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item, bool pref) {
+DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item) {
   // The thread index passes through an empty asm once per item, so values
   // derived from it (LDS addresses, tile offsets) are computed per item
   // instead of being hoisted out of the stage loop and held in registers
@@ -2300,7 +2242,7 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
       break;
     }
     case T_GEMV_Q8:
-      gemv_q8(tid, ka, t, sd.off_views, item, pref);
+      gemv_q8(tid, ka, t, sd.off_views, item);
       gemv_epilogue(tid, ka, t, sd.off_views, sd.off_ins, item);
       __syncthreads();  // the next item may overwrite the row sums and the slots
       return;
@@ -2340,24 +2282,17 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
 // monotonically across launches on a workspace (the base is kept in the
 // header), so flags never need resetting.  Every spin is bounded by the
 // deadline; a timeout sets the abort word, which every spinner also watches.
-// `pre` runs in every thread after this workgroup's release fence and before
-// its arrival: work that may stay in flight across the barrier (the first
-// wave, which runs the barrier's fences, issues no memory operation in it).
-// `post` runs in every thread right after the arrival: work that may stay in
-// flight while the barrier completes and must not delay the arrival (the
-// first wave's share of a weight prefetch, issued before it polls).
-template <class Pre, class Post>
-DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline, Pre pre, Post post) {
+DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline) {
   __shared__ uint32_t s_ok;
   GLOBAL uint32_t* arrive = (GLOBAL uint32_t*)(ka.ws + kHdrArrive);
   GLOBAL uint32_t* abort = (GLOBAL uint32_t*)(ka.ws + kHdrAbort);
   const uint32_t G = gridDim.x, bid = blockIdx.x;
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
-  pre();
-  if (threadIdx.x == 0) __hip_atomic_store(arrive + bid, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  post();
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+    __hip_atomic_store(arrive + bid, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
   if (threadIdx.x < 64) {
     uint32_t ok = 1;
     const uint32_t lane = threadIdx.x;
@@ -2454,7 +2389,6 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
   if ((ka.flags & K_TIMESTAMPS) && blockIdx.x == 0 && threadIdx.x == 0)
     ((GLOBAL uint64_t*)(ka.ws + kHdrStamps))[0] = __builtin_amdgcn_s_memrealtime();
   trace_stamp(ka, 0xffffffffu);
-  bool pref = false;  // this stage's first item of the workgroup had its weights prefetched
   for (uint32_t s = 0; s < n_stages; ++s) {
     uint32_t ti = 0;
     for (uint32_t item = blockIdx.x; item < sd.n_items; item += gridDim.x) {
@@ -2465,10 +2399,9 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
         for (uint32_t i = 0; i < n; ++i) __builtin_amdgcn_s_sleep(8);
       }
       trace_stamp(ka, 0x1000 + s);
-      run_item(ka, t, sd, item - t.item_begin, pref && item == blockIdx.x);
+      run_item(ka, t, sd, item - t.item_begin);
       trace_stamp(ka, 0x2000 + s);
     }
-    pref = false;
     if (s + 1 < n_stages) {
       const bool stamp = (ka.flags & K_TIMESTAMPS) && blockIdx.x == 0 && threadIdx.x == 0 && s < kMaxTimedStages;
       GLOBAL uint64_t* stamps = (GLOBAL uint64_t*)(ka.ws + kHdrStamps) + 4 * s;
@@ -2478,35 +2411,9 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
       sd = load_stage(stages, s + 1);
       stage_blob_to_lds(ka.plan, sd);
       if (stamp) stamps[2] = __builtin_amdgcn_s_memrealtime();
-      // the next stage's first item of this workgroup may prefetch its weights
-      // (decided inside the barrier, once the staged descriptors are visible
-      // to every thread)
-      bool will_pref = false;
-      auto pre = [&]() {
-        const uint32_t first = blockIdx.x;
-        if (first >= sd.n_items) return;
-        uint32_t nti = 0;
-        while (nti + 1 < sd.n_tasks && first >= task_item_begin(nti + 1)) ++nti;
-        const DTask nt = load_task(nti);
-        will_pref = gemv_prefetchable(ka, nt, sd.off_views);
-        // waves 1..3 issue their slots (every fourth) before the arrival,
-        // wave 0 its own after the arrival (post)
-        const uint32_t wave = uniform(threadIdx.x / 64);
-        if (will_pref && wave != 0) gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin, wave, 4);
-      };
-      auto post = [&]() {
-        if (!will_pref || threadIdx.x >= 64) return;
-        const uint32_t first = blockIdx.x;
-        uint32_t nti = 0;
-        while (nti + 1 < sd.n_tasks && first >= task_item_begin(nti + 1)) ++nti;
-        const DTask nt = load_task(nti);
-        gemv_prefetch(threadIdx.x, ka, nt, sd.off_views, first - nt.item_begin, 0, 4);
-      };
-      if (!grid_barrier(ka, epoch0 + s + 1, s, deadline, pre, post)) {
-        wait_vmcnt<0>();  // no prefetch may still be writing LDS when the workgroup ends
+      if (!grid_barrier(ka, epoch0 + s + 1, s, deadline)) {
         return;
       }
-      pref = will_pref;
       if (stamp) stamps[3] = __builtin_amdgcn_s_memrealtime();
       if (stamp && s + 1 < kMaxTimedStages) stamps[4] = stamps[3];
     }

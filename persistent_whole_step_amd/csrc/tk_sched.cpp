@@ -1922,15 +1922,6 @@ struct Builder {
       ops.push_back(operand_view(A, 0, 1));       // x over (row, k)
       ops.push_back(operand_view(B, 0, 1));       // q over (n, k)
       ops.push_back(operand_view(mm.S(), 0, 1));  // s over (n, block)
-      // weight and scales that are inputs no in-place output overwrites may
-      // be fetched before the barrier that precedes this stage
-      bool stable = true;
-      for (const std::string& b : {B.buf, mm.S().buf}) {
-        if (!is_input(b)) stable = false;
-        for (auto& kv : P.inplace)
-          if (P.inputs[kv.second].buf == b) stable = false;
-      }
-      if (stable && m == 1 && k <= 4096) t.flags |= F_QPREFETCH;
       if (mm.attrs.count("xq") && mm.attrs.at("xq") != 0.0f) t.flags |= F_XQ;
     } else {
       ops.push_back(operand_view(A, 0, 1));  // A over (m, k)
@@ -1953,7 +1944,6 @@ struct Builder {
     std::string desc = mm.name + " (" + mm.opcode + " " + std::to_string(m) + "x" + std::to_string(k) + "x" +
                        std::to_string(n) + ")";
     if (t.flags & F_FASTEPI) desc += " [register epilogue]";
-    if (t.flags & F_QPREFETCH) desc += " [weights fetched across the barrier]";
     if (t.flags & F_XQ) desc += " [activations quantised to Q8_0]";
     if (!e.chain.empty()) {
       desc += e.update ? " +update" : " +epilogue";

@@ -100,15 +100,21 @@ def _gemv_program(scale_kind: str):
     return p
 
 
-@pytest.mark.parametrize("kind,tagged", [("input", 2), ("computed", 1), ("updated", 0)])
-def test_gemv_weight_prefetch_only_for_stable_inputs(kind, tagged):
-    # weights and scales that are inputs nothing overwrites may be fetched
-    # before the barrier; a computed or in-place-updated scale may not
+@pytest.mark.parametrize("kind", ["input", "computed", "updated"])
+def test_gemv_scale_sources(kind):
+    # scales that are inputs, computed values or updated in place all plan as
+    # two int8 products; an in-place update of the scales waits for them
     p = _gemv_program(kind)
     if kind == "input":
         p.output(p.op("addmm_q8", [p.inputs[3], p.inputs[0], p.inputs[1], p.inputs[2]], "bf16", (1, 64)))
-    d = tk.compile(p.text(), device=-1).dump()
-    assert d.count("[weights fetched across the barrier]") == tagged
+    prog = tk.compile(p.text(), device=-1)
+    d = prog.dump()
+    assert sum(line.strip().startswith("gemv_q8") for line in d.splitlines()) == 2
+    if kind == "updated":
+        # both products read s in stage 0; the direct update of s runs after
+        stages = d.split("stage ")[1:]
+        assert "gemv_q8" in stages[0] and "gemv_q8" not in stages[1] and "ew items=1 : mul" in stages[1]
+        assert prog.query()["direct_state_commits"] == 1
 
 
 def test_activation_quantisation_flag():
