@@ -1124,10 +1124,26 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
 // 4096 columns are issued before any is used.  w = fl(q * s), then
 // acc = fma(x, w, acc).  Leaves the 16 row sums in LDS.
 
+// One DPP step: v + (v moved across lanes by `ctrl`) in the rows of
+// `rows` (other rows add zero).
+template <int ctrl, int rows>
+DEV float dpp_add(float v) {
+  const int m = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), ctrl, rows, 0xf, false);
+  return v + __builtin_bit_cast(float, m);
+}
+
+// Sum over the 64 lanes of a wave, in a fixed order, on DPP lane moves
+// instead of LDS permutes: lane pairs, quads, 16-lane rows (two rotations),
+// then the rows combined by broadcasts (row 0 into row 1 and row 2 into row 3,
+// then rows 0+1 into row 3).  The total is read from lane 63 (wave-uniform).
 DEV float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
-  return v;
+  v = dpp_add<0xb1, 0xf>(v);   // quad_perm [1,0,3,2]
+  v = dpp_add<0x4e, 0xf>(v);   // quad_perm [2,3,0,1]
+  v = dpp_add<0x124, 0xf>(v);  // row_ror:4
+  v = dpp_add<0x128, 0xf>(v);  // row_ror:8
+  v = dpp_add<0x142, 0xa>(v);  // row_bcast:15 into rows 1 and 3
+  v = dpp_add<0x143, 0xc>(v);  // row_bcast:31 into rows 2 and 3
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 constexpr uint32_t kGemvRed = kSmemBytes - 64 * kGemvRows;  // byte offset of the [rows][16] output sums
@@ -1428,8 +1444,42 @@ DEV void fin_batch(Batch& b, const DTask& t, uint32_t ins_off, uint32_t width) {
 // and arithmetic as the expression machine (vm_run), element by element, but
 // without a batch: a slab has too few outputs for the exchange and the
 // per-chunk machinery to pay.
+// The epilogue's operand loads that come before its first store, issued by
+// wave 0 ahead of the product (up to kGemvPre of them; no store of the
+// program precedes them, and the product writes no memory), so their latency
+// overlaps the weight stream.  Returns how many were issued.
+constexpr int kGemvPre = 4;
+DEV uint32_t gemv_epi_preload(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
+                              uint32_t item, float (&pre)[kGemvPre]) {
+  if (tid >= 64) return 0;
+  const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
+  const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
+  const uint32_t r = tid / 16, col = cb * 16 + tid % 16;
+  const bool ok = r < rows && col < t.n;
+  Batch b;
+  expr_batch(b, t, ins_off);
+  task_space(b, t);
+  uint32_t c[kMaxDims];
+  unravel(ok ? (r0 + r) * t.n + col : 0u, b, c);
+  uint32_t n = 0;
+  for (uint32_t pc = 0; pc < b.n && n < (uint32_t)kGemvPre; ++pc) {
+    const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + b.ins + pc * sizeof(DIns));
+    const uint32_t w0 = uniform(iw[0]), w1 = uniform(iw[1]);
+    const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff;
+    if (op == VM_STORE) break;
+    if (src != SRC_VIEW) continue;
+    const VView v = load_view(views_off + (w1 & 0xffff) * sizeof(DView));
+    const float x = load_elem(base_ptr(ka, v.base), v.dtype, view_index(v, c));
+#pragma unroll
+    for (int k = 0; k < kGemvPre; ++k)
+      if ((uint32_t)k == n) pre[k] = x;
+    ++n;
+  }
+  return n;
+}
+
 DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
-                       uint32_t item) {
+                       uint32_t item, const float (&pre)[kGemvPre], uint32_t npre) {
   if (tid >= 64) return;
   const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
   const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
@@ -1442,6 +1492,7 @@ DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t vie
   task_space(b, t);
   uint32_t c[kMaxDims];
   unravel(ok ? (r0 + r) * t.n + col : 0u, b, c);  // other threads address element 0
+  uint32_t used = 0;  // preloaded operands consumed (in program order)
   for (uint32_t pc = 0; pc < b.n; ++pc) {
     const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + b.ins + pc * sizeof(DIns));
     const uint32_t w0 = uniform(iw[0]), w1 = uniform(iw[1]);
@@ -1462,7 +1513,14 @@ DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t vie
         }
         continue;
       }
-      o = load_elem(p, v.dtype, idx);
+      if (used < npre) {
+#pragma unroll
+        for (int k = 0; k < kGemvPre; ++k)
+          if ((uint32_t)k == used) o = pre[k];
+        ++used;
+      } else {
+        o = load_elem(p, v.dtype, idx);
+      }
     } else if (src == SRC_SLOT) {
       o = slot_base(arg)[tid];
     } else if (src == SRC_SCALAR) {
@@ -2241,11 +2299,14 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
       if (t.flags & F_FASTEPI) wait_vmcnt<0>();
       break;
     }
-    case T_GEMV_Q8:
+    case T_GEMV_Q8: {
+      float pre[kGemvPre];
+      const uint32_t npre = gemv_epi_preload(tid, ka, t, sd.off_views, sd.off_ins, item, pre);
       gemv_q8(tid, ka, t, sd.off_views, item);
-      gemv_epilogue(tid, ka, t, sd.off_views, sd.off_ins, item);
+      gemv_epilogue(tid, ka, t, sd.off_views, sd.off_ins, item, pre, npre);
       __syncthreads();  // the next item may overwrite the row sums and the slots
       return;
+    }
     case T_RED_COLS:
       if (t.flags & F_COLDIRECT) red_cols_direct(tid, ka, t, sd, item, st);
       break;
