@@ -1447,10 +1447,13 @@ DEV void fin_batch(Batch& b, const DTask& t, uint32_t ins_off, uint32_t width) {
 // The epilogue's operand loads that come before its first store, issued by
 // wave 0 ahead of the product (up to kGemvPre of them; no store of the
 // program precedes them, and the product writes no memory), so their latency
-// overlaps the weight stream.  Returns how many were issued.
+// overlaps the weight stream.  Operand k goes to raw[k] as loaded (fp32 bits,
+// or the 16-bit pattern of an f16/bf16): nothing reads it before the
+// epilogue, so no wait for it is placed ahead of the product.  Returns how
+// many were issued.
 constexpr int kGemvPre = 4;
 DEV uint32_t gemv_epi_preload(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
-                              uint32_t item, float (&pre)[kGemvPre]) {
+                              uint32_t item, uint32_t (&raw)[kGemvPre]) {
   if (tid >= 64) return 0;
   const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
   const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
@@ -1461,25 +1464,41 @@ DEV uint32_t gemv_epi_preload(uint32_t tid, const Ctx& ka, const DTask& t, uint3
   task_space(b, t);
   uint32_t c[kMaxDims];
   unravel(ok ? (r0 + r) * t.n + col : 0u, b, c);
-  uint32_t n = 0;
-  for (uint32_t pc = 0; pc < b.n && n < (uint32_t)kGemvPre; ++pc) {
-    const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + b.ins + pc * sizeof(DIns));
-    const uint32_t w0 = uniform(iw[0]), w1 = uniform(iw[1]);
-    const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff;
-    if (op == VM_STORE) break;
-    if (src != SRC_VIEW) continue;
-    const VView v = load_view(views_off + (w1 & 0xffff) * sizeof(DView));
-    const float x = load_elem(base_ptr(ka, v.base), v.dtype, view_index(v, c));
+  uint32_t n = 0, pc = 0;
 #pragma unroll
-    for (int k = 0; k < kGemvPre; ++k)
-      if ((uint32_t)k == n) pre[k] = x;
+  for (int k = 0; k < kGemvPre; ++k) {
+    // the next operand load before the first store, if any (wave-uniform)
+    uint32_t arg = 0xffffffffu;
+    for (; pc < b.n; ++pc) {
+      const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + b.ins + pc * sizeof(DIns));
+      const uint32_t w0 = uniform(iw[0]);
+      if ((w0 & 0xff) == VM_STORE) {
+        pc = b.n;
+        break;
+      }
+      if (((w0 >> 8) & 0xff) == SRC_VIEW) {
+        arg = uniform(iw[1]) & 0xffff;
+        ++pc;
+        break;
+      }
+    }
+    if (arg == 0xffffffffu) break;
+    const VView v = load_view(views_off + arg * sizeof(DView));
+    const GLOBAL uint8_t* p = base_ptr(ka, v.base);
+    const int32_t idx = view_index(v, c);
+    if (v.dtype == DT_F32)
+      raw[k] = ((const GLOBAL uint32_t*)p)[idx];
+    else if (v.dtype == DT_I8)
+      raw[k] = (uint32_t)(int32_t)((const GLOBAL int8_t*)p)[idx];
+    else
+      raw[k] = ((const GLOBAL uint16_t*)p)[idx];
     ++n;
   }
   return n;
 }
 
 DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
-                       uint32_t item, const float (&pre)[kGemvPre], uint32_t npre) {
+                       uint32_t item, const uint32_t (&raw)[kGemvPre], uint32_t npre) {
   if (tid >= 64) return;
   const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
   const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
@@ -1514,9 +1533,13 @@ DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t vie
         continue;
       }
       if (used < npre) {
+        uint32_t bits = raw[0];
 #pragma unroll
-        for (int k = 0; k < kGemvPre; ++k)
-          if ((uint32_t)k == used) o = pre[k];
+        for (int k = 1; k < kGemvPre; ++k)
+          if ((uint32_t)k == used) bits = raw[k];
+        o = v.dtype == DT_F32 ? __uint_as_float(bits)
+            : v.dtype == DT_I8 ? (float)(int32_t)bits
+                               : half_bits_to_f32(bits, v.dtype == DT_BF16);
         ++used;
       } else {
         o = load_elem(p, v.dtype, idx);
@@ -2300,10 +2323,10 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
       break;
     }
     case T_GEMV_Q8: {
-      float pre[kGemvPre];
-      const uint32_t npre = gemv_epi_preload(tid, ka, t, sd.off_views, sd.off_ins, item, pre);
+      uint32_t raw[kGemvPre] = {0, 0, 0, 0};
+      const uint32_t npre = gemv_epi_preload(tid, ka, t, sd.off_views, sd.off_ins, item, raw);
       gemv_q8(tid, ka, t, sd.off_views, item);
-      gemv_epilogue(tid, ka, t, sd.off_views, sd.off_ins, item, pre, npre);
+      gemv_epilogue(tid, ka, t, sd.off_views, sd.off_ins, item, raw, npre);
       __syncthreads();  // the next item may overwrite the row sums and the slots
       return;
     }
