@@ -1439,41 +1439,36 @@ DEV void fin_batch(Batch& b, const DTask& t, uint32_t ins_off, uint32_t width) {
   set_1d(b, t.m);
 }
 
-// Epilogue of an int8-weight GEMV item: its 16 x rows outputs, one per thread
-// of wave 0, evaluated from the row sums in registers.  The same programs
-// and arithmetic as the expression machine (vm_run), element by element, but
-// without a batch: a slab has too few outputs for the exchange and the
-// per-chunk machinery to pay.
-// The epilogue's operand loads that come before its first store, issued by
-// wave 0 ahead of the product (up to kGemvPre of them; no store of the
-// program precedes them, and the product writes no memory), so their latency
-// overlaps the weight stream.  Operand k goes to raw[k] as loaded (fp32 bits,
-// or the 16-bit pattern of an f16/bf16): nothing reads it before the
-// epilogue, so no wait for it is placed ahead of the product.  Returns how
-// many were issued.
-constexpr int kGemvPre = 4;
-DEV uint32_t gemv_epi_preload(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
-                              uint32_t item, uint32_t (&raw)[kGemvPre]) {
-  if (tid >= 64) return 0;
-  const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
-  const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
-  const uint32_t r = tid / 16, col = cb * 16 + tid % 16;
-  const bool ok = r < rows && col < t.n;
-  Batch b;
-  expr_batch(b, t, ins_off);
-  task_space(b, t);
-  uint32_t c[kMaxDims];
-  unravel(ok ? (r0 + r) * t.n + col : 0u, b, c);
+// ------------------------------------------------- one-element programs --
+// A program evaluated for one element per thread, in registers, with
+// vm_run's arithmetic and rounding instruction by instruction (so results are
+// identical bit for bit): for work with too few elements per thread for the
+// batches' chunk machinery to pay (the int8 GEMV's epilogue, the finishing
+// programs of reductions).  `ins` is the byte offset of the first instruction
+// in the LDS plan; c holds the element's coordinates (views index with
+// them); stores are skipped where ok is false.  Slots are this thread's word
+// of the LDS slot arrays.
+//
+// The operand loads that come before the program's first store may be issued
+// ahead of the work that produces y (prog_preload, up to kPre of them): no
+// store of the program precedes them and the callers' work writes no memory
+// until the program runs.  Operand k lands in raw[k] as loaded (fp32 bits,
+// the 16-bit pattern of an f16/bf16, or the sign-extended int8): nothing
+// reads it before prog_run, so no wait for it is placed ahead of that work.
+constexpr int kPre = 4;
+
+DEV uint32_t prog_preload(const Ctx& ka, uint32_t views_off, uint32_t ins, uint32_t n_ins,
+                          const uint32_t (&c)[kMaxDims], uint32_t (&raw)[kPre]) {
   uint32_t n = 0, pc = 0;
 #pragma unroll
-  for (int k = 0; k < kGemvPre; ++k) {
+  for (int k = 0; k < kPre; ++k) {
     // the next operand load before the first store, if any (wave-uniform)
     uint32_t arg = 0xffffffffu;
-    for (; pc < b.n; ++pc) {
-      const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + b.ins + pc * sizeof(DIns));
+    for (; pc < n_ins; ++pc) {
+      const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + ins + pc * sizeof(DIns));
       const uint32_t w0 = uniform(iw[0]);
       if ((w0 & 0xff) == VM_STORE) {
-        pc = b.n;
+        pc = n_ins;
         break;
       }
       if (((w0 >> 8) & 0xff) == SRC_VIEW) {
@@ -1497,23 +1492,11 @@ DEV uint32_t gemv_epi_preload(uint32_t tid, const Ctx& ka, const DTask& t, uint3
   return n;
 }
 
-DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
-                       uint32_t item, const uint32_t (&raw)[kGemvPre], uint32_t npre) {
-  if (tid >= 64) return;
-  const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
-  const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
-  const uint32_t r = tid / 16, col = cb * 16 + tid % 16;
-  const bool ok = r < rows && col < t.n;
-  const LDS float* red = (const LDS float*)(g_smem + kGemvRed);
-  float y = ok ? red[r * 16 + tid % 16] : 0.0f;
-  Batch b;
-  expr_batch(b, t, ins_off);
-  task_space(b, t);
-  uint32_t c[kMaxDims];
-  unravel(ok ? (r0 + r) * t.n + col : 0u, b, c);  // other threads address element 0
+DEV void prog_run(uint32_t tid, const Ctx& ka, uint32_t views_off, uint32_t ins, uint32_t n_ins,
+                  const uint32_t (&c)[kMaxDims], bool ok, float y, const uint32_t (&raw)[kPre], uint32_t npre) {
   uint32_t used = 0;  // preloaded operands consumed (in program order)
-  for (uint32_t pc = 0; pc < b.n; ++pc) {
-    const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + b.ins + pc * sizeof(DIns));
+  for (uint32_t pc = 0; pc < n_ins; ++pc) {
+    const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + ins + pc * sizeof(DIns));
     const uint32_t w0 = uniform(iw[0]), w1 = uniform(iw[1]);
     const float a = __uint_as_float(uniform(iw[2])), sv = __uint_as_float(uniform(iw[3]));
     const uint32_t op = w0 & 0xff, src = (w0 >> 8) & 0xff, rnd = (w0 >> 16) & 0xff, rev = w0 >> 24;
@@ -1535,7 +1518,7 @@ DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t vie
       if (used < npre) {
         uint32_t bits = raw[0];
 #pragma unroll
-        for (int k = 1; k < kGemvPre; ++k)
+        for (int k = 1; k < kPre; ++k)
           if ((uint32_t)k == used) bits = raw[k];
         o = v.dtype == DT_F32 ? __uint_as_float(bits)
             : v.dtype == DT_I8 ? (float)(int32_t)bits
@@ -1580,6 +1563,43 @@ DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t vie
     else if (rnd == DT_F16)
       y = f16_bits_to_f32(f32_to_f16_bits(y));
   }
+}
+
+// Coordinates of the int8 GEMV item's output for this thread of wave 0:
+// output (r0 + tid / 16, cb * 16 + tid % 16); threads without one address
+// element 0.
+DEV bool gemv_out_coords(uint32_t tid, const DTask& t, uint32_t ins_off, uint32_t item, uint32_t (&c)[kMaxDims]) {
+  const uint32_t cb = item % t.tiles_n, r0 = (item / t.tiles_n) * kGemvRows;
+  const uint32_t rows = t.m - r0 < kGemvRows ? t.m - r0 : kGemvRows;
+  const uint32_t r = tid / 16, col = cb * 16 + tid % 16;
+  const bool ok = r < rows && col < t.n;
+  Batch b;
+  expr_batch(b, t, ins_off);
+  task_space(b, t);
+  unravel(ok ? (r0 + r) * t.n + col : 0u, b, c);
+  return ok;
+}
+
+// The GEMV epilogue's leading operand loads, issued by wave 0 before the
+// product (the product writes no memory).
+DEV uint32_t gemv_epi_preload(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
+                              uint32_t item, uint32_t (&raw)[kPre]) {
+  if (tid >= 64) return 0;
+  uint32_t c[kMaxDims];
+  gemv_out_coords(tid, t, ins_off, item, c);
+  return prog_preload(ka, views_off, ins_off + t.expr_first * sizeof(DIns), t.expr_len, c, raw);
+}
+
+// Epilogue of an int8-weight GEMV item: its 16 x rows outputs, one per thread
+// of wave 0, from the row sums in LDS.
+DEV void gemv_epilogue(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t ins_off,
+                       uint32_t item, const uint32_t (&raw)[kPre], uint32_t npre) {
+  if (tid >= 64) return;
+  uint32_t c[kMaxDims];
+  const bool ok = gemv_out_coords(tid, t, ins_off, item, c);
+  const LDS float* red = (const LDS float*)(g_smem + kGemvRed);
+  const float y = ok ? red[(tid / 16) * 16 + tid % 16] : 0.0f;
+  prog_run(tid, ka, views_off, ins_off + t.expr_first * sizeof(DIns), t.expr_len, c, ok, y, raw, npre);
 }
 
 // A contraction tile's batch (chunks q0 + q * kBlock + tid of the [bm][bn]
@@ -1747,8 +1767,8 @@ DEV bool fill(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, uin
       const uint32_t rb = part * t.kchunk;
       const uint32_t re = (rb + t.kchunk < R) ? rb + t.kchunk : R;
       const uint32_t per = 8 * C;
-      // F_COLDIRECT: the rows were summed before the first batch (red_cols_direct)
-      const uint32_t nb = (t.flags & F_COLDIRECT) ? 0u : re > rb ? (re - rb + per - 1) / per : 0u;
+      // (F_COLDIRECT items never come here: red_cols_item runs them)
+      const uint32_t nb = re > rb ? (re - rb + per - 1) / per : 0u;
       if (bi < nb) {
         expr_batch(b, t, ins_off);
         task_space(b, t);
@@ -1784,47 +1804,6 @@ DEV bool fill(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off, uin
           xe(tid, 0) = col;
           for (int j = 0; j < W; ++j) xv(tid, j) = tot[j];
         }
-      }
-      return true;
-    }
-    case T_RED_FINAL: {
-      // one thread per output: parts summed in order, eight loads in flight
-      if (bi > 0) return false;
-      fin_batch(b, t, ins_off, 1);
-      const GLOBAL float* P = ws_f32(ka, t.scratch);
-      const bool cols_layout = (t.tile & 1) != 0;  // [parts][rows] instead of [rows][parts]
-      if (t.flags & F_ROWWG) {
-        // output `item`: thread t sums parts t, t + 256, ... in order, then a
-        // fixed-order block sum
-        const uint32_t r = item;
-        float a = 0.0f;
-        for (uint32_t p = tid; p < t.split; p += kBlock)
-          a = a + (cols_layout ? P[(uint64_t)p * t.m + r] : P[(uint64_t)r * t.split + p]);
-        const float total = block_sum(tid, a);
-        if (tid == 0) {
-          live = 1;
-          xe(tid, 0) = r;
-          xv(tid, 0) = total;
-        }
-        return true;
-      }
-      const uint32_t row = item * kBlock + tid;
-      if (row < t.m) {
-        float a = 0.0f;
-        for (uint32_t p0 = 0; p0 < t.split; p0 += 8) {
-          float v8[8];
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            const uint32_t p = p0 + i;
-            v8[i] = p < t.split ? (cols_layout ? P[(uint64_t)p * t.m + row] : P[(uint64_t)row * t.split + p]) : 0.0f;
-          }
-#pragma unroll
-          for (int i = 0; i < 8; ++i)
-            if (p0 + i < t.split) a = a + v8[i];
-        }
-        live = 1;
-        xe(tid, 0) = row;
-        xv(tid, 0) = a;
       }
       return true;
     }
@@ -2249,6 +2228,84 @@ DEV void red_cols_direct(uint32_t tid, const Ctx& ka, const DTask& t, const DSta
   }
 }
 
+// Finish of a directly read column sum: after red_cols_direct each thread
+// holds the sums of its 8 columns over its row lane's rows.  The 8 row lanes
+// are combined through LDS in order (lane 0 first); then thread i takes
+// column cb * 256 + i and writes its part's partial (F_PARTIAL) or runs the
+// finishing program for it (operands preloaded before the sums).
+DEV void red_cols_finish(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item,
+                         const ItemState& st, const uint32_t (&raw)[kPre], uint32_t npre) {
+  const uint32_t cb = item / t.split, part = item % t.split;
+  const uint32_t cols = t.m;
+  const uint32_t cc = tid % 32, rl = tid / 32;
+  LDS float* red = (LDS float*)g_smem;  // [8 row lanes][256 columns]
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rl * 256 + cc * 8 + j] = st.acc8[j];
+  __syncthreads();
+  const uint32_t col = cb * 256 + tid;
+  float a = red[tid];
+#pragma unroll
+  for (int q = 1; q < 8; ++q) a = a + red[q * 256 + tid];
+  const bool ok = col < cols;
+  if (t.flags & F_PARTIAL) {
+    if (ok) ws_f32(ka, t.scratch)[(uint64_t)part * cols + col] = a;
+    return;
+  }
+  const uint32_t c[kMaxDims] = {ok ? col : 0u, 0u, 0u, 0u};
+  prog_run(tid, ka, sd.off_views, sd.off_ins + t.fin_first * sizeof(DIns), t.fin_len, c, ok, a, raw, npre);
+}
+
+// A column reduction read directly: its finishing program's leading operands
+// are loaded first, then the rows, then the finish.
+DEV void red_cols_item(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item, ItemState& st) {
+  uint32_t raw[kPre] = {0, 0, 0, 0};
+  uint32_t npre = 0;
+  if (!(t.flags & F_PARTIAL)) {
+    const uint32_t col = (item / t.split) * 256 + tid;
+    const uint32_t c[kMaxDims] = {col < t.m ? col : 0u, 0u, 0u, 0u};
+    npre = prog_preload(ka, sd.off_views, sd.off_ins + t.fin_first * sizeof(DIns), t.fin_len, c, raw);
+  }
+  red_cols_direct(tid, ka, t, sd, item, st);
+  red_cols_finish(tid, ka, t, sd, item, st, raw, npre);
+}
+
+// Combine of a two-phase reduction's partials.  Default: one thread per
+// output, its parts summed in order with sixteen loads in flight.  F_ROWWG
+// (few outputs, many parts): output `item`, thread t sums parts t, t + 256,
+// ... in order, then a fixed-order block sum.  Then the finishing program,
+// its leading operands preloaded before the partials.
+DEV void red_final_item(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item) {
+  const GLOBAL float* P = ws_f32(ka, t.scratch);
+  const bool cols_layout = (t.tile & 1) != 0;  // [parts][rows] instead of [rows][parts]
+  const uint32_t fin = sd.off_ins + t.fin_first * sizeof(DIns);
+  const bool rowwg = (t.flags & F_ROWWG) != 0;
+  const uint32_t row = rowwg ? item : item * kBlock + tid;
+  const bool exists = row < t.m;
+  const uint32_t c[kMaxDims] = {exists ? row : 0u, 0u, 0u, 0u};
+  uint32_t raw[kPre] = {0, 0, 0, 0};
+  const uint32_t npre = prog_preload(ka, sd.off_views, fin, t.fin_len, c, raw);
+  float a = 0.0f;
+  if (rowwg) {
+    for (uint32_t p = tid; p < t.split; p += kBlock)
+      a = a + (cols_layout ? P[(uint64_t)p * t.m + row] : P[(uint64_t)row * t.split + p]);
+    a = block_sum(tid, a);
+  } else {
+    const uint32_t rr = exists ? row : 0u;
+    for (uint32_t p0 = 0; p0 < t.split; p0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t pp = p0 + i < t.split ? p0 + i : 0u;
+        v[i] = cols_layout ? P[(uint64_t)pp * t.m + rr] : P[(uint64_t)rr * t.split + pp];
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i)
+        if (p0 + i < t.split) a = a + v[i];
+    }
+  }
+  prog_run(tid, ka, sd.off_views, fin, t.fin_len, c, exists && (!rowwg || tid == 0), a, raw, npre);
+}
+
 // A stage record from the plan (wave-uniform).
 DEV DStage load_stage(const GLOBAL uint8_t* stages, uint32_t s) {
   constexpr int N = sizeof(DStage) / 4;
@@ -2323,7 +2380,7 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
       break;
     }
     case T_GEMV_Q8: {
-      uint32_t raw[kGemvPre] = {0, 0, 0, 0};
+      uint32_t raw[kPre] = {0, 0, 0, 0};
       const uint32_t npre = gemv_epi_preload(tid, ka, t, sd.off_views, sd.off_ins, item, raw);
       gemv_q8(tid, ka, t, sd.off_views, item);
       gemv_epilogue(tid, ka, t, sd.off_views, sd.off_ins, item, raw, npre);
@@ -2331,8 +2388,16 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
       return;
     }
     case T_RED_COLS:
-      if (t.flags & F_COLDIRECT) red_cols_direct(tid, ka, t, sd, item, st);
+      if (t.flags & F_COLDIRECT) {
+        red_cols_item(tid, ka, t, sd, item, st);
+        __syncthreads();  // the next item may overwrite the LDS sums and the slots
+        return;
+      }
       break;
+    case T_RED_FINAL:
+      red_final_item(tid, ka, t, sd, item);
+      __syncthreads();  // the next item may overwrite the LDS sums and the slots
+      return;
     default:
       break;
   }
