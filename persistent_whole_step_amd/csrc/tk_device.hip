@@ -100,6 +100,27 @@ DEV uint32_t f32_to_f16_bits(float f) {
 }
 
 DEV float half_bits_to_f32(uint32_t h, bool bf) { return bf ? bf16_bits_to_f32(h) : f16_bits_to_f32(h); }
+
+// Eight 16-bit values (one 16-byte chunk) widened to fp32, the dtype fixed
+// per call (no per-element dtype select); and fp32 values narrowed (RNE) and
+// packed two to a word.
+template <bool BF>
+DEV void widen8(u32x4 v, float (&x)[8]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if (BF) {
+      x[2 * j] = __uint_as_float(v[j] << 16);
+      x[2 * j + 1] = __uint_as_float(v[j] & 0xffff0000u);
+    } else {
+      x[2 * j] = f16_bits_to_f32(v[j] & 0xffffu);
+      x[2 * j + 1] = f16_bits_to_f32(v[j] >> 16);
+    }
+  }
+}
+template <bool BF>
+DEV uint32_t narrow2(float lo, float hi) {
+  return BF ? f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16) : f32_to_f16_bits(lo) | (f32_to_f16_bits(hi) << 16);
+}
 DEV uint32_t f32_to_half_bits(float f, bool bf) { return bf ? f32_to_bf16_bits(f) : f32_to_f16_bits(f); }
 
 DEV uint32_t uniform(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
@@ -1940,54 +1961,31 @@ DEV bool fast_prefetch(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins
   return ok;
 }
 
-// One 8-wide chunk per index of a view with column stride s1 (1: 16-byte
-// vector loads; 0: one element broadcast), as load_chunks.
+// A view with column stride 0: one element per chunk, broadcast along the
+// chunk (the dtype branch taken once, outside the chunk loops).
 template <int G>
-DEV void fast_load(const GLOBAL uint8_t* p, uint32_t dt, uint32_t s1, const int32_t (&idx)[G], float (&x)[G][8]) {
+DEV void fast_load_bcast(const GLOBAL uint8_t* p, uint32_t dt, const int32_t (&idx)[G], float (&x)[G][8]) {
+  float e[G];
   if (dt == DT_F32) {
-    const GLOBAL float* q = (const GLOBAL float*)p;
-    if (s1) {
-      u32x4 r[G][2];
 #pragma unroll
-      for (int g = 0; g < G; ++g) {
-        r[g][0] = *(const GLOBAL u32x4*)(q + idx[g]);
-        r[g][1] = *(const GLOBAL u32x4*)(q + idx[g] + 4);
-      }
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[g][j] = __uint_as_float(r[g][j / 4][j % 4]);
-    } else {
-      float r[G];
-#pragma unroll
-      for (int g = 0; g < G; ++g) r[g] = q[idx[g]];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[g][j] = r[g];
-    }
+    for (int g = 0; g < G; ++g) e[g] = ((const GLOBAL float*)p)[idx[g]];
   } else {
     const GLOBAL uint16_t* q = (const GLOBAL uint16_t*)p;
-    const bool bf = dt == DT_BF16;
-    if (s1) {
-      u32x4 r[G];
+    uint32_t h[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) r[g] = *(const GLOBAL u32x4*)(q + idx[g]);
+    for (int g = 0; g < G; ++g) h[g] = q[idx[g]];
+    if (dt == DT_BF16) {
 #pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          x[g][j] = half_bits_to_f32((j & 1) ? r[g][j / 2] >> 16 : r[g][j / 2] & 0xffffu, bf);
+      for (int g = 0; g < G; ++g) e[g] = bf16_bits_to_f32(h[g]);
     } else {
-      uint32_t r[G];
 #pragma unroll
-      for (int g = 0; g < G; ++g) r[g] = q[idx[g]];
-#pragma unroll
-      for (int g = 0; g < G; ++g)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) x[g][j] = half_bits_to_f32(r[g], bf);
+      for (int g = 0; g < G; ++g) e[g] = f16_bits_to_f32(h[g]);
     }
   }
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) x[g][j] = e[g];
 }
 
 // Stores of the chunks in bounds, converted to the view's dtype (RNE), as
@@ -2009,16 +2007,24 @@ DEV void fast_store(GLOBAL uint8_t* p, uint32_t dt, const int32_t (&idx)[G], con
       *(GLOBAL u32x4*)(q + idx[g]) = r0;
       *(GLOBAL u32x4*)(q + idx[g] + 4) = r1;
     }
-  } else {
+  } else if (dt == DT_BF16) {
     GLOBAL uint16_t* q = (GLOBAL uint16_t*)p;
-    const bool bf = dt == DT_BF16;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       if (!ok[g]) continue;
       u32x4 r;
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        r[j] = f32_to_half_bits(y[g][2 * j], bf) | (f32_to_half_bits(y[g][2 * j + 1], bf) << 16);
+      for (int j = 0; j < 4; ++j) r[j] = narrow2<true>(y[g][2 * j], y[g][2 * j + 1]);
+      *(GLOBAL u32x4*)(q + idx[g]) = r;
+    }
+  } else {
+    GLOBAL uint16_t* q = (GLOBAL uint16_t*)p;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      if (!ok[g]) continue;
+      u32x4 r;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) r[j] = narrow2<false>(y[g][2 * j], y[g][2 * j + 1]);
       *(GLOBAL u32x4*)(q + idx[g]) = r;
     }
   }
@@ -2069,22 +2075,25 @@ DEV void fast_run(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off,
     }
     if (src == SRC_VIEW) {
       if (r.staged) {
-        const bool f32 = r.dt == DT_F32, bf = r.dt == DT_BF16;
+        // this lane's chunk g of the view sits at staged + 16 (g * kBlock + tid)
+        const LDS uint8_t* base = (const LDS uint8_t*)(g_smem + r.staged + 16u * tid);
+        if (r.dt == DT_F32) {
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-          const uint32_t q = (uint32_t)(g * kBlock) + tid;
-          const u32x4 v = *(const LDS u32x4*)(g_smem + r.staged + 16u * q);
-          if (f32) {
-            const u32x4 v2 = *(const LDS u32x4*)(g_smem + r.staged + kPlane + 16u * q);
+          for (int g = 0; g < G; ++g) {
+            const u32x4 v = *(const LDS u32x4*)(base + 16u * g * kBlock);
+            const u32x4 v2 = *(const LDS u32x4*)(base + kPlane + 16u * g * kBlock);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
               x[g][j] = __uint_as_float(v[j]);
               x[g][4 + j] = __uint_as_float(v2[j]);
             }
-          } else {
-#pragma unroll
-            for (int j = 0; j < 8; ++j) x[g][j] = half_bits_to_f32((j & 1) ? v[j / 2] >> 16 : v[j / 2] & 0xffffu, bf);
           }
+        } else if (r.dt == DT_BF16) {
+#pragma unroll
+          for (int g = 0; g < G; ++g) widen8<true>(*(const LDS u32x4*)(base + 16u * g * kBlock), x[g]);
+        } else {
+#pragma unroll
+          for (int g = 0; g < G; ++g) widen8<false>(*(const LDS u32x4*)(base + 16u * g * kBlock), x[g]);
         }
       } else {
         // column stride 0: one element per chunk, broadcast along the chunk
@@ -2092,7 +2101,7 @@ DEV void fast_run(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off,
         int32_t idx[G];
 #pragma unroll
         for (int g = 0; g < G; ++g) idx[g] = c.ok[g] ? r.off + c.row[g] * r.s0 : r.off;
-        fast_load<G>(p, r.dt, 0u, idx, x);
+        fast_load_bcast<G>(p, r.dt, idx, x);
       }
     } else {
       const float k = src == SRC_SCALAR ? r.s : 0.0f;
