@@ -111,6 +111,8 @@ constexpr uint32_t F_FASTEPI = 64u;    // contraction tile: the epilogue runs as
                                        //   views, no load after a store that may overlap it)
 constexpr uint32_t F_COLDIRECT = 128u;  // column reduction whose source program is one load of a 2-D view with
                                        //   column stride 1: rows are summed straight from memory, not in batches
+constexpr uint32_t F_COLLANES32 = 256u;  // direct column reduction in one part: an item is 8 column chunks (64
+                                        //   columns) x 32 row lanes instead of 32 chunks x 8 row lanes
 constexpr int kFastIns = 8;
 constexpr int kFastLoads = 3;
 // Register epilogues: the unit-stride loaded views of a tile are copied into

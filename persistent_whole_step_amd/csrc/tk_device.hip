@@ -2160,19 +2160,24 @@ DEV void fast_run(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins_off,
   }
 }
 
+// Geometry of a direct column reduction's item: CC column chunks of 8 by
+// 256 / CC row lanes (32 x 8, or 8 x 32 with F_COLLANES32).
+DEV uint32_t col_chunks(const DTask& t) { return (t.flags & F_COLLANES32) ? 8u : 32u; }
+
 // A column reduction whose source program is one load of a 2-D view with
-// column stride 1 (F_COLDIRECT): thread (row lane rl = tid / 32, chunk
-// cc = tid % 32) sums rows rb + rl, rb + rl + 8, ... of its 8 columns straight
-// from memory, 16 rows in flight at a time, into its running sums.  The rows
-// and the additions come in the order the batches would take them, so the
-// sums are bit-identical; the combine across row lanes and the finishing
-// program then run as for the batches.
+// column stride 1 (F_COLDIRECT): thread (row lane rl = tid / CC, chunk
+// cc = tid % CC) sums rows rb + rl, rb + rl + RL, ... of its 8 columns
+// straight from memory, 16 rows in flight at a time, into its running sums
+// (with 32 chunks by 8 lanes the rows and additions come in the order the
+// batches would take them, so the sums are bit-identical to theirs).
+template <uint32_t CC>
 DEV void red_cols_direct(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item,
                          ItemState& st) {
   const uint32_t cb = item / t.split, part = item % t.split;
   const uint32_t cols = t.m, R = t.k;
-  const uint32_t cc = tid % 32, rl = tid / 32;
-  const uint32_t col = cb * 256 + cc * 8;
+  constexpr uint32_t RL = kBlock / CC;
+  const uint32_t cc = tid % CC, rl = tid / CC;
+  const uint32_t col = cb * CC * 8 + cc * 8;
   const uint32_t rb = part * t.kchunk;
   const uint32_t re = (rb + t.kchunk < R) ? rb + t.kchunk : R;
   const LDS uint32_t* iw = (const LDS uint32_t*)(g_plan + sd.off_ins + t.expr_first * sizeof(DIns));
@@ -2183,12 +2188,12 @@ DEV void red_cols_direct(uint32_t tid, const Ctx& ka, const DTask& t, const DSta
   const bool vec = aligned16(p) && v.offset % epc == 0 && v.stride[0] % epc == 0;
   if (col >= cols || rb >= re) return;
   constexpr int U = 16;
-  for (uint32_t r0 = rb + rl; r0 < re; r0 += 8 * U) {
+  for (uint32_t r0 = rb + rl; r0 < re; r0 += RL * U) {
     float x[U][8];
     int32_t idx[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const uint32_t r = r0 + 8 * u;
+      const uint32_t r = r0 + RL * u;
       idx[u] = v.offset + (int32_t)(r < re ? r : rb) * v.stride[0] + (int32_t)col;
     }
     if (dt == DT_F32) {
@@ -2231,30 +2236,33 @@ DEV void red_cols_direct(uint32_t tid, const Ctx& ka, const DTask& t, const DSta
     }
 #pragma unroll
     for (int u = 0; u < U; ++u)
-      if (r0 + 8 * u < re)
+      if (r0 + RL * u < re)
 #pragma unroll
         for (int j = 0; j < 8; ++j) st.acc8[j] = st.acc8[j] + x[u][j];
   }
 }
 
 // Finish of a directly read column sum: after red_cols_direct each thread
-// holds the sums of its 8 columns over its row lane's rows.  The 8 row lanes
-// are combined through LDS in order (lane 0 first); then thread i takes
-// column cb * 256 + i and writes its part's partial (F_PARTIAL) or runs the
-// finishing program for it (operands preloaded before the sums).
+// holds the sums of its 8 columns over its row lane's rows.  The RL row lanes
+// are combined through LDS in order (lane 0 first); then thread i < 8 CC
+// takes column cb * 8 CC + i and writes its part's partial (F_PARTIAL) or
+// runs the finishing program for it (operands preloaded before the sums).
+template <uint32_t CC>
 DEV void red_cols_finish(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item,
                          const ItemState& st, const uint32_t (&raw)[kPre], uint32_t npre) {
   const uint32_t cb = item / t.split, part = item % t.split;
   const uint32_t cols = t.m;
-  const uint32_t cc = tid % 32, rl = tid / 32;
-  LDS float* red = (LDS float*)g_smem;  // [8 row lanes][256 columns]
+  constexpr uint32_t RL = kBlock / CC, W = CC * 8;
+  const uint32_t cc = tid % CC, rl = tid / CC;
+  LDS float* red = (LDS float*)g_smem;  // [RL row lanes][8 CC columns]
 #pragma unroll
-  for (int j = 0; j < 8; ++j) red[rl * 256 + cc * 8 + j] = st.acc8[j];
+  for (int j = 0; j < 8; ++j) red[rl * W + cc * 8 + j] = st.acc8[j];
   __syncthreads();
-  const uint32_t col = cb * 256 + tid;
+  if (tid >= W) return;
+  const uint32_t col = cb * W + tid;
   float a = red[tid];
 #pragma unroll
-  for (int q = 1; q < 8; ++q) a = a + red[q * 256 + tid];
+  for (uint32_t q = 1; q < RL; ++q) a = a + red[q * W + tid];
   const bool ok = col < cols;
   if (t.flags & F_PARTIAL) {
     if (ok) ws_f32(ka, t.scratch)[(uint64_t)part * cols + col] = a;
@@ -2270,12 +2278,17 @@ DEV void red_cols_item(uint32_t tid, const Ctx& ka, const DTask& t, const DStage
   uint32_t raw[kPre] = {0, 0, 0, 0};
   uint32_t npre = 0;
   if (!(t.flags & F_PARTIAL)) {
-    const uint32_t col = (item / t.split) * 256 + tid;
+    const uint32_t col = (item / t.split) * col_chunks(t) * 8 + tid;
     const uint32_t c[kMaxDims] = {col < t.m ? col : 0u, 0u, 0u, 0u};
     npre = prog_preload(ka, sd.off_views, sd.off_ins + t.fin_first * sizeof(DIns), t.fin_len, c, raw);
   }
-  red_cols_direct(tid, ka, t, sd, item, st);
-  red_cols_finish(tid, ka, t, sd, item, st, raw, npre);
+  if (t.flags & F_COLLANES32) {
+    red_cols_direct<8>(tid, ka, t, sd, item, st);
+    red_cols_finish<8>(tid, ka, t, sd, item, st, raw, npre);
+  } else {
+    red_cols_direct<32>(tid, ka, t, sd, item, st);
+    red_cols_finish<32>(tid, ka, t, sd, item, st, raw, npre);
+  }
 }
 
 // Combine of a two-phase reduction's partials.  Default: one thread per

@@ -1580,7 +1580,16 @@ struct Builder {
       const Arg& src = r.args[0];
       const int sp = src.scalar ? -2 : prod(src.spec.buf);
       const bool direct = !src.scalar && src.spec.dtype != DT_I8 && (sp == -1 || (sp >= 0 && !inlined.count(sp)));
-      int64_t parts = (rr <= 64 || (direct && rr <= 256)) ? 1 : std::min<int64_t>(64, (rr + 31) / 32);
+      // A direct source contiguous along its kept dim with outputs in 8-wide
+      // chunks takes the kernel's 32-row-lane form (64 columns per item, up
+      // to 32 rows per lane): one part from 513 to 1024 rows, no combine
+      // stage.  (Measured on MI355X: at 512 rows, 16 parts of 32 rows and a
+      // combine in the next stage finish sooner than 16 rows per lane.)
+      const bool lanes32 = direct && O.fast_epilogue && kept % 8 == 0 && !src.spec.strides.empty() &&
+                           src.spec.strides.back() == 1;
+      int64_t parts = (rr <= 64 || (direct && rr <= 256) || (lanes32 && rr > 512 && rr <= 1024))
+                          ? 1
+                          : std::min<int64_t>(64, (rr + 31) / 32);
       int64_t kc = (rr + parts - 1) / parts;
       parts = (rr + kc - 1) / std::max<int64_t>(1, kc);
       c.parts = (uint32_t)std::max<int64_t>(1, parts);
@@ -2115,7 +2124,9 @@ struct Builder {
         const DView& v = cx.vtab[code[0].arg];
         if (v.dtype != DT_I8 && v.stride[1] == 1) t.flags |= F_COLDIRECT;
       }
-      const uint32_t cols_per_item = 32u * t.width;
+      // one part read directly: 8 column chunks x 32 row lanes per item
+      if ((t.flags & F_COLDIRECT) && rc.parts == 1) t.flags |= F_COLLANES32;
+      const uint32_t cols_per_item = (t.flags & F_COLLANES32) ? 64u : 32u * t.width;
       t.tiles_n = (uint32_t)((rc.rows + cols_per_item - 1) / cols_per_item);
       t.n_items = rc.rows == 0 ? 0 : t.tiles_n * rc.parts;
       if (t.flags & F_COLDIRECT) desc += " [rows summed directly]";

@@ -31,7 +31,7 @@ import numpy as np
 
 # csrc/plan.h
 T_EW, T_GEMM_MFMA, T_GEMM_SIMT, T_GEMM_REDUCE, T_GEMV_Q8, T_GEMV, T_RED_ROWS, T_RED_COLS, T_RED_FINAL = range(1, 10)
-F_PARTIAL, F_ROWWG = 2, 4
+F_PARTIAL, F_ROWWG, F_COLLANES32 = 2, 4, 256  # plan.h flags
 VM_STORE = 12
 SRC_VIEW = 1
 KBLOCK = 256
@@ -382,10 +382,11 @@ class Checker:
                         self._linear_views(out, st, t, item, fin, row, row + 1, (t.m, 1, 1, 1), 1, name + " finish")
             elif t.kind == T_RED_COLS:
                 W = 8 if t.width == 8 else 1
+                per = 64 if t.flags & F_COLLANES32 else 32 * W  # columns per item
                 cols, R = t.m, t.k
                 for it in range(t.n_items):
                     cb, part = it // t.split, it % t.split
-                    c0, c1 = cb * 32 * W, min(cb * 32 * W + 32 * W, cols)
+                    c0, c1 = cb * per, min(cb * per + per, cols)
                     rb = part * t.kchunk
                     re_ = min(rb + t.kchunk, R)
                     item = (s, ti, it)

@@ -421,22 +421,50 @@ def test_fused_equals_unfused(name):
         parity.assert_bitexact(a, b, s.dtype, s.buf)
 
 
+def _column_sum_values(dump: str) -> set:
+    """Values a column reduction task writes: its root and its side values."""
+    names = set()
+    for line in dump.splitlines():
+        line = line.strip()
+        if not line.startswith("reduce_cols") and not line.startswith("reduce_final"):
+            continue
+        rest = line.split(" : ", 1)[1]
+        names.add(rest.split(" ", 1)[0])
+        if "+side" in rest:
+            side = rest.split("+side", 1)[1].split("(")[0].split("[")[0]
+            names.update(side.split())
+    return names
+
+
 @pytest.mark.parametrize("name", ["c1", "c2s", "c4s", "c5s", "c2sa"])
 def test_register_epilogue_matches_batches(name):
-    """Contraction epilogues run from registers and column sums read straight
-    from memory (the defaults where the scheduler marks them) give the same
-    bits as the expression machine's batches (batch_epilogues=1) on every
-    output."""
+    """Contraction epilogues run from registers (the default where the
+    scheduler marks them) give the same bits as the expression machine's
+    batches (batch_epilogues=1) on every output that no column sum feeds.  A
+    column sum read straight from memory by 32 row lanes adds its rows in
+    another order than the batches' 8 lanes, so the values it writes (the
+    bias gradients and their updates) agree within one unit in the last
+    place instead (both are checked against the oracle per node elsewhere)."""
     cfg = SMALL[name]
     say("register epilogue == batches", name)
     base = programs.build(cfg)
     ins = programs.inputs_for(cfg, 3)
     o1, p1 = parity.gpu_run(base, [a.copy() for a in ins])
     o2, _ = parity.gpu_run(base, [a.copy() for a in ins], batch_epilogues=1)
-    assert "[register epilogue]" in p1.dump()
-    assert "[rows summed directly]" in p1.dump()
+    d1 = p1.dump()
+    assert "[register epilogue]" in d1
+    assert "[rows summed directly]" in d1
+    summed = _column_sum_values(d1)
     for a, b, s in zip(o1, o2, base.outputs):
-        parity.assert_bitexact(a, b, s.dtype, s.buf)
+        if s.buf not in summed:
+            parity.assert_bitexact(a, b, s.dtype, s.buf)
+            continue
+        g, w = parity.f32_of(a, s.dtype), parity.f32_of(b, s.dtype)
+        if s.dtype == "f32":
+            tol = np.spacing(np.abs(w).astype(np.float32))
+        else:
+            tol = parity.ulp16(w, s.dtype)
+        assert np.all(np.abs(g - w) <= tol), f"{s.buf}: more than one ulp apart"
 
 
 @pytest.mark.parametrize("name", ["c2s", "c5s"])
