@@ -111,6 +111,8 @@ constexpr uint32_t F_FASTEPI = 64u;    // contraction tile: the epilogue runs as
                                        //   views, no load after a store that may overlap it)
 constexpr uint32_t F_COLDIRECT = 128u;  // column reduction whose source program is one load of a 2-D view with
                                        //   column stride 1: rows are summed straight from memory, not in batches
+constexpr uint32_t F_BSUM = 512u;       // contraction whose first tile row also sums its B operand over K per
+                                       //   column and runs a fused column reduction's finishing program
 constexpr uint32_t F_COLLANES32 = 256u;  // direct column reduction in one part: an item is 8 column chunks (64
                                         //   columns) x 32 row lanes instead of 32 chunks x 8 row lanes
 constexpr int kFastIns = 8;
@@ -154,6 +156,8 @@ struct DTask {
   uint64_t scratch;         // byte offset of fp32 partials in the workspace
   float count;              // mean divisor
   uint32_t group_m;         // contractions: tile rows per group of the tile order (see the kernel)
+  uint32_t bs_first;        // F_BSUM: finishing program of the column sums of B (one element per column)
+  uint32_t bs_len;
 };
 static_assert(sizeof(DTask) % 8 == 0, "DTask layout");
 

@@ -2328,6 +2328,82 @@ DEV void red_final_item(uint32_t tid, const Ctx& ka, const DTask& t, const DStag
   prog_run(tid, ka, sd.off_views, fin, t.fin_len, c, exists && (!rowwg || tid == 0), a, raw, npre);
 }
 
+// Column sums of a contraction's B operand over all of K, by the tiles of
+// the first tile row (F_BSUM): a column reduction of the same 2-D value B
+// reads runs here instead of as items of its own.  Thread (row lane rl,
+// chunk cc) sums rows rl, rl + RL, ... of 8 columns of the tile's column
+// block, 16 rows in flight (CC x RL = 16 x 16 for 128-wide tiles, 8 x 32 for
+// 64-wide); the row lanes are combined through LDS in order; then thread
+// i < bn runs the reduction's finishing program for column n0 + i, its
+// leading operands loaded before the sums.
+template <bool BF>
+DEV void bsum_rows(const GLOBAL uint16_t* p, const VView& B, uint32_t K, uint32_t N, uint32_t col, uint32_t rl,
+                   uint32_t RL, bool vec, float (&acc)[8]) {
+  constexpr int U = 16;
+  for (uint32_t r0 = rl; r0 < K; r0 += RL * U) {
+    if (vec) {
+      u32x4 v[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t r = r0 + RL * u < K ? r0 + RL * u : 0u;
+        v[u] = *(const GLOBAL u32x4*)(p + B.offset + (int64_t)r * B.stride[0] + col);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        if (r0 + RL * u >= K) continue;
+        float x[8];
+        widen8<BF>(v[u], x);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = acc[j] + x[j];
+      }
+    } else {
+      for (int u = 0; u < U; ++u) {
+        const uint32_t r = r0 + RL * u;
+        if (r >= K) break;
+        for (int j = 0; j < 8; ++j)
+          if (col + j < N)
+            acc[j] = acc[j] + half_bits_to_f32(p[B.offset + (int64_t)r * B.stride[0] + (int64_t)(col + j) * B.stride[1]], BF);
+      }
+    }
+  }
+}
+
+DEV void bsum_tile(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, const ItemState& st) {
+  if (st.m0 != 0) return;
+  // B's element (n, k) at off + k * stride[0] + n * stride[1]
+  const VView B = load_view(sd.off_views + t.vb * sizeof(DView));
+  const GLOBAL uint16_t* p = (const GLOBAL uint16_t*)base_ptr(ka, B.base);
+  const uint32_t bn = st.bn, n0 = st.n0, K = t.k, N = t.n;
+  const uint32_t CC = bn / 8, RL = kBlock / CC;
+  const uint32_t cc = tid % CC, rl = tid / CC;
+  const uint32_t col = n0 + cc * 8;
+  const uint32_t fin = sd.off_ins + t.bs_first * sizeof(DIns);
+  const uint32_t me = n0 + tid;
+  const uint32_t c[kMaxDims] = {me < N ? me : 0u, 0u, 0u, 0u};
+  uint32_t raw[kPre] = {0, 0, 0, 0};
+  const uint32_t npre = tid < bn ? prog_preload(ka, sd.off_views, fin, t.bs_len, c, raw) : 0u;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
+  if (col < N) {
+    const bool vec = aligned16(p) && B.stride[1] == 1 && N % 8 == 0 && (B.offset & 7) == 0 && (B.stride[0] & 7) == 0;
+    if (B.dtype == DT_BF16)
+      bsum_rows<true>(p, B, K, N, col, rl, RL, vec, acc);
+    else
+      bsum_rows<false>(p, B, K, N, col, rl, RL, vec, acc);
+  }
+  LDS float* red = (LDS float*)g_smem;  // [RL row lanes][bn columns]
+#pragma unroll
+  for (int j = 0; j < 8; ++j) red[rl * bn + cc * 8 + j] = acc[j];
+  __syncthreads();
+  if (tid < bn) {
+    float a = red[tid];
+    for (uint32_t q = 1; q < RL; ++q) a = a + red[q * bn + tid];
+    prog_run(tid, ka, sd.off_views, fin, t.bs_len, c, me < N, a, raw, npre);
+  }
+  __syncthreads();  // the next item may overwrite the LDS sums and the slots
+}
+
 // A stage record from the plan (wave-uniform).
 DEV DStage load_stage(const GLOBAL uint8_t* stages, uint32_t s) {
   constexpr int N = sizeof(DStage) / 4;
@@ -2394,6 +2470,7 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
         else
           fast_run<2>(tid, ka, t, sd.off_ins, st);
         __syncthreads();  // the next item may overwrite the LDS tile and the prefetched operands
+        if (t.flags & F_BSUM) bsum_tile(tid, ka, t, sd, st);
         return;
       }
       // a misaligned operand: the batches run the epilogue, over slots the
@@ -2439,6 +2516,7 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
   }
   // the next item may overwrite the LDS tile and scratch
   __syncthreads();
+  if (t.kind == T_GEMM_MFMA && (t.flags & F_BSUM)) bsum_tile(tid, ka, t, sd, st);
 }
 
 // Grid barrier: every workgroup gathers every arrival itself.

@@ -107,6 +107,8 @@ struct Builder {
   std::set<std::string> inlined_bufs;
   std::vector<Entry> sched;
   std::map<int, int> direct;       // output slot -> input index
+  std::map<int, int> colsum_of;    // contraction entry -> column reduction entry it also runs (F_BSUM)
+  std::map<int, int> colsum_host;  // that reduction entry -> the contraction entry
   std::map<std::string, int> bound;  // value -> output slot written directly
   std::map<std::string, Loc> loc;    // value -> storage
   std::map<std::string, uint64_t> arena_off;  // value -> byte offset in arena
@@ -887,6 +889,76 @@ struct Builder {
     }
   }
 
+  // Work items an entry puts into its stage (its first phase).
+  uint64_t entry_items(const Entry& e) const {
+    if (e.kind != 0) return ew_items(P.outputs[e.slot].numel());
+    const Op& o2 = op(e.op);
+    if (o2.cls == OC_POINTWISE) return ew_items(o2.out.numel());
+    if (o2.cls == OC_REDUCE) {
+      const RedChoice rc = choose_reduce(o2);
+      if (rc.kind == T_RED_COLS) return (uint64_t)((rc.rows + 255) / 256) * rc.parts;
+      return (uint64_t)rc.rows * rc.parts;
+    }
+    const GemmChoice g = choose_gemm(o2);
+    return (uint64_t)g.tm * g.tn * std::max<uint32_t>(1, g.split);
+  }
+
+  // ------------------------------------------------ fused column sums --
+  // A column reduction (sum or mean over dim 0) of a 2-D value V that is also
+  // the B operand of a contraction (B(k, n) = V[k][n], whole and contiguous)
+  // runs inside that contraction: its first tile row reads V's column block
+  // over all of K after the tile (V is an input of the tile, unchanged in the
+  // stage) and runs the reduction's finishing program per column.  Needed: an
+  // unsplit matrix-core tile, the reduction's values read by no other entry,
+  // and the reduction placed in the contraction's stage (its leveling
+  // constraint below).  Typical case: the bias gradient of a layer summed from
+  // the same gradient its weight-gradient product reads.  Worth it only when
+  // the reduction's own items would give some workgroups of its stage one
+  // more item than the rest have (otherwise they run on workgroups that
+  // would idle anyway) and K is at most 512 (at most two rounds of loads per
+  // row lane).  Runs on a first leveling; the stages are levelled again
+  // after.
+  void fuse_column_sums() {
+    if (!O.fuse_epilogues || !O.fast_epilogue || O.barrier_every_op) return;
+    const uint64_t G = (uint64_t)std::max(1, O.num_cus) * std::max(1, O.blocks_per_cu);
+    std::map<int, uint64_t> stage_items;
+    for (auto& e : sched) stage_items[e.level] += entry_items(e);
+    std::map<std::string, int> readers;  // value -> entries reading it
+    for (size_t i = 0; i < sched.size(); ++i)
+      for (auto& v : sched[i].reads_vals) readers[v]++;
+    for (size_t ri = 0; ri < sched.size(); ++ri) {
+      const Entry& r = sched[ri];
+      if (r.kind != 0 || op(r.op).cls != OC_REDUCE || colsum_host.count((int)ri)) continue;
+      const Op& ro = op(r.op);
+      const RedChoice rc = choose_reduce(ro);
+      if (rc.kind != T_RED_COLS || ro.args.size() != 1 || ro.args[0].scalar) continue;
+      const Spec& src = ro.args[0].spec;
+      if (src.shape.size() != 2 || src.offset != 0 || !src.contiguous() || is_input(src.buf)) continue;
+      if (inlined_bufs.count(src.buf) || src.dtype == DT_F32 || src.dtype == DT_I8) continue;
+      if (rc.R != src.shape[0] || rc.rows != src.shape[1]) continue;
+      bool used = false;  // another entry reads a value this reduction writes
+      for (auto& w : r.writes_vals)
+        if (readers.count(w)) used = true;
+      if (used) continue;
+      for (size_t xi = 0; xi < sched.size(); ++xi) {
+        const Entry& x = sched[xi];
+        if (x.kind != 0 || colsum_of.count((int)xi)) continue;
+        const Op& mo = op(x.op);
+        if (mo.cls != OC_MM) continue;
+        const Spec& B = mo.B();
+        if (B.buf != src.buf || B.shape != src.shape || B.offset != 0 || !B.contiguous()) continue;
+        const GemmChoice g = choose_gemm(mo);
+        if (g.kind != T_GEMM_MFMA || g.split > 1 || B.shape[0] > 512) continue;
+        const uint64_t here = stage_items[r.level], own = entry_items(r);
+        if ((here + G - 1) / G == (here - own + G - 1) / G) continue;
+        colsum_of[(int)xi] = (int)ri;
+        colsum_host[(int)ri] = (int)xi;
+        sched[ri].two_phase = false;
+        break;
+      }
+    }
+  }
+
   void level() {
     std::map<std::string, int> writer;
     for (size_t i = 0; i < sched.size(); ++i)
@@ -913,6 +985,9 @@ struct Builder {
             if (sched[r].kind == 0) L = std::max(L, sched[r].avail() + 1);
         }
         if (O.barrier_every_op && prev_last >= 0) L = std::max(L, prev_last + 1);
+        // a column reduction run by a contraction shares its stage
+        auto host = colsum_host.find((int)i);
+        if (host != colsum_host.end()) L = std::max(L, sched[host->second].level);
         if (L != e.level) {
           e.level = L;
           changed = true;
@@ -1953,6 +2028,22 @@ struct Builder {
     std::string desc = mm.name + " (" + mm.opcode + " " + std::to_string(m) + "x" + std::to_string(k) + "x" +
                        std::to_string(n) + ")";
     if (t.flags & F_FASTEPI) desc += " [register epilogue]";
+    auto cs = colsum_of.find((int)si);
+    if (cs != colsum_of.end()) {
+      // the fused column reduction's finishing program, over its n outputs
+      const Entry& re = sched[cs->second];
+      const Op& ro = op(re.op);
+      t.flags |= F_BSUM;
+      t.bs_first = reduction_finish(re, choose_reduce(ro));
+      t.bs_len = last_finish_len;
+      std::string rd = ro.name + " (" + ro.opcode + " " + std::to_string(n) + " outputs over " + std::to_string(k) + ")";
+      if (!re.side.empty()) {
+        rd += " +side";
+        for (int c : re.side) rd += " " + op(c).name;
+        if (re.discard_root) rd += " (root discarded)";
+      }
+      desc += " +column sums of B: " + rd;
+    }
     if (t.flags & F_XQ) desc += " [activations quantised to Q8_0]";
     if (!e.chain.empty()) {
       desc += e.update ? " +update" : " +epilogue";
@@ -1991,6 +2082,56 @@ struct Builder {
       put(e.level, t, desc);
     }
     if (g.kind == T_GEMM_MFMA) st.matrix_core_ops++;
+  }
+
+  // The finishing program of a reduction over its `rows` outputs (1-D): the
+  // mean's division, the rounding to the output dtype, then the side program
+  // (or the store of the root).  Returns its first instruction; its length is
+  // left in last_finish_len.
+  uint32_t last_finish_len = 0;
+  uint32_t reduction_finish(const Entry& e, const RedChoice& rc) {
+    const Op& r = op(e.op);
+    ExprCtx fx;
+    vstride_full.clear();
+    fx.space = {rc.rows};
+    std::vector<DIns> fin;
+    if (r.opcode == "mean") {
+      DIns dv{};
+      dv.op = VM_DIV;
+      dv.src = SRC_SCALAR;
+      dv.s = (float)rc.R;
+      dv.rnd = RND_NONE;
+      fin.push_back(dv);
+    }
+    if (r.out.dtype != DT_F32) {
+      DIns s{};
+      s.op = VM_SCALE;
+      s.a = 1.0f;
+      s.rnd = r.out.dtype;
+      fin.push_back(s);
+    }
+    if (!e.side.empty()) {
+      // side ops over the outputs, addressed as one flat index
+      if (r.out.shape.size() != 1) fx.flat = &r.out.shape;
+      emit_side_program(e, fx, fin, {0});
+      for (size_t v = 0; v < fx.vtab.size(); ++v) fx.vtab[v].stride[0] = vstride_full[v][0];
+    } else {
+      Spec flat = r.out;
+      flat.shape = {rc.rows};
+      flat.strides = {1};
+      DIns stv{};
+      stv.op = VM_STORE;
+      stv.rnd = RND_NONE;
+      stv.arg = (uint16_t)fx.vtab.size();
+      std::vector<int> m1 = {0};
+      fx.vtab.push_back(lift(flat, m1, storage_of(r.out.buf), 1));
+      fin.push_back(stv);
+      fx.vtab.back().stride[0] = vstride_full.back()[0];
+    }
+    uint32_t fvb = commit_views(fx);
+    const uint32_t first = commit_code(fin, fvb);  // (the peephole may shorten fin)
+    last_finish_len = (uint32_t)fin.size();
+    return first;
   }
 
   void emit_reduction(size_t si) {
@@ -2058,53 +2199,15 @@ struct Builder {
     }
     uint32_t vb = commit_views(cx);
     uint32_t src_first = commit_code(code, vb);
-    // finishing program over the output (1-D of `rows`)
-    ExprCtx fx;
-    vstride_full.clear();
-    fx.space = {rc.rows};
-    std::vector<DIns> fin;
-    if (r.opcode == "mean") {
-      DIns dv{};
-      dv.op = VM_DIV;
-      dv.src = SRC_SCALAR;
-      dv.s = (float)rc.R;
-      dv.rnd = RND_NONE;
-      fin.push_back(dv);
-    }
-    if (r.out.dtype != DT_F32) {
-      DIns s{};
-      s.op = VM_SCALE;
-      s.a = 1.0f;
-      s.rnd = r.out.dtype;
-      fin.push_back(s);
-    }
-    if (!e.side.empty()) {
-      // side ops over the outputs, addressed as one flat index
-      if (r.out.shape.size() != 1) fx.flat = &r.out.shape;
-      emit_side_program(e, fx, fin, {0});
-      for (size_t v = 0; v < fx.vtab.size(); ++v) fx.vtab[v].stride[0] = vstride_full[v][0];
-    } else {
-      Spec flat = r.out;
-      flat.shape = {rc.rows};
-      flat.strides = {1};
-      DIns stv{};
-      stv.op = VM_STORE;
-      stv.rnd = RND_NONE;
-      stv.arg = (uint16_t)fx.vtab.size();
-      std::vector<int> m1 = {0};
-      fx.vtab.push_back(lift(flat, m1, storage_of(r.out.buf), 1));
-      fin.push_back(stv);
-      fx.vtab.back().stride[0] = vstride_full.back()[0];
-    }
-    uint32_t fvb = commit_views(fx);
-    uint32_t fin_first = commit_code(fin, fvb);
+    const uint32_t fin_first = reduction_finish(e, rc);
+    const uint32_t fin_len = last_finish_len;
     DTask t = blank(rc.kind);
     t.ndim = (uint8_t)dims.size();
     for (size_t d = 0; d < dims.size(); ++d) t.dims[d] = (uint32_t)dims[d];
     t.expr_first = src_first;
     t.expr_len = (uint32_t)code.size();
     t.fin_first = fin_first;
-    t.fin_len = (uint32_t)fin.size();
+    t.fin_len = fin_len;
     t.split = rc.parts;
     t.kchunk = rc.kchunk;
     t.count = (float)rc.R;
@@ -2143,7 +2246,7 @@ struct Builder {
       f.split = rc.parts;
       f.scratch = t.scratch;
       f.fin_first = fin_first;
-      f.fin_len = (uint32_t)fin.size();
+      f.fin_len = fin_len;
       f.count = t.count;
       f.flags = t.flags & F_MEAN;
       f.tile = rc.kind == T_RED_COLS ? 1 : 0;  // partial layout: [parts][rows] (cols) or [rows][parts]
@@ -2246,6 +2349,8 @@ struct Builder {
     }
     collect_rw();
     level();
+    fuse_column_sums();
+    if (!colsum_host.empty()) level();
     size_scratch();
     plan_arena();
     check_hazards();
@@ -2258,10 +2363,11 @@ struct Builder {
       const Op& o2 = op(e.op);
       if (o2.cls == OC_POINTWISE)
         emit_pointwise(e);
-      else if (o2.cls == OC_REDUCE)
-        emit_reduction(i);
-      else
+      else if (o2.cls == OC_REDUCE) {
+        if (!colsum_host.count((int)i)) emit_reduction(i);
+      } else {
         emit_contraction(i);
+      }
     }
     return encode();
   }
@@ -2347,6 +2453,7 @@ struct Builder {
         }
         task.expr_first = task.expr_len ? mapcode(task.expr_first, task.expr_len) : 0;
         task.fin_first = task.fin_len ? mapcode(task.fin_first, task.fin_len) : 0;
+        task.bs_first = task.bs_len ? mapcode(task.bs_first, task.bs_len) : 0;
         tk.push_back(task);
         gd << "  " << kind_name(task.kind) << " items=" << task.n_items << " : " << gdesc[t] << "\n";
         auto prog = [&](const char* what, uint32_t first, uint32_t len) {
@@ -2357,6 +2464,7 @@ struct Builder {
         };
         prog("code", task.expr_first, task.expr_len);
         if (!(task.flags & F_FASTEPI)) prog("finish", task.fin_first, task.fin_len);
+        prog("column sums", task.bs_first, task.bs_len);
       }
       DStage& d = e.d;
       d = DStage{};

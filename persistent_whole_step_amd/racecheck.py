@@ -31,14 +31,14 @@ import numpy as np
 
 # csrc/plan.h
 T_EW, T_GEMM_MFMA, T_GEMM_SIMT, T_GEMM_REDUCE, T_GEMV_Q8, T_GEMV, T_RED_ROWS, T_RED_COLS, T_RED_FINAL = range(1, 10)
-F_PARTIAL, F_ROWWG, F_COLLANES32 = 2, 4, 256  # plan.h flags
+F_PARTIAL, F_ROWWG, F_COLLANES32, F_BSUM = 2, 4, 256, 512  # plan.h flags
 VM_STORE = 12
 SRC_VIEW = 1
 KBLOCK = 256
 GEMV_ROWS = 4
 ESIZE = {0: 4, 1: 2, 2: 2, 3: 1}
 
-_TASK = struct.Struct("<BBBBI6I4I4I4B3I4I4HQfI")
+_TASK = struct.Struct("<BBBBI6I4I4I4B3I4I4HQfI2I")
 _VIEW = struct.Struct("<q4qHB5x")
 _INS = struct.Struct("<BBBBHHff")
 _STAGE = struct.Struct("<8I")
@@ -71,6 +71,8 @@ class Task:
     vs: int
     vx: int
     scratch: int
+    bs_first: int = 0
+    bs_len: int = 0
 
 
 @dataclass
@@ -94,7 +96,7 @@ def decode(plan: bytes) -> list:
     magic, n_stages, off_stages, nbytes = _HEADER.unpack_from(plan, 0)[:4]
     if magic != 0x31706B74:
         raise ValueError("not a tk plan")
-    assert _TASK.size == 120 and _VIEW.size == 48 and _INS.size == 16
+    assert _TASK.size == 128 and _VIEW.size == 48 and _INS.size == 16
     stages = []
     for s in range(n_stages):
         blob_off, blob_bytes, n_tasks, n_items, off_views, off_ins, n_views, n_ins = _STAGE.unpack_from(
@@ -106,7 +108,7 @@ def decode(plan: bytes) -> list:
                               item_begin=f[6], expr_first=f[7], expr_len=f[8], fin_first=f[9], fin_len=f[10],
                               dims=tuple(f[11:15]), m=f[23], n=f[24], k=f[25], split=f[26], kchunk=f[27],
                               tiles_m=f[28], tiles_n=f[29], va=f[30], vb=f[31], vs=f[32], vx=f[33],
-                              scratch=f[34]))
+                              scratch=f[34], bs_first=f[37], bs_len=f[38]))
         assert off_views >= n_tasks * _TASK.size
         views = []
         for i in range(n_views):
@@ -309,6 +311,7 @@ class Checker:
         for ti, t in enumerate(st.tasks):
             epi = self._prog_views(st, t.expr_first, t.expr_len)
             fin = self._prog_views(st, t.fin_first, t.fin_len)
+            bsum = self._prog_views(st, t.bs_first, t.bs_len)
             name = f"stage {s} task {ti} kind {t.kind}"
             if t.kind in (T_GEMM_MFMA, T_GEMM_SIMT):
                 bm = 128 if (t.kind == T_GEMM_MFMA and t.tile == 0) else 64
@@ -336,6 +339,14 @@ class Checker:
                                       sp * mm * nn + rr[:, None] * nn + cc[None, :])
                     else:
                         self._grid_views(out, st, t, item, epi, m0, m1, n0, n1, name + " epilogue")
+                    if t.flags & F_BSUM and tm == 0:
+                        # the first tile row also sums B over all of K for its
+                        # columns and runs the fused reduction's finish on them
+                        kall = np.arange(0, t.k)
+                        self._acc(out, st, t.vb, False, item, name + " B column sums", [(0, t.k), (n0, n1)],
+                                  lambda B=B, kall=kall, cc=cc: _view_bytes(B, (kall[:, None], cc[None, :])))
+                        self._linear_views(out, st, t, item, bsum, n0, n1, (t.n, 1, 1, 1), 1,
+                                           name + " column sums")
             elif t.kind == T_GEMM_REDUCE:
                 total = t.m * t.n
                 for it in range(t.n_items):

@@ -395,14 +395,26 @@ def test_register_epilogue_marking(name, marked, gemms):
     assert d1.count("[register epilogue]") == 0 and d1.count("[rows summed directly]") == 0
 
 
-def test_column_sums_read_directly():
-    """Bias-gradient sums over at most 256 rows of a materialised gradient are
-    one part each (no combine stage) and are summed straight from memory;
-    the 3-layer bf16 MLP step then needs 6 stages."""
-    d = tk.compile(programs.build(programs.CONFIGS["c2"]).text(), device=-1)
+def test_column_sums_in_weight_gradient_tiles_or_read_directly():
+    """A bias-gradient sum whose own items would give some workgroups of its
+    stage one more item than the rest runs inside the weight-gradient
+    product that reads the same gradient (its first tile row sums B over K
+    and runs the sum's finish, the bias update included), when K is at most
+    512: in the 16-layer residual MLP every stage is full, so all 16 sums
+    move and the step needs 32 stages.  Otherwise the sums stay column
+    reductions read straight from memory: one part up to 256 rows (the
+    3-layer bf16 MLP, 6 stages), fp32 partials and a combine at 512 rows,
+    one 32-row-lane part from 513 to 1024 rows (the 4096-wide MLP)."""
+    c2 = programs.build(programs.CONFIGS["c2"]).text()
+    c5 = programs.build(programs.CONFIGS["c5"]).text()
+    d = tk.compile(c2, device=-1)
     text = d.dump()
-    assert text.count("[rows summed directly]") == 3
+    assert text.count("[rows summed directly]") == 3 and "+column sums of B: " not in text
     assert d.query()["n_stages"] == 6
-    # over 256 rows the sums keep their partials (combine stage) and still read directly
-    d5 = tk.compile(programs.build(programs.CONFIGS["c5"]).text(), device=-1).dump()
-    assert "reduce_final" in d5 and "[rows summed directly]" in d5
+    d5 = tk.compile(c5, device=-1)
+    t5 = d5.dump()
+    assert t5.count("+column sums of B: ") == 16 and "reduce_cols" not in t5 and d5.query()["n_stages"] == 32
+    u5 = tk.compile(c5, device=-1, fuse_epilogues=0).dump()
+    assert "reduce_final" in u5 and "[rows summed directly]" in u5 and "[16 partials]" in u5
+    d4 = tk.compile(programs.build(programs.CONFIGS["c4"]).text(), device=-1).dump()
+    assert "[rows summed directly]" in d4 and "+column sums of B: " not in d4
