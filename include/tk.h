@@ -93,7 +93,11 @@ typedef struct {
                                   is one load reads its rows straight into registers; 1: every
                                   epilogue and reduction source runs on the expression machine's
                                   batches (same partitions, same results, bit for bit) */
-  int32_t reserved[1];
+  int32_t colsum_fusion;       /* column sums of a contraction's B operand (a bias gradient
+                                  summed from the gradient its weight-gradient product reads)
+                                  computed by that product's first tile row: 0 (default) where
+                                  the reduction's own items would add a round of items to its
+                                  stage and K <= 512; 1 wherever legal; -1 never */
 } tk_options;
 
 /* Plan and kernel statistics (pages: `GeneratedKernel` and `resource_usage`). */

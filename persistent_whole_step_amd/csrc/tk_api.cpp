@@ -212,6 +212,7 @@ tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int3
     if (o.force_grid < 0) return fail(TK_E_ARG, "force_grid must not be negative");
     if (o.launch_mode != 0 && o.launch_mode != 1) return fail(TK_E_ARG, "launch_mode must be 0 or 1");
     if (o.gemm_tile < 0 || o.gemm_tile > 2) return fail(TK_E_ARG, "gemm_tile must be 0, 1 or 2");
+    if (o.colsum_fusion < -1 || o.colsum_fusion > 1) return fail(TK_E_ARG, "colsum_fusion must be -1, 0 or 1");
     so.blocks_per_cu = o.blocks_per_cu;
     so.max_blocks = o.max_blocks;
     so.fuse_pointwise = o.fuse_pointwise != 0;
@@ -224,6 +225,7 @@ tk_status tk_compile(const char* ir, size_t ir_len, const tk_options* opts, int3
     so.launch_mode = o.launch_mode;
     so.gemm_tile = o.gemm_tile;
     so.fast_epilogue = o.batch_epilogues == 0;
+    so.colsum_fusion = o.colsum_fusion;
     so.num_cus = o.num_cus > 0 ? o.num_cus : 256;
     int occupancy = 0;
     hipFuncAttributes attr{};

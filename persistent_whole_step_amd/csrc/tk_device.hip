@@ -53,6 +53,8 @@ constexpr int kVmElems = 16;                       // elements per thread per ma
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -811,6 +813,23 @@ DEV f32x16 mfma32(u32x4 a, u32x4 b, f32x16 c) {
                                                 0);
 }
 
+// s plus the eight 16-bit values of a fragment, as dot products with (1, 1)
+// (the products are exact; each step rounds once to fp32).
+template <bool BF16>
+DEV float frag_sum(u32x4 v, float s) {
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    // (a bit cast of the subscript v[q] itself reads element 0: copy it out)
+    const uint32_t w = v[q];
+    if (BF16)
+      s = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, w), __builtin_bit_cast(bf16x2, 0x3f803f80u), s,
+                                          false);
+    else
+      s = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, w), __builtin_bit_cast(f16x2, 0x3c003c00u), s, false);
+  }
+  return s;
+}
+
 // MFMA fragment of `row0 + lane%32` (rows of an R-row operand), k = kk + 8*(lane/32) .. +7.
 // KM: the operand is staged k-major (else row-major, read transposed).
 template <int R, bool KM>
@@ -880,10 +899,12 @@ DEV void read_frags(uint32_t tid, const LDS uint16_t* sa, const LDS uint16_t* sb
 // for slice k + 1, the workgroup meets (every wave has its fragments of slice
 // k in registers and every wave's copy of slice k + 1 has landed), slice
 // k + S is issued into slice k's stage, and the first fragments of slice
-// k + 1 are read under the last MFMAs of slice k.
-template <int BM, int BN, bool BF16, bool AKM, bool BKM, int S>
+// k + 1 are read under the last MFMAs of slice k.  CS: also sum each of the
+// wave's B fragments into bsum (lane l: column l % 32 of fragment j, the
+// half of every k step that the lane holds).
+template <int BM, int BN, bool BF16, bool AKM, bool BKM, int S, bool CS>
 DEV void direct_loop(uint32_t tid, const DirectOp<BM>& da, const DirectOp<BN>& db, uint32_t nk,
-                     f32x16 (&acc)[BM / 64][BN / 64]) {
+                     f32x16 (&acc)[BM / 64][BN / 64], float (&bsum)[BN / 64]) {
   constexpr int FM = BM / 64, FN = BN / 64, KS = kBK / 16;
   constexpr int SA = BM * kBK * 2, SB = BN * kBK * 2;
   constexpr int LPS = BM / 32 + BN / 32;  // direct loads per wave per slice
@@ -938,6 +959,10 @@ DEV void direct_loop(uint32_t tid, const DirectOp<BM>& da, const DirectOp<BN>& d
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j) acc[i][j] = mfma32<BF16>(fa[cur][i], fb[cur][j], acc[i][j]);
+      if constexpr (CS) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) bsum[j] = frag_sum<BF16>(fb[cur][j], bsum[j]);
+      }
       // interleave: MFMA, DPM fragment reads, MFMA, ...
 #pragma unroll
       for (int m = 0; m < NMF; ++m) {
@@ -956,10 +981,10 @@ DEV void direct_loop(uint32_t tid, const DirectOp<BM>& da, const DirectOp<BN>& d
 // into partial sum s % 4 (four independent chains), and the partials are
 // added in a fixed order at the end.  The fragments are double-buffered by
 // slice: all of slice k + 1's fragments are read from LDS while slice k's
-// four MFMAs run.
-template <bool BF16, bool AKM, bool BKM, int S>
+// four MFMAs run.  CS: as in direct_loop.
+template <bool BF16, bool AKM, bool BKM, int S, bool CS>
 DEV void direct_loop64(uint32_t tid, const DirectOp<64>& da, const DirectOp<64>& db, uint32_t nk,
-                       f32x16 (&acc)[1][1]) {
+                       f32x16 (&acc)[1][1], float (&cs)[1]) {
   constexpr int KS = kBK / 16;
   constexpr int SA = 64 * kBK * 2, SB = 64 * kBK * 2;
   constexpr int LPS = 4;                                  // direct loads per wave per slice
@@ -1017,6 +1042,10 @@ DEV void direct_loop64(uint32_t tid, const DirectOp<64>& da, const DirectOp<64>&
     }
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) part[ks] = mfma32<BF16>(fa[C][ks], fb[C][ks], part[ks]);
+    if constexpr (CS) {
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) cs[0] = frag_sum<BF16>(fb[C][ks], cs[0]);
+    }
 #pragma unroll
     for (int m = 0; m < KS; ++m) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
@@ -1039,9 +1068,11 @@ DEV void direct_loop64(uint32_t tid, const DirectOp<64>& da, const DirectOp<64>&
 // accumulators never change registers between the two instruction forms.
 // before_loop() runs once the tile's coordinates are in `st`, before the
 // first operand load: its loads complete ahead of the ring's (loads retire in
-// issue order) and land in the arena above the ring.
+// issue order) and land in the arena above the ring.  Returns whether B's
+// column sums came out of the main loop (then they are in the C tile's
+// padding, see the end).
 template <int BM, int BN, bool BF16, class BeforeLoop>
-DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st,
+DEV bool gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_off, uint32_t item, ItemState& st,
                    BeforeLoop before_loop) {
   constexpr int FM = BM / 64, FN = BN / 64;  // 32x32 blocks per wave along m / n
   constexpr int S = BM == 128 ? 3 : 4;       // ring stages (S * (BM + BN) * 128 bytes <= the arena)
@@ -1084,7 +1115,16 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
   const int64_t a_other = a_kc ? A.stride[0] : A.stride[1], b_other = b_kc ? B.stride[1] : B.stride[0];
   const bool a_ok = m0 + BM <= t.m && (a_kc || a_rc) && aligned16(pa) && (A.offset & 7) == 0 && (a_other & 7) == 0;
   const bool b_ok = n0 + BN <= t.n && (b_kc || b_rc) && aligned16(pb) && (B.offset & 7) == 0 && (b_other & 7) == 0;
-  if (nk > 0 && full_k && a_ok && b_ok) {
+  // B's column sums over all of K come out of the main loop for the first
+  // tile row of a product that carries them (A and B staged row-major, the
+  // whole of K in one part)
+  float cs[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) cs[j] = 0.0f;
+  const bool direct = nk > 0 && full_k && a_ok && b_ok;
+  const bool csum = direct && (t.flags & F_BSUM) && (t.flags & F_FASTEPI) && m0 == 0 && !a_kc && !b_kc &&
+                    kbeg == 0 && kend == t.k;
+  if (direct) {
     DirectOp<BM> da;
     DirectOp<BN> db;
     da.init(tid, a_kc, pa, A.offset, A.stride[0], A.stride[1], m0, kbeg);
@@ -1092,25 +1132,29 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
     if constexpr (BM == 64 && BN == 64) {
       if (a_kc) {
         if (b_kc)
-          direct_loop64<BF16, true, true, S>(tid, da, db, nk, acc);
+          direct_loop64<BF16, true, true, S, false>(tid, da, db, nk, acc, cs);
         else
-          direct_loop64<BF16, true, false, S>(tid, da, db, nk, acc);
+          direct_loop64<BF16, true, false, S, false>(tid, da, db, nk, acc, cs);
       } else {
         if (b_kc)
-          direct_loop64<BF16, false, true, S>(tid, da, db, nk, acc);
+          direct_loop64<BF16, false, true, S, false>(tid, da, db, nk, acc, cs);
+        else if (csum)
+          direct_loop64<BF16, false, false, S, true>(tid, da, db, nk, acc, cs);
         else
-          direct_loop64<BF16, false, false, S>(tid, da, db, nk, acc);
+          direct_loop64<BF16, false, false, S, false>(tid, da, db, nk, acc, cs);
       }
     } else if (a_kc) {
       if (b_kc)
-        direct_loop<BM, BN, BF16, true, true, S>(tid, da, db, nk, acc);
+        direct_loop<BM, BN, BF16, true, true, S, false>(tid, da, db, nk, acc, cs);
       else
-        direct_loop<BM, BN, BF16, true, false, S>(tid, da, db, nk, acc);
+        direct_loop<BM, BN, BF16, true, false, S, false>(tid, da, db, nk, acc, cs);
     } else {
       if (b_kc)
-        direct_loop<BM, BN, BF16, false, true, S>(tid, da, db, nk, acc);
+        direct_loop<BM, BN, BF16, false, true, S, false>(tid, da, db, nk, acc, cs);
+      else if (csum)
+        direct_loop<BM, BN, BF16, false, false, S, true>(tid, da, db, nk, acc, cs);
       else
-        direct_loop<BM, BN, BF16, false, false, S>(tid, da, db, nk, acc);
+        direct_loop<BM, BN, BF16, false, false, S, false>(tid, da, db, nk, acc, cs);
     }
   } else {
     LDS uint16_t* sa0 = (LDS uint16_t*)g_smem;
@@ -1137,6 +1181,16 @@ DEV void gemm_mfma(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t views_o
         const int col = wn * (BN / 2) + j * 32 + (lane % 32);
         C[row * pitch + col] = acc[i][j][r];
       }
+  // column sums -> the tile's padding: column c's two halves at padding
+  // slots 2c and 2c + 1 (slot p at row p / 4, column BN + p % 4)
+  if (csum && uniform((uint32_t)wm) == 0) {
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int p = 2 * (wn * (BN / 2) + j * 32 + lane % 32) + lane / 32;
+      C[(p / 4) * pitch + BN + p % 4] = cs[j];
+    }
+  }
+  return csum;
 }
 
 // ------------------------------------------------------ int8-weight GEMV --
@@ -2368,7 +2422,7 @@ DEV void bsum_rows(const GLOBAL uint16_t* p, const VView& B, uint32_t K, uint32_
   }
 }
 
-DEV void bsum_tile(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, const ItemState& st) {
+DEV void bsum_tile(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd, const ItemState& st, bool summed) {
   if (st.m0 != 0) return;
   // B's element (n, k) at off + k * stride[0] + n * stride[1]
   const VView B = load_view(sd.off_views + t.vb * sizeof(DView));
@@ -2382,6 +2436,17 @@ DEV void bsum_tile(uint32_t tid, const Ctx& ka, const DTask& t, const DStage& sd
   const uint32_t c[kMaxDims] = {me < N ? me : 0u, 0u, 0u, 0u};
   uint32_t raw[kPre] = {0, 0, 0, 0};
   const uint32_t npre = tid < bn ? prog_preload(ka, sd.off_views, fin, t.bs_len, c, raw) : 0u;
+  if (summed) {
+    // the main loop's sums, two halves per column in the C tile's padding
+    if (tid < bn) {
+      const LDS float* pad = (const LDS float*)g_smem + bn;
+      const uint32_t pitch = bn + 4, p = 2 * tid;
+      const float a = pad[(p / 4) * pitch + p % 4] + pad[((p + 1) / 4) * pitch + (p + 1) % 4];
+      prog_run(tid, ka, sd.off_views, fin, t.bs_len, c, me < N, a, raw, npre);
+    }
+    __syncthreads();  // the next item may overwrite the tile and the slots
+    return;
+  }
   float acc[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) acc[j] = 0.0f;
@@ -2452,16 +2517,17 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
         if (!(t.flags & F_FASTEPI)) return;
         fast = t.tile == 0 ? fast_prefetch<8>(tid, ka, t, sd.off_ins, st) : fast_prefetch<2>(tid, ka, t, sd.off_ins, st);
       };
+      bool csum;
       if (t.tile == 0) {
         if (bf16)
-          gemm_mfma<128, 128, true>(tid, ka, t, sd.off_views, item, st, before_loop);
+          csum = gemm_mfma<128, 128, true>(tid, ka, t, sd.off_views, item, st, before_loop);
         else
-          gemm_mfma<128, 128, false>(tid, ka, t, sd.off_views, item, st, before_loop);
+          csum = gemm_mfma<128, 128, false>(tid, ka, t, sd.off_views, item, st, before_loop);
       } else {
         if (bf16)
-          gemm_mfma<64, 64, true>(tid, ka, t, sd.off_views, item, st, before_loop);
+          csum = gemm_mfma<64, 64, true>(tid, ka, t, sd.off_views, item, st, before_loop);
         else
-          gemm_mfma<64, 64, false>(tid, ka, t, sd.off_views, item, st, before_loop);
+          csum = gemm_mfma<64, 64, false>(tid, ka, t, sd.off_views, item, st, before_loop);
       }
       __syncthreads();
       if (fast) {
@@ -2470,7 +2536,7 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
         else
           fast_run<2>(tid, ka, t, sd.off_ins, st);
         __syncthreads();  // the next item may overwrite the LDS tile and the prefetched operands
-        if (t.flags & F_BSUM) bsum_tile(tid, ka, t, sd, st);
+        if (t.flags & F_BSUM) bsum_tile(tid, ka, t, sd, st, csum);
         return;
       }
       // a misaligned operand: the batches run the epilogue, over slots the
@@ -2516,7 +2582,8 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
   }
   // the next item may overwrite the LDS tile and scratch
   __syncthreads();
-  if (t.kind == T_GEMM_MFMA && (t.flags & F_BSUM)) bsum_tile(tid, ka, t, sd, st);
+  // (the batches may have overwritten the sums in the tile's padding)
+  if (t.kind == T_GEMM_MFMA && (t.flags & F_BSUM)) bsum_tile(tid, ka, t, sd, st, false);
 }
 
 // Grid barrier: every workgroup gathers every arrival itself.

@@ -86,6 +86,7 @@ struct Options {
   int launch_mode = 0;  // 0 cooperative, 1 ordinary launch of a co-resident grid
   int gemm_tile = 0;    // 0 automatic, 1 force 128x128, 2 force 64x64
   bool fast_epilogue = true;  // contraction epilogues may run as register programs, column sums read directly
+  int colsum_fusion = 0;      // 0 where it saves a round of items, 1 wherever legal, -1 never
 };
 
 // Compiled plan: device bytes plus host-side description for queries/dumps.

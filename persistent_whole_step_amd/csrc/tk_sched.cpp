@@ -906,20 +906,23 @@ struct Builder {
   // ------------------------------------------------ fused column sums --
   // A column reduction (sum or mean over dim 0) of a 2-D value V that is also
   // the B operand of a contraction (B(k, n) = V[k][n], whole and contiguous)
-  // runs inside that contraction: its first tile row reads V's column block
-  // over all of K after the tile (V is an input of the tile, unchanged in the
-  // stage) and runs the reduction's finishing program per column.  Needed: an
+  // runs inside that contraction: its first tile row sums V's column block
+  // over all of K (from the B fragments of its main loop, or by reading V
+  // again after the tile; V is an input of the tile, unchanged in the stage)
+  // and runs the reduction's finishing program per column.  Needed: an
   // unsplit matrix-core tile, the reduction's values read by no other entry,
   // and the reduction placed in the contraction's stage (its leveling
   // constraint below).  Typical case: the bias gradient of a layer summed from
-  // the same gradient its weight-gradient product reads.  Worth it only when
-  // the reduction's own items would give some workgroups of its stage one
-  // more item than the rest have (otherwise they run on workgroups that
-  // would idle anyway) and K is at most 512 (at most two rounds of loads per
-  // row lane).  Runs on a first leveling; the stages are levelled again
-  // after.
+  // the same gradient its weight-gradient product reads.  By default only
+  // where the reduction's own items would give some workgroups of its stage
+  // one more item than the rest have (otherwise they run on workgroups that
+  // would idle anyway) and K is at most 512 (the first tile row's longer
+  // epilogue then costs less than a round of items); colsum_fusion = 1 fuses
+  // wherever legal, -1 never.  Runs on a first leveling; the stages are
+  // levelled again after.
   void fuse_column_sums() {
-    if (!O.fuse_epilogues || !O.fast_epilogue || O.barrier_every_op) return;
+    if (!O.fuse_epilogues || !O.fast_epilogue || O.barrier_every_op || O.colsum_fusion < 0) return;
+    const bool always = O.colsum_fusion > 0;
     const uint64_t G = (uint64_t)std::max(1, O.num_cus) * std::max(1, O.blocks_per_cu);
     std::map<int, uint64_t> stage_items;
     for (auto& e : sched) stage_items[e.level] += entry_items(e);
@@ -948,9 +951,9 @@ struct Builder {
         const Spec& B = mo.B();
         if (B.buf != src.buf || B.shape != src.shape || B.offset != 0 || !B.contiguous()) continue;
         const GemmChoice g = choose_gemm(mo);
-        if (g.kind != T_GEMM_MFMA || g.split > 1 || B.shape[0] > 512) continue;
+        if (g.kind != T_GEMM_MFMA || g.split > 1) continue;
         const uint64_t here = stage_items[r.level], own = entry_items(r);
-        if ((here + G - 1) / G == (here - own + G - 1) / G) continue;
+        if (!always && (B.shape[0] > 512 || (here + G - 1) / G == (here - own + G - 1) / G)) continue;
         colsum_of[(int)xi] = (int)ri;
         colsum_host[(int)ri] = (int)xi;
         sched[ri].two_phase = false;

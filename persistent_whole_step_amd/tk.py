@@ -36,8 +36,7 @@ class TkOptions(ctypes.Structure):
     _fields_ = [(n, ctypes.c_int32) for n in (
         "blocks_per_cu", "max_blocks", "fuse_pointwise", "fuse_epilogues", "inline_input_casts",
         "split_k_gemv", "threads_per_block", "fuse_updates", "barrier_every_op", "num_cus",
-        "gemm_split_k", "force_grid", "launch_mode", "gemm_tile", "batch_epilogues")] + [
-            ("reserved", ctypes.c_int32 * 1)]
+        "gemm_split_k", "force_grid", "launch_mode", "gemm_tile", "batch_epilogues", "colsum_fusion")]
 
 
 STATS_FIELDS = ["n_stages", "grid_barriers", "materialized_ops", "inlined_ops", "fused_epilogues",

@@ -440,6 +440,16 @@ def _column_sum_values(dump: str) -> set:
     return names
 
 
+def _assert_sums_within_one_ulp(got, want, spec):
+    """Column-sum values added in another row order: one ulp apart at most."""
+    g, w = parity.f32_of(got, spec.dtype), parity.f32_of(want, spec.dtype)
+    if spec.dtype == "f32":
+        tol = np.spacing(np.abs(w).astype(np.float32))
+    else:
+        tol = parity.ulp16(w, spec.dtype)
+    assert np.all(np.abs(g - w) <= tol), f"{spec.buf}: more than one ulp apart"
+
+
 @pytest.mark.parametrize("name", ["c1", "c2s", "c4s", "c5s", "c2sa"])
 def test_register_epilogue_matches_batches(name):
     """Contraction epilogues run from registers (the default where the
@@ -463,13 +473,49 @@ def test_register_epilogue_matches_batches(name):
     for a, b, s in zip(o1, o2, base.outputs):
         if s.buf not in summed:
             parity.assert_bitexact(a, b, s.dtype, s.buf)
-            continue
-        g, w = parity.f32_of(a, s.dtype), parity.f32_of(b, s.dtype)
-        if s.dtype == "f32":
-            tol = np.spacing(np.abs(w).astype(np.float32))
         else:
-            tol = parity.ulp16(w, s.dtype)
-        assert np.all(np.abs(g - w) <= tol), f"{s.buf}: more than one ulp apart"
+            _assert_sums_within_one_ulp(a, b, s)
+
+
+# Bias gradients summed by the first tile row of their weight-gradient
+# product (colsum_fusion=1 forces it where the default would not).  A batch
+# of 128 or 192 rows puts K on whole 64-deep slices, so the sums come out of
+# the product's main loop (an even and an odd number of slices); the 160 and
+# 96 rows of the small configs do not, and their tiles read the rows again
+# after the product; 48 output columns leave a partial tile.
+COLSUM = {
+    "mlp-bf16-k128": dict(kind="mlp", dims=(256, 384, 256, 128), batch=128, dtype="bf16", lr=1e-4),
+    "res-f16-k192": dict(kind="residual", width=256, layers=4, batch=192, dtype="f16", lr=1e-4),
+    "c4s": SMALL["c4s"],
+    "c2s": SMALL["c2s"],
+}
+
+
+@pytest.mark.parametrize("tile", [1, 2])
+@pytest.mark.parametrize("name", list(COLSUM))
+def test_column_sums_in_weight_gradient_tiles(oracle_mod, name, tile):
+    """Per node against the oracle with the sums in the tiles (128x128 and
+    64x64 tiles), and against the same step with the sums run as reductions
+    of their own: bit-identical except the summed values (one ulp)."""
+    cfg = COLSUM[name]
+    say("column sums in weight-gradient tiles", name, "tile", tile)
+    base = programs.build(cfg)
+    probe = base.probe()
+    ins = programs.inputs_for(cfg, 4)
+    outs, pp = parity.gpu_run(probe, [a.copy() for a in ins], colsum_fusion=1, gemm_tile=tile)
+    assert "+column sums of B: " in pp.dump()
+    vals = parity.probe_values(base, probe, outs)
+    assert parity.check_per_node(oracle_mod, base, ins, vals) == len(base.ops)
+    o1, p1 = parity.gpu_run(base, [a.copy() for a in ins], colsum_fusion=1, gemm_tile=tile)
+    o2, p2 = parity.gpu_run(base, [a.copy() for a in ins], colsum_fusion=-1, gemm_tile=tile)
+    d1 = p1.dump()
+    assert "+column sums of B: " in d1 and "+column sums of B: " not in p2.dump()
+    summed = _column_sum_values(d1)
+    for a, b, s in zip(o1, o2, base.outputs):
+        if s.buf not in summed:
+            parity.assert_bitexact(a, b, s.dtype, s.buf)
+        else:
+            _assert_sums_within_one_ulp(a, b, s)
 
 
 @pytest.mark.parametrize("name", ["c2s", "c5s"])

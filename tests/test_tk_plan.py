@@ -418,3 +418,18 @@ def test_column_sums_in_weight_gradient_tiles_or_read_directly():
     assert "reduce_final" in u5 and "[rows summed directly]" in u5 and "[16 partials]" in u5
     d4 = tk.compile(programs.build(programs.CONFIGS["c4"]).text(), device=-1).dump()
     assert "[rows summed directly]" in d4 and "+column sums of B: " not in d4
+
+
+def test_column_sum_fusion_option():
+    """colsum_fusion = 1 moves every legal bias-gradient sum into its
+    weight-gradient tiles (all three of the 4096-wide MLP, K = 1024), -1 none
+    (the residual MLP's 16 stay reductions); other values are rejected."""
+    c4 = programs.build(programs.CONFIGS["c4"]).text()
+    c5 = programs.build(programs.CONFIGS["c5"]).text()
+    d4 = tk.compile(c4, device=-1, colsum_fusion=1).dump()
+    assert d4.count("+column sums of B: ") == 3 and "reduce_cols" not in d4
+    d5 = tk.compile(c5, device=-1, colsum_fusion=-1).dump()
+    assert "+column sums of B: " not in d5 and d5.count("reduce_cols") == 16
+    for bad in (2, -2):
+        with pytest.raises(tk.TkError, match="colsum_fusion"):
+            tk.compile(c5, device=-1, colsum_fusion=bad)
