@@ -97,7 +97,8 @@ typedef struct {
                                   summed from the gradient its weight-gradient product reads)
                                   computed by that product's first tile row: 0 (default) where
                                   the reduction's own items would add a round of items to its
-                                  stage and K <= 512; 1 wherever legal; -1 never */
+                                  stage (and K <= 512 unless K is a multiple of 64); 1 wherever
+                                  legal; -1 never */
 } tk_options;
 
 /* Plan and kernel statistics (pages: `GeneratedKernel` and `resource_usage`). */

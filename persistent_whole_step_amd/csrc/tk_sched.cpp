@@ -916,9 +916,9 @@ struct Builder {
   // the same gradient its weight-gradient product reads.  By default only
   // where the reduction's own items would give some workgroups of its stage
   // one more item than the rest have (otherwise they run on workgroups that
-  // would idle anyway) and K is at most 512 (the first tile row's longer
-  // epilogue then costs less than a round of items); colsum_fusion = 1 fuses
-  // wherever legal, -1 never.  Runs on a first leveling; the stages are
+  // would idle anyway), and where K is not a multiple of 64 only up to 512
+  // rows (the rows read again after the tile then cost less than a round of
+  // items); colsum_fusion = 1 fuses wherever legal, -1 never.  Runs on a first leveling; the stages are
   // levelled again after.
   void fuse_column_sums() {
     if (!O.fuse_epilogues || !O.fast_epilogue || O.barrier_every_op || O.colsum_fusion < 0) return;
@@ -953,7 +953,10 @@ struct Builder {
         const GemmChoice g = choose_gemm(mo);
         if (g.kind != T_GEMM_MFMA || g.split > 1) continue;
         const uint64_t here = stage_items[r.level], own = entry_items(r);
-        if (!always && (B.shape[0] > 512 || (here + G - 1) / G == (here - own + G - 1) / G)) continue;
+        // K on whole 64-deep slices: the sums come out of the tile's main loop
+        // (else the tile reads K rows again after the product)
+        const bool in_loop = B.shape[0] % 64 == 0;
+        if (!always && ((!in_loop && B.shape[0] > 512) || (here + G - 1) / G == (here - own + G - 1) / G)) continue;
         colsum_of[(int)xi] = (int)ri;
         colsum_host[(int)ri] = (int)xi;
         sched[ri].two_phase = false;

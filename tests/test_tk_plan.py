@@ -399,12 +399,13 @@ def test_column_sums_in_weight_gradient_tiles_or_read_directly():
     """A bias-gradient sum whose own items would give some workgroups of its
     stage one more item than the rest runs inside the weight-gradient
     product that reads the same gradient (its first tile row sums B over K
-    and runs the sum's finish, the bias update included), when K is at most
-    512: in the 16-layer residual MLP every stage is full, so all 16 sums
-    move and the step needs 32 stages.  Otherwise the sums stay column
-    reductions read straight from memory: one part up to 256 rows (the
-    3-layer bf16 MLP, 6 stages), fp32 partials and a combine at 512 rows,
-    one 32-row-lane part from 513 to 1024 rows (the 4096-wide MLP)."""
+    and runs the sum's finish, the bias update included): in the 16-layer
+    residual MLP every stage is full, so all 16 sums move and the step needs
+    32 stages; in the 4096-wide MLP (K = 1024, whole 64-deep slices) all
+    three move.  Otherwise the sums stay column reductions read straight from
+    memory: one part up to 256 rows (the 3-layer bf16 MLP, 6 stages), fp32
+    partials and a combine at 512 rows, one 32-row-lane part of 64 columns
+    per item from 513 to 1024 rows (the 4096-wide MLP unfused)."""
     c2 = programs.build(programs.CONFIGS["c2"]).text()
     c5 = programs.build(programs.CONFIGS["c5"]).text()
     d = tk.compile(c2, device=-1)
@@ -416,18 +417,22 @@ def test_column_sums_in_weight_gradient_tiles_or_read_directly():
     assert t5.count("+column sums of B: ") == 16 and "reduce_cols" not in t5 and d5.query()["n_stages"] == 32
     u5 = tk.compile(c5, device=-1, fuse_epilogues=0).dump()
     assert "reduce_final" in u5 and "[rows summed directly]" in u5 and "[16 partials]" in u5
-    d4 = tk.compile(programs.build(programs.CONFIGS["c4"]).text(), device=-1).dump()
-    assert "[rows summed directly]" in d4 and "+column sums of B: " not in d4
+    c4 = programs.build(programs.CONFIGS["c4"]).text()
+    d4 = tk.compile(c4, device=-1).dump()
+    assert d4.count("+column sums of B: ") == 3 and "reduce_cols" not in d4
+    u4 = tk.compile(c4, device=-1, colsum_fusion=-1).dump()
+    assert u4.count("[rows summed directly]") == 3 and "reduce_cols items=64 : gb1" in u4
 
 
 def test_column_sum_fusion_option():
     """colsum_fusion = 1 moves every legal bias-gradient sum into its
-    weight-gradient tiles (all three of the 4096-wide MLP, K = 1024), -1 none
-    (the residual MLP's 16 stay reductions); other values are rejected."""
-    c4 = programs.build(programs.CONFIGS["c4"]).text()
+    weight-gradient tiles (all three of the 3-layer bf16 MLP, where the
+    default keeps them: they add no round of items), -1 none (the residual
+    MLP's 16 stay reductions); other values are rejected."""
+    c2 = programs.build(programs.CONFIGS["c2"]).text()
     c5 = programs.build(programs.CONFIGS["c5"]).text()
-    d4 = tk.compile(c4, device=-1, colsum_fusion=1).dump()
-    assert d4.count("+column sums of B: ") == 3 and "reduce_cols" not in d4
+    d2 = tk.compile(c2, device=-1, colsum_fusion=1).dump()
+    assert d2.count("+column sums of B: ") == 3 and "reduce_cols" not in d2
     d5 = tk.compile(c5, device=-1, colsum_fusion=-1).dump()
     assert "+column sums of B: " not in d5 and d5.count("reduce_cols") == 16
     for bad in (2, -2):
