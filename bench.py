@@ -221,7 +221,9 @@ class Runner:
 
     def stage_stamps(self):
         """In-situ stage timing of one launch (workgroup 0's stamps: items
-        done, descriptors staged, barrier passed), in microseconds."""
+        done, then barrier passed; the next stage's descriptors are staged
+        inside the barrier, so the staging stamp equals the first and
+        sum_staging_us is 0), in microseconds."""
         import torch
         self.p.set_debug(timestamps=True)
         for i in range(3):

@@ -2598,7 +2598,13 @@ DEV void run_item(const Ctx& ka, const DTask& t, const DStage& sd, uint32_t item
 // monotonically across launches on a workspace (the base is kept in the
 // header), so flags never need resetting.  Every spin is bounded by the
 // deadline; a timeout sets the abort word, which every spinner also watches.
-DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline) {
+// next(copy) runs once every wave is past its last read of the current
+// stage's descriptors: in wave 0 after the arrival, under the polls (copy
+// false), and in waves 1-3 while wave 0 polls (copy true: they also copy the
+// next stage's descriptors into LDS); the plan never changes during a launch,
+// so those reads need no ordering against the barrier.
+template <class Next>
+DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t deadline, Next next) {
   __shared__ uint32_t s_ok;
   GLOBAL uint32_t* arrive = (GLOBAL uint32_t*)(ka.ws + kHdrArrive);
   GLOBAL uint32_t* abort = (GLOBAL uint32_t*)(ka.ws + kHdrAbort);
@@ -2610,6 +2616,7 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
     __hip_atomic_store(arrive + bid, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   if (threadIdx.x < 64) {
+    next(false);
     uint32_t ok = 1;
     const uint32_t lane = threadIdx.x;
     const uint64_t t0 = __builtin_amdgcn_s_memrealtime();
@@ -2646,6 +2653,8 @@ DEV bool grid_barrier(const Ctx& ka, uint32_t epoch, uint32_t stage, uint64_t de
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
     const uint32_t all_ok = __builtin_amdgcn_readfirstlane(ok) & (uint32_t)__all(ok);
     if (lane == 0) s_ok = all_ok;
+  } else {
+    next(true);
   }
   __syncthreads();
   return s_ok != 0;
@@ -2660,13 +2669,24 @@ DEV uint32_t hash32(uint32_t x) {
   return x;
 }
 
-// Copy a stage blob into LDS (all threads; 16-byte chunks).  The scheduler
-// keeps every stage blob within kPlanLds bytes.
-DEV void stage_blob_to_lds(const GLOBAL uint8_t* plan, const DStage& st) {
+// Copy a stage blob into LDS (threads first .. kBlock - 1; 16-byte chunks).
+// The scheduler keeps every stage blob within kPlanLds bytes.
+DEV void stage_blob_to_lds(const GLOBAL uint8_t* plan, const DStage& st, uint32_t first) {
   const GLOBAL u32x4* src = (const GLOBAL u32x4*)(plan + st.blob_off);
   LDS u32x4* dst = (LDS u32x4*)g_plan;
   const uint32_t n = (st.blob_bytes < kPlanLds ? st.blob_bytes : kPlanLds) / 16;
-  for (uint32_t i = threadIdx.x; i < n; i += kBlock) dst[i] = src[i];
+  for (uint32_t i = threadIdx.x - first; i < n; i += kBlock - first) dst[i] = src[i];
+}
+
+// A stage record assigned in divergent-looking code, made wave-uniform again.
+DEV DStage uniform_stage(const DStage& sd) {
+  constexpr int N = sizeof(DStage) / 4;
+  struct Words {
+    uint32_t u[N];
+  } r = __builtin_bit_cast(Words, sd);
+#pragma unroll
+  for (int k = 0; k < N; ++k) r.u[k] = uniform(r.u[k]);
+  return __builtin_bit_cast(DStage, r);
 }
 
 }  // namespace
@@ -2700,7 +2720,7 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
   const uint32_t epoch0 = *(volatile GLOBAL uint32_t*)(ka.ws + kHdrEpoch);
   if (n_stages == 0) return;
   DStage sd = load_stage(stages, 0);
-  stage_blob_to_lds(ka.plan, sd);
+  stage_blob_to_lds(ka.plan, sd, 0);
   __syncthreads();
   if ((ka.flags & K_TIMESTAMPS) && blockIdx.x == 0 && threadIdx.x == 0)
     ((GLOBAL uint64_t*)(ka.ws + kHdrStamps))[0] = __builtin_amdgcn_s_memrealtime();
@@ -2721,15 +2741,19 @@ __global__ __launch_bounds__(kBlock, 1) void tk_persistent(KArgs) {
     if (s + 1 < n_stages) {
       const bool stamp = (ka.flags & K_TIMESTAMPS) && blockIdx.x == 0 && threadIdx.x == 0 && s < kMaxTimedStages;
       GLOBAL uint64_t* stamps = (GLOBAL uint64_t*)(ka.ws + kHdrStamps) + 4 * s;
-      if (stamp) stamps[1] = __builtin_amdgcn_s_memrealtime();
-      // stage the next stage's descriptors while the barrier completes (every
-      // thread of this workgroup is past its last read of the current blob)
-      sd = load_stage(stages, s + 1);
-      stage_blob_to_lds(ka.plan, sd);
-      if (stamp) stamps[2] = __builtin_amdgcn_s_memrealtime();
-      if (!grid_barrier(ka, epoch0 + s + 1, s, deadline)) {
-        return;
+      if (stamp) {
+        const uint64_t now = __builtin_amdgcn_s_memrealtime();
+        stamps[1] = now;
+        stamps[2] = now;  // (the next stage's descriptors are staged inside the barrier)
       }
+      // the next stage's descriptors are read and staged while the barrier
+      // completes, off the path from the last item to the arrival
+      const bool ok = grid_barrier(ka, epoch0 + s + 1, s, deadline, [&](bool copy) {
+        sd = load_stage(stages, s + 1);
+        if (copy) stage_blob_to_lds(ka.plan, sd, 64);
+      });
+      if (!ok) return;
+      sd = uniform_stage(sd);
       if (stamp) stamps[3] = __builtin_amdgcn_s_memrealtime();
       if (stamp && s + 1 < kMaxTimedStages) stamps[4] = stamps[3];
     }
