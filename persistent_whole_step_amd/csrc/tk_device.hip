@@ -2384,12 +2384,14 @@ DEV void red_final_item(uint32_t tid, const Ctx& ka, const DTask& t, const DStag
 
 // Column sums of a contraction's B operand over all of K, by the tiles of
 // the first tile row (F_BSUM): a column reduction of the same 2-D value B
-// reads runs here instead of as items of its own.  Thread (row lane rl,
-// chunk cc) sums rows rl, rl + RL, ... of 8 columns of the tile's column
-// block, 16 rows in flight (CC x RL = 16 x 16 for 128-wide tiles, 8 x 32 for
-// 64-wide); the row lanes are combined through LDS in order; then thread
-// i < bn runs the reduction's finishing program for column n0 + i, its
-// leading operands loaded before the sums.
+// reads runs here instead of as items of its own.  Where the main loop
+// summed B's fragments (gemm_mfma's direct path), the two halves per column
+// come from the C tile's padding.  Otherwise the tile reads B again: thread
+// (row lane rl, chunk cc) sums rows rl, rl + RL, ... of 8 columns of the
+// tile's column block, 16 rows in flight (CC x RL = 16 x 16 for 128-wide
+// tiles, 8 x 32 for 64-wide), and the row lanes are combined through LDS in
+// order.  Then thread i < bn runs the reduction's finishing program for
+// column n0 + i, its leading operands loaded before the sums.
 template <bool BF>
 DEV void bsum_rows(const GLOBAL uint16_t* p, const VView& B, uint32_t K, uint32_t N, uint32_t col, uint32_t rl,
                    uint32_t RL, bool vec, float (&acc)[8]) {
