@@ -1992,8 +1992,19 @@ DEV bool fast_prefetch(uint32_t tid, const Ctx& ka, const DTask& t, uint32_t ins
   const uint32_t lds = (uint32_t)(uintptr_t)(LDS uint8_t*)g_smem;
   constexpr uint32_t kPlane = 16u * G * kBlock;
   bool ok = true;
-  for (uint32_t pc = 0; pc < t.expr_len; ++pc) {
-    const FRec r = frec_decode(frec_word(ins_off, t.fin_first + 2 * pc), frec_word(ins_off, t.fin_first + 2 * pc + 1));
+  const uint32_t n = t.expr_len;
+  // the next record's words are read while this one is handled
+  u32x4 cA = {0, 0, 0, 0}, cB = {0, 0, 0, 0};
+  if (n > 0) {
+    cA = frec_word(ins_off, t.fin_first);
+    cB = frec_word(ins_off, t.fin_first + 1);
+  }
+  for (uint32_t pc = 0; pc < n; ++pc) {
+    const uint32_t nx = t.fin_first + 2 * (pc + 1 < n ? pc + 1 : pc);
+    const u32x4 nA = frec_word(ins_off, nx), nB = frec_word(ins_off, nx + 1);
+    const FRec r = frec_decode(cA, cB);
+    cA = nA;
+    cB = nB;
     const uint32_t op = r.w0 & 0xff, src = (r.w0 >> 8) & 0xff;
     if (op != VM_STORE && src != SRC_VIEW) continue;
     const GLOBAL uint8_t* p = base_ptr(ka, r.base < (uint32_t)kMaxBases ? r.base : 0u);
